@@ -1,0 +1,127 @@
+/*
+ * oracle.h -- plain, slow CPU reference of the MoE FFN layer (one GPU's expert slice).
+ *
+ * TEST INFRASTRUCTURE ONLY. This library is used by the tests, by the smoke check and by the
+ * benchmark's CPU-baseline leg; the GPU library never links, loads or calls it, and it shares no
+ * code with the GPU library.
+ *
+ * Every function works on host memory, in double precision unless a step's decision is defined in
+ * fp32 (top-k selection on fp32 logits; the quantisers, whose codes are fp32 decisions).
+ *
+ * Sources (the pages, cited by title and section):
+ *   [P1] "Hosting Qwen on Blackwell" (Perplexity): sections "Prefillers", "Expert parallel",
+ *        "MoE GEMM", "Quantization".
+ *   [P2] "How we served a 397B MoE model with 4.7x speedup on TPU v7" (infolabhq): sections on the
+ *        architectural constraints (512 experts, top-10, shared expert), "Three collectives become
+ *        two" (routing arrays [T,k] int + float), "Roofline validation".
+ *   [P3] "CuTeDSL at Perplexity": section "MoE dispatch and combine" (local kernel: per-expert
+ *        counts, unique index per token within its expert, copy into expert buffers, weighted
+ *        combine using those positions), and the Blackwell section (absmax over 32 elements for
+ *        MX formats).
+ *   [P4] "Driving vLLM WideEP and Large-Scale Serving Toward Maturity on Blackwell (Part I)":
+ *        section on lower-precision operations (4-bit MoE weights, two values per byte with
+ *        per-group scales; activations quantised before dispatch).
+ * The router function (softmax / sigmoid), SwiGLU, e4m3, e2m1 and E8M0 are not named on the pages;
+ * they come from the workload definitions. e4m3 and e2m1/E8M0 follow the OCP 8-bit floating point
+ * specification and the OCP Microscaling (MX) v1.0 specification.
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { ORACLE_SOFTMAX = 0, ORACLE_SIGMOID = 1 };
+
+/* formats of a weight / activation matrix */
+enum {
+  ORACLE_F32 = 0,   /* float values (fp32 and bf16 workloads)                                   */
+  ORACLE_FP8 = 2,   /* e4m3 codes [G,N,K] + fp32 scales [G, ceil(N/bn), ceil(K/bk)]           */
+  ORACLE_MX4 = 3    /* e2m1 codes, 2 per byte, [G,N,K/2] + E8M0 scales [G, N, K/32]            */
+};
+
+/* A stack of G matrices of shape [N, K] (K contiguous) in one of the formats above. */
+typedef struct {
+  int fmt;
+  int G, N, K;
+  int bn, bk;             /* fp8 block shape (rows x cols); ignored otherwise                     */
+  const void* q;          /* float values, e4m3 codes, or packed e2m1 codes                       */
+  const void* s;          /* NULL, fp32 block scales, or E8M0 scale bytes                         */
+} oracle_mat;
+
+/* ---- number formats ------------------------------------------------------------------------ */
+double  oracle_e4m3_value(uint8_t code);              /* OCP e4m3 code -> value (NaN for S.1111.111) */
+uint8_t oracle_e4m3_encode(float v);                  /* round to nearest even, saturate to +-448    */
+double  oracle_e2m1_value(uint8_t nibble);            /* OCP e2m1 code (4 bits) -> value             */
+uint8_t oracle_e2m1_encode(float v);                  /* round to nearest even, saturate to +-6      */
+double  oracle_e8m0_value(uint8_t code);              /* 2^(code-127)                                */
+
+/* fp8 quantiser: one fp32 scale per bn x bk block of a [rows, cols] matrix: s = amax/448 (1 if
+ * amax = 0), code = e4m3(v / s) with an fp32 division. scales: [ceil(rows/bn), ceil(cols/bk)]. */
+void oracle_quant_fp8(int rows, int cols, int bn, int bk, const float* src,
+                      uint8_t* codes, float* scales);
+/* MXFP4 quantiser: per row, per 32 consecutive columns: shared exponent
+ * e = floor(log2(amax)) - 2 (clamped to [-127, 127]; -127 when amax = 0), E8M0 code e + 127,
+ * element code = e2m1(v * 2^-e). Element 2i sits in bits 0-3 of byte i, element 2i+1 in bits 4-7.
+ * cols % 32 == 0. packed: [rows, cols/2]; scales: [rows, cols/32]. */
+void oracle_quant_mx4(int rows, int cols, const float* src, uint8_t* packed, uint8_t* scales);
+
+/* value of element (g, n, kk) of a matrix stack */
+double oracle_mat_at(const oracle_mat* m, int g, int n, int kk);
+/* dequantise a whole stack into doubles [G, N, K] */
+void oracle_mat_dequant(const oracle_mat* m, double* out);
+
+/* ---- routing --------------------------------------------------------------------------------- */
+/* logits[t,e] = sum_h x[t,h] * w_r[e,h] + bias[e] in double; absdot[t,e] = sum |x*w| + |bias|
+ * (both may be computed for a subset of tokens: tok = NULL means all T tokens, else n_tok token
+ * indices; rows of the outputs follow the subset order). */
+void oracle_logits(int T, int H, int E, const float* x, const float* w_r, const float* bias,
+                   int n_tok, const int32_t* tok, double* logits, double* absdot);
+
+/* top-k on fp32 logits [T,E]: the k largest values, equal values ranked by lower expert index,
+ * listed in rank order; weights per scoring / renormalisation in double. */
+void oracle_topk(int T, int E, int k, const float* logits, int scoring, int renormalize,
+                 int32_t* ids, double* w);
+
+/* ---- dispatch (permutation) -------------------------------------------------------------------- */
+/* Stable, expert-major placement of the local slots: rows of local expert e' (0 <= e' < E_loc,
+ * global id e0+e') appear in ascending flat index t*k+j. Returns R. slot_to_row = -1 for slots
+ * whose expert is not local. row_to_flat must hold T*k entries (R are written). */
+int oracle_permute(int T, int k, int e0, int E_loc, const int32_t* ids, int32_t* counts,
+                   int32_t* offsets, int32_t* slot_to_row, int32_t* row_to_flat);
+
+/* ---- expert FFN and the whole layer --------------------------------------------------------------- */
+typedef struct {
+  int T, H, E, e0, E_loc, I, k, I_s;
+  int scoring, renormalize;
+  int act_fmt;            /* ORACLE_F32: activations fed as they are; ORACLE_FP8: h -> e4m3 with
+                             1x128 fp32 scales; ORACLE_MX4: h -> MXFP4 (x arrives pre-quantised in
+                             `xa` for both quantised formats)                                      */
+} oracle_desc;
+
+/* SwiGLU FFN of one activation row a[H] through matrix g of the gate/up/down stacks:
+ * h = silu(a . Wg^T) * (a . Wu^T), h quantised per act_fmt, y = h . Wd^T. y: [H]. */
+void oracle_ffn_row(const oracle_desc* d, int I, const double* a, const oracle_mat* gate,
+                    const oracle_mat* up, const oracle_mat* down, int g, double* y);
+
+/* The layer for n_tok tokens (tok = NULL: all T in order):
+ *   logits from the unquantised x and w_r (double, rounded to fp32 for the selection),
+ *   top-k, then out[t] = sum_j w_tj * FFN_{e_tj}(a_t) over local slots (j ascending)
+ *                        + FFN_shared(a_t) if I_s > 0,
+ * where a_t is row t of `xa` (x itself, or x after the activation quantiser).
+ * Optional outputs (NULL to skip): logits64 [n,E], logits32 [n,E], ids [n,k], w [n,k]. */
+void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, const float* bias,
+                      const oracle_mat* xa, const oracle_mat* gate, const oracle_mat* up,
+                      const oracle_mat* down, const oracle_mat* sh_gate, const oracle_mat* sh_up,
+                      const oracle_mat* sh_down, int n_tok, const int32_t* tok, double* out,
+                      double* logits64, float* logits32, int32_t* ids, double* w);
+
+int oracle_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,426 @@
+"""Pins of the CPU oracle against what the pages, the format specifications and the mathematics
+fix, independently of the oracle's own code (library routines, closed forms, brute force, worked
+numbers). CPU only."""
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit, softmax
+
+import oracle
+from moe_inputs import gen
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_pairs(name):
+    out = []
+    for line in open(os.path.join(GOLD, name)):
+        line = line.split("#")[0].strip()
+        if line:
+            a, b = line.split()
+            out.append((int(a, 0), float(b)))
+    return out
+
+
+# ------------------------------------------------------------------------------------------
+# number formats
+# ------------------------------------------------------------------------------------------
+
+def test_e4m3_spec_points():
+    for code, val in _read_pairs("ocp_e4m3_points.txt"):
+        assert oracle.e4m3_value(code) == val
+        if code != 0x80:
+            assert oracle.e4m3_encode(val) == code
+    assert np.isnan(oracle.e4m3_value(0x7F)) and np.isnan(oracle.e4m3_value(0xFF))
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    ours = np.array([oracle.e4m3_value(c) for c in codes])
+    both_nan = np.isnan(ref) & np.isnan(ours)
+    assert np.all(both_nan | (ref == ours))
+
+
+def test_e4m3_encode_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 50,
+        rng.standard_normal(5000).astype(np.float32) * 0.01,      # subnormal range
+        np.float32(2.0) ** np.arange(-12, 9, dtype=np.float32),   # powers of two
+        # exact midpoints between neighbouring codes (ties)
+        np.array([(oracle.e4m3_value(c) + oracle.e4m3_value(c + 1)) / 2 for c in range(0, 0x7E)],
+                 np.float32),
+    ]).astype(np.float32)
+    v = np.clip(v, -448, 448).astype(np.float32)
+    ours = np.array([oracle.e4m3_encode(a) for a in v], np.uint8)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, ref)
+    # saturation (torch's cast does not saturate, the quantiser's definition does)
+    assert oracle.e4m3_encode(1e6) == 0x7E and oracle.e4m3_encode(-470.0) == 0xFE
+
+
+def _e2m1_rne_numpy(v):
+    """RNE onto the E2M1 grid written binade by binade with numpy's rint (ties to even)."""
+    a = abs(float(v))
+    if a < 2.0:
+        q = np.rint(a * 2.0) / 2.0          # step 0.5 on [0, 2)
+    elif a < 4.0:
+        q = np.rint(a)                      # step 1 on [2, 4)
+    else:
+        q = min(2.0 * np.rint(a / 2.0), 6.0)  # step 2 on [4, 6], saturate
+    return -q if np.signbit(v) else q
+
+
+def test_e2m1_spec_points_and_rne():
+    for code, val in _read_pairs("ocp_e2m1_points.txt"):
+        assert oracle.e2m1_value(code) == val
+    grid = np.concatenate([np.arange(-8, 8.0001, 0.0625), [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]])
+    for v in grid.astype(np.float32):
+        assert oracle.e2m1_value(oracle.e2m1_encode(v)) == _e2m1_rne_numpy(v), v
+
+
+def test_e8m0_values():
+    assert oracle.e8m0_value(127) == 1.0
+    assert oracle.e8m0_value(0) == 2.0 ** -127
+    assert oracle.e8m0_value(254) == 2.0 ** 127
+    assert np.isnan(oracle.e8m0_value(255))
+
+
+def test_mx4_hand_example():
+    lines = {}
+    for line in open(os.path.join(GOLD, "mx4_packing_example.txt")):
+        if line.startswith("#") or ":" not in line:
+            continue
+        key, val = line.split(":", 1)
+        lines[key.strip()] = val.split()
+    vals = np.array([float(v) for v in lines["values"]], np.float32)[None]
+    packed, scales = oracle.quant_mx4(vals)
+    assert scales[0, 0] == int(lines["scale"][0])
+    assert [int(b) for b in packed[0]] == [int(b, 0) for b in lines["bytes"]]
+
+
+def test_mx4_scale_rule_and_roundtrip():
+    rng = np.random.default_rng(2)
+    for e in range(-20, 20):
+        # amax in [2^(e+2), 2^(e+3)) must give shared exponent e
+        amax = np.float32(2.0 ** (e + 2) * (1 + rng.random() * 0.999))
+        v = (rng.random(32).astype(np.float32) * 2 - 1) * amax
+        v[rng.integers(32)] = amax
+        _, s = oracle.quant_mx4(v[None].astype(np.float32))
+        assert int(s[0, 0]) == e + 127
+    # values on the grid (E2M1 value x 2^e, amax hitting 6 * 2^e) survive exactly
+    mags = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+    for e in (-8, -1, 0, 3):
+        v = rng.choice(mags, size=(4, 64)) * rng.choice([-1, 1], size=(4, 64))
+        v[:, 0] = 6.0
+        v[:, 32] = 6.0
+        v = (v * 2.0 ** e).astype(np.float32)
+        p, s = oracle.quant_mx4(v)
+        m = oracle.Mat(oracle.MX4, p[None], s[None])
+        assert np.array_equal(m.dequant()[0], v.astype(np.float64))
+    # an all-zero group gets the smallest scale and zero codes
+    p, s = oracle.quant_mx4(np.zeros((1, 32), np.float32))
+    assert s[0, 0] == 0 and not p.any()
+    # error: at most half the top grid step (2^e) inside the E2M1 range, and below 2 * 2^e where
+    # values between 6 * 2^e and amax < 8 * 2^e saturate
+    v = rng.standard_normal((16, 256)).astype(np.float32)
+    p, s = oracle.quant_mx4(v)
+    dq = oracle.Mat(oracle.MX4, p[None], s[None]).dequant()[0]
+    unit = np.repeat(2.0 ** (s.astype(np.int32) - 127), 32, axis=1)
+    inside = np.abs(v) <= 6 * unit
+    err = np.abs(dq - v)
+    assert np.all(err[inside] <= unit[inside]) and np.all(err[~inside] < 2 * unit[~inside])
+    assert np.all(np.abs(dq[~inside]) == 6 * unit[~inside])
+
+
+def test_fp8_block_quantiser():
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((256, 384)).astype(np.float32) * 0.02
+    w[5, 7] = 0.5                                   # block (0,0) amax
+    codes, scales = oracle.quant_fp8(w)
+    assert scales.shape == (2, 3)
+    assert scales[0, 0] == np.float32(0.5) / np.float32(448.0)
+    # the block's largest magnitude maps exactly onto 448
+    assert codes[5, 7] == 0x7E
+    # the codes are torch's round-to-nearest-even cast of the fp32 quotient
+    q = w / np.repeat(np.repeat(scales, 128, 0), 128, 1)
+    ref = torch.from_numpy(q.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+    # ragged shapes: partial blocks use their own amax
+    codes2, scales2 = oracle.quant_fp8(w[:200, :300])
+    assert scales2.shape == (2, 3)
+    z, zs = oracle.quant_fp8(np.zeros((128, 128), np.float32))
+    assert zs[0, 0] == 1.0 and not z.any()
+    # dequantised values within half an e4m3 step (relative 2^-4) of the input
+    m = oracle.Mat(oracle.FP8, codes[None], scales[None])
+    dq = m.dequant()[0]
+    assert np.all(np.abs(dq - w) <= np.abs(w) * 2.0 ** -4 + 2.0 ** -10 * scales.max())
+
+
+# ------------------------------------------------------------------------------------------
+# routing
+# ------------------------------------------------------------------------------------------
+
+def test_logits_match_numpy_matmul():
+    rng = np.random.default_rng(4)
+    x = gen.bf16_round(rng.standard_normal((37, 96)).astype(np.float32))
+    w = gen.bf16_round(rng.standard_normal((20, 96)).astype(np.float32) * 0.02)
+    b = rng.standard_normal(20).astype(np.float32)
+    L, A = oracle.logits(x, w, b)
+    ref = x.astype(np.float64) @ w.astype(np.float64).T + b.astype(np.float64)
+    assert np.allclose(L, ref, rtol=0, atol=1e-12)
+    assert np.allclose(A, np.abs(x.astype(np.float64)) @ np.abs(w.astype(np.float64)).T
+                       + np.abs(b), rtol=1e-12)
+    Ls, _ = oracle.logits(x, w, b, tok=np.array([5, 0, 36]))
+    assert np.array_equal(Ls, L[[5, 0, 36]])
+
+
+def _topk_bruteforce(L, k):
+    T, E = L.shape
+    ids = np.empty((T, k), np.int32)
+    for t in range(T):
+        # full stable sort by (value descending, index ascending); -0.0 == +0.0 in numpy
+        order = np.lexsort((np.arange(E), -L[t].astype(np.float64)))
+        ids[t] = order[:k]
+    return ids
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (512, 10), (256, 8), (16, 16), (5, 1)])
+def test_topk_matches_full_sort(E, k):
+    L = gen.tie_heavy_logits(64, E, seed=E + k)
+    ids, w = oracle.topk(L, k)
+    assert np.array_equal(ids, _topk_bruteforce(L, k))
+    L2 = gen.random_logits(64, E, seed=E)
+    ids2, _ = oracle.topk(L2, k)
+    assert np.array_equal(ids2, _topk_bruteforce(L2, k))
+
+
+def test_topk_special_cases():
+    L = np.full((3, 16), 0.75, np.float32)
+    ids, w = oracle.topk(L, 4)
+    assert np.array_equal(ids, np.tile(np.arange(4), (3, 1)))        # all equal -> 0..k-1
+    assert np.allclose(w, 0.25, atol=1e-15)
+    Lz = np.zeros((1, 8), np.float32)
+    Lz[0, ::2] = -0.0                                                  # -0 equals +0
+    ids, _ = oracle.topk(Lz, 3)
+    assert list(ids[0]) == [0, 1, 2]
+    L = gen.random_logits(4, 12, seed=9)
+    ids, _ = oracle.topk(L, 12)                                        # k = E: full order
+    assert np.array_equal(ids, _topk_bruteforce(L, 12))
+
+
+def test_softmax_weights():
+    L = gen.random_logits(50, 128, seed=5, scale=2.0)
+    ids, w = oracle.topk(L, 8, oracle.SOFTMAX, 1)
+    sel = np.take_along_axis(L.astype(np.float64), ids, 1)
+    assert np.allclose(w, softmax(sel, axis=1), rtol=0, atol=1e-14)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-14)
+    assert np.all(np.diff(w, axis=1) <= 0)                             # rank order
+    # without renormalisation: the full softmax at the chosen experts
+    ids0, w0 = oracle.topk(L, 8, oracle.SOFTMAX, 0)
+    full = softmax(L.astype(np.float64), axis=1)
+    assert np.allclose(w0, np.take_along_axis(full, ids0, 1), rtol=0, atol=1e-14)
+
+
+def test_sigmoid_weights():
+    L = gen.random_logits(50, 256, seed=6, scale=3.0)
+    ids, w = oracle.topk(L, 8, oracle.SIGMOID, 1)
+    p = expit(np.take_along_axis(L.astype(np.float64), ids, 1))
+    assert np.allclose(w, p / p.sum(1, keepdims=True), rtol=0, atol=1e-14)
+    ids0, w0 = oracle.topk(L, 8, oracle.SIGMOID, 0)
+    assert np.allclose(w0, p, rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------------------------------------
+# dispatch
+# ------------------------------------------------------------------------------------------
+
+def _check_perm(ids, e0, E_loc):
+    T, k = ids.shape
+    counts, offsets, s2r, r2f = oracle.permute(ids, e0, E_loc)
+    flat = ids.reshape(-1)
+    local = (flat >= e0) & (flat < e0 + E_loc)
+    R = int(local.sum())
+    assert offsets[-1] == R == len(r2f)
+    assert np.array_equal(counts, np.bincount(flat[local] - e0, minlength=E_loc))
+    assert np.array_equal(offsets, np.concatenate([[0], np.cumsum(counts)]))
+    # brute force: stable sort of the local flat indices by local expert
+    fl = np.nonzero(local)[0]
+    order = fl[np.argsort(flat[fl], kind="stable")]
+    assert np.array_equal(r2f, order)
+    s = s2r.reshape(-1)
+    assert np.all(s[~local] == -1)
+    assert np.array_equal(r2f[s[local]], np.nonzero(local)[0])          # exact inverse
+    assert np.array_equal(np.sort(s[local]), np.arange(R))              # bijection onto [0,R)
+    return counts
+
+
+@pytest.mark.parametrize("T,E,k,e0,E_loc", [(64, 8, 2, 0, 8), (333, 128, 8, 0, 32),
+                                             (200, 512, 10, 64, 64), (1, 16, 4, 12, 4),
+                                             (50, 8, 8, 0, 8)])
+def test_permute_bruteforce(T, E, k, e0, E_loc):
+    ids = gen.random_topk_ids(T, E, k, seed=T, hot=[e0], hot_frac=0.3)
+    _check_perm(ids, e0, E_loc)
+
+
+def test_permute_no_local_rows():
+    ids = gen.random_topk_ids(40, 64, 4, seed=1)
+    ids = np.where(ids < 8, ids + 8, ids)                                # nothing in [0, 8)
+    counts, offsets, s2r, r2f = oracle.permute(ids, 0, 8)
+    assert offsets[-1] == 0 and not counts.any() and np.all(s2r == -1) and len(r2f) == 0
+
+
+def test_worked_example_tokens_per_expert():
+    """Hosting Qwen on Blackwell, section "Prefillers": 6000 tokens, top-8, 128 experts give
+    6000 * 8 / 128 = 375 tokens per expert on average."""
+    vals = {}
+    for line in open(os.path.join(GOLD, "prefillers_tokens_per_expert.txt")):
+        if not line.startswith("#") and line.strip():
+            key, v = line.split()
+            vals[key] = int(v)
+    T, k, E = vals["T"], vals["k"], vals["E"]
+    ids = gen.random_topk_ids(T, E, k, seed=0)
+    counts = _check_perm(ids, 0, E)
+    assert counts.sum() / E == vals["mean_tokens_per_expert"]
+
+
+# ------------------------------------------------------------------------------------------
+# expert FFN and the layer
+# ------------------------------------------------------------------------------------------
+
+def _dense_swiglu(a, wg, wu, wd):
+    g = a @ wg.T
+    u = a @ wu.T
+    return (g * expit(g) * u) @ wd.T
+
+
+def _tiny(T=12, H=64, E=4, I=32, k=2, e0=0, E_loc=4, I_s=0, scoring=0, seed=0, same=False):
+    rng = np.random.default_rng([seed, 77])
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wr = (rng.standard_normal((E, H)) * 0.3).astype(np.float32)
+    if same:
+        one = [(rng.standard_normal((I, H)) * 0.1).astype(np.float32) for _ in range(2)]
+        d1 = (rng.standard_normal((H, I)) * 0.1).astype(np.float32)
+        g = np.stack([one[0]] * E_loc)
+        u = np.stack([one[1]] * E_loc)
+        d = np.stack([d1] * E_loc)
+    else:
+        g = (rng.standard_normal((E_loc, I, H)) * 0.1).astype(np.float32)
+        u = (rng.standard_normal((E_loc, I, H)) * 0.1).astype(np.float32)
+        d = (rng.standard_normal((E_loc, H, I)) * 0.1).astype(np.float32)
+    sh = None
+    if I_s:
+        sh = [(rng.standard_normal(s) * 0.1).astype(np.float32)
+              for s in ((I_s, H), (I_s, H), (H, I_s))]
+    desc = dict(T=T, H=H, E=E, e0=e0, E_loc=E_loc, I=I, k=k, I_s=I_s, scoring=scoring,
+                renormalize=1, act_fmt=oracle.F32)
+    return desc, x, wr, g, u, d, sh
+
+
+def _run(desc, x, wr, g, u, d, sh, bias=None, tok=None):
+    M = oracle.Mat
+    shared = None if sh is None else tuple(M(oracle.F32, s) for s in sh)
+    return oracle.moe_layer(desc, x, wr, bias, M(oracle.F32, x), M(oracle.F32, g), M(oracle.F32, u),
+                            M(oracle.F32, d), shared, tok)
+
+
+def test_single_expert_is_dense_ffn():
+    desc, x, wr, g, u, d, _ = _tiny(E=1, E_loc=1, k=1)
+    r = _run(desc, x, wr, g, u, d, None)
+    ref = _dense_swiglu(x.astype(np.float64), g[0].astype(np.float64), u[0].astype(np.float64),
+                        d[0].astype(np.float64))
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+    assert np.allclose(r["w"], 1.0)
+
+
+def test_identical_experts_equal_dense_ffn():
+    desc, x, wr, g, u, d, _ = _tiny(E=6, E_loc=6, k=3, same=True)
+    r = _run(desc, x, wr, g, u, d, None)
+    ref = _dense_swiglu(x.astype(np.float64), g[0].astype(np.float64), u[0].astype(np.float64),
+                        d[0].astype(np.float64))
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_equals_dense_per_token_loop():
+    for scoring in (oracle.SOFTMAX, oracle.SIGMOID):
+        desc, x, wr, g, u, d, sh = _tiny(T=10, E=8, E_loc=4, e0=2, k=3, I_s=16, scoring=scoring)
+        bias = np.linspace(-1, 1, 8).astype(np.float32)
+        r = _run(desc, x, wr, g, u, d, sh, bias=bias)
+        L = x.astype(np.float64) @ wr.astype(np.float64).T + bias
+        L32 = L.astype(np.float32)
+        ids = _topk_bruteforce(L32, 3)
+        sel = np.take_along_axis(L32.astype(np.float64), ids, 1)
+        if scoring == oracle.SOFTMAX:
+            w = softmax(sel, axis=1)
+        else:
+            w = expit(sel) / expit(sel).sum(1, keepdims=True)
+        x64 = x.astype(np.float64)
+        ref = np.zeros((10, desc["H"]))
+        for t in range(10):
+            for j in range(3):
+                el = ids[t, j] - 2
+                if 0 <= el < 4:
+                    ref[t] += w[t, j] * _dense_swiglu(x64[t:t + 1], g[el].astype(np.float64),
+                                                      u[el].astype(np.float64),
+                                                      d[el].astype(np.float64))[0]
+            ref[t] += _dense_swiglu(x64[t:t + 1], *(s.astype(np.float64) for s in sh))[0]
+        assert np.array_equal(r["ids"], ids)
+        assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_zero_down_projection_leaves_shared_only():
+    desc, x, wr, g, u, d, sh = _tiny(I_s=16)
+    r = _run(desc, x, wr, g, u, np.zeros_like(d), sh)
+    ref = _dense_swiglu(x.astype(np.float64), *(s.astype(np.float64) for s in sh))
+    assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
+    r0 = _run(desc, np.zeros_like(x), wr, g, u, d, sh)                 # silu(0) * 0 = 0
+    assert not np.any(r0["out"])
+
+
+def test_layer_token_subset_and_permutation_equivariance():
+    desc, x, wr, g, u, d, sh = _tiny(T=16, I_s=8)
+    full = _run(desc, x, wr, g, u, d, sh)
+    tok = np.array([7, 3, 15, 0], np.int32)
+    sub = _run(desc, x, wr, g, u, d, sh, tok=tok)
+    assert np.array_equal(sub["out"], full["out"][tok])
+    perm = np.random.default_rng(0).permutation(16)
+    px = _run(desc, x[perm], wr, g, u, d, sh)
+    assert np.allclose(px["out"], full["out"][perm], rtol=0, atol=1e-13)
+
+
+def test_ffn_quantised_activations_fp8():
+    """h quantised to e4m3 with 1x128 scales: equals the dense FFN with h passed through torch's
+    e4m3 cast at scale amax/448 per 128 columns."""
+    rng = np.random.default_rng(8)
+    H, I = 128, 256
+    a = rng.standard_normal(H)
+    wg, wu = (rng.standard_normal((I, H)) * 0.1 for _ in range(2))
+    wd = rng.standard_normal((H, I)) * 0.1
+    M = oracle.Mat
+    y = oracle.ffn_row(a, M(oracle.F32, wg.astype(np.float32)), M(oracle.F32, wu.astype(np.float32)),
+                       M(oracle.F32, wd.astype(np.float32)), act_fmt=oracle.FP8)
+    wg32, wu32, wd32 = (w.astype(np.float32).astype(np.float64) for w in (wg, wu, wd))
+    gg, uu = a @ wg32.T, a @ wu32.T
+    h = (gg * expit(gg) * uu).astype(np.float32)
+    hq = np.empty(I)
+    for b in range(0, I, 128):
+        blk = h[b:b + 128]
+        s = np.float32(np.abs(blk).max()) / np.float32(448.0)
+        c = torch.from_numpy((blk / s).astype(np.float32)).to(torch.float8_e4m3fn).float().numpy()
+        hq[b:b + 128] = c.astype(np.float64) * np.float64(s)
+    assert np.allclose(y, hq @ wd32.T, rtol=1e-12, atol=1e-12)
+
+
+def test_quantised_weight_stack_dequantises_blockwise():
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((2, 256, 256)) * 0.02).astype(np.float32)
+    m = oracle.quantise_stack(oracle.FP8, w)
+    assert m.s.shape == (2, 2, 2)
+    dq = m.dequant()
+    assert np.abs(dq - w).max() <= np.abs(w).max() * 2.0 ** -4
+    assert m.at(1, 130, 7) == dq[1, 130, 7]
+    m4 = oracle.quantise_stack(oracle.MX4, w)
+    assert m4.q.shape == (2, 256, 128) and m4.s.shape == (2, 256, 8)
