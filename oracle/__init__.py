@@ -202,6 +202,33 @@ def permute(ids, e0, E_loc):
     return counts, offsets, s2r, r2f[:R].copy()
 
 
+# ---- grouped GEMM and combine on their own ------------------------------------------------
+
+def grouped_gemm(offsets, A, B, B2=None, a_rows=None, a_row_div=1, bias=None):
+    """A: Mat [1, rows_a, K]; B, B2: Mat [G, N, K]. Returns float64 [offsets[-1], N]."""
+    off = _c(offsets, np.int32)
+    G = len(off) - 1
+    ar = None if a_rows is None else _c(a_rows, np.int32)
+    b = None if bias is None else _c(bias, np.float32)
+    out = np.empty((int(off[-1]), B.N), np.float64)
+    null = ctypes.c_void_p(None)
+    lib().oracle_grouped_gemm(G, _p(off), A.ref, _p(ar), int(a_row_div), B.ref,
+                              B2.ref if B2 is not None else null, _p(b), _p(out))
+    return out
+
+
+def combine(y, w, slot_to_row, shared=None):
+    y = _c(y, np.float32)
+    w = _c(w, np.float32)
+    s2r = _c(slot_to_row, np.int32)
+    T, k = s2r.shape
+    H = y.shape[1]
+    sh = None if shared is None else _c(shared, np.float32)
+    out = np.empty((T, H), np.float64)
+    lib().oracle_combine(T, H, k, _p(y), _p(w), _p(s2r), _p(sh), _p(out))
+    return out
+
+
 # ---- the layer -------------------------------------------------------------------------
 
 def ffn_row(a, gate, up, down, g=0, act_fmt=F32):

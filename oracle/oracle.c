@@ -392,3 +392,59 @@ void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, co
     free(L64); free(L32); free(sel); free(wt); free(taken); free(a); free(y);
   }
 }
+
+/* ---------------------------------------------------------------------------------------------- */
+/* The grouped GEMM and the combine as separate steps                                             */
+/* ---------------------------------------------------------------------------------------------- */
+
+void oracle_grouped_gemm(int G, const int32_t* offsets, const oracle_mat* A, const int32_t* a_rows,
+                         int a_row_div, const oracle_mat* B, const oracle_mat* B2,
+                         const float* bias, double* out)
+{
+  int K = B->K, N = B->N;
+  int rows = offsets[G];
+#pragma omp parallel
+  {
+    double* a = (double*)malloc(sizeof(double) * (size_t)K);
+    double* b = (double*)malloc(sizeof(double) * (size_t)K);
+#pragma omp for schedule(dynamic, 4)
+    for (int r = 0; r < rows; ++r) {
+      int g = 0;
+      while (offsets[g + 1] <= r) ++g;              /* group of row r */
+      int src = a_rows ? a_rows[r] / a_row_div : r;
+      mat_row(A, 0, src, a);
+      for (int n = 0; n < N; ++n) {
+        double d = 0.0;
+        mat_row(B, g, n, b);
+        for (int kk = 0; kk < K; ++kk) d += a[kk] * b[kk];
+        if (bias) d += (double)bias[n];
+        if (B2) {
+          double u = 0.0;
+          mat_row(B2, g, n, b);
+          for (int kk = 0; kk < K; ++kk) u += a[kk] * b[kk];
+          d = d / (1.0 + exp(-d)) * u;
+        }
+        out[(size_t)r * N + n] = d;
+      }
+    }
+    free(a);
+    free(b);
+  }
+}
+
+void oracle_combine(int T, int H, int k, const float* y, const float* w, const int32_t* slot_to_row,
+                    const float* shared, double* out)
+{
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    double* o = out + (size_t)t * H;
+    for (int c = 0; c < H; ++c) o[c] = 0.0;
+    for (int j = 0; j < k; ++j) {
+      int r = slot_to_row[t * k + j];
+      if (r < 0) continue;
+      for (int c = 0; c < H; ++c) o[c] += (double)w[t * k + j] * (double)y[(size_t)r * H + c];
+    }
+    if (shared)
+      for (int c = 0; c < H; ++c) o[c] += (double)shared[(size_t)t * H + c];
+  }
+}

@@ -119,6 +119,20 @@ void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, co
                       const oracle_mat* sh_down, int n_tok, const int32_t* tok, double* out,
                       double* logits64, float* logits32, int32_t* ids, double* w);
 
+/* ---- the grouped GEMM and the combine on their own ---------------------------------------------- */
+/* For each group g and row r in [offsets[g], offsets[g+1]): with a(r) = a_rows ? a_rows[r] / div : r,
+ *   d_n = sum_k A(a(r), k) * B(g, n, k) (+ bias[n]);  out[r, n] = d_n            (B2 == NULL)
+ *   out[r, n] = silu(d_n) * sum_k A(a(r), k) * B2(g, n, k)                         (B2 != NULL)
+ * A is a one-matrix stack [1, rows_a, K]; out is double [offsets[G], N]. */
+void oracle_grouped_gemm(int G, const int32_t* offsets, const oracle_mat* A, const int32_t* a_rows,
+                         int a_row_div, const oracle_mat* B, const oracle_mat* B2,
+                         const float* bias, double* out);
+
+/* out[t, :] = sum_{j ascending, slot_to_row[t,j] >= 0} w[t,j] * y[slot_to_row[t,j], :]
+ *             (+ shared[t, :] if shared != NULL); y, shared float; out double [T, H]. */
+void oracle_combine(int T, int H, int k, const float* y, const float* w, const int32_t* slot_to_row,
+                    const float* shared, double* out);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

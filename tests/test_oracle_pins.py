@@ -424,3 +424,80 @@ def test_quantised_weight_stack_dequantises_blockwise():
     assert m.at(1, 130, 7) == dq[1, 130, 7]
     m4 = oracle.quantise_stack(oracle.MX4, w)
     assert m4.q.shape == (2, 256, 128) and m4.s.shape == (2, 256, 8)
+
+
+# ------------------------------------------------------------------------------------------
+# grouped GEMM and combine as separate steps
+# ------------------------------------------------------------------------------------------
+
+def test_grouped_gemm_matches_numpy_per_group():
+    rng = np.random.default_rng(11)
+    G, N, K = 3, 48, 64
+    counts = np.array([5, 0, 9])
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    T = 7
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    a_rows = rng.integers(0, T * 2, size=off[-1]).astype(np.int32)   # flat slots, k = 2
+    B = (rng.standard_normal((G, N, K)) * 0.1).astype(np.float32)
+    B2 = (rng.standard_normal((G, N, K)) * 0.1).astype(np.float32)
+    bias = rng.standard_normal(N).astype(np.float32)
+    M = oracle.Mat
+    st = oracle.grouped_gemm(off, M(oracle.F32, x), M(oracle.F32, B), a_rows=a_rows, a_row_div=2,
+                             bias=bias)
+    sw = oracle.grouped_gemm(off, M(oracle.F32, x), M(oracle.F32, B), M(oracle.F32, B2),
+                             a_rows=a_rows, a_row_div=2)
+    x64 = x.astype(np.float64)
+    for g in range(G):
+        rows = slice(off[g], off[g + 1])
+        a = x64[a_rows[rows] // 2]
+        d = a @ B[g].astype(np.float64).T
+        assert np.allclose(st[rows], d + bias, rtol=0, atol=1e-12)
+        u = a @ B2[g].astype(np.float64).T
+        assert np.allclose(sw[rows], d * expit(d) * u, rtol=0, atol=1e-12)
+
+
+def test_grouped_gemm_fp8_blocks_equal_dequantised_matmul():
+    rng = np.random.default_rng(12)
+    K, N, T = 256, 128, 200
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((1, N, K)) * 0.02).astype(np.float32)
+    xc, xs = oracle.quant_fp8(x, 128, 128)                 # 128-token x 128-channel blocks
+    xa = oracle.Mat(oracle.FP8, xc[None], xs[None], bn=128, bk=128)
+    wm = oracle.quantise_stack(oracle.FP8, w)
+    off = np.array([0, T], np.int32)
+    out = oracle.grouped_gemm(off, xa, wm)
+    ref = xa.dequant()[0] @ wm.dequant()[0].T
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    # the codes of x are torch's e4m3 cast of x / s with s = amax / 448 over each 128 x 128 block
+    s = np.abs(x[:128, :128]).max() / np.float32(448.0)
+    assert xs[0, 0] == np.float32(s)
+    ref_codes = torch.from_numpy((x[:128, :128] / xs[0, 0]).astype(np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(xc[:128, :128], ref_codes)
+
+
+def test_combine_matches_gather_formula_and_layer():
+    rng = np.random.default_rng(13)
+    T, k, H, R = 9, 3, 16, 20
+    y = rng.standard_normal((R, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    s2r = rng.integers(-1, R, size=(T, k)).astype(np.int32)
+    sh = rng.standard_normal((T, H)).astype(np.float32)
+    out = oracle.combine(y, w, s2r, sh)
+    wm = np.where(s2r >= 0, w.astype(np.float64), 0.0)
+    ref = np.einsum("tj,tjh->th", wm, y.astype(np.float64)[np.maximum(s2r, 0)]) + sh
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    assert np.allclose(oracle.combine(y, np.zeros_like(w), s2r, sh), sh)
+    # the layer's output is the combine of per-slot FFN rows placed by the permutation
+    desc, x, wr, g, u, d, shw = _tiny(T=8, E=6, E_loc=3, e0=1, k=2, I_s=8)
+    full = _run(desc, x, wr, g, u, d, shw)
+    counts, offsets, s2r, r2f = oracle.permute(full["ids"], 1, 3)
+    M = oracle.Mat
+    ys = np.zeros((max(len(r2f), 1), desc["H"]), np.float32)
+    for r, f in enumerate(r2f):
+        t, j = divmod(int(f), 2)
+        ys[r] = oracle.ffn_row(x[t], M(oracle.F32, g), M(oracle.F32, u), M(oracle.F32, d),
+                               g=int(full["ids"][t, j]) - 1)
+    shy = np.stack([oracle.ffn_row(x[t], *(M(oracle.F32, s) for s in shw)) for t in range(8)])
+    comb = oracle.combine(ys, full["w"].astype(np.float32), s2r, shy.astype(np.float32))
+    assert np.allclose(comb, full["out"], rtol=1e-5, atol=1e-5)
