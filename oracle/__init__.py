@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, FP8, MX4 = 0, 2, 3
+F32, BF16, FP8, MX4 = 0, 1, 2, 3
 SOFTMAX, SIGMOID = 0, 1
 
 
@@ -57,6 +57,8 @@ def lib():
         L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
         L.oracle_e2m1_encode.restype = ctypes.c_uint8
         L.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        L.oracle_bf16_round.restype = ctypes.c_float
+        L.oracle_bf16_round.argtypes = [ctypes.c_float]
         L.oracle_e8m0_value.restype = ctypes.c_double
         L.oracle_e8m0_value.argtypes = [ctypes.c_uint8]
         L.oracle_mat_at.restype = ctypes.c_double
@@ -90,6 +92,10 @@ def e2m1_value(code):
 
 def e2m1_encode(v):
     return lib().oracle_e2m1_encode(float(v))
+
+
+def bf16_round(v):
+    return lib().oracle_bf16_round(float(v))
 
 
 def e8m0_value(code):

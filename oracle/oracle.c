@@ -84,6 +84,20 @@ uint8_t oracle_e2m1_encode(float v)
   return sign | (uint8_t)best;
 }
 
+/* bf16 keeps the top 16 bits of an fp32 value: 8 exponent bits and 7 mantissa bits. Rounding to
+ * the nearest of the two bf16 neighbours of v, ties to the one with an even last mantissa bit. */
+float oracle_bf16_round(float v)
+{
+  int ex;
+  double a = fabs((double)v);
+  if (a == 0.0) return v;
+  frexp(a, &ex);                                      /* a in [2^(ex-1), 2^ex) */
+  double step = ldexp(1.0, ex - 1 - 7);               /* spacing of bf16 values in this binade */
+  if (ex - 1 < -126) step = ldexp(1.0, -126 - 7);     /* subnormal range: fixed spacing */
+  double q = rint(a / step) * step;                   /* rint: nearest, ties to even multiple */
+  return (float)(signbit(v) ? -q : q);
+}
+
 double oracle_e8m0_value(uint8_t code)
 {
   if (code == 255) return NAN;
@@ -299,7 +313,10 @@ int oracle_permute(int T, int k, int e0, int E_loc, const int32_t* ids, int32_t*
 
 static void quantise_h(int act_fmt, int I, double* h)
 {
-  if (act_fmt == ORACLE_FP8) {
+  if (act_fmt == ORACLE_BF16) {
+    /* the down projection of a bf16 layer reads h as a bf16 tensor (rounded from fp32) */
+    for (int i = 0; i < I; ++i) h[i] = (double)oracle_bf16_round((float)h[i]);
+  } else if (act_fmt == ORACLE_FP8) {
     /* 1 x 128 blocks along the intermediate dimension */
     for (int b = 0; b < I; b += 128) {
       int e = b + 128 < I ? b + 128 : I;

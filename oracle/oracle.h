@@ -39,6 +39,7 @@ enum { ORACLE_SOFTMAX = 0, ORACLE_SIGMOID = 1 };
 /* formats of a weight / activation matrix */
 enum {
   ORACLE_F32 = 0,   /* float values (fp32 and bf16 workloads)                                   */
+  ORACLE_BF16 = 1,  /* activation format only: h rounded to bf16 before the down projection      */
   ORACLE_FP8 = 2,   /* e4m3 codes [G,N,K] + fp32 scales [G, ceil(N/bn), ceil(K/bk)]           */
   ORACLE_MX4 = 3    /* e2m1 codes, 2 per byte, [G,N,K/2] + E8M0 scales [G, N, K/32]            */
 };
@@ -58,6 +59,7 @@ uint8_t oracle_e4m3_encode(float v);                  /* round to nearest even, 
 double  oracle_e2m1_value(uint8_t nibble);            /* OCP e2m1 code (4 bits) -> value             */
 uint8_t oracle_e2m1_encode(float v);                  /* round to nearest even, saturate to +-6      */
 double  oracle_e8m0_value(uint8_t code);              /* 2^(code-127)                                */
+float   oracle_bf16_round(float v);                   /* nearest bf16 value, ties to even (finite v) */
 
 /* fp8 quantiser: one fp32 scale per bn x bk block of a [rows, cols] matrix: s = amax/448 (1 if
  * amax = 0), code = e4m3(v / s) with an fp32 division. scales: [ceil(rows/bn), ceil(cols/bk)]. */
@@ -97,9 +99,10 @@ int oracle_permute(int T, int k, int e0, int E_loc, const int32_t* ids, int32_t*
 typedef struct {
   int T, H, E, e0, E_loc, I, k, I_s;
   int scoring, renormalize;
-  int act_fmt;            /* ORACLE_F32: activations fed as they are; ORACLE_FP8: h -> e4m3 with
-                             1x128 fp32 scales; ORACLE_MX4: h -> MXFP4 (x arrives pre-quantised in
-                             `xa` for both quantised formats)                                      */
+  int act_fmt;            /* format of h, the input of the down projection: ORACLE_F32: as
+                             computed; ORACLE_BF16: rounded to bf16; ORACLE_FP8: e4m3 with 1x128
+                             fp32 scales; ORACLE_MX4: MXFP4 (x arrives pre-quantised in `xa` for
+                             both quantised formats)                                               */
 } oracle_desc;
 
 /* SwiGLU FFN of one activation row a[H] through matrix g of the gate/up/down stacks:

@@ -501,3 +501,28 @@ def test_combine_matches_gather_formula_and_layer():
     shy = np.stack([oracle.ffn_row(x[t], *(M(oracle.F32, s) for s in shw)) for t in range(8)])
     comb = oracle.combine(ys, full["w"].astype(np.float32), s2r, shy.astype(np.float32))
     assert np.allclose(comb, full["out"], rtol=1e-5, atol=1e-5)
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(14)
+    v = np.concatenate([rng.standard_normal(20000).astype(np.float32) * 3,
+                        rng.standard_normal(2000).astype(np.float32) * 1e-30,
+                        # exact midpoints between neighbouring bf16 values (ties)
+                        (np.arange(1, 3000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)]
+                       ).astype(np.float32)
+    ours = np.array([oracle.bf16_round(a) for a in v], np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_ffn_bf16_activation_rounds_h():
+    rng = np.random.default_rng(15)
+    H, I = 64, 96
+    a = rng.standard_normal(H)
+    wg, wu = ((rng.standard_normal((I, H)) * 0.2).astype(np.float32) for _ in range(2))
+    wd = (rng.standard_normal((H, I)) * 0.2).astype(np.float32)
+    M = oracle.Mat
+    y = oracle.ffn_row(a, M(oracle.F32, wg), M(oracle.F32, wu), M(oracle.F32, wd), act_fmt=oracle.BF16)
+    gg, uu = a @ wg.astype(np.float64).T, a @ wu.astype(np.float64).T
+    h = torch.from_numpy((gg * expit(gg) * uu).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.allclose(y, h @ wd.astype(np.float64).T, rtol=1e-12, atol=1e-12)
