@@ -1,0 +1,258 @@
+"""Benchmark of the MoE FFN layer on one MI355X.
+
+Workload: the Qwen3-235B-shaped layer slice (experts 0..31 of 128 on this GPU, hidden 4096,
+intermediate 1536, softmax top-8 with renormalisation, Zipf(1.1) router bias), 16384 tokens, bf16
+inputs and weights, seeded synthetic data. One step = one full moe_layer call (router, top-k,
+dispatch, gate/up GEMM + SwiGLU, down GEMM, combine) with every input already resident in HBM.
+
+Prints one JSON line (rank 0) with the headline throughput, the roofline of the dominant kernel
+(the gate/up grouped GEMM, timed with HIP events on its launch stream), a decode-size (64 tokens)
+measurement of the same layer against HBM bandwidth, and the CPU oracle's rate on a token sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (2.5 PFLOP/s class, 2.4 GHz)
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="C2p")
+    p.add_argument("--decode-workload", default="C2d")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--profile-only", action="store_true",
+                   help="only the timed moe_layer steps (for profilers)")
+    return p.parse_args()
+
+
+class Layer:
+    """Device-resident inputs, weights, outputs and workspace of one workload."""
+
+    def __init__(self, wl, weights=None):
+        import torch
+        import moe_layer_softmax_amd as moe
+        from moe_inputs import gen
+        self.wl = wl
+        dt = torch.bfloat16
+        dev = "cuda"
+        t = lambda a, d=dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)
+        self.x_np = gen.tokens(wl)
+        self.bias_np = gen.router_bias(wl)
+        if weights is None:
+            self.wr_np = gen.router_weight(wl)
+            self.experts_np = gen.expert_weights(wl)
+            self.w_dev = [t(self.wr_np)] + [t(a) for a in self.experts_np]
+        else:
+            self.wr_np, self.experts_np, self.w_dev = weights
+        self.x = t(self.x_np)
+        self.bias = None if self.bias_np is None else t(self.bias_np, torch.float32)
+        self.desc = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
+                                  wl.renormalize, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_F32)
+        self.weights = moe.make_weights(*self.w_dev)
+        self.out = torch.empty((wl.T, wl.H), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device=dev)
+        self.ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(moe.moe_layer_workspace_bytes(self.desc), dtype=torch.uint8,
+                              device=dev)
+        self.moe = moe
+
+    def shared_weights(self):
+        return self.wr_np, self.experts_np, self.w_dev
+
+    def step(self, stream):
+        self.moe.moe_layer(self.desc, self.weights, self.x, self.bias, self.out, self.logits,
+                           self.ids, self.w, self.ws, stream)
+
+
+def step_breakdown(L, stream, iters):
+    """The layer's steps through the public entry points, each bracketed by HIP events recorded on
+    the launch stream. Returns per-step mean ms and the local row count R."""
+    import torch
+    moe = L.moe
+    wl = L.wl
+    d = L.desc
+    dev = "cuda"
+    slots = wl.T * wl.k
+    counts = torch.empty(wl.E_loc, dtype=torch.int32, device=dev)
+    offsets = torch.empty(wl.E_loc + 1, dtype=torch.int32, device=dev)
+    s2r = torch.empty((wl.T, wl.k), dtype=torch.int32, device=dev)
+    r2f = torch.empty(slots, dtype=torch.int32, device=dev)
+    pws = torch.empty(max(moe.moe_permute_workspace_bytes(d), 16), dtype=torch.uint8, device=dev)
+    h = torch.empty((slots, wl.I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((slots, wl.H), dtype=torch.float32, device=dev)
+    g_up = moe.moe_gemm_desc(wl.E_loc, slots, wl.H, wl.I, moe.MOE_BF16, moe.MOE_EPI_SWIGLU,
+                             moe.MOE_BF16, wl.k, 1)
+    g_dn = moe.moe_gemm_desc(wl.E_loc, slots, wl.I, wl.H, moe.MOE_BF16, moe.MOE_EPI_STORE,
+                             moe.MOE_F32, 1, 1)
+    _, wg, wu, wd = L.w_dev
+    names = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
+    calls = [
+        lambda: moe.moe_route(d, L.x, L.w_dev[0], L.bias, L.logits, L.ids, L.w, stream),
+        lambda: moe.moe_permute(d, L.ids, None, None, counts, offsets, s2r, r2f, None, None, pws,
+                                stream),
+        lambda: moe.moe_grouped_gemm(g_up, L.x, None, r2f, wg, None, wu, None, offsets, h, None,
+                                     stream),
+        lambda: moe.moe_grouped_gemm(g_dn, h, None, None, wd, None, None, None, offsets, y, None,
+                                     stream),
+        lambda: moe.moe_combine(d, moe.MOE_F32, y, L.w, s2r, None, L.out, stream),
+    ]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+          for _ in range(iters)]
+    with torch.cuda.stream(stream):
+        for c in calls:                       # warm
+            c()
+        torch.cuda.synchronize()
+        for it in range(iters):
+            ev[it][0].record(stream)
+            for i, c in enumerate(calls):
+                c()
+                ev[it][i + 1].record(stream)
+        torch.cuda.synchronize()
+    ms = {n: float(np.mean([ev[it][i].elapsed_time(ev[it][i + 1]) for it in range(iters)]))
+          for i, n in enumerate(names)}
+    R = int(offsets[-1].item())
+    cnt = counts.cpu().numpy()
+    return ms, R, cnt
+
+
+def compulsory_bytes(wl, counts):
+    """Weights of the local experts with at least one row, router weight, x read once, out (fp32)
+    written once, routing arrays."""
+    active = int((counts > 0).sum())
+    w = active * 3 * wl.I * wl.H * 2 + wl.E * wl.H * 2
+    return w + wl.T * wl.H * 2 + wl.T * wl.H * 4 + wl.T * wl.k * 8
+
+
+def layer_flops(wl, R):
+    return 2.0 * wl.T * wl.H * wl.E + 6.0 * R * wl.H * wl.I + 6.0 * wl.T * wl.H * wl.I_s
+
+
+def cpu_baseline(L, target_s):
+    import oracle
+    wl = L.wl
+    g, u, d = L.experts_np
+    M = oracle.Mat
+    desc = dict(T=wl.T, H=wl.H, E=wl.E, e0=wl.e0, E_loc=wl.E_loc, I=wl.I, k=wl.k, I_s=wl.I_s,
+                scoring=wl.scoring, renormalize=wl.renormalize, act_fmt=oracle.BF16)
+    mats = (M(oracle.F32, L.x_np), M(oracle.F32, g), M(oracle.F32, u), M(oracle.F32, d))
+    rng = np.random.default_rng(123)
+    n = 4
+    while True:
+        tok = np.sort(rng.choice(wl.T, n, replace=False)).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.moe_layer(desc, L.x_np, L.wr_np, L.bias_np, *mats, None, tok)
+        dt = time.perf_counter() - t0
+        if dt >= target_s * 0.5 or n >= wl.T:
+            break
+        n = int(min(wl.T, max(n * 2, n * target_s / max(dt, 1e-3) * 0.9)))
+    return dict(value=n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{n} random tokens of the same {wl.T}-token layer (routing, all local "
+                       f"experts of each token, combine), fp64, {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; the whole-job value for N=1 is the one-GPU throughput.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_inputs as mi
+
+    wl = mi.WORKLOADS[args.workload]
+    L = Layer(wl)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        L.step(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        L.step(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    tokens_per_s = wl.T / (ms_per_step / 1e3)
+    if args.profile_only:
+        print(json.dumps({"workload": wl.name, "ms_per_step": ms_per_step}))
+        return
+
+    steps_ms, R, counts = step_breakdown(L, stream, max(5, min(args.steps, 20)))
+    flops_gu = 4.0 * R * wl.H * wl.I
+    achieved = flops_gu / (steps_ms["gemm_gate_up"] * 1e-3) / 1e12
+    layer_tf = layer_flops(wl, R) / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": "MoE-layer tokens/s + % of MFMA peak (prefill) / % HBM BW (decode), 1 MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,0.02) weights, Zipf(1.1) router bias)",
+        "config": {"workload": "Qwen3-235B-shaped MoE layer, EP=4 slice (experts 0-31 of 128), "
+                               "prefill", "T": wl.T, "H": wl.H, "E": wl.E, "E_loc": wl.E_loc,
+                   "I": wl.I, "k": wl.k, "router": "softmax top-8, renormalised",
+                   "local_rows_R": R, "parallelism": "single GPU expert slice"},
+        "layer_tflops": round(layer_tf, 1),
+        "layer_frac_mfma": round(layer_tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "grouped GEMM gate/up + SwiGLU (moe_grouped_gemm)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": flops_gu,
+                     "avg_launch_ms": round(steps_ms["gemm_gate_up"], 4)},
+        "steps_ms": {k: round(v, 4) for k, v in steps_ms.items()},
+    }
+    if not args.no_decode:
+        dwl = mi.WORKLOADS[args.decode_workload]
+        D = Layer(dwl, weights=L.shared_weights())
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                D.step(stream)
+            for a, b in ev:
+                flush.fill_(1.0)             # evict the weights from the caches between steps
+                a.record(stream)
+                D.step(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        dms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        _, dR, dcounts = step_breakdown(D, stream, 5)
+        dbytes = compulsory_bytes(dwl, dcounts)
+        result["decode"] = {"workload": f"same layer, {dwl.T} tokens", "ms": round(dms, 4),
+                            "tokens_per_s": round(dwl.T / (dms * 1e-3), 1), "local_rows_R": dR,
+                            "compulsory_bytes": dbytes,
+                            "hbm_gbps": round(dbytes / (dms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+                            "caches": "1 GiB written between steps"}
+        del D, flush
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

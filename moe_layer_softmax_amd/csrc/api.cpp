@@ -1,0 +1,426 @@
+// api.cpp -- the C ABI of the MoE layer library: argument checks, workspace layout and the order
+// of kernel launches. Nothing here synchronises the host with the device.
+//
+// Step order of the layer follows the pages: route, dispatch (count / index / copy), MoE GEMM,
+// weighted combine ("Hosting Qwen on Blackwell", sections "MoE dispatch and combine" and
+// "Expert parallel"; "CuTeDSL at Perplexity", section "MoE dispatch and combine"). The dispatch
+// variant (one workgroup for small routing tables, split count/scan/scatter kernels for large
+// ones) is chosen on the host from the table size, as the pages choose their decode and prefill
+// dispatch kernels ("CuTeDSL at Perplexity", section on grid synchronisation).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+using namespace moe;
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+moe_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MOE_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return MOE_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+size_t round_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
+
+int io_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// format of the per-slot expert outputs y inside moe_layer
+int y_dtype_of(const moe_desc* d) {
+  return (d->expert_dtype == MOE_FP8_E4M3 || d->expert_dtype == MOE_MXFP4) ? MOE_BF16 : MOE_F32;
+}
+
+// bytes of one activation row of `cols` elements in expert format dt
+long long row_bytes(int dt, long long cols) {
+  switch (dt) {
+    case MOE_F32: return cols * 4;
+    case MOE_BF16: return cols * 2;
+    case MOE_FP8_E4M3: return cols;
+    case MOE_MXFP4: return cols / 2;
+    default: return 0;
+  }
+}
+
+bool valid_io(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+bool valid_expert(int dt) {
+  return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_FP8_E4M3 || dt == MOE_MXFP4;
+}
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->T < 0 || d->H <= 0 || d->E < 1 || d->E > 1024 || d->k < 1 || d->k > 16 || d->k > d->E)
+    return MOE_ERR_INVALID_ARG;
+  if (d->e0 < 0 || d->E_loc < 1 || d->e0 + d->E_loc > d->E) return MOE_ERR_INVALID_ARG;
+  if (d->I <= 0 || d->I_s < 0) return MOE_ERR_INVALID_ARG;
+  if (d->scoring != MOE_SOFTMAX && d->scoring != MOE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (d->renormalize != 0 && d->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (!valid_io(d->io_dtype) || !valid_io(d->out_dtype) || !valid_expert(d->expert_dtype))
+    return MOE_ERR_INVALID_ARG;
+  if ((long long)d->T * d->k >= (1ll << 31)) return MOE_ERR_INVALID_ARG;
+  // the router and the expert GEMMs read 128-byte row slices
+  const int kalign = d->io_dtype == MOE_F32 ? 16 : 64;
+  if (d->H % kalign) return MOE_ERR_INVALID_ARG;
+  if (d->H % 8) return MOE_ERR_INVALID_ARG;                 // combine: 8 columns per thread
+  return MOE_OK;
+}
+
+moe_status check_expert_shapes(const moe_desc* d) {
+  const int dt = d->expert_dtype;
+  if (dt == MOE_F32 && d->io_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (dt != MOE_F32 && d->io_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  const int align = (dt == MOE_F32) ? 16 : (dt == MOE_BF16 ? 64 : 128);
+  if (d->H % align || d->I % align || (d->I_s && d->I_s % align)) return MOE_ERR_INVALID_ARG;
+  if (d->I % 64 || d->H % 64) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status gemm_supported(int dt) {
+  return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+}
+
+// ---- layer workspace layout (identical in the size query and in moe_layer) ----------------------
+struct LayerWs {
+  size_t logits, ids, w, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, y, total;
+};
+
+LayerWs layer_ws(const moe_desc* d) {
+  LayerWs L{};
+  const size_t T = d->T, k = d->k, E = d->E, H = d->H, I = d->I;
+  const size_t slots = T * k;
+  const size_t rows = slots + (d->I_s ? T : 0);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o += round_up(bytes); return at; };
+  L.logits = take(T * E * 4);
+  L.ids = take(slots * 4);
+  L.w = take(slots * 4);
+  L.counts = take(d->E_loc * 4);
+  L.offsets = take((d->E_loc + 1) * 4);
+  L.s2r = take(slots * 4);
+  L.r2f = take(slots * 4);
+  L.perm = take(permute_ws_bytes(slots, d->E_loc));
+  const int dt = d->expert_dtype;
+  if (dt == MOE_FP8_E4M3) {
+    L.xq = take(T * H);
+    L.xs = take((T + 127) / 128 * (H / 128) * 4);
+    L.h = take(rows * I);
+    L.hs = take(rows * (I / 128) * 4);
+  } else if (dt == MOE_MXFP4) {
+    L.xq = take(T * H / 2);
+    L.xs = take(T * (H / 32));
+    L.h = take(rows * I / 2);
+    L.hs = take(rows * (I / 32));
+  } else {
+    L.h = take(rows * I * io_bytes(d->io_dtype));
+  }
+  L.y = take(rows * H * io_bytes(y_dtype_of(d)));
+  L.total = o;
+  return L;
+}
+
+// logits = x . w_router^T + bias, as one extra-group GEMM with no routed groups
+moe_status run_router(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                      float* logits, hipStream_t s) {
+  GemmArgs a{};
+  a.dtype = d->io_dtype;
+  a.epilogue = MOE_EPI_STORE;
+  a.out_dtype = MOE_F32;
+  a.K = d->H;
+  a.N = d->E;
+  a.A = x;
+  a.a_pitch = (long long)d->H * io_bytes(d->io_dtype);
+  a.a_row_div = 1;
+  a.a_scale_rows = 1;
+  a.G = 0;
+  a.x_rows = d->T;
+  a.x_row0 = 0;
+  a.x_a_off = 0;
+  a.xB = w_router;
+  a.bias = bias;
+  a.C = logits;
+  a.c_pitch = (long long)d->E * 4;
+  return hip_status(launch_gemm(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported combination";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t moe_last_hip_error(void) { return g_last_hip_error; }
+
+moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                     float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_w) || !ok_opt(x) || !ok_opt(bias))
+    return d->T == 0 ? MOE_OK : MOE_ERR_INVALID_ARG;
+  if (x && !ok_ptr(w_router)) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  if (x) {
+    st = run_router(d, x, w_router, bias, logits, stream);
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_topk(d->T, d->E, d->k, d->scoring, d->renormalize, logits, topk_ids,
+                                topk_w, stream));
+}
+
+size_t moe_permute_workspace_bytes(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return permute_ws_bytes((long long)d->T * d->k, d->E_loc);
+}
+
+moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a_in,
+                       const void* a_in_scales, int32_t* counts, int32_t* offsets,
+                       int32_t* slot_to_row, int32_t* row_to_flat, void* a_perm,
+                       void* a_perm_scales, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!ok_ptr(counts) || !ok_ptr(offsets)) return MOE_ERR_INVALID_ARG;
+  const long long slots = (long long)d->T * d->k;
+  if (slots > 0 && (!ok_ptr(topk_ids) || !ok_ptr(slot_to_row) || !ok_ptr(row_to_flat)))
+    return MOE_ERR_INVALID_ARG;
+  if (!ok_opt(a_perm) || !ok_opt(a_perm_scales) || !ok_opt(ws)) return MOE_ERR_INVALID_ARG;
+  const int dt = d->expert_dtype;
+  const bool quant = dt == MOE_FP8_E4M3 || dt == MOE_MXFP4;
+  if (a_perm) {
+    if (!ok_ptr(a_in)) return MOE_ERR_INVALID_ARG;
+    if (quant && (!ok_ptr(a_in_scales) || !ok_ptr(a_perm_scales))) return MOE_ERR_INVALID_ARG;
+    if (dt == MOE_FP8_E4M3 && d->H % 128) return MOE_ERR_INVALID_ARG;
+    if (dt == MOE_MXFP4 && d->H % 128) return MOE_ERR_INVALID_ARG;
+    if (dt == MOE_F32 && d->io_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  }
+  if (ws_bytes < permute_ws_bytes(slots, d->E_loc) || (slots > 16 * 1024 && !ws))
+    return MOE_ERR_WORKSPACE;
+  // (with no slots the maps kernel still writes zero counts and offsets)
+  hipError_t e = launch_permute_maps(d->T, d->k, d->e0, d->E_loc, topk_ids, counts, offsets,
+                                     slot_to_row, row_to_flat, ws, stream);
+  if (e != hipSuccess || !a_perm) return hip_status(e);
+  long long sbytes = 0;
+  int sblock = 1;
+  if (dt == MOE_FP8_E4M3) { sbytes = (long long)(d->H / 128) * 4; sblock = 128; }
+  if (dt == MOE_MXFP4) sbytes = d->H / 32;
+  e = launch_gather_rows(slots, d->k, offsets + d->E_loc, row_to_flat, a_in, row_bytes(dt, d->H),
+                         a_perm, quant ? a_in_scales : nullptr, sbytes, sblock,
+                         quant ? a_perm_scales : nullptr, stream);
+  return hip_status(e);
+}
+
+moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A_scales,
+                            const int32_t* a_rows, const void* B, const void* B_scales,
+                            const void* B2, const void* B2_scales, const int32_t* group_offsets,
+                            void* C, void* C_scales, hipStream_t stream) {
+  if (!g || g->G < 0 || g->max_rows < 0 || g->K <= 0 || g->N <= 0 || g->a_row_div < 1)
+    return MOE_ERR_INVALID_ARG;
+  if (!valid_expert(g->dtype)) return MOE_ERR_INVALID_ARG;
+  if (g->epilogue != MOE_EPI_STORE && g->epilogue != MOE_EPI_SWIGLU) return MOE_ERR_INVALID_ARG;
+  if (g->G == 0 || g->max_rows == 0) return MOE_OK;
+  if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(group_offsets) || !ok_opt(a_rows))
+    return MOE_ERR_INVALID_ARG;
+  if (g->epilogue == MOE_EPI_SWIGLU && !ok_ptr(B2)) return MOE_ERR_INVALID_ARG;
+  const int kalign = g->dtype == MOE_F32 ? 16 : (g->dtype == MOE_BF16 ? 64 : 128);
+  if (g->K % kalign || g->N % 64) return MOE_ERR_INVALID_ARG;
+  moe_status st = gemm_supported(g->dtype);
+  if (st != MOE_OK) return st;
+  if (g->dtype == MOE_F32 && g->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (g->out_dtype != MOE_F32 && g->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  GemmArgs a{};
+  a.dtype = g->dtype;
+  a.epilogue = g->epilogue;
+  a.out_dtype = g->out_dtype;
+  a.K = g->K;
+  a.N = g->N;
+  a.A = A;
+  a.A_scales = A_scales;
+  a.a_pitch = row_bytes(g->dtype, g->K);
+  a.a_scale_rows = g->a_scale_rows;
+  a.a_rows = a_rows;
+  a.a_row_div = g->a_row_div;
+  a.G = g->G;
+  a.offsets = group_offsets;
+  a.max_rows = g->max_rows;
+  a.B = B;
+  a.Bs = B_scales;
+  a.B2 = B2;
+  a.B2s = B2_scales;
+  a.b_stride = row_bytes(g->dtype, g->K) * (long long)g->N;
+  a.C = C;
+  a.C_scales = C_scales;
+  a.c_pitch = (long long)g->N * (g->out_dtype == MOE_F32 ? 4 : 2);
+  return hip_status(launch_gemm(a, stream));
+}
+
+moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const float* topk_w,
+                       const int32_t* slot_to_row, const void* shared, void* out,
+                       hipStream_t stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!valid_io(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (d->T == 0) return MOE_OK;
+  if (!ok_ptr(y) || !ok_ptr(topk_w) || !ok_ptr(slot_to_row) || !ok_ptr(out) || !ok_opt(shared))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_combine(d->T, d->H, d->k, y_dtype, d->out_dtype, y, topk_w, slot_to_row,
+                                   shared, out, stream));
+}
+
+moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int32_t rows,
+                        int32_t cols, int32_t block_rows, const void* src, void* codes,
+                        void* scales, hipStream_t stream) {
+  if (batch < 0 || rows < 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (batch == 0 || rows == 0) return MOE_OK;
+  if (!ok_ptr(src) || !ok_ptr(codes) || !ok_ptr(scales)) return MOE_ERR_INVALID_ARG;
+  if (dst_dtype == MOE_FP8_E4M3) {
+    if (cols % 128 || (block_rows != 1 && block_rows != 128)) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_fp8(src_dtype, batch, rows, cols, block_rows, src,
+                                       static_cast<uint8_t*>(codes), static_cast<float*>(scales),
+                                       stream));
+  }
+  if (dst_dtype == MOE_MXFP4) {
+    if (cols % 32) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_mx4(src_dtype, batch, rows, cols, src,
+                                       static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                       stream));
+  }
+  return MOE_ERR_INVALID_ARG;
+}
+
+size_t moe_layer_workspace_bytes(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return layer_ws(d).total;
+}
+
+moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, const float* bias,
+                     void* out, float* logits, int32_t* topk_ids, float* topk_w, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (!w) return MOE_ERR_INVALID_ARG;
+  st = check_expert_shapes(d);
+  if (st != MOE_OK) return st;
+  st = gemm_supported(d->expert_dtype);
+  if (st != MOE_OK) return st;
+  if (d->I_s != 0 && d->I_s != d->I) return MOE_ERR_UNSUPPORTED;
+  if (d->T == 0) return MOE_OK;
+  const bool quant = d->expert_dtype == MOE_FP8_E4M3 || d->expert_dtype == MOE_MXFP4;
+  if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(w->w_router) || !ok_ptr(w->w_gate) ||
+      !ok_ptr(w->w_up) || !ok_ptr(w->w_down) || !ok_opt(bias) || !ok_opt(logits) ||
+      !ok_opt(topk_ids) || !ok_opt(topk_w) || !ok_ptr(ws))
+    return MOE_ERR_INVALID_ARG;
+  if (quant && (!ok_ptr(w->w_gate_scales) || !ok_ptr(w->w_up_scales) ||
+                !ok_ptr(w->w_down_scales)))
+    return MOE_ERR_INVALID_ARG;
+  if (d->I_s && (!ok_ptr(w->sh_gate) || !ok_ptr(w->sh_up) || !ok_ptr(w->sh_down)))
+    return MOE_ERR_INVALID_ARG;
+  if (d->I_s && quant && (!ok_ptr(w->sh_gate_scales) || !ok_ptr(w->sh_up_scales) ||
+                          !ok_ptr(w->sh_down_scales)))
+    return MOE_ERR_INVALID_ARG;
+  const LayerWs L = layer_ws(d);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  float* lg = logits ? logits : reinterpret_cast<float*>(base + L.logits);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(base + L.ids);
+  float* tw = topk_w ? topk_w : reinterpret_cast<float*>(base + L.w);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + L.offsets);
+  int32_t* s2r = reinterpret_cast<int32_t*>(base + L.s2r);
+  int32_t* r2f = reinterpret_cast<int32_t*>(base + L.r2f);
+  const int T = d->T, k = d->k, H = d->H, I = d->I;
+  const int slots = T * k;
+  const int io = d->io_dtype, dt = d->expert_dtype;
+
+  // 1. route
+  st = run_router(d, x, w->w_router, bias, lg, stream);
+  if (st != MOE_OK) return st;
+  st = hip_status(launch_topk(T, d->E, k, d->scoring, d->renormalize, lg, ids, tw, stream));
+  if (st != MOE_OK) return st;
+  // 2. dispatch maps (the rows themselves are gathered inside the gate/up GEMM)
+  st = hip_status(launch_permute_maps(T, k, d->e0, d->E_loc, ids, counts, offsets, s2r, r2f,
+                                      base + L.perm, stream));
+  if (st != MOE_OK) return st;
+
+  // 3. gate/up GEMM with the SwiGLU epilogue; routed rows gather x through row_to_flat / k,
+  //    shared-expert rows (C rows slots..slots+T) read x in token order
+  GemmArgs a{};
+  a.dtype = dt;
+  a.epilogue = MOE_EPI_SWIGLU;
+  a.out_dtype = dt == MOE_F32 ? MOE_F32 : MOE_BF16;
+  a.K = H;
+  a.N = I;
+  a.A = x;
+  a.a_pitch = row_bytes(dt, H);
+  a.a_scale_rows = 1;
+  a.a_rows = r2f;
+  a.a_row_div = k;
+  a.G = d->E_loc;
+  a.offsets = offsets;
+  a.max_rows = slots;
+  a.B = w->w_gate;
+  a.B2 = w->w_up;
+  a.b_stride = row_bytes(dt, H) * (long long)I;
+  if (d->I_s) {
+    a.x_rows = T;
+    a.x_row0 = slots;
+    a.x_a_off = slots;
+    a.xB = w->sh_gate;
+    a.xB2 = w->sh_up;
+  }
+  a.C = base + L.h;
+  a.c_pitch = (long long)I * io_bytes(io);
+  st = hip_status(launch_gemm(a, stream));
+  if (st != MOE_OK) return st;
+
+  // 4. down GEMM: y rows = h rows
+  const int ydt = y_dtype_of(d);
+  GemmArgs b{};
+  b.dtype = dt;
+  b.epilogue = MOE_EPI_STORE;
+  b.out_dtype = ydt;
+  b.K = I;
+  b.N = H;
+  b.A = base + L.h;
+  b.a_pitch = (long long)I * io_bytes(io);
+  b.a_scale_rows = 1;
+  b.a_row_div = 1;
+  b.G = d->E_loc;
+  b.offsets = offsets;
+  b.max_rows = slots;
+  b.B = w->w_down;
+  b.b_stride = row_bytes(dt, I) * (long long)H;
+  if (d->I_s) {
+    b.x_rows = T;
+    b.x_row0 = slots;
+    b.x_a_off = 0;
+    b.xB = w->sh_down;
+  }
+  b.C = base + L.y;
+  b.c_pitch = (long long)H * io_bytes(ydt);
+  st = hip_status(launch_gemm(b, stream));
+  if (st != MOE_OK) return st;
+
+  // 5. combine (+ shared expert rows)
+  const void* shared = d->I_s ? base + L.y + (size_t)slots * H * io_bytes(ydt) : nullptr;
+  return hip_status(launch_combine(T, H, k, ydt, d->out_dtype, base + L.y, tw, s2r, shared, out,
+                                   stream));
+}
+
+}  // extern "C"

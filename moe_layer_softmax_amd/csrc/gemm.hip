@@ -1,0 +1,434 @@
+// gemm.hip -- grouped (per-expert) GEMM on gfx950 MFMA with fused epilogues.
+//
+// The expert GEMMs of a MoE layer: at prefill each expert gets a dense problem (a 6000-token input
+// routed top-8 over 128 experts gives ~375 rows per expert, "Hosting Qwen on Blackwell", section
+// "Prefillers"), at decode the problem is bound by reading the weights from HBM (same page,
+// section "Decoders"; "CuTeDSL at Perplexity", section on prefill versus decode kernels).
+//
+// Structure (all variants):
+//   * Tile scheduler on the device: workgroup -> (group, m-tile, n-tile) from the device-resident
+//     group offsets (a wave-wide prefix sum over per-group tile counts), so no host synchronisation
+//     is needed to learn the number of rows per expert. The grid is sized for the worst case and
+//     workgroups without a tile exit at once. Workgroups are remapped so that the n-tiles of one
+//     m-tile run on one XCD (they share the A rows in that XCD's L2).
+//   * A rows are optionally gathered through a row map (the dispatch's row_to_flat / k), so the
+//     layer can read expert rows straight from the token-order activations.
+//   * K loop: 128-byte row slices of A and B (64 bf16 / 128 fp8 / 256 fp4 elements) staged through
+//     LDS in a double buffer, 16-byte chunks XOR-swizzled by row so MFMA fragment reads
+//     (ds_read_b128) are bank-conflict free; global loads for step k+1 are in flight while step k
+//     is computed.
+//   * Epilogues: STORE (optional per-column bias, fp32 or bf16 out) and SWIGLU, where each wave
+//     holds matching gate and up columns so h = silu(g) * u is formed in registers.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "quant_dev.hpp"
+
+namespace moe {
+
+struct Tile {
+  int row0, row1;       // rows of C covered by this tile
+  int nt;               // n-tile
+  bool extra;           // the extra (shared-expert) group
+  const char* B;
+  const char* B2;
+  const char* Bs;
+  const char* B2s;
+};
+
+// Find the group and row range of routed m-tile `mt` (every lane of the wave calls this; the
+// result is wave-uniform). Returns false if `mt` is past the last tile.
+__device__ __forceinline__ bool find_group(const int32_t* __restrict__ off, int G, int BM, int mt,
+                                           int& g_out, int& row0, int& row1) {
+  const int lane = lane_id();
+  int base = 0;
+  for (int g0 = 0; g0 < G; g0 += 64) {
+    const int g = g0 + lane;
+    int beg = 0, end = 0, tiles = 0;
+    if (g < G) {
+      beg = off[g];
+      end = off[g + 1];
+      tiles = (end - beg + BM - 1) / BM;
+    }
+    int inc = tiles;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    const unsigned long long hit = __ballot(base + inc > mt);
+    if (hit) {
+      const int first = __builtin_ctzll(hit);
+      const int before = __shfl(inc - tiles, first, 64) + base;
+      const int b = __shfl(beg, first, 64), e = __shfl(end, first, 64);
+      g_out = uniform(g0 + first);
+      row0 = uniform(b + (mt - before) * BM);
+      row1 = uniform(min(row0 + BM, e));
+      return true;
+    }
+    base += __shfl(inc, 63, 64);
+  }
+  return false;
+}
+
+__device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int BM, int n_tiles, int x_tiles,
+                                             int logical, Tile& t) {
+  const int mt = logical / n_tiles;
+  t.nt = logical - mt * n_tiles;
+  if (mt < x_tiles) {
+    t.extra = true;
+    t.row0 = p.x_row0 + mt * BM;
+    t.row1 = min(t.row0 + BM, p.x_row0 + p.x_rows);
+    t.B = static_cast<const char*>(p.xB);
+    t.B2 = static_cast<const char*>(p.xB2);
+    t.Bs = static_cast<const char*>(p.xBs);
+    t.B2s = static_cast<const char*>(p.xB2s);
+    return true;
+  }
+  int g;
+  if (!find_group(p.offsets, p.G, BM, mt - x_tiles, g, t.row0, t.row1)) return false;
+  t.extra = false;
+  t.B = static_cast<const char*>(p.B) + g * p.b_stride;
+  t.B2 = p.B2 ? static_cast<const char*>(p.B2) + g * p.b_stride : nullptr;
+  t.Bs = p.Bs ? static_cast<const char*>(p.Bs) + g * p.bs_stride : nullptr;
+  t.B2s = p.B2s ? static_cast<const char*>(p.B2s) + g * p.bs_stride : nullptr;
+  return true;
+}
+
+// source row of A for row r of C (r clamped into the tile so padding rows read valid memory)
+__device__ __forceinline__ long long a_src_row(const GemmArgs& p, const Tile& t, int r) {
+  r = r < t.row1 ? r : t.row1 - 1;
+  if (t.extra) return r - p.x_a_off;
+  if (p.a_rows) return p.a_rows[r] / p.a_row_div;
+  return r;
+}
+
+// ------------------------------------------------------------------------------------------------
+// bf16 MFMA kernel
+//   BM x BN tile, 4 waves (WM x WN), each wave a (BM/WM) x (BN/WN) block of MI x MI MFMA tiles
+//   (MI = 32: v_mfma_f32_32x32x16_bf16, MI = 16: v_mfma_f32_16x16x32_bf16).
+//   SWIGLU: the B tile of wave column wn holds BN/(2*WN) gate rows followed by the same number of
+//   up rows, so the h tile is BM x BN/2.
+// ------------------------------------------------------------------------------------------------
+template <int BM, int BN, int WM, int WN, int MI, bool SWIGLU, bool OUT_F32>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_bf16_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 64;                 // bf16 per 128-byte row slice
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / MI, FN = TN / MI;
+  constexpr int MK = (MI == 32) ? 16 : 32;
+  constexpr int KS = BK / MK;
+  constexpr int CPR = 8;                 // 16-byte chunks per row slice
+  constexpr int RPP = NT / CPR;          // rows covered by one pass of the workgroup
+  constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
+  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of NT/8");
+  static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * BK];
+
+  const int logical = xcd_remap(blockIdx.x, span);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t)) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int K = p.K;
+  const int nk = K / BK;
+  const int ch = tid % CPR;
+  const int rbase = tid / CPR;
+
+  // global source pointers of this thread's A and B rows
+  const char* a_ptr[A_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int r = t.row0 + rbase + i * RPP;
+    a_ptr[i] = static_cast<const char*>(p.A) + a_src_row(p, t, r) * p.a_pitch + ch * 16;
+  }
+  const char* b_ptr[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int rb = rbase + i * RPP;
+    long long n;
+    const char* base = t.B;
+    if (SWIGLU) {
+      const int within = rb % TN;
+      const int half = TN / 2;
+      n = (long long)t.nt * (BN / 2) + (rb / TN) * half + (within % half);
+      if (within >= half) base = t.B2;
+    } else {
+      n = (long long)t.nt * BN + rb;
+    }
+    if (n >= p.N) n = p.N - 1;             // columns past N: read a valid row, never stored
+    b_ptr[i] = base + n * (long long)K * 2 + ch * 16;
+  }
+
+  i32x4 ra[A_LD], rb_[B_LD];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const i32x4*>(a_ptr[i] + kt * 128);
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) rb_[i] = *reinterpret_cast<const i32x4*>(b_ptr[i] + kt * 128);
+  };
+  auto lstore = [&](int buf) {
+    uint16_t* la = lds[buf];
+    uint16_t* lb = lds[buf] + BM * BK;
+#pragma unroll
+    for (int i = 0; i < A_LD; ++i) {
+      const int r = rbase + i * RPP;
+      *reinterpret_cast<i32x4*>(la + r * BK + ((ch ^ (r & 7)) * 8)) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_LD; ++i) {
+      const int r = rbase + i * RPP;
+      *reinterpret_cast<i32x4*>(lb + r * BK + ((ch ^ (r & 7)) * 8)) = rb_[i];
+    }
+  };
+
+  f32x16 acc32[MI == 32 ? FM : 1][MI == 32 ? FN : 1];
+  f32x4 acc16[MI == 16 ? FM : 1][MI == 16 ? FN : 1];
+  if constexpr (MI == 32) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc32[i][j] = f32x16{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc16[i][j] = f32x4{};
+  }
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint16_t* la = lds[buf];
+    const uint16_t* lb = lds[buf] + BM * BK;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int cidx = s * (MK / 8) + lane / MI;
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * MI + (lane % MI);
+        af[i] = *reinterpret_cast<const bf16x8*>(la + r * BK + ((cidx ^ (r & 7)) * 8));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * MI + (lane % MI);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + r * BK + ((cidx ^ (r & 7)) * 8));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (MI == 32)
+            acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc32[i][j], 0, 0, 0);
+          else
+            acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc16[i][j], 0, 0, 0);
+        }
+    }
+    if (kt + 1 < nk) lstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  constexpr int VPF = (MI == 32) ? 16 : 4;
+  auto acc_at = [&](int i, int j, int v) -> float {
+    if constexpr (MI == 32) return acc32[i][j][v];
+    else return acc16[i][j][v];
+  };
+  auto row_of = [&](int v) -> int {
+    if constexpr (MI == 32) return (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
+    else return (lane / 16) * 4 + v;
+  };
+  const int colw = lane % MI;
+  char* C = static_cast<char*>(p.C);
+  if constexpr (SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN / 2; ++j)
+#pragma unroll
+        for (int v = 0; v < VPF; ++v) {
+          const int r = t.row0 + wm * TM + i * MI + row_of(v);
+          if (r >= t.row1) continue;
+          const float g = acc_at(i, j, v), u = acc_at(i, j + FN / 2, v);
+          const float h = g / (1.0f + expf(-g)) * u;
+          const long long col = (long long)t.nt * (BN / 2) + wn * (TN / 2) + j * MI + colw;
+          if (col >= p.N) continue;
+          if (OUT_F32) reinterpret_cast<float*>(C + r * p.c_pitch)[col] = h;
+          else reinterpret_cast<uint16_t*>(C + r * p.c_pitch)[col] = f32_to_bf16(h);
+        }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const long long col = (long long)t.nt * BN + wn * TN + j * MI + colw;
+        if (col >= p.N) continue;
+        const float bias = p.bias ? p.bias[col] : 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPF; ++v) {
+          const int r = t.row0 + wm * TM + i * MI + row_of(v);
+          if (r >= t.row1) continue;
+          const float val = acc_at(i, j, v) + bias;
+          if (OUT_F32) reinterpret_cast<float*>(C + r * p.c_pitch)[col] = val;
+          else reinterpret_cast<uint16_t*>(C + r * p.c_pitch)[col] = f32_to_bf16(val);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// fp32 kernel (VALU FMA; the fp32 vector rate equals the fp32 matrix rate on this chip)
+//   64 x 64 tile, BK = 16, 256 threads with 4 x 4 outputs each: rows 4*ty.., columns
+//   {2tx, 2tx+1, 32+2tx, 33+2tx} so that for SWIGLU the gate column c and up column c + 32 sit in
+//   the same thread (h tile 64 x 32).
+// ------------------------------------------------------------------------------------------------
+template <bool SWIGLU>
+__global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs p, int n_tiles, int x_tiles,
+                                                       int span, int total) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  const int logical = xcd_remap(blockIdx.x, span);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t)) return;
+  const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
+  const int K = p.K;
+  // loads: 64 rows x 16 k per operand = 1024 floats = 4 per thread: row tid/4, k (tid%4)*4..+3
+  const int lr = tid / 4, lk = (tid % 4) * 4;
+  const float* arow = reinterpret_cast<const float*>(static_cast<const char*>(p.A) +
+                                                     a_src_row(p, t, t.row0 + lr) * p.a_pitch);
+  long long n;
+  const char* bb = t.B;
+  if (SWIGLU) {
+    n = (long long)t.nt * (BN / 2) + (lr % 32);
+    if (lr >= 32) bb = t.B2;
+  } else {
+    n = (long long)t.nt * BN + lr;
+  }
+  if (n >= p.N) n = p.N - 1;
+  const float* brow = reinterpret_cast<const float*>(bb) + n * K;
+  const int cols[4] = {2 * tx, 2 * tx + 1, 32 + 2 * tx, 33 + 2 * tx};
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const f32x4 av = *reinterpret_cast<const f32x4*>(arow + k0 + lk);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(brow + k0 + lk);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { As[lk + q][lr] = av[q]; Bs[lk + q][lr] = bv[q]; }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][4 * ty + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][cols[j]];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  char* C = static_cast<char*>(p.C);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = t.row0 + 4 * ty + i;
+    if (r >= t.row1) continue;
+    float* crow = reinterpret_cast<float*>(C + r * p.c_pitch);
+    if (SWIGLU) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float g = acc[i][j], u = acc[i][j + 2];
+        const long long col = (long long)t.nt * (BN / 2) + cols[j];
+        if (col < p.N) crow[col] = g / (1.0f + expf(-g)) * u;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long long col = (long long)t.nt * BN + cols[j];
+        if (col < p.N) crow[col] = acc[i][j] + (p.bias ? p.bias[col] : 0.0f);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// host side
+// ------------------------------------------------------------------------------------------------
+namespace {
+
+struct Grid {
+  int n_tiles, x_tiles, span, total;
+  unsigned blocks;
+};
+
+Grid make_grid(const GemmArgs& a, int BM, int n_cols_per_tile) {
+  Grid g;
+  g.n_tiles = (a.N + n_cols_per_tile - 1) / n_cols_per_tile;
+  g.x_tiles = a.x_rows > 0 ? (a.x_rows + BM - 1) / BM : 0;
+  // routed tiles: sum_g ceil(m_g / BM) <= floor(max_rows / BM) + G
+  const long long routed = a.G > 0 ? (long long)a.max_rows / BM + a.G : 0;
+  g.total = static_cast<int>((g.x_tiles + routed) * g.n_tiles);
+  g.span = g.n_tiles;
+  const long long blk = (long long)kNumXcd * g.span;
+  g.blocks = static_cast<unsigned>(((g.total + blk - 1) / blk) * blk);
+  return g;
+}
+
+template <int BM, int BN, int WM, int WN, int MI>
+hipError_t run_bf16(const GemmArgs& a, hipStream_t s) {
+  const bool sw = a.epilogue == MOE_EPI_SWIGLU;
+  Grid g = make_grid(a, BM, sw ? BN / 2 : BN);
+  if (g.total == 0) return hipSuccess;
+  dim3 grid(g.blocks), block(WM * WN * 64);
+  const bool f32 = a.out_dtype == MOE_F32;
+  if (sw && f32)
+    gemm_bf16_kernel<BM, BN, WM, WN, MI, true, true><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  else if (sw)
+    gemm_bf16_kernel<BM, BN, WM, WN, MI, true, false><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  else if (f32)
+    gemm_bf16_kernel<BM, BN, WM, WN, MI, false, true><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  else
+    gemm_bf16_kernel<BM, BN, WM, WN, MI, false, false><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  return hipGetLastError();
+}
+
+hipError_t run_f32(const GemmArgs& a, hipStream_t s) {
+  const bool sw = a.epilogue == MOE_EPI_SWIGLU;
+  Grid g = make_grid(a, 64, sw ? 32 : 64);
+  if (g.total == 0) return hipSuccess;
+  dim3 grid(g.blocks), block(256);
+  if (sw) gemm_f32_kernel<true><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  else gemm_f32_kernel<false><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile shape choice: the expected rows per group decide between a compute-shaped tile (large
+// groups, MFMA-bound) and a weight-streaming tile (few rows per group, HBM-bound).
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
+  if (a.dtype == MOE_F32) return run_f32(a, s);
+  if (a.dtype == MOE_BF16) {
+    const long long rows = (long long)a.max_rows + a.x_rows;
+    const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
+    const long long per_group = groups ? rows / groups : rows;
+    const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
+    if (per_group >= 512 && n_full >= 256) return run_bf16<256, 256, 2, 2, 32>(a, s);
+    if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32>(a, s);
+    return run_bf16<32, 128, 1, 4, 16>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,66 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Arguments of one grouped-GEMM launch.
+//   routed groups g < G: rows [offsets[g], offsets[g+1]) of C, weights B + g * b_stride
+//   optional extra group ("shared expert"): rows [x_row0, x_row0 + x_rows) of C, A row = r - x_row0,
+//   weights xB / xB2
+struct GemmArgs {
+  int dtype;            // moe_dtype of A and B
+  int epilogue;         // moe_epilogue
+  int out_dtype;        // moe_dtype of C
+  int K, N;             // reduction length; output columns
+  const void* A;        // [rows of A, K] in dtype (row pitch a_pitch bytes)
+  const void* A_scales;
+  long long a_pitch;    // bytes between A rows
+  int a_scale_rows;     // FP8: A scales per a_scale_rows-row block
+  const int32_t* a_rows;
+  int a_row_div;
+  int G;
+  const int32_t* offsets;
+  int max_rows;         // bound on offsets[G] (sizes the grid)
+  const void* B; const void* Bs; const void* B2; const void* B2s;
+  long long b_stride;   // bytes between groups' B (and B2)
+  long long bs_stride;  // bytes between groups' scales
+  int x_rows, x_row0;   // extra group rows of C
+  int x_a_off;          // extra group: A row = C row - x_a_off
+  const void* xB; const void* xBs; const void* xB2; const void* xB2s;
+  const float* bias;    // STORE epilogue: per-column fp32 bias, or null
+  void* C;
+  void* C_scales;
+  long long c_pitch;    // bytes between C rows
+};
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+hipError_t launch_topk(int T, int E, int k, int scoring, int renormalize, const float* logits,
+                       int32_t* ids, float* w, hipStream_t s);
+
+// Dispatch maps. ws must hold permute_ws_bytes(T*k, E_loc) bytes.
+size_t permute_ws_bytes(long long slots, int E_loc);
+hipError_t launch_permute_maps(int T, int k, int e0, int E_loc, const int32_t* ids, int32_t* counts,
+                               int32_t* offsets, int32_t* slot_to_row, int32_t* row_to_flat,
+                               void* ws, hipStream_t s);
+// a_perm[r] = a_in[row_to_flat[r] / k] for r < offsets[E_loc]; row_bytes % 16 == 0.
+// With scales: the same gather of scale rows (scale_row_bytes % 4 == 0), the source scale row of
+// token t being t / scale_rows_per_block.
+hipError_t launch_gather_rows(long long max_rows, int k, const int32_t* offsets_end,
+                              const int32_t* row_to_flat, const void* src, long long row_bytes,
+                              void* dst, const void* src_scales, long long scale_row_bytes,
+                              int scale_rows_per_block, void* dst_scales, hipStream_t s);
+
+hipError_t launch_combine(int T, int H, int k, int y_dtype, int out_dtype, const void* y, const float* w,
+                          const int32_t* slot_to_row, const void* shared, void* out,
+                          hipStream_t s);
+
+hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int block_rows,
+                            const void* src, uint8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const void* src,
+                            uint8_t* packed, uint8_t* scales, hipStream_t s);
+
+}  // namespace moe

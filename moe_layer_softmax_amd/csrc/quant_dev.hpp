@@ -1,0 +1,58 @@
+// quant_dev.hpp -- device-side element conversions (OCP e4m3, OCP MX v1.0 e2m1 / E8M0), shared by
+// the quantiser kernels and the GEMM epilogues that re-quantise the intermediate activations.
+#pragma once
+
+#include "common.hpp"
+
+namespace moe {
+
+// fp32 -> e4m3 (bias 7, no infinities, max 448): round to nearest even, saturate to +-448, keep the
+// sign bit (a negative value rounding to zero gives negative zero).
+__device__ __forceinline__ uint8_t e4m3_rne_sat(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint8_t sign = static_cast<uint8_t>((u >> 24) & 0x80u);
+  const float a = fabsf(q);
+  if (!(a < 448.0f)) return sign | 0x7Eu;
+  if (a < 0.015625f) {                                     // below 2^-6: steps of 2^-9
+    return sign | static_cast<uint8_t>(rintf(a * 512.0f));  // exact scaling; 8 -> 2^-6
+  }
+  uint32_t ua = __float_as_uint(a);
+  ua += 0x7FFFFu + ((ua >> 20) & 1u);                      // round the mantissa to 3 bits (RNE)
+  ua &= 0xFFF00000u;
+  const int e = static_cast<int>(ua >> 23) - 127;
+  const uint32_t m = (ua >> 20) & 7u;
+  return sign | static_cast<uint8_t>(((e + 7) << 3) | m);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  const int ef = (c >> 3) & 15, m = c & 7;
+  float v = (ef == 0) ? ldexpf(static_cast<float>(m), -9) : ldexpf(1.0f + m * 0.125f, ef - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+// fp32 -> e2m1 (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6): nearest, ties to the even code, saturate.
+__device__ __forceinline__ uint8_t e2m1_rne_sat(float y) {
+  const uint8_t sign = static_cast<uint8_t>((__float_as_uint(y) >> 28) & 8u);
+  const float a = fabsf(y);
+  uint8_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return sign | c;
+}
+
+// shared exponent of an MX block: floor(log2(amax)) - 2, clamped to [-127, 127]; -127 for amax = 0
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (amax == 0.0f) return -127;
+  int ex;
+  frexpf(amax, &ex);
+  int e = ex - 1 - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+}  // namespace moe

@@ -1,0 +1,142 @@
+"""The whole layer (moe_layer through the C ABI) against the oracle on the workloads, at full size
+(sampled tokens where the oracle cannot do all of them in seconds), plus edge cases."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import moe_layer_softmax_amd as moe
+import oracle
+from moe_inputs import gen
+
+from gpu_util import (gamma, io_torch, rel_err, routing_consistent, to_dev, tol_for, topk_numpy)
+
+pytestmark = pytest.mark.gpu
+
+_FMT = {mi.FMT_F32: moe.MOE_F32, mi.FMT_BF16: moe.MOE_BF16, mi.FMT_FP8: moe.MOE_FP8_E4M3,
+        mi.FMT_MX4: moe.MOE_MXFP4}
+
+
+def make_inputs(wl, bias_override=None):
+    x, wr = gen.tokens(wl), gen.router_weight(wl)
+    bias = gen.router_bias(wl) if bias_override is None else bias_override
+    g, u, d = gen.expert_weights(wl)
+    sh = gen.shared_weights(wl)
+    return x, wr, bias, (g, u, d), sh
+
+
+def gpu_layer(wl, x, wr, bias, experts, sh):
+    dt = io_torch(wl.io_fmt)
+    desc = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
+                         wl.renormalize, _FMT[wl.io_fmt], _FMT[wl.fmt])
+    ew = [to_dev(a, dt) for a in experts]
+    shw = None if sh is None else [to_dev(a, dt) for a in sh]
+    weights = moe.make_weights(to_dev(wr, dt), *ew, shared=shw)
+    out = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+    logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((wl.T, wl.k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(moe.moe_layer_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    xb = to_dev(x, dt)
+    bt = None if bias is None else to_dev(bias, torch.float32)
+    moe.moe_layer(desc, weights, xb, bt, out, logits, ids, w, ws)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), logits.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy(),
+            (desc, weights, xb, bt, out, logits, ids, w, ws))
+
+
+def oracle_layer(wl, x, wr, bias, experts, sh, tok):
+    # h enters the down projection in the expert format (bf16 for the bf16 layers)
+    act = {mi.FMT_F32: oracle.F32, mi.FMT_BF16: oracle.BF16}[wl.fmt]
+    desc = dict(T=wl.T, H=wl.H, E=wl.E, e0=wl.e0, E_loc=wl.E_loc, I=wl.I, k=wl.k, I_s=wl.I_s,
+                scoring=wl.scoring, renormalize=wl.renormalize, act_fmt=act)
+    M = oracle.Mat
+    shared = None if sh is None else tuple(M(oracle.F32, a) for a in sh)
+    return oracle.moe_layer(desc, x, wr, bias, M(oracle.F32, x), *(M(oracle.F32, a) for a in experts),
+                            shared, tok)
+
+
+def check_layer(wl, n_sample=None, bias_override=None, seed=0):
+    print(f"[layer] {wl.name} T={wl.T} H={wl.H} E={wl.E} E_loc={wl.E_loc} I={wl.I} k={wl.k} "
+          f"I_s={wl.I_s}", flush=True)
+    x, wr, bias, experts, sh = make_inputs(wl, bias_override)
+    out, lg, ids, w, _ = gpu_layer(wl, x, wr, bias, experts, sh)
+    T = wl.T
+    if n_sample is None or n_sample >= T:
+        tok = np.arange(T, dtype=np.int32)
+    else:
+        rng = np.random.default_rng([seed, T])
+        tok = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample, replace=False)]))
+        tok = tok.astype(np.int32)
+    ref = oracle_layer(wl, x, wr, bias, experts, sh, tok)
+    # logits inside the fp32 accumulation bound
+    L64, absdot = oracle.logits(x, wr, bias, tok=tok)
+    bound = gamma(wl.H + 1) * absdot
+    assert np.all(np.abs(lg[tok].astype(np.float64) - L64) <= bound)
+    # the selection was made on exactly the logits written (every token, numpy brute force)
+    assert np.array_equal(ids, topk_numpy(lg, wl.k))
+    # against the oracle's own routing: equal, or a valid choice within the bound
+    diff = np.nonzero((ids[tok] != ref["ids"]).any(1))[0]
+    assert len(diff) <= max(1, len(tok) // 50), len(diff)
+    for i in diff:
+        assert routing_consistent(ids[tok[i]], L64[i], bound[i])
+    keep = np.setdiff1d(np.arange(len(tok)), diff)
+    assert np.abs(w[tok[keep]] - ref["w"][keep]).max() <= 1e-4
+    err, rms = rel_err(out[tok[keep]], ref["out"][keep])
+    print(f"[layer] {wl.name}: max|err|/rms = {err:.3e} (rms {rms:.3e}), tokens {len(keep)}, "
+          f"near-tie flips {len(diff)}", flush=True)
+    assert err <= tol_for(wl.fmt)
+    return out
+
+
+@pytest.mark.parametrize("name,n_sample", [("C1", None), ("C2d", None), ("C3a", 96),
+                                           ("C2p", 48), ("C3b", 64)])
+def test_layer_workloads(name, n_sample):
+    check_layer(mi.WORKLOADS[name], n_sample)
+
+
+def _small(**kw):
+    base = mi.Workload("edge", 64, 512, 16, 0, 8, 256, 4, 0, mi.SOFTMAX, 1, mi.FMT_BF16,
+                       mi.FMT_BF16, 0.0)
+    return replace(base, **kw)
+
+
+def test_layer_single_token_full_shape():
+    check_layer(mi.WORKLOADS["C2p"].with_tokens(1))
+
+
+def test_layer_no_local_rows():
+    wl = _small(e0=8)
+    bias = np.zeros(16, np.float32)
+    bias[8:] = -100.0                                    # nobody routes to the local slice
+    out = check_layer(wl, bias_override=bias)
+    assert not out.any()
+
+
+def test_layer_no_local_rows_with_shared():
+    wl = _small(e0=8, I_s=256)
+    bias = np.zeros(16, np.float32)
+    bias[8:] = -100.0
+    check_layer(wl, bias_override=bias)
+
+
+def test_layer_all_tokens_one_expert():
+    wl = _small(T=700)
+    bias = np.zeros(16, np.float32)
+    bias[3] = 30.0
+    check_layer(wl, bias_override=bias)
+
+
+def test_layer_k_equals_E_sigmoid_ragged():
+    check_layer(_small(T=37, E=16, k=16, e0=8, E_loc=8, scoring=mi.SIGMOID))
+    check_layer(_small(T=37, E=16, k=3, e0=4, E_loc=12, I_s=256))
+
+
+def test_layer_deterministic():
+    wl = mi.WORKLOADS["C3a"]
+    x, wr, bias, experts, sh = make_inputs(wl)
+    a = gpu_layer(wl, x, wr, bias, experts, sh)[0]
+    b = gpu_layer(wl, x, wr, bias, experts, sh)[0]
+    assert np.array_equal(a, b)

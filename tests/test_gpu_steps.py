@@ -1,0 +1,283 @@
+"""Per-step parity of the HIP path against the oracle, through the C ABI: quantisers, routing,
+dispatch, grouped GEMM and combine. Integer results bit-exact; floating results within the stated
+tolerances."""
+import numpy as np
+import pytest
+import torch
+
+import moe_layer_softmax_amd as moe
+import oracle
+from moe_inputs import gen
+
+from gpu_util import (gamma, rel_err, routing_consistent, to_dev, topk_numpy)
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------------------------
+# quantisers: codes and scales bit-exact
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols,block_rows,src", [(256, 384, 128, "f32"), (200, 256, 128, "bf16"),
+                                                       (37, 1024, 1, "f32"), (128, 7168, 128, "bf16")])
+def test_quantize_fp8_bitexact(rows, cols, block_rows, src):
+    rng = np.random.default_rng(rows + cols)
+    a = (rng.standard_normal((2, rows, cols)) * rng.choice([0.02, 1.0, 30.0])).astype(np.float32)
+    a[0, :7, :] = 0.0                               # an all-zero region
+    if src == "bf16":
+        a = gen.bf16_round(a)
+    t = to_dev(a, torch.float32 if src == "f32" else torch.bfloat16)
+    nbr = (rows + block_rows - 1) // block_rows
+    codes = torch.empty((2, rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((2, nbr, cols // 128), dtype=torch.float32, device="cuda")
+    moe.moe_quantize(moe.MOE_FP8_E4M3, moe.MOE_F32 if src == "f32" else moe.MOE_BF16, 2, rows,
+                     cols, block_rows, t, codes, scales)
+    _sync()
+    for b in range(2):
+        c_ref, s_ref = oracle.quant_fp8(a[b], block_rows, 128)
+        assert np.array_equal(scales[b].cpu().numpy(), s_ref)
+        assert np.array_equal(codes[b].cpu().numpy(), c_ref)
+
+
+@pytest.mark.parametrize("rows,cols,src", [(64, 256, "f32"), (333, 7168, "bf16"), (5, 2048, "f32")])
+def test_quantize_mx4_bitexact(rows, cols, src):
+    rng = np.random.default_rng(rows * cols)
+    a = rng.standard_normal((3, rows, cols)).astype(np.float32)
+    a[1] *= 1e-3
+    a[2, :, :32] = 0.0
+    a[2, 0, 40:72] = np.array([0.25, -0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0] * 4, np.float32)
+    if src == "bf16":
+        a = gen.bf16_round(a)
+    t = to_dev(a, torch.float32 if src == "f32" else torch.bfloat16)
+    packed = torch.empty((3, rows, cols // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((3, rows, cols // 32), dtype=torch.uint8, device="cuda")
+    moe.moe_quantize(moe.MOE_MXFP4, moe.MOE_F32 if src == "f32" else moe.MOE_BF16, 3, rows, cols, 1,
+                     t, packed, scales)
+    _sync()
+    for b in range(3):
+        p_ref, s_ref = oracle.quant_mx4(a[b])
+        assert np.array_equal(scales[b].cpu().numpy(), s_ref)
+        assert np.array_equal(packed[b].cpu().numpy(), p_ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# routing
+# ---------------------------------------------------------------------------------------------
+
+def _route_given_logits(L, k, scoring, renorm, e0=0, E_loc=None):
+    T, E = L.shape
+    d = moe.make_desc(T, 64, E, e0, E_loc or E, 64, k, 0, scoring, renorm)
+    lt = to_dev(L, torch.float32)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(d, None, None, None, lt, ids, w)
+    _sync()
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (512, 10), (256, 8), (16, 16), (1024, 16),
+                                 (5, 1), (70, 3)])
+@pytest.mark.parametrize("scoring,renorm", [(0, 1), (1, 1), (0, 0), (1, 0)])
+def test_topk_bitexact(E, k, scoring, renorm):
+    for T, L in ((333, gen.tie_heavy_logits(333, E, seed=E)),
+                 (1000, gen.random_logits(1000, E, seed=k, scale=2.0)),
+                 (257, gen.random_logits(257, E, seed=1, scale=1.0,
+                                         bias=gen.router_bias(_zipf_wl(E))))):
+        ids, w = _route_given_logits(L, k, scoring, renorm)
+        ids_ref, w_ref = oracle.topk(L, k, scoring, renorm)
+        assert np.array_equal(ids, ids_ref)
+        assert np.abs(w - w_ref).max() <= 1e-6
+
+
+def _zipf_wl(E):
+    from moe_inputs.workloads import Workload
+    return Workload("z", 1, 64, E, 0, E, 64, 1, 0, 0, 1, 1, 1, 1.1)
+
+
+@pytest.mark.parametrize("T,H,E,k,zipf,scoring", [(300, 4096, 128, 8, 1.1, 0), (64, 7168, 256, 8, 1.2, 1),
+                                                  (40, 4096, 512, 10, 0.0, 0), (33, 256, 8, 2, 0.0, 0)])
+def test_route_from_x(T, H, E, k, zipf, scoring):
+    from moe_inputs.workloads import Workload
+    io = 0 if H == 256 else 1
+    wl = Workload("r", T, H, E, 0, E, 64, k, 0, scoring, 1, io, io, zipf)
+    x, wr, bias = gen.tokens(wl), gen.router_weight(wl), gen.router_bias(wl)
+    dt = torch.float32 if io == 0 else torch.bfloat16
+    d = moe.make_desc(T, H, E, 0, E, 64, k, 0, scoring, 1, io, io)
+    lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(d, to_dev(x, dt), to_dev(wr, dt), None if bias is None else to_dev(bias, torch.float32),
+                  lg, ids, w)
+    _sync()
+    lg, ids, w = lg.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
+    L64, absdot = oracle.logits(x, wr, bias)
+    bound = gamma(H + 1) * absdot
+    assert np.all(np.abs(lg.astype(np.float64) - L64) <= bound)
+    # the GPU chose from exactly the fp32 logits it wrote (selection rule checked in numpy)
+    assert np.array_equal(ids, topk_numpy(lg, k))
+    # against the oracle's own routing: equal, or a valid choice inside the logit bound
+    ids_ref, w_ref = oracle.topk(L64.astype(np.float32), k, scoring, 1)
+    diff = np.nonzero((ids != ids_ref).any(1))[0]
+    assert len(diff) <= max(1, T // 100)
+    for t in diff:
+        assert routing_consistent(ids[t], L64[t], bound[t])
+    same = np.setdiff1d(np.arange(T), diff)
+    assert np.abs(w[same] - w_ref[same]).max() <= 1e-4
+
+
+# ---------------------------------------------------------------------------------------------
+# dispatch
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,E,k,e0,E_loc,hot", [(64, 8, 2, 0, 8, 0.0), (333, 128, 8, 0, 32, 0.3),
+                                                (2048, 512, 10, 64, 64, 0.0), (1, 16, 4, 12, 4, 0.0),
+                                                (16384, 128, 8, 0, 32, 0.5), (3000, 256, 8, 96, 32, 0.2),
+                                                (2047, 1024, 16, 0, 1024, 0.0), (50, 8, 8, 0, 8, 0.0)])
+def test_permute_bitexact(T, E, k, e0, E_loc, hot):
+    ids_np = gen.random_topk_ids(T, E, k, seed=T + E, hot=[e0, e0 + 1], hot_frac=hot)
+    H = 128
+    rng = np.random.default_rng(T)
+    x = gen.bf16_round(rng.standard_normal((T, H)).astype(np.float32))
+    d = moe.make_desc(T, H, E, e0, E_loc, 64, k)
+    ws = torch.empty(moe.moe_permute_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(E_loc, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E_loc + 1, dtype=torch.int32, device="cuda")
+    s2r = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    r2f = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    a_perm = torch.zeros((T * k, H), dtype=torch.bfloat16, device="cuda")
+    moe.moe_permute(d, to_dev(ids_np, torch.int32), to_dev(x, torch.bfloat16), None, counts,
+                    offsets, s2r, r2f, a_perm, None, ws)
+    _sync()
+    c_ref, o_ref, s_ref, r_ref = oracle.permute(ids_np, e0, E_loc)
+    R = len(r_ref)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(s2r.cpu().numpy(), s_ref)
+    r2f_g = r2f.cpu().numpy()
+    assert np.array_equal(r2f_g[:R], r_ref)
+    assert np.all(r2f_g[R:] == -7)                      # rows >= R untouched
+    ap = a_perm.float().cpu().numpy()
+    assert np.array_equal(ap[:R], x[r_ref // k])         # bytes of the gathered rows
+
+
+def test_permute_no_local_rows():
+    T, E, k = 100, 64, 4
+    ids_np = gen.random_topk_ids(T, E, k, seed=3)
+    ids_np = np.where(ids_np < 8, ids_np + 8, ids_np).astype(np.int32)
+    d = moe.make_desc(T, 128, E, 0, 8, 64, k)
+    ws = torch.empty(moe.moe_permute_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+    counts = torch.full((8,), 5, dtype=torch.int32, device="cuda")
+    offsets = torch.full((9,), 5, dtype=torch.int32, device="cuda")
+    s2r = torch.zeros((T, k), dtype=torch.int32, device="cuda")
+    r2f = torch.zeros((T * k,), dtype=torch.int32, device="cuda")
+    moe.moe_permute(d, to_dev(ids_np, torch.int32), None, None, counts, offsets, s2r, r2f, None,
+                    None, ws)
+    _sync()
+    assert not counts.cpu().numpy().any() and not offsets.cpu().numpy().any()
+    assert np.all(s2r.cpu().numpy() == -1)
+
+
+# ---------------------------------------------------------------------------------------------
+# grouped GEMM
+# ---------------------------------------------------------------------------------------------
+
+def _gemm_case(counts, K, N, swiglu, gather, out_f32, dtype_in="bf16", seed=0):
+    rng = np.random.default_rng([seed, K, N, len(counts)])
+    G = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    max_rows = R + 17
+    f32 = dtype_in == "f32"
+    rnd = (lambda a: a) if f32 else gen.bf16_round
+    tdt = torch.float32 if f32 else torch.bfloat16
+    if gather:
+        T, kk = max(R // 3, 1), 4
+        A = rnd(rng.standard_normal((T, K)).astype(np.float32))
+        a_rows = rng.integers(0, T * kk, size=max_rows).astype(np.int32)
+    else:
+        kk = 1
+        A = rnd(rng.standard_normal((max_rows, K)).astype(np.float32))
+        a_rows = None
+    B = rnd((rng.standard_normal((G, N, K)) * 0.05).astype(np.float32))
+    B2 = rnd((rng.standard_normal((G, N, K)) * 0.05).astype(np.float32)) if swiglu else None
+    g = moe.moe_gemm_desc(G, max_rows, K, N, moe.MOE_F32 if f32 else moe.MOE_BF16,
+                          moe.MOE_EPI_SWIGLU if swiglu else moe.MOE_EPI_STORE,
+                          moe.MOE_F32 if out_f32 else moe.MOE_BF16, kk, 1)
+    C = torch.full((max_rows, N), 1024.0, dtype=torch.float32 if out_f32 else torch.bfloat16,
+                   device="cuda")
+    moe.moe_grouped_gemm(g, to_dev(A, tdt), None, None if a_rows is None else to_dev(a_rows, torch.int32),
+                         to_dev(B, tdt), None, None if B2 is None else to_dev(B2, tdt), None,
+                         to_dev(off, torch.int32), C, None)
+    _sync()
+    Cg = C.float().cpu().numpy()
+    M = oracle.Mat
+    ref = oracle.grouped_gemm(off, M(oracle.F32, A), M(oracle.F32, B),
+                              None if B2 is None else M(oracle.F32, B2), a_rows=a_rows, a_row_div=kk)
+    return Cg, ref, R
+
+
+@pytest.mark.parametrize("counts", [[0, 37, 130, 1, 9], [700, 1200, 0, 513], [150, 97, 200, 0, 101]])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_gemm_bf16(counts, swiglu, gather):
+    Cg, ref, R = _gemm_case(counts, K=512, N=256, swiglu=swiglu, gather=gather, out_f32=False)
+    err = np.abs(Cg[:R] - ref)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.all(err <= 2 ** -8 * np.abs(ref) + 1e-3 * rms), err.max() / rms
+    assert np.all(Cg[R:] == 1024.0)                      # rows outside every group untouched
+
+
+@pytest.mark.parametrize("counts,K,N", [([3, 70, 0, 5], 4096, 128), ([600, 40], 256, 1536)])
+def test_grouped_gemm_bf16_f32_out(counts, K, N):
+    Cg, ref, R = _gemm_case(counts, K=K, N=N, swiglu=False, gather=False, out_f32=True)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.abs(Cg[:R] - ref).max() <= 1e-4 * rms * np.sqrt(K / 256)
+
+
+@pytest.mark.parametrize("swiglu", [False, True])
+def test_grouped_gemm_f32(swiglu):
+    Cg, ref, R = _gemm_case([20, 0, 65, 7], K=256, N=128, swiglu=swiglu, gather=True, out_f32=True,
+                            dtype_in="f32")
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.abs(Cg[:R] - ref).max() <= 1e-5 * rms
+
+
+# ---------------------------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,H,shared,io,out_bf16", [(64, 2, 256, False, "f32", False),
+                                                      (300, 8, 4096, False, "bf16", False),
+                                                      (77, 10, 1024, True, "bf16", True),
+                                                      (5, 16, 7168, True, "f32", True)])
+def test_combine(T, k, H, shared, io, out_bf16):
+    rng = np.random.default_rng(T * k)
+    R = T * k
+    rnd = (lambda a: a) if io == "f32" else gen.bf16_round
+    tdt = torch.float32 if io == "f32" else torch.bfloat16
+    y = rnd(rng.standard_normal((R, H)).astype(np.float32))
+    w = rng.random((T, k)).astype(np.float32)
+    s2r = rng.permutation(R).reshape(T, k).astype(np.int32)
+    s2r[rng.random((T, k)) < 0.3] = -1
+    s2r[0, :] = -1                                        # a token with no local expert
+    sh = rnd(rng.standard_normal((T, H)).astype(np.float32)) if shared else None
+    ydt = moe.MOE_F32 if io == "f32" else moe.MOE_BF16
+    d = moe.make_desc(T, H, 64, 0, 8, 64, k, 0, 0, 1, ydt, ydt,
+                      out_dtype=moe.MOE_BF16 if out_bf16 else moe.MOE_F32)
+    out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
+    moe.moe_combine(d, ydt, to_dev(y, tdt), to_dev(w, torch.float32), to_dev(s2r, torch.int32),
+                    None if sh is None else to_dev(sh, tdt), out)
+    _sync()
+    ref = oracle.combine(y, w, s2r, sh)
+    og = out.float().cpu().numpy()
+    rms = np.sqrt(np.mean(ref ** 2))
+    if not out_bf16:
+        assert np.abs(og - ref).max() <= 1e-5 * rms
+    else:
+        assert np.all(np.abs(og - ref) <= 2 ** -8 * np.abs(ref) + 1e-5 * rms)
+    if not shared:
+        assert not og[0].any()
