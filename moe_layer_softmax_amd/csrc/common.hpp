@@ -53,6 +53,33 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v)
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Device-only builtins, wrapped so that the host compilation pass (which only emits kernel launch
+// stubs) never sees them in a kernel body.
+// 16 bytes per lane from global memory straight into LDS: lane i writes lds_region + 16 * i.
+__device__ __forceinline__ void dma_16b(const void* g, void* lds_region) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, lds_region, 16, 0, 0);
+#endif
+}
+// s_waitcnt vmcnt(0): all of this wave's vector memory loads (including LDS DMA) have completed
+__device__ __forceinline__ void wait_vmem() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+}
+// Workgroup barrier for LDS filled by dma_16b. __syncthreads() carries a workgroup memory fence,
+// which makes every wave drain ALL of its outstanding LDS DMA first; a pipelined K loop only needs
+// the stage it is about to read. Callers therefore wait for that stage's DMA explicitly
+// (wait_vmem_n) and then use this plain hardware barrier; the empty asm statements with memory
+// clobbers keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// scheduling hint: `count` instructions of class `mask` (0x008 MFMA, 0x100 DS read, ...) next
+#define MOE_SCHED_GROUP(mask, count) __builtin_amdgcn_sched_group_barrier((mask), (count), 0)
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Workgroup order -> logical tile order: consecutive groups of `span` logical tiles run on one XCD

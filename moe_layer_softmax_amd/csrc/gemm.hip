@@ -13,10 +13,9 @@
 //     m-tile run on one XCD (they share the A rows in that XCD's L2).
 //   * A rows are optionally gathered through a row map (the dispatch's row_to_flat / k), so the
 //     layer can read expert rows straight from the token-order activations.
-//   * K loop: 128-byte row slices of A and B (64 bf16 / 128 fp8 / 256 fp4 elements) staged through
-//     LDS in a double buffer, 16-byte chunks XOR-swizzled by row so MFMA fragment reads
-//     (ds_read_b128) are bank-conflict free; global loads for step k+1 are in flight while step k
-//     is computed.
+//   * K loop: row slices of A and B go from global memory straight into a ring of LDS stages
+//     (direct-to-LDS loads), several K-steps ahead of the MFMAs; 16-byte chunks are XOR-swizzled
+//     by row so MFMA fragment reads (ds_read_b128) are bank-conflict free.
 //   * Epilogues: STORE (optional per-column bias, fp32 or bf16 out) and SWIGLU, where each wave
 //     holds matching gate and up columns so h = silu(g) * u is formed in registers.
 #include "common.hpp"
@@ -70,10 +69,16 @@ __device__ __forceinline__ bool find_group(const int32_t* __restrict__ off, int 
   return false;
 }
 
+// logical tile -> (m-tile, n-tile): m-tiles are taken in groups of gm; inside a group the m-tile
+// index runs fastest, so consecutive logical tiles share B (same expert, same n-tile) and a short
+// run of them shares A rows.
 __device__ __forceinline__ bool resolve_tile(const GemmArgs& p, int BM, int n_tiles, int x_tiles,
-                                             int logical, Tile& t) {
-  const int mt = logical / n_tiles;
-  t.nt = logical - mt * n_tiles;
+                                             int logical, Tile& t, int gm = 1) {
+  const int per_group = gm * n_tiles;
+  const int grp = logical / per_group;
+  const int within = logical - grp * per_group;
+  const int mt = grp * gm + within % gm;
+  t.nt = within / gm;
   if (mt < x_tiles) {
     t.extra = true;
     t.row0 = p.x_row0 + mt * BM;
@@ -102,54 +107,77 @@ __device__ __forceinline__ long long a_src_row(const GemmArgs& p, const Tile& t,
   return r;
 }
 
-// ------------------------------------------------------------------------------------------------
-// bf16 MFMA kernel
-//   BM x BN tile, 4 waves (WM x WN), each wave a (BM/WM) x (BN/WN) block of MI x MI MFMA tiles
-//   (MI = 32: v_mfma_f32_32x32x16_bf16, MI = 16: v_mfma_f32_16x16x32_bf16).
-//   SWIGLU: the B tile of wave column wn holds BN/(2*WN) gate rows followed by the same number of
-//   up rows, so the h tile is BM x BN/2.
-// ------------------------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int MI, bool SWIGLU, bool OUT_F32>
+// silu(g) = g * sigmoid(g) with the hardware exp2 and reciprocal (about 1 ulp each); the result is
+// rounded to the expert format (bf16 or coarser) right after, far above their error.
+__device__ __forceinline__ float silu_fast(float g) {
+  return __fdividef(g, 1.0f + __expf(-g));
+}
+
+template <int BK>
+struct SliceGeo {
+  static constexpr int kRowBytes = BK * 2;             // bytes of one row slice
+  static constexpr int kChunks = kRowBytes / 16;       // 16-byte chunks per row slice
+  static constexpr int kRowsPerIns = 64 / kChunks;     // rows one wave-wide DMA instruction covers
+  static constexpr int kRowsPerLine = 256 / kRowBytes; // rows sharing one 256-byte LDS bank line
+  // gfx950's LDS serves a ds_read_b128 16 lanes at a time from 64 four-byte banks; an MFMA fragment
+  // read has 16 lanes on 16 consecutive rows at one logical chunk. XOR-ing the chunk with
+  // (row / rows-per-line) mod chunks gives those lanes 16 distinct bank groups.
+  __device__ static __forceinline__ int swz(int r) { return (r / kRowsPerLine) & (kChunks - 1); }
+};
+
+// s_waitcnt vmcnt(n) with every other counter left alone (n is a compile-time count)
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | 0x70 | 0xF00);
+#endif
+}
+
+template <int BM, int BN, int WM, int WN, int MI, int BK, int S, bool SWIGLU, bool OUT_F32>
 __global__ void __launch_bounds__(WM * WN * 64)
-gemm_bf16_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = 64;                 // bf16 per 128-byte row slice
+gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
+  using Geo = SliceGeo<BK>;
+  constexpr int NW = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / MI, FN = TN / MI;
   constexpr int MK = (MI == 32) ? 16 : 32;
   constexpr int KS = BK / MK;
-  constexpr int CPR = 8;                 // 16-byte chunks per row slice
-  constexpr int RPP = NT / CPR;          // rows covered by one pass of the workgroup
-  constexpr int A_LD = BM / RPP, B_LD = BN / RPP;
-  static_assert(BM % RPP == 0 && BN % RPP == 0, "tile rows must be a multiple of NT/8");
+  constexpr int RPI = Geo::kRowsPerIns;
+  constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
+  constexpr int INS = A_INS + B_INS;                   // DMA instructions per wave per K-step
+  constexpr int STAGE = (BM + BN) * BK;                // uint16 per LDS stage
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows per wave region");
+  static_assert(KS % 2 == 0, "fragment double buffer assumes an even number of substeps");
   static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
+  static_assert(S >= 3 && (S - 2) * INS < 64, "pipeline depth");
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][(BM + BN) * BK];
+  // dynamic LDS (S * STAGE uint16), written only by the DMA loads
+  extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
 
   const int logical = xcd_remap(blockIdx.x, span);
   if (logical >= total) return;
   Tile t;
-  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t)) return;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int K = p.K;
   const int nk = K / BK;
-  const int ch = tid % CPR;
-  const int rbase = tid / CPR;
+  const int lrow = lane / Geo::kChunks;
 
-  // global source pointers of this thread's A and B rows
-  const char* a_ptr[A_LD];
+  const char* a_src[A_INS];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int r = t.row0 + rbase + i * RPP;
-    a_ptr[i] = static_cast<const char*>(p.A) + a_src_row(p, t, r) * p.a_pitch + ch * 16;
+  for (int j = 0; j < A_INS; ++j) {
+    const int r = (j * NW + wave) * RPI + lrow;
+    const int lch = (lane % Geo::kChunks) ^ Geo::swz(r);
+    a_src[j] = static_cast<const char*>(p.A) + a_src_row(p, t, t.row0 + r) * p.a_pitch + lch * 16;
   }
-  const char* b_ptr[B_LD];
+  const char* b_src[B_INS];
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int rb = rbase + i * RPP;
+  for (int j = 0; j < B_INS; ++j) {
+    const int rb = (j * NW + wave) * RPI + lrow;
+    const int lch = (lane % Geo::kChunks) ^ Geo::swz(rb);
     long long n;
     const char* base = t.B;
     if (SWIGLU) {
@@ -161,28 +189,36 @@ gemm_bf16_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total) {
       n = (long long)t.nt * BN + rb;
     }
     if (n >= p.N) n = p.N - 1;             // columns past N: read a valid row, never stored
-    b_ptr[i] = base + n * (long long)K * 2 + ch * 16;
+    b_src[j] = base + n * (long long)K * 2 + lch * 16;
   }
 
-  i32x4 ra[A_LD], rb_[B_LD];
-  auto gload = [&](int kt) {
+  // K-step kt's slices into stage kt % S (steps past the end issue nothing)
+  auto issue = [&](int kt) {
+    if (kt >= nk) return;
+    uint16_t* la = lds + (kt % S) * STAGE;
+    uint16_t* lb = la + BM * BK;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = *reinterpret_cast<const i32x4*>(a_ptr[i] + kt * 128);
+    for (int j = 0; j < A_INS; ++j)
+      dma_16b(a_src[j] + (long long)kt * Geo::kRowBytes, la + (j * NW + wave) * RPI * BK);
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb_[i] = *reinterpret_cast<const i32x4*>(b_ptr[i] + kt * 128);
+    for (int j = 0; j < B_INS; ++j)
+      dma_16b(b_src[j] + (long long)kt * Geo::kRowBytes, lb + (j * NW + wave) * RPI * BK);
   };
-  auto lstore = [&](int buf) {
-    uint16_t* la = lds[buf];
-    uint16_t* lb = lds[buf] + BM * BK;
+
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto lfrag = [&](int stage, int s, int slot) {
+    const uint16_t* la = lds + stage * STAGE;
+    const uint16_t* lb = la + BM * BK;
+    const int cidx = s * (MK / 8) + lane / MI;
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-      const int r = rbase + i * RPP;
-      *reinterpret_cast<i32x4*>(la + r * BK + ((ch ^ (r & 7)) * 8)) = ra[i];
+    for (int i = 0; i < FM; ++i) {
+      const int r = wm * TM + i * MI + (lane % MI);
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(la + r * BK + ((cidx ^ Geo::swz(r)) * 8));
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-      const int r = rbase + i * RPP;
-      *reinterpret_cast<i32x4*>(lb + r * BK + ((ch ^ (r & 7)) * 8)) = rb_[i];
+    for (int j = 0; j < FN; ++j) {
+      const int r = wn * TN + j * MI + (lane % MI);
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(lb + r * BK + ((cidx ^ Geo::swz(r)) * 8));
     }
   };
 
@@ -200,44 +236,51 @@ gemm_bf16_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total) {
       for (int j = 0; j < FN; ++j) acc16[i][j] = f32x4{};
   }
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // prologue: steps 0 .. S-2 in flight, wait for step 0
+#pragma unroll
+  for (int q = 0; q < S - 1; ++q) issue(q);
+  if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
+  else wait_vmem();
+  barrier_lds();
+  lfrag(0, 0, 0);
 
+  // Step kt: substeps 0..KS-2 on fragments already in registers (each prefetching the next
+  // substep's); then wait for step kt+1's slices and pass the barrier while those MFMAs drain
+  // (the barrier also releases stage kt-1, read during step kt-1, for step kt+S-1's loads); the
+  // last substep's MFMAs then overlap the reads of step kt+1's first fragments.
   for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* la = lds[buf];
-    const uint16_t* lb = lds[buf] + BM * BK;
+    const int stage = kt % S;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int cidx = s * (MK / 8) + lane / MI;
-      bf16x8 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * TM + i * MI + (lane % MI);
-        af[i] = *reinterpret_cast<const bf16x8*>(la + r * BK + ((cidx ^ (r & 7)) * 8));
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * TN + j * MI + (lane % MI);
-        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + r * BK + ((cidx ^ (r & 7)) * 8));
+      const int slot = s & 1;
+      if (s == KS - 1) {
+        if (kt + S - 2 < nk) wait_vmem_n<(S - 3) * INS>();   // step kt+1 landed
+        else wait_vmem();
+        barrier_lds();
+        issue(kt + S - 1);
+        if (kt + 1 < nk) lfrag((kt + 1) % S, 0, slot ^ 1);
+      } else {
+        lfrag(stage, s + 1, slot ^ 1);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           if constexpr (MI == 32)
-            acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc32[i][j], 0, 0, 0);
+            acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc32[i][j], 0, 0, 0);
           else
-            acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc16[i][j], 0, 0, 0);
+            acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc16[i][j], 0, 0, 0);
         }
+#pragma unroll
+      for (int q = 0; q < FM + FN; ++q) {
+        MOE_SCHED_GROUP(0x100, 1);
+        MOE_SCHED_GROUP(0x008, (FM * FN) / (FM + FN) > 0 ? (FM * FN) / (FM + FN) : 1);
+      }
+      MOE_SCHED_GROUP(0x008, FM * FN);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
   }
 
-  // ---- epilogue ----
+// ---- epilogue ----
   constexpr int VPF = (MI == 32) ? 16 : 4;
   auto acc_at = [&](int i, int j, int v) -> float {
     if constexpr (MI == 32) return acc32[i][j][v];
@@ -259,7 +302,7 @@ gemm_bf16_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total) {
           const int r = t.row0 + wm * TM + i * MI + row_of(v);
           if (r >= t.row1) continue;
           const float g = acc_at(i, j, v), u = acc_at(i, j + FN / 2, v);
-          const float h = g / (1.0f + expf(-g)) * u;
+          const float h = silu_fast(g) * u;
           const long long col = (long long)t.nt * (BN / 2) + wn * (TN / 2) + j * MI + colw;
           if (col >= p.N) continue;
           if (OUT_F32) reinterpret_cast<float*>(C + r * p.c_pitch)[col] = h;
@@ -368,38 +411,49 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(GemmArgs p, int n_tiles, 
 namespace {
 
 struct Grid {
-  int n_tiles, x_tiles, span, total;
+  int n_tiles, x_tiles, span, total, gm;
   unsigned blocks;
 };
 
-Grid make_grid(const GemmArgs& a, int BM, int n_cols_per_tile) {
+// gm: m-tiles per tile-order group; span: consecutive logical tiles given to one XCD
+Grid make_grid(const GemmArgs& a, int BM, int n_cols_per_tile, int gm = 1, int span = 0) {
   Grid g;
   g.n_tiles = (a.N + n_cols_per_tile - 1) / n_cols_per_tile;
   g.x_tiles = a.x_rows > 0 ? (a.x_rows + BM - 1) / BM : 0;
   // routed tiles: sum_g ceil(m_g / BM) <= floor(max_rows / BM) + G
   const long long routed = a.G > 0 ? (long long)a.max_rows / BM + a.G : 0;
-  g.total = static_cast<int>((g.x_tiles + routed) * g.n_tiles);
-  g.span = g.n_tiles;
+  const long long m_tiles = g.x_tiles + routed;
+  g.gm = gm;
+  g.total = static_cast<int>(((m_tiles + gm - 1) / gm) * gm * g.n_tiles);
+  g.span = span > 0 ? span : g.n_tiles;
   const long long blk = (long long)kNumXcd * g.span;
   g.blocks = static_cast<unsigned>(((g.total + blk - 1) / blk) * blk);
   return g;
 }
 
-template <int BM, int BN, int WM, int WN, int MI>
-hipError_t run_bf16(const GemmArgs& a, hipStream_t s) {
+// Tile order of the 256 x 256 configurations: groups of 8 m-tiles with the m-tile index fastest,
+// 64 consecutive logical tiles per XCD. The 32 tiles an XCD runs at once then cover 8 m-tiles x 4
+// n-tiles, so each K-step slice of A is shared by 4 tiles and each slice of B by 8 in that XCD's L2
+// (12 distinct slices per 32 tiles).
+constexpr int kTileGroupM = 8;
+constexpr int kTileSpan = 64;
+
+template <int BM, int BN, int WM, int WN, int MI, int BK, int S>
+hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) {
   const bool sw = a.epilogue == MOE_EPI_SWIGLU;
-  Grid g = make_grid(a, BM, sw ? BN / 2 : BN);
+  Grid g = make_grid(a, BM, sw ? BN / 2 : BN, gm, span);
   if (g.total == 0) return hipSuccess;
   dim3 grid(g.blocks), block(WM * WN * 64);
   const bool f32 = a.out_dtype == MOE_F32;
-  if (sw && f32)
-    gemm_bf16_kernel<BM, BN, WM, WN, MI, true, true><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
-  else if (sw)
-    gemm_bf16_kernel<BM, BN, WM, WN, MI, true, false><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
-  else if (f32)
-    gemm_bf16_kernel<BM, BN, WM, WN, MI, false, true><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
-  else
-    gemm_bf16_kernel<BM, BN, WM, WN, MI, false, false><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.span, g.total);
+  const size_t lds_bytes = (size_t)S * (BM + BN) * BK * sizeof(uint16_t);
+#define MOE_RUN(SWI, F32)                                                                    \
+  gemm_bf16_pipe_kernel<BM, BN, WM, WN, MI, BK, S, SWI, F32><<<grid, block, lds_bytes, s>>>(  \
+      a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm)
+  if (sw && f32) MOE_RUN(true, true);
+  else if (sw) MOE_RUN(true, false);
+  else if (f32) MOE_RUN(false, true);
+  else MOE_RUN(false, false);
+#undef MOE_RUN
   return hipGetLastError();
 }
 
@@ -424,9 +478,15 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
     const long long per_group = groups ? rows / groups : rows;
     const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
-    if (per_group >= 512 && n_full >= 256) return run_bf16<256, 256, 2, 2, 32>(a, s);
-    if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32>(a, s);
-    return run_bf16<32, 128, 1, 4, 16>(a, s);
+    if (per_group >= 512 && n_full >= 256) {
+      // 256 x 256 tiles, K-steps of 32 through LDS stages of 32 KB. SwiGLU: 8 waves (2 per SIMD),
+      // each 128 x 64, 4 stages; plain store: 16 waves, each 64 x 64, 5 stages.
+      if (a.epilogue == MOE_EPI_SWIGLU)
+        return run_bf16<256, 256, 2, 4, 32, 32, 4>(a, s, kTileGroupM, kTileSpan);
+      return run_bf16<256, 256, 4, 4, 32, 32, 5>(a, s, kTileGroupM, kTileSpan);
+    }
+    if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
+    return run_bf16<32, 128, 1, 4, 16, 64, 4>(a, s);
   }
   return hipErrorInvalidValue;
 }
