@@ -11,7 +11,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "combine.hip", "quant.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_q.hip", "combine.hip", "quant.hip"]
 # Packed fp32 VALU ops are disabled for all device code (the compiler otherwise forms
 # v_pk_{add,mul,fma}_f32 from ordinary float code).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

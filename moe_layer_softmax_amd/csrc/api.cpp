@@ -74,18 +74,32 @@ moe_status check_desc(const moe_desc* d) {
   return MOE_OK;
 }
 
+// K (and N) granularity of the expert GEMMs: one K-step row slice is 128 bytes for bf16 / fp8 /
+// MXFP4 (64 / 128 / 256 elements), 16 elements for fp32
+int k_align(int dt) {
+  switch (dt) {
+    case MOE_F32: return 16;
+    case MOE_BF16: return 64;
+    case MOE_FP8_E4M3: return 128;
+    default: return 256;
+  }
+}
+
 moe_status check_expert_shapes(const moe_desc* d) {
   const int dt = d->expert_dtype;
   if (dt == MOE_F32 && d->io_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (dt != MOE_F32 && d->io_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
-  const int align = (dt == MOE_F32) ? 16 : (dt == MOE_BF16 ? 64 : 128);
+  const int align = k_align(dt);
   if (d->H % align || d->I % align || (d->I_s && d->I_s % align)) return MOE_ERR_INVALID_ARG;
   if (d->I % 64 || d->H % 64) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
-moe_status gemm_supported(int dt) {
-  return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_ERR_UNSUPPORTED;
+// bytes between consecutive experts' scale arrays of an [N, K] weight matrix
+long long scale_bytes(int dt, long long N, long long K) {
+  if (dt == MOE_FP8_E4M3) return (N / 128) * (K / 128) * 4;
+  if (dt == MOE_MXFP4) return N * (K / 32);
+  return 0;
 }
 
 // ---- layer workspace layout (identical in the size query and in moe_layer) ----------------------
@@ -237,12 +251,22 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
   if (!ok_ptr(A) || !ok_ptr(B) || !ok_ptr(C) || !ok_ptr(group_offsets) || !ok_opt(a_rows))
     return MOE_ERR_INVALID_ARG;
   if (g->epilogue == MOE_EPI_SWIGLU && !ok_ptr(B2)) return MOE_ERR_INVALID_ARG;
-  const int kalign = g->dtype == MOE_F32 ? 16 : (g->dtype == MOE_BF16 ? 64 : 128);
-  if (g->K % kalign || g->N % 64) return MOE_ERR_INVALID_ARG;
-  moe_status st = gemm_supported(g->dtype);
-  if (st != MOE_OK) return st;
+  if (g->K % k_align(g->dtype) || g->N % 64) return MOE_ERR_INVALID_ARG;
+  const bool quant = g->dtype == MOE_FP8_E4M3 || g->dtype == MOE_MXFP4;
   if (g->dtype == MOE_F32 && g->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
-  if (g->out_dtype != MOE_F32 && g->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (quant) {
+    if (!ok_ptr(A_scales) || !ok_ptr(B_scales)) return MOE_ERR_INVALID_ARG;
+    if (g->epilogue == MOE_EPI_SWIGLU && !ok_ptr(B2_scales)) return MOE_ERR_INVALID_ARG;
+    if (g->N % 128) return MOE_ERR_INVALID_ARG;
+    if (g->dtype == MOE_FP8_E4M3 && g->a_scale_rows != 1 && g->a_scale_rows != 128)
+      return MOE_ERR_INVALID_ARG;
+    const bool requant = g->epilogue == MOE_EPI_SWIGLU && g->out_dtype == g->dtype;
+    if (requant && !ok_ptr(C_scales)) return MOE_ERR_INVALID_ARG;
+    if (!requant && g->out_dtype != MOE_BF16 && !(g->epilogue == MOE_EPI_STORE && g->out_dtype == MOE_F32))
+      return MOE_ERR_UNSUPPORTED;
+  } else if (g->out_dtype != MOE_F32 && g->out_dtype != MOE_BF16) {
+    return MOE_ERR_UNSUPPORTED;
+  }
   GemmArgs a{};
   a.dtype = g->dtype;
   a.epilogue = g->epilogue;
@@ -263,9 +287,11 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
   a.B2 = B2;
   a.B2s = B2_scales;
   a.b_stride = row_bytes(g->dtype, g->K) * (long long)g->N;
+  a.bs_stride = scale_bytes(g->dtype, g->N, g->K);
   a.C = C;
   a.C_scales = C_scales;
-  a.c_pitch = (long long)g->N * (g->out_dtype == MOE_F32 ? 4 : 2);
+  a.c_pitch = g->out_dtype == g->dtype && quant ? row_bytes(g->dtype, g->N)
+                                                : (long long)g->N * (g->out_dtype == MOE_F32 ? 4 : 2);
   return hip_status(launch_gemm(a, stream));
 }
 
@@ -317,8 +343,6 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   if (!w) return MOE_ERR_INVALID_ARG;
   st = check_expert_shapes(d);
   if (st != MOE_OK) return st;
-  st = gemm_supported(d->expert_dtype);
-  if (st != MOE_OK) return st;
   if (d->I_s != 0 && d->I_s != d->I) return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
   const bool quant = d->expert_dtype == MOE_FP8_E4M3 || d->expert_dtype == MOE_MXFP4;
@@ -358,38 +382,64 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
                                       base + L.perm, stream));
   if (st != MOE_OK) return st;
 
-  // 3. gate/up GEMM with the SwiGLU epilogue; routed rows gather x through row_to_flat / k,
-  //    shared-expert rows (C rows slots..slots+T) read x in token order
+  // 3. activations for the expert GEMMs: x itself, or x quantised once in token order (fp8 with
+  //    128-token x 128-channel blocks, MXFP4 with 1 x 32 groups) before the rows are dispatched
+  // (quant: expert_dtype is fp8 or MXFP4)
+  const void* xa = x;
+  const void* xs = nullptr;
+  if (dt == MOE_FP8_E4M3) {
+    st = hip_status(launch_quant_fp8(io, 1, T, H, 128, x, reinterpret_cast<uint8_t*>(base + L.xq),
+                                     reinterpret_cast<float*>(base + L.xs), stream));
+    xa = base + L.xq;
+    xs = base + L.xs;
+  } else if (dt == MOE_MXFP4) {
+    st = hip_status(launch_quant_mx4(io, 1, T, H, x, reinterpret_cast<uint8_t*>(base + L.xq),
+                                     reinterpret_cast<uint8_t*>(base + L.xs), stream));
+    xa = base + L.xq;
+    xs = base + L.xs;
+  }
+  if (st != MOE_OK) return st;
+
+  // 4. gate/up GEMM with the SwiGLU epilogue; routed rows gather the activations through
+  //    row_to_flat / k, shared-expert rows (C rows slots..slots+T) read them in token order. h
+  //    leaves in the down projection's input format (bf16 / fp32, or re-quantised fp8 / MXFP4).
   GemmArgs a{};
   a.dtype = dt;
   a.epilogue = MOE_EPI_SWIGLU;
-  a.out_dtype = dt == MOE_F32 ? MOE_F32 : MOE_BF16;
+  a.out_dtype = dt == MOE_BF16 ? MOE_BF16 : dt;
   a.K = H;
   a.N = I;
-  a.A = x;
+  a.A = xa;
+  a.A_scales = xs;
   a.a_pitch = row_bytes(dt, H);
-  a.a_scale_rows = 1;
+  a.a_scale_rows = dt == MOE_FP8_E4M3 ? 128 : 1;
   a.a_rows = r2f;
   a.a_row_div = k;
   a.G = d->E_loc;
   a.offsets = offsets;
   a.max_rows = slots;
   a.B = w->w_gate;
+  a.Bs = w->w_gate_scales;
   a.B2 = w->w_up;
+  a.B2s = w->w_up_scales;
   a.b_stride = row_bytes(dt, H) * (long long)I;
+  a.bs_stride = scale_bytes(dt, I, H);
   if (d->I_s) {
     a.x_rows = T;
     a.x_row0 = slots;
     a.x_a_off = slots;
     a.xB = w->sh_gate;
+    a.xBs = w->sh_gate_scales;
     a.xB2 = w->sh_up;
+    a.xB2s = w->sh_up_scales;
   }
   a.C = base + L.h;
-  a.c_pitch = (long long)I * io_bytes(io);
+  a.C_scales = quant ? base + L.hs : nullptr;
+  a.c_pitch = quant ? row_bytes(dt, I) : (long long)I * io_bytes(io);
   st = hip_status(launch_gemm(a, stream));
   if (st != MOE_OK) return st;
 
-  // 4. down GEMM: y rows = h rows
+  // 5. down GEMM: y rows = h rows
   const int ydt = y_dtype_of(d);
   GemmArgs b{};
   b.dtype = dt;
@@ -398,26 +448,30 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   b.K = I;
   b.N = H;
   b.A = base + L.h;
-  b.a_pitch = (long long)I * io_bytes(io);
+  b.A_scales = quant ? base + L.hs : nullptr;
+  b.a_pitch = quant ? row_bytes(dt, I) : (long long)I * io_bytes(io);
   b.a_scale_rows = 1;
   b.a_row_div = 1;
   b.G = d->E_loc;
   b.offsets = offsets;
   b.max_rows = slots;
   b.B = w->w_down;
+  b.Bs = w->w_down_scales;
   b.b_stride = row_bytes(dt, I) * (long long)H;
+  b.bs_stride = scale_bytes(dt, H, I);
   if (d->I_s) {
     b.x_rows = T;
     b.x_row0 = slots;
     b.x_a_off = 0;
     b.xB = w->sh_down;
+    b.xBs = w->sh_down_scales;
   }
   b.C = base + L.y;
   b.c_pitch = (long long)H * io_bytes(ydt);
   st = hip_status(launch_gemm(b, stream));
   if (st != MOE_OK) return st;
 
-  // 5. combine (+ shared expert rows)
+  // 6. combine (+ shared expert rows)
   const void* shared = d->I_s ? base + L.y + (size_t)slots * H * io_bytes(ydt) : nullptr;
   return hip_status(launch_combine(T, H, k, ydt, d->out_dtype, base + L.y, tw, s2r, shared, out,
                                    stream));

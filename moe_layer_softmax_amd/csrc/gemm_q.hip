@@ -1,0 +1,340 @@
+// gemm_q.hip -- grouped (per-expert) GEMM for block-scaled 8-bit and 4-bit expert formats on the
+// gfx950 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4).
+//
+// Formats (weights and the activations fed to the expert GEMMs):
+//   * fp8: OCP e4m3 codes with one fp32 scale per 128 x 128 block of each weight matrix and, for
+//     activations, per 128-token x 128-channel block of x or per 1 x 128 block of h (block scaling
+//     "as used for models like DeepSeek", "Hosting Qwen on Blackwell", section "Quantization").
+//     A K-step is 128 elements = one scale block: the MFMA runs with unit scales into a temporary
+//     and the product of the two fp32 block scales is applied in fp32 before accumulation.
+//   * MXFP4: OCP e2m1 codes, two per byte, with one E8M0 scale per 32 elements along K (4-bit
+//     weights packed two per byte with per-group scales, "Driving vLLM WideEP ... on Blackwell
+//     (Part I)", section on lower-precision operations; absmax over 32 elements for MX formats,
+//     "CuTeDSL at Perplexity", Blackwell section). The E8M0 scales go straight into the MFMA's
+//     per-lane scale operands, so the dequantisation happens inside the matrix core.
+//
+// Tile: 128 rows x 256 B-rows, 4 waves each owning 32 rows x all 256 B-rows (so a wave holds the
+// full 128 h-columns of the SwiGLU tile: the epilogue can form fp8 1x128 or MXFP4 1x32 blocks of h
+// in registers, with the row amax reduced across 16 lanes by shuffles). K-steps are 128-byte row
+// slices (128 fp8 or 256 fp4 elements) staged through a 3-stage direct-to-LDS ring, with the same
+// bank swizzle, tile scheduler and row gathering as the bf16 kernel.
+#include "gemm_common.hpp"
+#include "quant_dev.hpp"
+
+namespace moe {
+
+enum { QEPI_STORE_F32 = 0, QEPI_STORE_BF16 = 1, QEPI_SWIGLU_BF16 = 2, QEPI_SWIGLU_Q = 3 };
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+template <int FMT, int EPI>
+__global__ void __launch_bounds__(256)
+gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
+  constexpr bool MX = FMT == MOE_MXFP4;
+  constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
+  constexpr int BM = 128, BN = 256, NW = 4, TM = 32, FM = 2, FN = 16, S = 3;
+  constexpr int RB = 128;                  // bytes per row slice (one K-step)
+  constexpr int KE = MX ? 256 : 128;       // elements per K-step
+  constexpr int SUB = MX ? 2 : 1;          // 128-element MFMA substeps per K-step
+  constexpr int A_INS = BM / (8 * NW), B_INS = BN / (8 * NW);
+  constexpr int INS = A_INS + B_INS;
+  constexpr int STAGE = (BM + BN) * RB;    // bytes per LDS stage
+  constexpr int NB = 4;                    // B fragments per MFMA batch
+  constexpr int FMT_CODE = MX ? 4 : 0;     // f8f6f4 operand format: 0 = fp8 e4m3, 4 = fp4 e2m1
+  using Geo = SliceGeo<64>;                // 128-byte rows
+  static_assert((S - 2) * INS < 64, "pipeline depth");
+
+  extern __shared__ __attribute__((aligned(1024))) uint8_t ldsq[];
+
+  const int logical = xcd_remap(blockIdx.x, span);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = p.K;
+  const int nk = K / KE;
+  const long long b_row_bytes = MX ? K / 2 : K;
+  const int lrow = lane >> 3;
+
+  // ---- DMA sources of this lane's rows ----
+  const char* a_src[A_INS];
+#pragma unroll
+  for (int j = 0; j < A_INS; ++j) {
+    const int r = (j * NW + wave) * 8 + lrow;
+    a_src[j] = static_cast<const char*>(p.A) + a_src_row(p, t, t.row0 + r) * p.a_pitch +
+               ((lane & 7) ^ Geo::swz(r)) * 16;
+  }
+  // B row (and matrix) behind tile row rb
+  auto b_row = [&](int rb, const char*& base, const char*& sbase) -> long long {
+    long long n;
+    base = t.B;
+    sbase = t.Bs;
+    if (SWIGLU) {
+      n = (long long)t.nt * (BN / 2) + (rb % (BN / 2));
+      if (rb >= BN / 2) { base = t.B2; sbase = t.B2s; }
+    } else {
+      n = (long long)t.nt * BN + rb;
+    }
+    return n < p.N ? n : p.N - 1;
+  };
+  const char* b_src[B_INS];
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j) {
+    const int rb = (j * NW + wave) * 8 + lrow;
+    const char *base, *sb;
+    const long long n = b_row(rb, base, sb);
+    b_src[j] = base + n * b_row_bytes + ((lane & 7) ^ Geo::swz(rb)) * 16;
+  }
+  auto issue = [&](int kt) {
+    if (kt >= nk) return;
+    uint8_t* la = ldsq + (kt % S) * STAGE;
+    uint8_t* lb = la + BM * RB;
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) dma_16b(a_src[j] + (long long)kt * RB, la + (j * NW + wave) * 8 * RB);
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) dma_16b(b_src[j] + (long long)kt * RB, lb + (j * NW + wave) * 8 * RB);
+  };
+
+  // ---- scale sources ----
+  // fp8: A scale of each accumulator row (rows (lane/16)*4 + v of fragment i), one per K-step;
+  //      B scales are uniform per 128 columns (gate/up halves, or two 128-column blocks).
+  // MXFP4: E8M0 bytes of each operand row of fragment i / j, 8 per K-step (256 elements).
+  const float* sa_ptr[MX ? 1 : FM * 4];
+  const uint8_t* sa_mx[MX ? FM : 1];
+  const uint8_t* sb_mx[MX ? FN : 1];
+  const float* sb_fp8[2];
+  if constexpr (!MX) {
+    const int kb = K / 128;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = t.row0 + wave * TM + i * 16 + (lane >> 4) * 4 + v;
+        sa_ptr[i * 4 + v] = static_cast<const float*>(p.A_scales) + (a_src_row(p, t, r) / p.a_scale_rows) * kb;
+      }
+    if (SWIGLU) {
+      sb_fp8[0] = reinterpret_cast<const float*>(t.Bs) + (long long)t.nt * kb;    // 128 h-columns = one block
+      sb_fp8[1] = reinterpret_cast<const float*>(t.B2s) + (long long)t.nt * kb;
+    } else {
+      sb_fp8[0] = reinterpret_cast<const float*>(t.Bs) + (long long)(t.nt * 2) * kb;
+      sb_fp8[1] = reinterpret_cast<const float*>(t.Bs) + (long long)min(t.nt * 2 + 1, (p.N - 1) / 128) * kb;
+    }
+  } else {
+    const int gpr = K / 32;                  // scale bytes per row
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = t.row0 + wave * TM + i * 16 + (lane & 15);
+      sa_mx[i] = static_cast<const uint8_t*>(p.A_scales) + a_src_row(p, t, r) * gpr;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const char *base, *sb;
+      const long long n = b_row(j * 16 + (lane & 15), base, sb);
+      sb_mx[j] = reinterpret_cast<const uint8_t*>(sb) + n * gpr;
+    }
+  }
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
+
+  // fragment readers (operand layout of the 16x16x128 f8f6f4 MFMA: lane l holds row/column
+  // l % 16 and the 32 K-elements [32 (l / 16), 32 (l / 16) + 32) of the 128)
+  const int q = lane >> 4;
+  auto read_frag = [&](const uint8_t* base, int r, int s) -> i32x8 {
+    i32x8 out;
+    if constexpr (MX) {
+      const int c = s * 4 + q;                       // 16 bytes = 32 fp4
+      const i32x4 v = *reinterpret_cast<const i32x4*>(base + r * RB + ((c ^ Geo::swz(r)) * 16));
+      out = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    } else {
+      const int c0 = 2 * q, c1 = 2 * q + 1;          // 32 bytes = 32 fp8
+      const i32x4 v0 = *reinterpret_cast<const i32x4*>(base + r * RB + ((c0 ^ Geo::swz(r)) * 16));
+      const i32x4 v1 = *reinterpret_cast<const i32x4*>(base + r * RB + ((c1 ^ Geo::swz(r)) * 16));
+      out = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+    return out;
+  };
+
+  // prologue: steps 0 .. S-2 in flight, wait for step 0
+#pragma unroll
+  for (int qq = 0; qq < S - 1; ++qq) issue(qq);
+  if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
+  else wait_vmem();
+  barrier_lds();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    issue(kt + S - 1);                     // its stage was released by the last barrier
+    const uint8_t* la = ldsq + (kt % S) * STAGE;
+    const uint8_t* lb = la + BM * RB;
+
+    // scales of this K-step
+    float fs[MX ? 1 : FM * 4][2];
+    u32x2 sam[MX ? FM : 1], sbm[MX ? FN : 1];
+    if constexpr (!MX) {
+      const float g0 = sb_fp8[0][kt], g1 = sb_fp8[1][kt];
+#pragma unroll
+      for (int i = 0; i < FM * 4; ++i) {
+        const float a = sa_ptr[i][kt];
+        fs[i][0] = a * g0;
+        fs[i][1] = a * g1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) sam[i] = *reinterpret_cast<const u32x2*>(sa_mx[i] + kt * 8);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) sbm[j] = *reinterpret_cast<const u32x2*>(sb_mx[j] + kt * 8);
+    }
+
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      i32x8 fa[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[i] = read_frag(la, wave * TM + i * 16 + (lane & 15), s);
+#pragma unroll
+      for (int b0 = 0; b0 < FN; b0 += NB) {
+        i32x8 fb[NB];
+#pragma unroll
+        for (int jj = 0; jj < NB; ++jj) fb[jj] = read_frag(lb, (b0 + jj) * 16 + (lane & 15), s);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < NB; ++jj) {
+            const int j = b0 + jj;
+            if constexpr (MX) {
+              const int sa = static_cast<int>((sam[i][s] >> (8 * q)) & 0xFFu);
+              const int sb = static_cast<int>((sbm[j][s] >> (8 * q)) & 0xFFu);
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  fa[i], fb[jj], acc[i][j], FMT_CODE, FMT_CODE, 0, sa, 0, sb);
+            } else {
+              const f32x4 tmp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                  fa[i], fb[jj], f32x4{}, FMT_CODE, FMT_CODE, 0, 127, 0, 127);
+              const int half = j >= FN / 2 ? 1 : 0;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(tmp[v], fs[i * 4 + v][half], acc[i][j][v]);
+            }
+          }
+      }
+    }
+    if (kt + S - 1 < nk) wait_vmem_n<(S - 2) * INS>();   // step kt+1 landed
+    else wait_vmem();
+    barrier_lds();
+  }
+
+  // ---- epilogue ----
+  char* C = static_cast<char*>(p.C);
+  const int colw = lane & 15;
+  if constexpr (!SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const long long col = (long long)t.nt * BN + j * 16 + colw;
+        if (col >= p.N) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int r = t.row0 + wave * TM + i * 16 + q * 4 + v;
+          if (r >= t.row1) continue;
+          if (EPI == QEPI_STORE_F32) reinterpret_cast<float*>(C + r * p.c_pitch)[col] = acc[i][j][v];
+          else reinterpret_cast<uint16_t*>(C + r * p.c_pitch)[col] = f32_to_bf16(acc[i][j][v]);
+        }
+      }
+  } else {
+    constexpr int HF = FN / 2;             // h fragments: 8 x 16 = 128 columns
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = t.row0 + wave * TM + i * 16 + q * 4 + v;
+        const bool live = r < t.row1;       // uniform per 16-lane group
+        float h[HF];
+#pragma unroll
+        for (int j = 0; j < HF; ++j) h[j] = silu_fast(acc[i][j][v]) * acc[i][j + HF][v];
+        if constexpr (EPI == QEPI_SWIGLU_BF16) {
+          if (!live) continue;
+#pragma unroll
+          for (int j = 0; j < HF; ++j) {
+            const long long col = (long long)t.nt * (BN / 2) + j * 16 + colw;
+            if (col < p.N) reinterpret_cast<uint16_t*>(C + r * p.c_pitch)[col] = f32_to_bf16(h[j]);
+          }
+        } else if constexpr (!MX) {
+          // fp8 h: one 1 x 128 block per row per tile (the 128 h-columns of this tile)
+          float amax = 0.0f;
+#pragma unroll
+          for (int j = 0; j < HF; ++j) amax = fmaxf(amax, fabsf(h[j]));
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+          const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+          if (!live) continue;
+          uint8_t* crow = reinterpret_cast<uint8_t*>(C + r * p.c_pitch);
+#pragma unroll
+          for (int j = 0; j < HF; ++j) {
+            const long long col = (long long)t.nt * (BN / 2) + j * 16 + colw;
+            crow[col] = e4m3_rne_sat(h[j] / sc);
+          }
+          if (colw == 0)
+            reinterpret_cast<float*>(p.C_scales)[(long long)r * (p.N / 128) + t.nt] = sc;
+        } else {
+          // MXFP4 h: four 1 x 32 groups per row (fragments 2g, 2g+1)
+          uint8_t* crow = reinterpret_cast<uint8_t*>(C + r * p.c_pitch);
+#pragma unroll
+          for (int g = 0; g < HF / 2; ++g) {
+            float amax = fmaxf(fabsf(h[2 * g]), fabsf(h[2 * g + 1]));
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const int e = mx_shared_exp(amax);
+            const float mul = ldexpf(1.0f, -e);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const uint32_t code = e2m1_rne_sat(h[2 * g + hh] * mul);
+              const uint32_t other = __shfl_xor(code, 1, 64);     // neighbouring column
+              const long long col = (long long)t.nt * (BN / 2) + (2 * g + hh) * 16 + colw;
+              if (live && (colw & 1) == 0) crow[col / 2] = static_cast<uint8_t>(code | (other << 4));
+            }
+            if (live && colw == 0)
+              reinterpret_cast<uint8_t*>(p.C_scales)[(long long)r * (p.N / 32) + (t.nt * (BN / 2)) / 32 + g] =
+                  static_cast<uint8_t>(e + 127);
+          }
+        }
+      }
+  }
+}
+
+namespace {
+
+template <int FMT, int EPI>
+hipError_t run_q(const GemmArgs& a, hipStream_t s) {
+  constexpr int BM = 128, BN = 256, S = 3;
+  constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
+  Grid g = make_grid(a, BM, SWIGLU ? BN / 2 : BN, 8, 64);
+  if (g.total == 0) return hipSuccess;
+  const size_t lds = (size_t)S * (BM + BN) * 128;
+  gemm_q_kernel<FMT, EPI><<<dim3(g.blocks), dim3(256), lds, s>>>(a, g.n_tiles, g.x_tiles, g.span,
+                                                                  g.total, g.gm);
+  return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t run_q_fmt(const GemmArgs& a, hipStream_t s) {
+  if (a.epilogue == MOE_EPI_SWIGLU) {
+    if (a.out_dtype == FMT) return run_q<FMT, QEPI_SWIGLU_Q>(a, s);
+    if (a.out_dtype == MOE_BF16) return run_q<FMT, QEPI_SWIGLU_BF16>(a, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.out_dtype == MOE_F32) return run_q<FMT, QEPI_STORE_F32>(a, s);
+  if (a.out_dtype == MOE_BF16) return run_q<FMT, QEPI_STORE_BF16>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm_q(const GemmArgs& a, hipStream_t s) {
+  if (a.dtype == MOE_FP8_E4M3) return run_q_fmt<MOE_FP8_E4M3>(a, s);
+  if (a.dtype == MOE_MXFP4) return run_q_fmt<MOE_MXFP4>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

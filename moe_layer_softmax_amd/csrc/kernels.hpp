@@ -37,6 +37,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// block-scaled fp8 / MXFP4 grouped GEMM (A and B in a.dtype)
+hipError_t launch_gemm_q(const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_topk(int T, int E, int k, int scoring, int renormalize, const float* logits,
                        int32_t* ids, float* w, hipStream_t s);

@@ -4,6 +4,8 @@ import numpy as np
 import torch
 
 import moe_inputs as mi
+import moe_layer_softmax_amd as moe
+import oracle
 from moe_inputs import gen
 
 DEV = "cuda"
@@ -52,3 +54,55 @@ def rel_err(gpu, ref):
 
 def tol_for(fmt):
     return 6e-2 if fmt in (mi.FMT_FP8, mi.FMT_MX4) else 2e-2
+
+
+# ---- quantised formats ------------------------------------------------------------------
+
+FMTS = {"fp8": (moe.MOE_FP8_E4M3, oracle.FP8), "mx4": (moe.MOE_MXFP4, oracle.MX4)}
+E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
+
+
+def gpu_quant(fmt, a, block_rows):
+    """Quantise float32 [G, R, C] on the GPU: (codes, scales) device tensors."""
+    a = np.ascontiguousarray(a, np.float32)
+    if a.ndim == 2:
+        a = a[None]
+    G, R, C = a.shape
+    src = to_dev(a, torch.float32)
+    if fmt == moe.MOE_FP8_E4M3:
+        codes = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((G, (R + block_rows - 1) // block_rows, C // 128), dtype=torch.float32,
+                             device="cuda")
+    else:
+        codes = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
+    moe.moe_quantize(fmt, moe.MOE_F32, G, R, C, block_rows, src, codes, scales)
+    return codes, scales
+
+
+def oracle_quant(ofmt, a, block_rows):
+    a = np.ascontiguousarray(a, np.float32)
+    if a.ndim == 2:
+        a = a[None]
+    if ofmt == oracle.FP8:
+        qs = [oracle.quant_fp8(a[g], block_rows, 128) for g in range(a.shape[0])]
+        return oracle.Mat(oracle.FP8, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]),
+                          bn=block_rows, bk=128)
+    qs = [oracle.quant_mx4(a[g]) for g in range(a.shape[0])]
+    return oracle.Mat(oracle.MX4, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]))
+
+
+def decode(fmt, codes, scales, cols):
+    """Dequantise GPU-written h (numpy / torch decoders, independent of both sides' code)."""
+    codes = codes.cpu().numpy()
+    scales = scales.cpu().numpy()
+    if fmt == moe.MOE_FP8_E4M3:
+        v = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+        return v * np.repeat(scales.astype(np.float64), 128, axis=1)[:, :cols]
+    lo, hi = codes & 15, codes >> 4
+    v = np.empty((codes.shape[0], cols))
+    v[:, 0::2] = E2M1[lo]
+    v[:, 1::2] = E2M1[hi]
+    return v * np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)[:, :cols]
+
+

@@ -11,7 +11,8 @@ import moe_layer_softmax_amd as moe
 import oracle
 from moe_inputs import gen
 
-from gpu_util import (gamma, io_torch, rel_err, routing_consistent, to_dev, tol_for, topk_numpy)
+from gpu_util import (gamma, gpu_quant, io_torch, oracle_quant, rel_err, routing_consistent, to_dev,
+                      tol_for, topk_numpy)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,9 +32,20 @@ def gpu_layer(wl, x, wr, bias, experts, sh):
     dt = io_torch(wl.io_fmt)
     desc = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
                          wl.renormalize, _FMT[wl.io_fmt], _FMT[wl.fmt])
-    ew = [to_dev(a, dt) for a in experts]
-    shw = None if sh is None else [to_dev(a, dt) for a in sh]
-    weights = moe.make_weights(to_dev(wr, dt), *ew, shared=shw)
+    if wl.fmt in (mi.FMT_FP8, mi.FMT_MX4):
+        # expert weights quantised on the GPU (128 x 128 fp8 blocks / MXFP4 groups of 32)
+        f = _FMT[wl.fmt]
+        eq = [gpu_quant(f, a, 128) for a in experts]
+        shq = None if sh is None else [gpu_quant(f, a, 128) for a in sh]
+        weights = moe.make_weights(to_dev(wr, dt), *(c for c, _ in eq),
+                                   scales=tuple(s for _, s in eq),
+                                   shared=None if shq is None else tuple(c for c, _ in shq),
+                                   shared_scales=(None, None, None) if shq is None
+                                   else tuple(s for _, s in shq))
+    else:
+        ew = [to_dev(a, dt) for a in experts]
+        shw = None if sh is None else [to_dev(a, dt) for a in sh]
+        weights = moe.make_weights(to_dev(wr, dt), *ew, shared=shw)
     out = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
     logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
@@ -48,14 +60,23 @@ def gpu_layer(wl, x, wr, bias, experts, sh):
 
 
 def oracle_layer(wl, x, wr, bias, experts, sh, tok):
-    # h enters the down projection in the expert format (bf16 for the bf16 layers)
-    act = {mi.FMT_F32: oracle.F32, mi.FMT_BF16: oracle.BF16}[wl.fmt]
+    # h enters the down projection in the expert format (bf16 / fp8 1x128 / MXFP4)
+    act = {mi.FMT_F32: oracle.F32, mi.FMT_BF16: oracle.BF16, mi.FMT_FP8: oracle.FP8,
+           mi.FMT_MX4: oracle.MX4}[wl.fmt]
     desc = dict(T=wl.T, H=wl.H, E=wl.E, e0=wl.e0, E_loc=wl.E_loc, I=wl.I, k=wl.k, I_s=wl.I_s,
                 scoring=wl.scoring, renormalize=wl.renormalize, act_fmt=act)
     M = oracle.Mat
-    shared = None if sh is None else tuple(M(oracle.F32, a) for a in sh)
-    return oracle.moe_layer(desc, x, wr, bias, M(oracle.F32, x), *(M(oracle.F32, a) for a in experts),
-                            shared, tok)
+    if wl.fmt in (mi.FMT_FP8, mi.FMT_MX4):
+        # the oracle quantises x (fp8: 128-token x 128-channel blocks; MXFP4: 1 x 32) and the
+        # weights with its own quantisers
+        xa = oracle_quant(act, x, 128)
+        mats = [oracle_quant(act, a, 128) for a in experts]
+        shared = None if sh is None else tuple(oracle_quant(act, a, 128) for a in sh)
+    else:
+        xa = M(oracle.F32, x)
+        mats = [M(oracle.F32, a) for a in experts]
+        shared = None if sh is None else tuple(M(oracle.F32, a) for a in sh)
+    return oracle.moe_layer(desc, x, wr, bias, xa, *mats, shared, tok)
 
 
 def check_layer(wl, n_sample=None, bias_override=None, seed=0):
@@ -92,7 +113,8 @@ def check_layer(wl, n_sample=None, bias_override=None, seed=0):
 
 
 @pytest.mark.parametrize("name,n_sample", [("C1", None), ("C2d", None), ("C3a", 96),
-                                           ("C2p", 48), ("C3b", 64)])
+                                           ("C2p", 48), ("C3b", 64), ("C4d", 64), ("C4p", 48),
+                                           ("C5d", None), ("C5p", 48)])
 def test_layer_workloads(name, n_sample):
     check_layer(mi.WORKLOADS[name], n_sample)
 

@@ -1,0 +1,77 @@
+"""Block-scaled fp8 (e4m3, 128x128 fp32 scales) and MXFP4 (e2m1 + E8M0 per 32) grouped GEMMs
+against the oracle. Each side quantises the same float32 inputs with its own quantiser (the codes
+are checked equal in test_gpu_steps); the GPU GEMM runs on its own codes, the oracle dequantises
+its own."""
+import numpy as np
+import pytest
+import torch
+
+import moe_layer_softmax_amd as moe
+import oracle
+from moe_inputs import gen
+
+from gpu_util import FMTS, decode, gpu_quant, oracle_quant, to_dev
+
+pytestmark = pytest.mark.gpu
+
+@pytest.mark.parametrize("fmt", ["fp8", "mx4"])
+@pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
+@pytest.mark.parametrize("counts", [[0, 37, 130, 1, 9], [300, 140, 0, 513]])
+def test_grouped_gemm_quant(fmt, epi, counts):
+    dfmt, ofmt = FMTS[fmt]
+    rng = np.random.default_rng([len(counts), sum(counts)])
+    K = 512
+    swiglu = epi.startswith("swiglu")
+    N = 256 if swiglu else 384                 # 384: a partial 256-column tile
+    G = len(counts)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(off[-1])
+    max_rows = R + 9
+    T, kk = max(R // 3, 5), 4
+    x = gen.bf16_round(rng.standard_normal((T, K)).astype(np.float32))
+    a_rows = rng.integers(0, T * kk, size=max_rows).astype(np.int32)
+    B = (rng.standard_normal((G, N, K)) * 0.05).astype(np.float32)
+    B2 = (rng.standard_normal((G, N, K)) * 0.05).astype(np.float32)
+    a_block = 128 if fmt == "fp8" else 1
+    xq, xs = gpu_quant(dfmt, x, a_block)
+    bq, bs = gpu_quant(dfmt, B, 128)
+    b2q, b2s = gpu_quant(dfmt, B2, 128)
+    out_dt = {"store_f32": moe.MOE_F32, "store_bf16": moe.MOE_BF16, "swiglu_bf16": moe.MOE_BF16,
+              "swiglu_q": dfmt}[epi]
+    g = moe.moe_gemm_desc(G, max_rows, K, N, dfmt, moe.MOE_EPI_SWIGLU if swiglu else moe.MOE_EPI_STORE,
+                          out_dt, kk, a_block)
+    C_scales = None
+    if epi == "swiglu_q":
+        C = torch.zeros((max_rows, N if fmt == "fp8" else N // 2), dtype=torch.uint8, device="cuda")
+        C_scales = torch.zeros((max_rows, N // 128) if fmt == "fp8" else (max_rows, N // 32),
+                               dtype=torch.float32 if fmt == "fp8" else torch.uint8, device="cuda")
+    else:
+        C = torch.full((max_rows, N), 1024.0,
+                       dtype=torch.float32 if out_dt == moe.MOE_F32 else torch.bfloat16, device="cuda")
+    moe.moe_grouped_gemm(g, xq[0], xs[0], to_dev(a_rows, torch.int32), bq, bs,
+                         b2q if swiglu else None, b2s if swiglu else None,
+                         to_dev(off, torch.int32), C, C_scales)
+    torch.cuda.synchronize()
+    A = oracle_quant(ofmt, x, a_block)
+    ref = oracle.grouped_gemm(off, A, oracle_quant(ofmt, B, 128),
+                              oracle_quant(ofmt, B2, 128) if swiglu else None,
+                              a_rows=a_rows, a_row_div=kk)
+    rms = np.sqrt(np.mean(ref ** 2)) if R else 1.0
+    if epi == "swiglu_q":
+        h = decode(dfmt, C[:R], C_scales[:R], N)
+        if fmt == "fp8":
+            # within one e4m3 step of the block's scale grid (fp32 vs fp64 h may round differently)
+            s = np.repeat(C_scales[:R].cpu().numpy().astype(np.float64), 128, axis=1)
+            assert np.all(np.abs(h - ref) <= 2.0 ** -3 * np.abs(ref) + s * 2.0 ** -8)
+        else:
+            unit = np.repeat(2.0 ** (C_scales[:R].cpu().numpy().astype(np.int64) - 127), 32, axis=1)
+            assert np.all(np.abs(h - ref) <= 2.0 * unit + 1e-30)
+    else:
+        Cg = C.float().cpu().numpy()
+        err = np.abs(Cg[:R] - ref)
+        if out_dt == moe.MOE_F32:
+            # fp32 accumulation bound gamma_K * sum|a b| with u = 2^-23 is ~1e-3 rms at K = 512
+            assert err.max() <= 2e-3 * rms, err.max() / rms
+        else:
+            assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-3 * rms), err.max() / rms
+        assert np.all(Cg[R:] == 1024.0)
