@@ -61,10 +61,44 @@ __device__ __forceinline__ void dma_16b(const void* g, void* lds_region) {
   __builtin_amdgcn_global_load_lds(g, lds_region, 16, 0, 0);
 #endif
 }
+// The two inline-assembly forms below write M0, which the compiler reserves. That is sound here
+// because nothing in these kernels relies on a compiler-set M0 across them: the only M0 user is the
+// direct-to-LDS load, and the compiler sets M0 immediately before each one it emits itself.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// The same load written as inline assembly. The compiler's wait-count pass does not see it, so it
+// neither treats it as an LDS access (which makes every LDS-read wait in a loop a full drain) nor
+// counts it: the caller owns every vmcnt wait for these loads. M0 holds the wave's LDS base; the
+// s_nop covers the M0-write-to-use hazard.
+__device__ __forceinline__ void dma_16b_asm(const void* g, const void* lds_region) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds_region)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(base), "v"(g) : "memory", "m0");
+#endif
+}
+// The same load with a scalar base address and a 32-bit per-lane byte offset, and the LDS target
+// given as a wave-uniform byte address for M0. A K loop then advances the scalar base only, so the
+// loads cost no per-lane address arithmetic (vector ALU instructions in the loop take issue cycles
+// from the MFMAs of the same SIMD).
+__device__ __forceinline__ void dma_16b_sbase(const void* sbase, unsigned voff, unsigned lds_addr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr), "v"(voff), "s"(sbase) : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
 // s_waitcnt vmcnt(0): all of this wave's vector memory loads (including LDS DMA) have completed
 __device__ __forceinline__ void wait_vmem() {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_s_waitcnt(0x0F70);
+#endif
+}
+// s_waitcnt lgkmcnt(0): all of this wave's LDS (and scalar memory) reads have completed
+__device__ __forceinline__ void wait_lgkm() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_s_waitcnt(0xC07F);
 #endif
 }
 // Workgroup barrier for LDS filled by dma_16b. __syncthreads() carries a workgroup memory fence,

@@ -18,163 +18,22 @@
 //     by row so MFMA fragment reads (ds_read_b128) are bank-conflict free.
 //   * Epilogues: STORE (optional per-column bias, fp32 or bf16 out) and SWIGLU, where each wave
 //     holds matching gate and up columns so h = silu(g) * u is formed in registers.
+#include <type_traits>
+
 #include "gemm_common.hpp"
 #include "quant_dev.hpp"
 
 namespace moe {
 
-template <int BM, int BN, int WM, int WN, int MI, int BK, int S, bool SWIGLU, bool OUT_F32>
-__global__ void __launch_bounds__(WM * WN * 64)
-gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
-  using Geo = SliceGeo<BK>;
-  constexpr int NW = WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN;
-  constexpr int FM = TM / MI, FN = TN / MI;
-  constexpr int MK = (MI == 32) ? 16 : 32;
-  constexpr int KS = BK / MK;
-  constexpr int RPI = Geo::kRowsPerIns;
-  constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
-  constexpr int INS = A_INS + B_INS;                   // DMA instructions per wave per K-step
-  constexpr int STAGE = (BM + BN) * BK;                // uint16 per LDS stage
-  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows per wave region");
-  static_assert(KS % 2 == 0, "fragment double buffer assumes an even number of substeps");
-  static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
-  static_assert(S >= 3 && (S - 2) * INS < 64, "pipeline depth");
-
-  // dynamic LDS (S * STAGE uint16), written only by the DMA loads
-  extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
-
-  const int logical = xcd_remap(blockIdx.x, span);
-  if (logical >= total) return;
-  Tile t;
-  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int K = p.K;
-  const int nk = K / BK;
-  const int lrow = lane / Geo::kChunks;
-
-  const char* a_src[A_INS];
-#pragma unroll
-  for (int j = 0; j < A_INS; ++j) {
-    const int r = (j * NW + wave) * RPI + lrow;
-    const int lch = (lane % Geo::kChunks) ^ Geo::swz(r);
-    a_src[j] = static_cast<const char*>(p.A) + a_src_row(p, t, t.row0 + r) * p.a_pitch + lch * 16;
-  }
-  const char* b_src[B_INS];
-#pragma unroll
-  for (int j = 0; j < B_INS; ++j) {
-    const int rb = (j * NW + wave) * RPI + lrow;
-    const int lch = (lane % Geo::kChunks) ^ Geo::swz(rb);
-    long long n;
-    const char* base = t.B;
-    if (SWIGLU) {
-      const int within = rb % TN;
-      const int half = TN / 2;
-      n = (long long)t.nt * (BN / 2) + (rb / TN) * half + (within % half);
-      if (within >= half) base = t.B2;
-    } else {
-      n = (long long)t.nt * BN + rb;
-    }
-    if (n >= p.N) n = p.N - 1;             // columns past N: read a valid row, never stored
-    b_src[j] = base + n * (long long)K * 2 + lch * 16;
-  }
-
-  // K-step kt's slices into stage kt % S (steps past the end issue nothing)
-  auto issue = [&](int kt) {
-    if (kt >= nk) return;
-    uint16_t* la = lds + (kt % S) * STAGE;
-    uint16_t* lb = la + BM * BK;
-#pragma unroll
-    for (int j = 0; j < A_INS; ++j)
-      dma_16b(a_src[j] + (long long)kt * Geo::kRowBytes, la + (j * NW + wave) * RPI * BK);
-#pragma unroll
-    for (int j = 0; j < B_INS; ++j)
-      dma_16b(b_src[j] + (long long)kt * Geo::kRowBytes, lb + (j * NW + wave) * RPI * BK);
-  };
-
-  bf16x8 fa[2][FM], fb[2][FN];
-  auto lfrag = [&](int stage, int s, int slot) {
-    const uint16_t* la = lds + stage * STAGE;
-    const uint16_t* lb = la + BM * BK;
-    const int cidx = s * (MK / 8) + lane / MI;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = wm * TM + i * MI + (lane % MI);
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(la + r * BK + ((cidx ^ Geo::swz(r)) * 8));
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int r = wn * TN + j * MI + (lane % MI);
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(lb + r * BK + ((cidx ^ Geo::swz(r)) * 8));
-    }
-  };
-
-  f32x16 acc32[MI == 32 ? FM : 1][MI == 32 ? FN : 1];
-  f32x4 acc16[MI == 16 ? FM : 1][MI == 16 ? FN : 1];
-  if constexpr (MI == 32) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc32[i][j] = f32x16{};
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc16[i][j] = f32x4{};
-  }
-
-  // prologue: steps 0 .. S-2 in flight, wait for step 0
-#pragma unroll
-  for (int q = 0; q < S - 1; ++q) issue(q);
-  if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
-  else wait_vmem();
-  barrier_lds();
-  lfrag(0, 0, 0);
-
-  // Step kt: substeps 0..KS-2 on fragments already in registers (each prefetching the next
-  // substep's); then wait for step kt+1's slices and pass the barrier while those MFMAs drain
-  // (the barrier also releases stage kt-1, read during step kt-1, for step kt+S-1's loads); the
-  // last substep's MFMAs then overlap the reads of step kt+1's first fragments.
-  for (int kt = 0; kt < nk; ++kt) {
-    const int stage = kt % S;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const int slot = s & 1;
-      if (s == KS - 1) {
-        if (kt + S - 2 < nk) wait_vmem_n<(S - 3) * INS>();   // step kt+1 landed
-        else wait_vmem();
-        barrier_lds();
-        issue(kt + S - 1);
-        if (kt + 1 < nk) lfrag((kt + 1) % S, 0, slot ^ 1);
-      } else {
-        lfrag(stage, s + 1, slot ^ 1);
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if constexpr (MI == 32)
-            acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc32[i][j], 0, 0, 0);
-          else
-            acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc16[i][j], 0, 0, 0);
-        }
-#pragma unroll
-      for (int q = 0; q < FM + FN; ++q) {
-        MOE_SCHED_GROUP(0x100, 1);
-        MOE_SCHED_GROUP(0x008, (FM * FN) / (FM + FN) > 0 ? (FM * FN) / (FM + FN) : 1);
-      }
-      MOE_SCHED_GROUP(0x008, FM * FN);
-    }
-  }
-
-// ---- epilogue ----
+// Write one wave's accumulators (FM x FN fragments of MI x MI, the wave's TM x TN block of the
+// BM x BN tile at wave position (wm, wn)). SWIGLU: fragment j < FN/2 holds gate columns and
+// j + FN/2 the matching up columns; h = silu(g) * u is stored. STORE: optional per-column bias.
+// Rows past the tile's end and columns past N are skipped.
+template <int MI, int FM, int FN, int TM, int TN, int BN, bool SWIGLU, bool OUT_F32, class AccAt>
+__device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t, int wm, int wn,
+                                           AccAt acc_at) {
   constexpr int VPF = (MI == 32) ? 16 : 4;
-  auto acc_at = [&](int i, int j, int v) -> float {
-    if constexpr (MI == 32) return acc32[i][j][v];
-    else return acc16[i][j][v];
-  };
+  const int lane = lane_id();
   auto row_of = [&](int v) -> int {
     if constexpr (MI == 32) return (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
     else return (lane / 16) * 4 + v;
@@ -215,6 +74,343 @@ gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total,
         }
       }
   }
+}
+
+// Per-wave direct-to-LDS load plan of one BM x BN tile. Slot j of A moves tile rows
+// (j * NW + wave) * RPI ... + RPI - 1 of a K-slice (RPI rows per wave-wide instruction, lanes on
+// 16-byte chunks, swizzled), likewise slot j of B (SWIGLU: the B rows of each wave column are TN/2
+// gate rows then TN/2 up rows; a slot never straddles the two). Each slot has a wave-uniform base
+// pointer and a fixed per-lane byte offset, so a K-step only moves the base (scalar arithmetic).
+// If some lane's offset needs more than 32 bits the wave uses the 64-bit per-lane address form.
+template <class Geo, int BM, int BN, int TN, int NW, bool SWIGLU>
+struct LoadPlan {
+  static constexpr int RPI = Geo::kRowsPerIns;
+  static constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
+  static constexpr int BK = Geo::kRowBytes / 2;
+  const char* a_base;
+  const char* b_base[B_INS];
+  unsigned long long a_off[A_INS], b_off[B_INS];
+  bool wide;
+
+  __device__ __forceinline__ void init(const GemmArgs& p, const Tile& t, int wave, int lane) {
+    const int lrow = lane / Geo::kChunks;
+    a_base = static_cast<const char*>(p.A);
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) {
+      const int r = (j * NW + wave) * RPI + lrow;
+      const int lch = (lane % Geo::kChunks) ^ Geo::swz(r);
+      a_off[j] = (unsigned long long)a_src_row(p, t, t.row0 + r) * p.a_pitch + lch * 16;
+    }
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+      const int rb0 = (j * NW + wave) * RPI;           // wave-uniform
+      const int rb = rb0 + lrow;
+      const int lch = (lane % Geo::kChunks) ^ Geo::swz(rb);
+      long long n;
+      if (SWIGLU) {
+        const int half = TN / 2;
+        b_base[j] = (rb0 % TN) >= half ? t.B2 : t.B;
+        n = (long long)t.nt * (BN / 2) + (rb / TN) * half + (rb % TN) % half;
+      } else {
+        b_base[j] = t.B;
+        n = (long long)t.nt * BN + rb;
+      }
+      if (n >= p.N) n = p.N - 1;           // columns past N: read a valid row, never stored
+      b_off[j] = (unsigned long long)n * p.K * 2 + lch * 16;
+    }
+    bool w = false;
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) w |= (a_off[j] >> 32) != 0;
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) w |= (b_off[j] >> 32) != 0;
+    wide = __ballot(w) != 0;
+  }
+
+  // K-slice starting at byte kb of every row into the stage at `stage` (ring pointer) whose LDS
+  // byte address is st
+  template <bool WIDE>
+  __device__ __forceinline__ void issue(long long kb, uint16_t* stage, unsigned st, int wave) const {
+#pragma unroll
+    for (int j = 0; j < A_INS; ++j) {
+      const int row = (j * NW + wave) * RPI;
+      if constexpr (WIDE) dma_16b_asm(a_base + a_off[j] + kb, stage + row * BK);
+      else dma_16b_sbase(a_base + kb, static_cast<unsigned>(a_off[j]), st + row * BK * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < B_INS; ++j) {
+      const int row = BM + (j * NW + wave) * RPI;
+      if constexpr (WIDE) dma_16b_asm(b_base[j] + b_off[j] + kb, stage + row * BK);
+      else dma_16b_sbase(b_base[j] + kb, static_cast<unsigned>(b_off[j]), st + row * BK * 2);
+    }
+  }
+};
+
+// A lane's byte offset of its MFMA fragment row inside a stage region for substep s: fragments
+// cover MI-row blocks starting at multiples of 16 rows, where the chunk swizzle repeats, so the
+// offset depends on the lane only (the block adds an immediate).
+template <class Geo, int MI, int MK>
+__device__ __forceinline__ unsigned frag_lane_off(int s, int lane) {
+  constexpr int BK = Geo::kRowBytes / 2;
+  const int r = lane % MI;
+  const int cidx = s * (MK / 8) + lane / MI;
+  return (r * BK + ((cidx ^ Geo::swz(r)) * 8)) * 2;
+}
+
+template <int BM, int BN, int WM, int WN, int MI, int BK, int S, bool SWIGLU, bool OUT_F32>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
+  using Geo = SliceGeo<BK>;
+  constexpr int NW = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / MI, FN = TN / MI;
+  constexpr int MK = (MI == 32) ? 16 : 32;
+  constexpr int KS = BK / MK;
+  constexpr int RPI = Geo::kRowsPerIns;
+  constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
+  constexpr int INS = A_INS + B_INS;                   // DMA instructions per wave per K-step
+  constexpr int STAGE = (BM + BN) * BK;                // uint16 per LDS stage
+  static_assert(BM % (RPI * NW) == 0 && BN % (RPI * NW) == 0, "tile rows per wave region");
+  static_assert(KS % 2 == 0, "fragment double buffer assumes an even number of substeps");
+  static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
+  static_assert(S >= 3 && (S - 2) * INS < 64, "pipeline depth");
+
+  // dynamic LDS (S * STAGE uint16), written only by the DMA loads
+  extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
+
+  const int logical = xcd_remap(blockIdx.x, span);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
+
+  const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int nk = p.K / BK;
+
+  LoadPlan<Geo, BM, BN, TN, NW, SWIGLU> lp;
+  lp.init(p, t, wave, lane);
+  const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds));
+  // K-step kt's slices into stage kt % S (steps past the end issue nothing)
+  auto issue = [&](int kt, auto wide_tag) {
+    if (kt >= nk) return;
+    lp.template issue<decltype(wide_tag)::value>((long long)kt * Geo::kRowBytes, lds + (kt % S) * STAGE,
+                                                 lds0 + (kt % S) * (STAGE * 2), wave);
+  };
+
+  bf16x8 fa[2][FM], fb[2][FN];
+  unsigned lane_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) lane_off[s] = frag_lane_off<Geo, MI, MK>(s, lane);
+  const char* const lds_bytes = reinterpret_cast<const char*>(lds);
+  auto lfrag = [&](int stage, int s, int slot) {
+    const char* lb = lds_bytes + stage * (STAGE * 2) + lane_off[s];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(lb + (wm * TM + i * MI) * BK * 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(lb + (BM + wn * TN + j * MI) * BK * 2);
+  };
+
+  f32x16 acc32[MI == 32 ? FM : 1][MI == 32 ? FN : 1];
+  f32x4 acc16[MI == 16 ? FM : 1][MI == 16 ? FN : 1];
+  if constexpr (MI == 32) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc32[i][j] = f32x16{};
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc16[i][j] = f32x4{};
+  }
+
+  auto k_loop = [&](auto wide_tag) {
+    // prologue: steps 0 .. S-2 in flight, wait for step 0
+  #pragma unroll
+    for (int q = 0; q < S - 1; ++q) issue(q, wide_tag);
+    if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
+    else wait_vmem();
+    barrier_lds();
+    lfrag(0, 0, 0);
+    wait_lgkm();   // nothing but these reads pending on entry, so the loop can count them in order
+
+    // Step kt: substeps 0..KS-2 on fragments already in registers (each prefetching the next
+    // substep's); then wait for step kt+1's slices and pass the barrier while those MFMAs drain
+    // (the barrier also releases stage kt-1, read during step kt-1, for step kt+S-1's loads); the
+    // last substep's MFMAs then overlap the reads of step kt+1's first fragments.
+    for (int kt = 0; kt < nk; ++kt) {
+      const int stage = kt % S;
+  #pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int slot = s & 1;
+        if (s == KS - 1) {
+          if (kt + S - 2 < nk) wait_vmem_n<(S - 3) * INS>();   // step kt+1 landed
+          else wait_vmem();
+          barrier_lds();
+          issue(kt + S - 1, wide_tag);
+          // unconditional (past the last step it reads a stale stage, never used): a branch here
+          // would make the compiler wait for these reads before the MFMAs below
+          lfrag((kt + 1) % S, 0, slot ^ 1);
+        } else {
+          lfrag(stage, s + 1, slot ^ 1);
+        }
+  #pragma unroll
+        for (int i = 0; i < FM; ++i)
+  #pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            if constexpr (MI == 32)
+              acc32[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][j], acc32[i][j], 0, 0, 0);
+            else
+              acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[slot][i], fb[slot][j], acc16[i][j], 0, 0, 0);
+          }
+        // the next substep's fragment reads go out first, so they have this substep's MFMAs to land
+        MOE_SCHED_GROUP(0x100, FM + FN);
+        MOE_SCHED_GROUP(0x008, FM * FN);
+      }
+    }
+  };
+  if (lp.wide) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
+
+// ---- epilogue ----
+  store_tile<MI, FM, FN, TM, TN, BN, SWIGLU, OUT_F32>(p, t, wm, wn, [&](int i, int j, int v) -> float {
+    if constexpr (MI == 32) return acc32[i][j][v];
+    else return acc16[i][j][v];
+  });
+}
+
+// ------------------------------------------------------------------------------------------------
+// Ping-pong variant of the 256 x 256 tile (8 waves, each 128 x 64, K-steps of 32).
+//
+// The waves form two groups of four, one wave of each group per SIMD (waves 0-3: tile rows 0-127,
+// waves 4-7: rows 128-255). Between two workgroup barriers one group is in its memory phase
+// (reads all of one K-step's fragments from LDS into registers and issues its share of the DMA for
+// a later step) while the other is in its compute phase (the 16 MFMAs of the K-step it read in its
+// previous phase). Each barrier swaps the roles, so a SIMD's MFMA unit is fed by one wave while
+// its sibling's LDS traffic and waits are hidden, instead of both waves reading, computing and
+// stalling in lockstep.
+//
+// Barrier schedule (b0 after the prologue; group 1 passes one extra barrier b1 first):
+//   group 0: M(0) b1 C(0) b2 M(1) b3 C(1) b4 ... M(kt) = (b2kt, b2kt+1), C(kt) = (b2kt+1, b2kt+2)
+//   group 1: b1 M(0) b2 C(0) b3 M(1) ...           M(kt) = (b2kt+1, b2kt+2), C(kt) = (b2kt+2, ...)
+// so both groups pass 2 nk + 1 barriers (group 1 skips the one after its last compute phase).
+//   * stage of step j is read in M(j) by group 0 before b2j+1 and by group 1 before b2j+2 (each
+//     wave drains its LDS reads before the barrier that ends its memory phase);
+//   * the DMA for step j + S - 1 is issued in M(j), after b2j (group 0) or b2j+1 (group 1) --
+//     after the previous user of that stage, step j - 1, was drained at b2j;
+//   * step j + 1 must have landed, from every wave, before b2j+2: group 0 waits for its own share at
+//     the end of C(j), group 1 at the end of M(j); the barrier then publishes it.
+// ------------------------------------------------------------------------------------------------
+__device__ __forceinline__ void phase_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_lds();
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
+template <bool SWIGLU, bool OUT_F32, int S>
+__global__ void __launch_bounds__(512)
+gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
+  constexpr int BM = 256, BN = 256, WN = 4, MI = 32, BK = 32;
+  constexpr int NW = 8, TM = 128, TN = 64, FM = TM / MI, FN = TN / MI, MK = 16, KS = BK / MK;
+  using Geo = SliceGeo<BK>;
+  constexpr int RPI = Geo::kRowsPerIns;
+  constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
+  constexpr int INS = A_INS + B_INS;                   // DMA instructions per wave per K-step
+  constexpr int STAGE = (BM + BN) * BK;                // uint16 per LDS stage
+  static_assert(S >= 3 && (S - 2) * INS < 64, "pipeline depth");
+  static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
+
+  extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
+
+  const int logical = xcd_remap(blockIdx.x, span);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int grp = wave >> 2;                           // wave-uniform (scalar branches below)
+  const int wm = grp, wn = wave & (WN - 1);
+  const int nk = p.K / BK;
+
+  LoadPlan<Geo, BM, BN, TN, NW, SWIGLU> lp;
+  lp.init(p, t, wave, lane);
+  const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds));
+  auto issue = [&](int kt, auto wide_tag) {
+    if (kt >= nk) return;
+    lp.template issue<decltype(wide_tag)::value>((long long)kt * Geo::kRowBytes, lds + (kt % S) * STAGE,
+                                                 lds0 + (kt % S) * (STAGE * 2), wave);
+  };
+  // this wave's share of step kt + 1 has landed (steps up to kt + S - 1 may have been issued)
+  auto wait_next = [&](int kt) {
+    if (kt + S - 1 < nk) wait_vmem_n<(S - 2) * INS>();
+    else wait_vmem();
+  };
+
+  // Fragment reads: every fragment row is (32-row block) + lane % 32, and the swizzle only depends
+  // on row % 32, so a lane's byte offset is a per-substep constant plus an immediate per fragment.
+  bf16x8 fa[KS][FM], fb[KS][FN];
+  unsigned lane_off[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) lane_off[s] = frag_lane_off<Geo, MI, MK>(s, lane);
+  const char* const lds_bytes = reinterpret_cast<const char*>(lds);
+  auto read_step = [&](int stage) {
+    const char* sb = lds_bytes + stage * (STAGE * 2);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const char* lb = sb + lane_off[s];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[s][i] = *reinterpret_cast<const bf16x8*>(lb + (wm * TM + i * MI) * BK * 2);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[s][j] = *reinterpret_cast<const bf16x8*>(lb + (BM + wn * TN + j * MI) * BK * 2);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  // The K loop, instantiated for the 32-bit-offset and the 64-bit-address load forms.
+  auto k_loop = [&](auto wide_tag) {
+    // prologue: steps 0 .. S-2 in flight; step 0 published by b0
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q) issue(q, wide_tag);
+    if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
+    else wait_vmem();
+    phase_barrier();                                   // b0
+    if (grp == 1) phase_barrier();                     // b1 (group 1 starts one phase later)
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // memory phase
+      read_step(kt % S);
+      issue(kt + S - 1, wide_tag);
+      if (grp == 1) wait_next(kt);
+      wait_lgkm();
+      phase_barrier();
+      // compute phase
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+      if (grp == 0) wait_next(kt);
+      if (grp == 0 || kt + 1 < nk) phase_barrier();
+    }
+  };
+  if (lp.wide) k_loop(std::true_type{});
+  else k_loop(std::false_type{});
+
+  store_tile<MI, FM, FN, TM, TN, BN, SWIGLU, OUT_F32>(p, t, wm, wn,
+                                                      [&](int i, int j, int v) { return acc[i][j][v]; });
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -305,6 +501,7 @@ namespace {
 // (12 distinct slices per 32 tiles).
 constexpr int kTileGroupM = 8;
 constexpr int kTileSpan = 64;
+constexpr int kPPStages = 5;
 
 template <int BM, int BN, int WM, int WN, int MI, int BK, int S>
 hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) {
@@ -317,6 +514,25 @@ hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) 
 #define MOE_RUN(SWI, F32)                                                                    \
   gemm_bf16_pipe_kernel<BM, BN, WM, WN, MI, BK, S, SWI, F32><<<grid, block, lds_bytes, s>>>(  \
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm)
+  if (sw && f32) MOE_RUN(true, true);
+  else if (sw) MOE_RUN(true, false);
+  else if (f32) MOE_RUN(false, true);
+  else MOE_RUN(false, false);
+#undef MOE_RUN
+  return hipGetLastError();
+}
+
+template <int S>
+hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
+  const bool sw = a.epilogue == MOE_EPI_SWIGLU;
+  Grid g = make_grid(a, 256, sw ? 128 : 256, gm, span);
+  if (g.total == 0) return hipSuccess;
+  dim3 grid(g.blocks), block(512);
+  const bool f32 = a.out_dtype == MOE_F32;
+  const size_t lds_bytes = (size_t)S * (256 + 256) * 32 * sizeof(uint16_t);
+#define MOE_RUN(SWI, F32)                                                                        \
+  gemm_bf16_pp_kernel<SWI, F32, S><<<grid, block, lds_bytes, s>>>(a, g.n_tiles, g.x_tiles, g.span, \
+                                                                  g.total, g.gm)
   if (sw && f32) MOE_RUN(true, true);
   else if (sw) MOE_RUN(true, false);
   else if (f32) MOE_RUN(false, true);
@@ -348,10 +564,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const long long per_group = groups ? rows / groups : rows;
     const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
     if (per_group >= 512 && n_full >= 256) {
-      // 256 x 256 tiles, K-steps of 32 through LDS stages of 32 KB. SwiGLU: 8 waves (2 per SIMD),
-      // each 128 x 64, 4 stages; plain store: 16 waves, each 64 x 64, 5 stages.
-      if (a.epilogue == MOE_EPI_SWIGLU)
-        return run_bf16<256, 256, 2, 4, 32, 32, 4>(a, s, kTileGroupM, kTileSpan);
+      // 256 x 256 tiles, K-steps of 32 through 5 LDS stages of 32 KB. SwiGLU (K = hidden size,
+      // long K loops): ping-pong schedule of 8 waves of 128 x 64. Plain store (the down projection,
+      // short K): 16 waves of 64 x 64 (measured a few percent faster there than ping-pong).
+      if (a.epilogue == MOE_EPI_SWIGLU) return run_bf16_pp<kPPStages>(a, s, kTileGroupM, kTileSpan);
       return run_bf16<256, 256, 4, 4, 32, 32, 5>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);

@@ -231,7 +231,19 @@ def test_grouped_gemm_bf16(counts, swiglu, gather):
     assert np.all(Cg[R:] == 1024.0)                      # rows outside every group untouched
 
 
-@pytest.mark.parametrize("counts,K,N", [([3, 70, 0, 5], 4096, 128), ([600, 40], 256, 1536)])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("N", [320, 384])
+def test_grouped_gemm_bf16_large_tiles_ragged_n(swiglu, N):
+    # enough rows per group for the 256 x 256 tiles; N leaves a partial last n-tile
+    Cg, ref, R = _gemm_case([1500, 300, 0, 701], K=1024, N=N, swiglu=swiglu, gather=swiglu,
+                            out_f32=False)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.all(np.abs(Cg[:R] - ref) <= 2 ** -8 * np.abs(ref) + 1e-3 * rms)
+    assert np.all(Cg[R:] == 1024.0)
+
+
+@pytest.mark.parametrize("counts,K,N", [([3, 70, 0, 5], 4096, 128), ([600, 40], 256, 1536),
+                                        ([1500, 300, 0, 701], 1536, 4096)])
 def test_grouped_gemm_bf16_f32_out(counts, K, N):
     Cg, ref, R = _gemm_case(counts, K=K, N=N, swiglu=False, gather=False, out_f32=True)
     rms = np.sqrt(np.mean(ref ** 2))
