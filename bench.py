@@ -36,7 +36,54 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--profile-only", action="store_true",
                    help="only the timed moe_layer steps (for profilers)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
     return p.parse_args()
+
+
+# Source files of the grouped GEMM kernels; HBM counters taken on an older version of them are
+# not reported.
+GEMM_SOURCES = ["moe_layer_softmax_amd/csrc/gemm.hip", "moe_layer_softmax_amd/csrc/gemm_common.hpp",
+                "moe_layer_softmax_amd/csrc/common.hpp", "moe_layer_softmax_amd/csrc/kernels.hpp",
+                "moe_layer_softmax_amd/csrc/quant_dev.hpp", "include/moe.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the factor that maps the same counter
+    on a copy of known size to its true bytes), or None if the kernel sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    rd = t["fetch_kib_per_dispatch"] * 1024.0 * t["fetch_factor"]
+    wr = t["write_kib_per_dispatch"] * 1024.0 * t["write_factor"]
+    return rd, wr
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
 
 
 class Layer:
@@ -172,6 +219,9 @@ def main():
               "multi-GPU path; the whole-job value for N=1 is the one-GPU throughput.",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import moe_inputs as mi
 
@@ -197,6 +247,7 @@ def main():
     flops_gu = 4.0 * R * wl.H * wl.I
     achieved = flops_gu / (steps_ms["gemm_gate_up"] * 1e-3) / 1e12
     layer_tf = layer_flops(wl, R) / (ms_per_step * 1e-3) / 1e12
+    traffic = measured_traffic() if args.workload == "C2p" else None
 
     result = {
         "metric": "MoE-layer tokens/s + % of MFMA peak (prefill) / % HBM BW (decode), 1 MI355X",
@@ -220,7 +271,10 @@ def main():
         "roofline": {"kernel": "grouped GEMM gate/up + SwiGLU (moe_grouped_gemm)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "flops_per_launch": flops_gu,
+                     "traffic": None if traffic is None else round(sum(traffic)),
+                     "traffic_read_bytes": None if traffic is None else round(traffic[0]),
+                     "traffic_write_bytes": None if traffic is None else round(traffic[1]),
+                     "flops_per_launch": flops_gu,
                      "avg_launch_ms": round(steps_ms["gemm_gate_up"], 4)},
         "steps_ms": {k: round(v, 4) for k, v in steps_ms.items()},
     }
