@@ -113,9 +113,13 @@ typedef struct {
  * If x == NULL: logits[T,E] (fp32) are read as given and w_router is ignored.
  * topk_ids[T,k] (int32, global ids, rank order: topk_ids[t,0] is the largest logit; equal values
  * rank the lower id first; -0 equals +0) and topk_w[T,k] (fp32). The selection is made on exactly
- * the fp32 values in `logits`. bias[E] (fp32) may be NULL. Pointers: 16-byte aligned. */
+ * the fp32 values in `logits`. bias[E] (fp32) may be NULL. Pointers: 16-byte aligned.
+ * ws: moe_route_workspace_bytes(d) bytes of device scratch (the K-split partial sums of a
+ * few-token bf16 router); may be NULL when that size is 0 or x is NULL, else MOE_ERR_WORKSPACE. */
 moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,
-                     float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream);
+                     float* logits, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+size_t moe_route_workspace_bytes(const moe_desc* d);
 
 /* ---- dispatch (count, offsets, unique row per local slot, copy) ------------------------------
  * counts[E_loc]: local slots per expert. offsets[E_loc+1]: exclusive prefix sum, offsets[E_loc] = R.

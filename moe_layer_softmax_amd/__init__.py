@@ -55,7 +55,9 @@ _D = ctypes.POINTER(moe_desc)
 _lib.moe_status_str.restype = ctypes.c_char_p
 _lib.moe_status_str.argtypes = [ctypes.c_int]
 _lib.moe_last_hip_error.restype = ctypes.c_int32
-_lib.moe_route.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P]
+_lib.moe_route.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.moe_route_workspace_bytes.argtypes = [_D]
+_lib.moe_route_workspace_bytes.restype = ctypes.c_size_t
 _lib.moe_permute.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
 _lib.moe_permute_workspace_bytes.argtypes = [_D]
 _lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
@@ -100,9 +102,15 @@ def make_desc(T, H, E, e0, E_loc, I, k, I_s=0, scoring=MOE_SOFTMAX, renormalize=
                     expert_dtype)
 
 
-def moe_route(d, x, w_router, bias, logits, topk_ids, topk_w, stream=None):
+def moe_route_workspace_bytes(d):
+    return _lib.moe_route_workspace_bytes(ctypes.byref(d))
+
+
+def moe_route(d, x, w_router, bias, logits, topk_ids, topk_w, stream=None, ws=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(_lib.moe_route(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits),
-                          _ptr(topk_ids), _ptr(topk_w), _stream(stream)), "moe_route")
+                          _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)),
+           "moe_route")
 
 
 def moe_permute_workspace_bytes(d):

@@ -70,7 +70,7 @@ moe_status check_desc(const moe_desc* d) {
   // the router and the expert GEMMs read 128-byte row slices
   const int kalign = d->io_dtype == MOE_F32 ? 16 : 64;
   if (d->H % kalign) return MOE_ERR_INVALID_ARG;
-  if (d->H % 8) return MOE_ERR_INVALID_ARG;                 // combine: 8 columns per thread
+  if (d->H % 8) return MOE_ERR_INVALID_ARG;                 // combine: 4-column vectors
   return MOE_OK;
 }
 
@@ -102,9 +102,15 @@ long long scale_bytes(int dt, long long N, long long K) {
   return 0;
 }
 
+// the bf16 router kernel takes widths in multiples of 16 experts; other cases run the router as a
+// grouped GEMM with one extra group
+bool router_fast(const moe_desc* d) { return d->io_dtype == MOE_BF16 && d->E % 16 == 0; }
+int route_splits(const moe_desc* d) { return router_fast(d) ? router_splits(d->T, d->H, d->E) : 1; }
+size_t route_ws(const moe_desc* d) { return router_fast(d) ? router_ws_bytes(d->T, d->H, d->E) : 0; }
+
 // ---- layer workspace layout (identical in the size query and in moe_layer) ----------------------
 struct LayerWs {
-  size_t logits, ids, w, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, y, total;
+  size_t logits, ids, w, rpart, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, y, total;
 };
 
 LayerWs layer_ws(const moe_desc* d) {
@@ -117,6 +123,7 @@ LayerWs layer_ws(const moe_desc* d) {
   L.logits = take(T * E * 4);
   L.ids = take(slots * 4);
   L.w = take(slots * 4);
+  L.rpart = take(route_ws(d));
   L.counts = take(d->E_loc * 4);
   L.offsets = take((d->E_loc + 1) * 4);
   L.s2r = take(slots * 4);
@@ -140,6 +147,11 @@ LayerWs layer_ws(const moe_desc* d) {
   L.total = o;
   return L;
 }
+
+// Router logits (+ top-k): logits = x . w_router^T + bias, then the top-k selection and weights.
+// `partial` holds route_ws(d) bytes (the K-split partial sums of a few-token router).
+moe_status run_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                     float* logits, float* partial, int32_t* ids, float* w, hipStream_t s);
 
 // logits = x . w_router^T + bias, as one extra-group GEMM with no routed groups
 moe_status run_router(const moe_desc* d, const void* x, const void* w_router, const float* bias,
@@ -165,6 +177,24 @@ moe_status run_router(const moe_desc* d, const void* x, const void* w_router, co
   return hip_status(launch_gemm(a, s));
 }
 
+moe_status run_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,
+                     float* logits, float* partial, int32_t* ids, float* w, hipStream_t s) {
+  int ns = 1;
+  if (x) {
+    if (router_fast(d)) {
+      ns = route_splits(d);
+      moe_status st = hip_status(launch_router(d->T, d->H, d->E, x, w_router, bias, logits, partial,
+                                               ns, s));
+      if (st != MOE_OK) return st;
+    } else {
+      moe_status st = run_router(d, x, w_router, bias, logits, s);
+      if (st != MOE_OK) return st;
+    }
+  }
+  return hip_status(launch_topk(d->T, d->E, d->k, d->scoring, d->renormalize, logits, partial, ns,
+                                ns > 1 ? bias : nullptr, ids, w, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -182,20 +212,24 @@ const char* moe_status_str(moe_status s) {
 
 int32_t moe_last_hip_error(void) { return g_last_hip_error; }
 
+size_t moe_route_workspace_bytes(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return route_ws(d);
+}
+
 moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,
-                     float* logits, int32_t* topk_ids, float* topk_w, hipStream_t stream) {
+                     float* logits, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
-  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_w) || !ok_opt(x) || !ok_opt(bias))
+  if (!ok_ptr(logits) || !ok_ptr(topk_ids) || !ok_ptr(topk_w) || !ok_opt(x) || !ok_opt(bias) ||
+      !ok_opt(ws))
     return d->T == 0 ? MOE_OK : MOE_ERR_INVALID_ARG;
   if (x && !ok_ptr(w_router)) return MOE_ERR_INVALID_ARG;
   if (d->T == 0) return MOE_OK;
-  if (x) {
-    st = run_router(d, x, w_router, bias, logits, stream);
-    if (st != MOE_OK) return st;
-  }
-  return hip_status(launch_topk(d->T, d->E, d->k, d->scoring, d->renormalize, logits, topk_ids,
-                                topk_w, stream));
+  const size_t need = x ? route_ws(d) : 0;
+  if (need && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
+  return run_route(d, x, w_router, bias, logits, static_cast<float*>(ws), topk_ids, topk_w, stream);
 }
 
 size_t moe_permute_workspace_bytes(const moe_desc* d) {
@@ -373,9 +407,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   const int io = d->io_dtype, dt = d->expert_dtype;
 
   // 1. route
-  st = run_router(d, x, w->w_router, bias, lg, stream);
-  if (st != MOE_OK) return st;
-  st = hip_status(launch_topk(T, d->E, k, d->scoring, d->renormalize, lg, ids, tw, stream));
+  st = run_route(d, x, w->w_router, bias, lg, reinterpret_cast<float*>(base + L.rpart), ids, tw,
+                 stream);
   if (st != MOE_OK) return st;
   // 2. dispatch maps (the rows themselves are gathered inside the gate/up GEMM)
   st = hip_status(launch_permute_maps(T, k, d->e0, d->E_loc, ids, counts, offsets, s2r, r2f,

@@ -113,6 +113,8 @@ __device__ __forceinline__ void barrier_lds() {
 }
 // scheduling hint: `count` instructions of class `mask` (0x008 MFMA, 0x100 DS read, ...) next
 #define MOE_SCHED_GROUP(mask, count) __builtin_amdgcn_sched_group_barrier((mask), (count), 0)
+// no instruction is scheduled across this point
+#define MOE_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

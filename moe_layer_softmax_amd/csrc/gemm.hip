@@ -25,6 +25,9 @@
 
 namespace moe {
 
+// m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel
+constexpr int kStreamGroupM = 8;
+
 // Write one wave's accumulators (FM x FN fragments of MI x MI, the wave's TM x TN block of the
 // BM x BN tile at wave position (wm, wn)). SWIGLU: fragment j < FN/2 holds gate columns and
 // j + FN/2 the matching up columns; h = silu(g) * u is stored. STORE: optional per-column bias.
@@ -414,6 +417,155 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 }
 
 // ------------------------------------------------------------------------------------------------
+// Weight-streaming kernel for decode-sized groups ("Hosting Qwen on Blackwell", section
+// "Decoders": decode is limited by reading the weights from HBM).
+//
+// One wave per workgroup and per tile of 16 * FM C rows x 64 weight rows (SWIGLU: 32 gate rows and
+// the 32 matching up rows). The weights are the MFMA's first operand, so the 16 x 16 accumulator
+// fragment gives each lane four consecutive output columns of one C row. Both operands go from
+// global memory straight into registers -- every weight byte is used by this wave only, so no LDS
+// staging is needed. K advances in pairs of 32-wide steps (128 bytes of every row):
+//   * weights: one load instruction covers 8 rows x 128 contiguous bytes (measured on MI355X: a
+//     weight stream read as 16 rows x 64 bytes per instruction, the MFMA operand's own shape,
+//     reaches ~4.8 TB/s; 8 rows x 128 bytes reaches ~5.8 TB/s). Cross-lane permutes (ds_bpermute,
+//     no LDS storage) then move each 16-byte piece to the lane that holds it in the MFMA operand;
+//   * activations (a few rows, resident in L2): loaded in the operand's layout directly.
+// Pairs are double-buffered: the loads of pair c + 1 are issued before the MFMAs of pair c (the
+// loop is unrolled by two so the register sets alternate statically; scheduling barriers keep the
+// loads where they are written -- left alone, the scheduler sinks each load next to its use).
+// Loads past the end re-read the last pair and rows past the group's end re-read its last row, so
+// every load is unconditional and in bounds. Rows of C beyond 16 * FM per group take further tiles.
+// ------------------------------------------------------------------------------------------------
+template <int FM, bool SWIGLU, bool OUT_F32>
+__global__ void __launch_bounds__(64)
+gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
+  constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
+  // tile order: groups of 8 m-tiles with the m-tile fastest, 8 consecutive tiles per XCD, so the
+  // m-tiles of one group that needs several (the same weights) read them through one L2
+  const int logical = xcd_remap(blockIdx.x, kStreamGroupM);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kStreamGroupM)) return;
+
+  const int lane = lane_id();
+  const int lr = lane & 15, kq = lane >> 4;            // operand row; 16-byte quarter of a step
+  const long long kbytes = (long long)p.K * 2;
+  // weight loads: fragment j, row half h: lane -> row h * 8 + lane / 8, 16-byte chunk lane % 8
+  const char* wp[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = h * 8 + (lane >> 3);
+      long long n;
+      const char* base = t.B;
+      if (SWIGLU) {
+        n = (long long)t.nt * 32 + (j & 1) * 16 + r;
+        if (j >= 2) base = t.B2;
+      } else {
+        n = (long long)t.nt * 64 + j * 16 + r;
+      }
+      if (n >= p.N) n = p.N - 1;                        // columns past N: valid row, never stored
+      wp[j][h] = base + n * kbytes + (lane & 7) * 16;
+    }
+  const char* A = static_cast<const char*>(p.A);
+  const char* ap[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) ap[i] = A + a_src_row(p, t, t.row0 + i * 16 + lr) * p.a_pitch + kq * 16;
+  // operand lane (row lr, quarter kq) of step s holds chunk s * 4 + kq of row lr: loaded by row
+  // half lr / 8, lane (lr % 8) * 8 + s * 4 + kq (byte index for ds_bpermute)
+  const int src0 = ((lr & 7) * 8 + kq) * 4, src1 = src0 + 16;
+  const bool upper = lr >= 8;
+
+  const int np = p.K / 64;                             // pairs of K-steps
+  i32x4 wraw[2][4][2];
+  bf16x8 av[2][FM][2];
+  auto load = [&](int c, int set) {
+    const long long off = (long long)min(c, np - 1) * 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) wraw[set][j][h] = *reinterpret_cast<const i32x4*>(wp[j][h] + off);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) av[set][i][s2] = *reinterpret_cast<const bf16x8*>(ap[i] + off + s2 * 64);
+  };
+  f32x4 acc[4][FM];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{};
+  auto compute = [&](int set) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int src = s2 ? src1 : src0;
+      bf16x8 wf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        i32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lo = __builtin_amdgcn_ds_bpermute(src, wraw[set][j][0][q]);
+          const int hi = __builtin_amdgcn_ds_bpermute(src, wraw[set][j][1][q]);
+          w[q] = upper ? hi : lo;
+        }
+        wf[j] = __builtin_bit_cast(bf16x8, w);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], av[set][i][s2], acc[j][i], 0, 0, 0);
+    }
+  };
+  load(0, 0);
+  int c = 0;
+  for (; c + 1 < np; c += 2) {
+    MOE_SCHED_FENCE();
+    load(c + 1, 1);
+    MOE_SCHED_FENCE();
+    compute(0);
+    MOE_SCHED_FENCE();
+    load(c + 2, 0);
+    MOE_SCHED_FENCE();
+    compute(1);
+  }
+  MOE_SCHED_FENCE();
+  if (c < np) compute(0);                              // odd number of pairs: the last is in set 0
+
+  // acc[j][i][v]: weight row j * 16 + kq * 4 + v of the tile, C row row0 + i * 16 + lr
+  char* C = static_cast<char*>(p.C);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = t.row0 + i * 16 + lr;
+    if (r >= t.row1) continue;
+    char* crow = C + (long long)r * p.c_pitch;
+#pragma unroll
+    for (int j = 0; j < (SWIGLU ? 2 : 4); ++j) {
+      float v4[4];
+      long long col;
+      if (SWIGLU) {
+        col = (long long)t.nt * 32 + j * 16 + kq * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) v4[v] = silu_fast(acc[j][i][v]) * acc[j + 2][i][v];
+      } else {
+        col = (long long)t.nt * 64 + j * 16 + kq * 4;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) v4[v] = acc[j][i][v] + (p.bias ? p.bias[min(col + v, (long long)p.N - 1)] : 0.0f);
+      }
+      if (col >= p.N) continue;                       // N is a multiple of 16: all four or none
+      if (OUT_F32) {
+        *reinterpret_cast<f32x4*>(crow + col * 4) = f32x4{v4[0], v4[1], v4[2], v4[3]};
+      } else {
+        const uint32_t lo = pack_bf16x2(v4[0], v4[1]), hi = pack_bf16x2(v4[2], v4[3]);
+        *reinterpret_cast<uint2*>(crow + col * 2) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
 // fp32 kernel (VALU FMA; the fp32 vector rate equals the fp32 matrix rate on this chip)
 //   64 x 64 tile, BK = 16, 256 threads with 4 x 4 outputs each: rows 4*ty.., columns
 //   {2tx, 2tx+1, 32+2tx, 33+2tx} so that for SWIGLU the gate column c and up column c + 32 sit in
@@ -502,6 +654,8 @@ namespace {
 constexpr int kTileGroupM = 8;
 constexpr int kTileSpan = 64;
 constexpr int kPPStages = 5;
+// weight-streaming tiles of 32 rows up to this many rows per group on average, 64 rows above
+constexpr int kStreamRows32 = 24;
 
 template <int BM, int BN, int WM, int WN, int MI, int BK, int S>
 hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) {
@@ -541,6 +695,23 @@ hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   return hipGetLastError();
 }
 
+template <int FM>
+hipError_t run_bf16_stream(const GemmArgs& a, hipStream_t s) {
+  const bool sw = a.epilogue == MOE_EPI_SWIGLU;
+  Grid g = make_grid(a, 16 * FM, sw ? 32 : 64, kStreamGroupM, kStreamGroupM);
+  if (g.total == 0) return hipSuccess;
+  dim3 grid(g.blocks), block(64);
+  const bool f32 = a.out_dtype == MOE_F32;
+#define MOE_RUN(SWI, F32) \
+  gemm_bf16_stream_kernel<FM, SWI, F32><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.total)
+  if (sw && f32) MOE_RUN(true, true);
+  else if (sw) MOE_RUN(true, false);
+  else if (f32) MOE_RUN(false, true);
+  else MOE_RUN(false, false);
+#undef MOE_RUN
+  return hipGetLastError();
+}
+
 hipError_t run_f32(const GemmArgs& a, hipStream_t s) {
   const bool sw = a.epilogue == MOE_EPI_SWIGLU;
   Grid g = make_grid(a, 64, sw ? 32 : 64);
@@ -571,6 +742,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       return run_bf16<256, 256, 4, 4, 32, 32, 5>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
+    // decode-sized groups: stream the weights once per 32 (or 64) rows of each group
+    if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32))
+      return per_group <= kStreamRows32 ? run_bf16_stream<2>(a, s) : run_bf16_stream<4>(a, s);
     return run_bf16<32, 128, 1, 4, 16, 64, 4>(a, s);
   }
   return hipErrorInvalidValue;

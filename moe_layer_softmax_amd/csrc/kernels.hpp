@@ -40,8 +40,19 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // block-scaled fp8 / MXFP4 grouped GEMM (A and B in a.dtype)
 hipError_t launch_gemm_q(const GemmArgs& a, hipStream_t s);
 
-hipError_t launch_topk(int T, int E, int k, int scoring, int renormalize, const float* logits,
-                       int32_t* ids, float* w, hipStream_t s);
+// Top-k selection and weights. With nsplit > 1, logits[t, e] is first formed as the sum of the
+// router's K-split partials partial[s][t][e] (s ascending) plus bias[e] and written to `logits`.
+hipError_t launch_topk(int T, int E, int k, int scoring, int renormalize, float* logits,
+                       const float* partial, int nsplit, const float* bias, int32_t* ids, float* w,
+                       hipStream_t s);
+// bf16 router logits (E % 16 == 0, H % 64 == 0); nsplit = router_splits(T, H, E). With nsplit > 1
+// the partial sums go to `partial` ([nsplit, T, E] fp32, router_ws_bytes) and the top-k kernel
+// finishes the logits; otherwise logits (+ bias) are written directly.
+int router_splits(int T, int H, int E);
+size_t router_ws_bytes(int T, int H, int E);
+hipError_t launch_router(int T, int H, int E, const void* x, const void* w_router,
+                         const float* bias, float* logits, float* partial, int nsplit,
+                         hipStream_t s);
 
 // Dispatch maps. ws must hold permute_ws_bytes(T*k, E_loc) bytes.
 size_t permute_ws_bytes(long long slots, int E_loc);

@@ -21,15 +21,20 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
   return __uint_as_float(u);
 }
 
+// With nsplit > 1 the logits are first formed from the router's K-split partial sums
+// (partial[s][t][e], s ascending, then the bias) and written to `logits`; the selection then uses
+// exactly the values written.
 template <int VPL>
 __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scoring, int renorm,
-                                                   const float* __restrict__ logits,
+                                                   float* __restrict__ logits,
+                                                   const float* __restrict__ partial, int nsplit,
+                                                   const float* __restrict__ bias,
                                                    int32_t* __restrict__ ids,
                                                    float* __restrict__ w) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;                       // uniform per wave
   const int lane = threadIdx.x & 63;
-  const float* L = logits + (size_t)t * E;
+  float* L = logits + (size_t)t * E;
 
   unsigned long long key[VPL];
   float val[VPL];
@@ -37,12 +42,45 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
   for (int v = 0; v < VPL; ++v) {
     int e = v * 64 + lane;
     if (e < E) {
-      val[v] = L[e];
+      val[v] = nsplit > 1 ? 0.0f : L[e];
       key[v] = (static_cast<unsigned long long>(ordered_bits(val[v])) << 32) |
                static_cast<uint32_t>(~e);
     } else {
       val[v] = 0.0f;
       key[v] = 0ull;                        // below every real key
+    }
+  }
+
+  if (nsplit > 1) {
+    // logits from the router's K-split partials, added in slice order (then the bias); a batch of
+    // partials of every value is loaded before any is added so that their latencies overlap
+    constexpr int BATCH = VPL <= 2 ? 16 : (VPL <= 4 ? 8 : 4);
+    const size_t stride = (size_t)T * E;
+    const float* pp = partial + (size_t)t * E;
+    for (int sp0 = 0; sp0 < nsplit; sp0 += BATCH) {
+      float pv[VPL][BATCH];
+      // unconditional loads (clamped indices): a predicated load becomes a branch that the
+      // wait-count pass must drain at
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int q = 0; q < BATCH; ++q)
+          pv[v][q] = pp[min(sp0 + q, nsplit - 1) * stride + min(v * 64 + lane, E - 1)];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int q = 0; q < BATCH; ++q)
+          if (sp0 + q < nsplit) val[v] = (sp0 + q == 0) ? pv[v][q] : val[v] + pv[v][q];
+    }
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int e = v * 64 + lane;
+      if (e < E) {
+        if (bias) val[v] += bias[e];
+        L[e] = val[v];
+        key[v] = (static_cast<unsigned long long>(ordered_bits(val[v])) << 32) |
+                 static_cast<uint32_t>(~e);
+      }
     }
   }
 
@@ -89,21 +127,163 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
   }
 }
 
-hipError_t launch_topk(int T, int E, int k, int scoring, int renormalize, const float* logits,
-                       int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_topk(int T, int E, int k, int scoring, int renormalize, float* logits,
+                       const float* partial, int nsplit, const float* bias, int32_t* ids, float* w,
+                       hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + 3) / 4), block(256);
   int vpl = (E + 63) / 64;
-  if (vpl <= 1)
-    topk_kernel<1><<<grid, block, 0, s>>>(T, E, k, scoring, renormalize, logits, ids, w);
-  else if (vpl <= 2)
-    topk_kernel<2><<<grid, block, 0, s>>>(T, E, k, scoring, renormalize, logits, ids, w);
-  else if (vpl <= 4)
-    topk_kernel<4><<<grid, block, 0, s>>>(T, E, k, scoring, renormalize, logits, ids, w);
-  else if (vpl <= 8)
-    topk_kernel<8><<<grid, block, 0, s>>>(T, E, k, scoring, renormalize, logits, ids, w);
+#define MOE_TOPK(V) \
+  topk_kernel<V><<<grid, block, 0, s>>>(T, E, k, scoring, renormalize, logits, partial, nsplit, bias, ids, w)
+  if (vpl <= 1) MOE_TOPK(1);
+  else if (vpl <= 2) MOE_TOPK(2);
+  else if (vpl <= 4) MOE_TOPK(4);
+  else if (vpl <= 8) MOE_TOPK(8);
+  else MOE_TOPK(16);
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------------------------------
+// Router logits, bf16: L[t, e] = sum_h x[t, h] * W_r[e, h] (+ bias[e]) with fp32 accumulation.
+//
+// The router is a skinny GEMM (E = 128..512 output columns) whose shape swings from 64 tokens
+// (decode: a 1-8 MB weight read) to 16K tokens. One wave owns 16 * FT tokens x 64 experts over one
+// slice of K; the slices (K-split) multiply the number of waves when there are few tokens, and
+// their fp32 partial sums are added in slice order by the top-k kernel, so the result does not
+// depend on timing. The router weight is the MFMA's first operand, so each lane's accumulator
+// fragment holds four consecutive experts of one token (16-byte stores). Operands go from global
+// memory straight into registers in double-buffered chunks of D K-steps; loads are unconditional
+// (clamped to the slice and to the last token / expert), only the MFMAs past the slice's end are
+// skipped.
+// ------------------------------------------------------------------------------------------------
+template <int FT, int D>
+__global__ void __launch_bounds__(256)
+router_kernel(int T, int H, int E, const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+              const float* __restrict__ bias, float* __restrict__ out, int n_tb, int n_eb,
+              int nsplit, int kps) {
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= n_tb * n_eb * nsplit) return;             // uniform per wave
+  const int eb = wid % n_eb;
+  const int rest = wid / n_eb;
+  const int tb = rest % n_tb, sp = rest / n_tb;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int k0 = sp * kps;                              // first K-step (32 elements) of the slice
+
+  const uint16_t* wp[4];
+  const uint16_t* xp[FT];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = min(eb * 64 + j * 16 + lr, E - 1);
+    wp[j] = wr + (size_t)e * H + k0 * 32 + kq * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < FT; ++i) {
+    const int t = min(tb * 16 * FT + i * 16 + lr, T - 1);
+    xp[i] = x + (size_t)t * H + k0 * 32 + kq * 8;
+  }
+  // chunks of D K-steps, double-buffered (loads of chunk c + 1 before the MFMAs of chunk c; the
+  // chunk loop is unrolled by two so the register sets alternate statically, and scheduling
+  // barriers keep the loads where they are written)
+  bf16x8 wv[2][D][4], xv[2][D][FT];
+  auto load = [&](int c, int set) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int off = min(c * D + d, kps - 1) * 32;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wv[set][d][j] = *reinterpret_cast<const bf16x8*>(wp[j] + off);
+#pragma unroll
+      for (int i = 0; i < FT; ++i) xv[set][d][i] = *reinterpret_cast<const bf16x8*>(xp[i] + off);
+    }
+  };
+  f32x4 acc[4][FT];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < FT; ++i) acc[j][i] = f32x4{};
+  auto compute = [&](int c, int set) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c * D + d < kps) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < FT; ++i)
+            acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wv[set][d][j], xv[set][d][i], acc[j][i], 0, 0, 0);
+      }
+    }
+  };
+  const int nc = (kps + D - 1) / D;
+  load(0, 0);
+  for (int c = 0; c < nc; c += 2) {
+    MOE_SCHED_FENCE();
+    load(c + 1, 1);
+    MOE_SCHED_FENCE();
+    compute(c, 0);
+    MOE_SCHED_FENCE();
+    load(c + 2, 0);
+    MOE_SCHED_FENCE();
+    compute(c + 1, 1);
+  }
+  MOE_SCHED_FENCE();
+  // acc[j][i][v]: expert eb * 64 + j * 16 + kq * 4 + v, token tb * 16 FT + i * 16 + lr
+  float* dst = nsplit > 1 ? out + (size_t)sp * T * E : out;
+#pragma unroll
+  for (int i = 0; i < FT; ++i) {
+    const int t = tb * 16 * FT + i * 16 + lr;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = eb * 64 + j * 16 + kq * 4;
+      if (e >= E) continue;                             // E % 16 == 0: all four or none
+      f32x4 v = acc[j][i];
+      if (nsplit == 1 && bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += bias[e + q];
+      }
+      *reinterpret_cast<f32x4*>(dst + (size_t)t * E + e) = v;
+    }
+  }
+}
+
+namespace {
+constexpr int kRouterMinWaves = 512;    // K-split until the router has about 2 waves per CU
+constexpr int kRouterMaxSplit = 32;
+int router_ft(int T) { return T >= 1024 ? 4 : 1; }
+}  // namespace
+
+int router_splits(int T, int H, int E) {
+  if (T <= 0) return 1;
+  const int ft = router_ft(T);
+  const long long base = (long long)((T + 16 * ft - 1) / (16 * ft)) * ((E + 63) / 64);
+  const int nk = H / 32;
+  int ns = 1;
+  while (ns < kRouterMaxSplit && base * ns < kRouterMinWaves && nk % (ns * 2) == 0) ns *= 2;
+  return ns;
+}
+
+size_t router_ws_bytes(int T, int H, int E) {
+  const int ns = router_splits(T, H, E);
+  return ns > 1 ? (size_t)ns * T * E * sizeof(float) : 0;
+}
+
+hipError_t launch_router(int T, int H, int E, const void* x, const void* w_router,
+                         const float* bias, float* logits, float* partial, int nsplit,
+                         hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int ft = router_ft(T);
+  const int n_tb = (T + 16 * ft - 1) / (16 * ft), n_eb = (E + 63) / 64;
+  const int kps = H / 32 / nsplit;
+  const long long waves = (long long)n_tb * n_eb * nsplit;
+  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
+  float* out = nsplit > 1 ? partial : logits;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const uint16_t* wb = static_cast<const uint16_t*>(w_router);
+  if (ft == 4)
+    router_kernel<4, 2><<<grid, block, 0, s>>>(T, H, E, xb, wb, bias, out, n_tb, n_eb, nsplit, kps);
   else
-    topk_kernel<16><<<grid, block, 0, s>>>(T, E, k, scoring, renormalize, logits, ids, w);
+    router_kernel<1, 2><<<grid, block, 0, s>>>(T, H, E, xb, wb, bias, out, n_tb, n_eb, nsplit, kps);
   return hipGetLastError();
 }
 

@@ -54,6 +54,26 @@ def test_workspace_queries():
     assert m.moe_layer_workspace_bytes(big) > 16384 * 8 * 4096 * 2     # holds y
     assert m.moe_permute_workspace_bytes(big) > 0
     assert m.moe_layer_workspace_bytes(_desc(k=0)) == 0                 # invalid desc -> 0
+    # the router's K-split partial sums: a decode-sized bf16 router needs them, a prefill-sized
+    # one and the fp32 router do not
+    dec = _desc(T=64, H=4096, E=128, E_loc=32, I=1536, k=8, io_dtype=m.MOE_BF16,
+                expert_dtype=m.MOE_BF16)
+    r = m.moe_route_workspace_bytes(dec)
+    assert r > 0 and r % (64 * 128 * 4) == 0
+    assert m.moe_layer_workspace_bytes(dec) >= r
+    assert m.moe_route_workspace_bytes(big) == 0
+    assert m.moe_route_workspace_bytes(d) == 0
+
+
+def test_route_workspace_too_small():
+    import moe_layer_softmax_amd as m
+    lib = m.lib()
+    ok = ctypes.c_void_p(4096)
+    dec = _desc(T=64, H=4096, E=128, E_loc=32, I=1536, k=8, io_dtype=m.MOE_BF16,
+                expert_dtype=m.MOE_BF16)
+    need = m.moe_route_workspace_bytes(dec)
+    assert lib.moe_route(ctypes.byref(dec), ok, ok, None, ok, ok, ok, None, 0, None) == m.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(dec), ok, ok, None, ok, ok, ok, ok, need - 4, None) == m.MOE_ERR_WORKSPACE
 
 
 @pytest.mark.parametrize("bad", [dict(k=0), dict(k=17), dict(E=0), dict(E=2000), dict(T=-1),
@@ -63,7 +83,7 @@ def test_route_rejects_bad_descriptors(bad):
     import moe_layer_softmax_amd as m
     d = _desc(**bad)
     fake = ctypes.c_void_p(256)
-    st = m.lib().moe_route(ctypes.byref(d), fake, fake, None, fake, fake, fake, None)
+    st = m.lib().moe_route(ctypes.byref(d), fake, fake, None, fake, fake, fake, None, 0, None)
     assert st == m.MOE_ERR_INVALID_ARG
 
 
@@ -73,8 +93,9 @@ def test_null_and_misaligned_pointers_are_rejected():
     ok = ctypes.c_void_p(4096)
     bad = ctypes.c_void_p(4100)
     lib = m.lib()
-    assert lib.moe_route(ctypes.byref(d), ok, ok, None, None, ok, ok, None) == m.MOE_ERR_INVALID_ARG
-    assert lib.moe_route(ctypes.byref(d), bad, ok, None, ok, ok, ok, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(d), ok, ok, None, None, ok, ok, None, 0, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(d), bad, ok, None, ok, ok, ok, None, 0, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(d), ok, ok, None, ok, ok, ok, bad, 64, None) == m.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, ok, ok, ok, None, bad, None) == m.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(ctypes.byref(d), 9, ok, ok, ok, None, ok, None) == m.MOE_ERR_INVALID_ARG
     g = m.moe_gemm_desc(2, 64, 256, 128, m.MOE_BF16, m.MOE_EPI_SWIGLU, m.MOE_BF16, 1, 1)
@@ -113,7 +134,7 @@ def test_zero_tokens_is_a_no_op():
     lib = m.lib()
     d = _desc(T=0)
     w = m.moe_weights(*([4096] * 13))
-    assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None) == m.MOE_OK
+    assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None, 0, None) == m.MOE_OK
     assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, None, None, None, None, None, None) == m.MOE_OK
     assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), None, None, None, None, None, None,
                          None, 0, None) == m.MOE_OK

@@ -98,8 +98,14 @@ def _zipf_wl(E):
     return Workload("z", 1, 64, E, 0, E, 64, 1, 0, 0, 1, 1, 1, 1.1)
 
 
+# Router shapes: few tokens (K-split partial sums finished by the top-k kernel), many tokens
+# (64-token waves, split or not), a ragged token tail, an expert count that is not a multiple of 16
+# (grouped-GEMM router) and the fp32 router.
 @pytest.mark.parametrize("T,H,E,k,zipf,scoring", [(300, 4096, 128, 8, 1.1, 0), (64, 7168, 256, 8, 1.2, 1),
-                                                  (40, 4096, 512, 10, 0.0, 0), (33, 256, 8, 2, 0.0, 0)])
+                                                  (40, 4096, 512, 10, 0.0, 0), (33, 256, 8, 2, 0.0, 0),
+                                                  (64, 4096, 128, 8, 1.1, 0), (1, 4096, 128, 8, 1.1, 0),
+                                                  (1500, 4096, 256, 8, 0.0, 1), (4096, 4096, 128, 8, 1.1, 0),
+                                                  (100, 4096, 72, 4, 0.0, 0), (17, 1024, 16, 16, 0.0, 0)])
 def test_route_from_x(T, H, E, k, zipf, scoring):
     from moe_inputs.workloads import Workload
     io = 0 if H == 256 else 1
@@ -110,8 +116,9 @@ def test_route_from_x(T, H, E, k, zipf, scoring):
     lg = torch.empty((T, E), dtype=torch.float32, device="cuda")
     ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    rws = torch.empty(max(moe.moe_route_workspace_bytes(d), 16), dtype=torch.uint8, device="cuda")
     moe.moe_route(d, to_dev(x, dt), to_dev(wr, dt), None if bias is None else to_dev(bias, torch.float32),
-                  lg, ids, w)
+                  lg, ids, w, ws=rws)
     _sync()
     lg, ids, w = lg.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy()
     L64, absdot = oracle.logits(x, wr, bias)
@@ -229,6 +236,22 @@ def test_grouped_gemm_bf16(counts, swiglu, gather):
     rms = np.sqrt(np.mean(ref ** 2))
     assert np.all(err <= 2 ** -8 * np.abs(ref) + 1e-3 * rms), err.max() / rms
     assert np.all(Cg[R:] == 1024.0)                      # rows outside every group untouched
+
+
+# decode-sized groups (the weight-streaming kernel): groups of 0, 1, 63, 64 and 65 rows (a second
+# 64-row tile), K with an odd number of 64-wide steps (the 2-deep register ring) and the 4-deep one
+@pytest.mark.parametrize("K", [320, 1536])
+@pytest.mark.parametrize("swiglu", [False, True])
+@pytest.mark.parametrize("gather", [False, True])
+def test_grouped_gemm_bf16_decode_groups(K, swiglu, gather):
+    counts = [5, 0, 64, 65, 1, 12, 63, 2, 0, 30]
+    Cg, ref, R = _gemm_case(counts, K=K, N=192, swiglu=swiglu, gather=gather, out_f32=not swiglu)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if swiglu:
+        assert np.all(np.abs(Cg[:R] - ref) <= 2 ** -8 * np.abs(ref) + 1e-3 * rms)
+    else:
+        assert np.abs(Cg[:R] - ref).max() <= 1e-4 * rms * np.sqrt(K / 256)
+    assert np.all(Cg[R:] == 1024.0)
 
 
 @pytest.mark.parametrize("swiglu", [False, True])
