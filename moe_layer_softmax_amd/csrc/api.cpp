@@ -102,9 +102,16 @@ long long scale_bytes(int dt, long long N, long long K) {
   return 0;
 }
 
-// the bf16 router kernel takes widths in multiples of 16 experts; other cases run the router as a
-// grouped GEMM with one extra group
-bool router_fast(const moe_desc* d) { return d->io_dtype == MOE_BF16 && d->E % 16 == 0; }
+// The router of many bf16 tokens runs as a tiled GEMM (32 or 64 tokens x 128 experts per
+// workgroup) once that gives at least half a workgroup per CU; fewer tokens use the K-split router
+// kernel (widths in multiples of 16 experts); the fp32 router and other widths run as a grouped
+// GEMM with one extra group.
+bool router_tiled(const moe_desc* d) {
+  return d->io_dtype == MOE_BF16 && (long long)((d->T + 31) / 32) * ((d->E + 127) / 128) >= 128;
+}
+bool router_fast(const moe_desc* d) {
+  return d->io_dtype == MOE_BF16 && d->E % 16 == 0 && !router_tiled(d);
+}
 int route_splits(const moe_desc* d) { return router_fast(d) ? router_splits(d->T, d->H, d->E) : 1; }
 size_t route_ws(const moe_desc* d) { return router_fast(d) ? router_ws_bytes(d->T, d->H, d->E) : 0; }
 
@@ -174,7 +181,7 @@ moe_status run_router(const moe_desc* d, const void* x, const void* w_router, co
   a.bias = bias;
   a.C = logits;
   a.c_pitch = (long long)d->E * 4;
-  return hip_status(launch_gemm(a, s));
+  return hip_status(router_tiled(d) ? launch_gemm_router(a, s) : launch_gemm(a, s));
 }
 
 moe_status run_route(const moe_desc* d, const void* x, const void* w_router, const float* bias,

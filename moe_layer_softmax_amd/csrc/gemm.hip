@@ -724,6 +724,16 @@ hipError_t run_f32(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Router logits of many tokens (an extra group of T rows, no routed groups, N = E experts): 64 (or
+// 32) tokens x 128 experts per workgroup, so the tokens are read from HBM once per 128 experts, with
+// 6-7 LDS stages (one workgroup per CU) to keep ~120 KB of loads in flight per CU.
+hipError_t launch_gemm_router(const GemmArgs& a, hipStream_t s) {
+  if (a.dtype != MOE_BF16) return launch_gemm(a, s);
+  if ((long long)((a.x_rows + 63) / 64) * ((a.N + 127) / 128) >= 256)
+    return run_bf16<64, 128, 1, 4, 16, 64, 6>(a, s);
+  return run_bf16<32, 128, 1, 4, 16, 64, 7>(a, s);
+}
+
 // Tile shape choice: the expected rows per group decide between a compute-shaped tile (large
 // groups, MFMA-bound) and a weight-streaming tile (few rows per group, HBM-bound).
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {

@@ -37,6 +37,8 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// the router as a grouped GEMM (one extra group of T rows): a tile shape for N = E and many rows
+hipError_t launch_gemm_router(const GemmArgs& a, hipStream_t s);
 // block-scaled fp8 / MXFP4 grouped GEMM (A and B in a.dtype)
 hipError_t launch_gemm_q(const GemmArgs& a, hipStream_t s);
 
