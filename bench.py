@@ -38,7 +38,102 @@ def parse():
                    help="only the timed moe_layer steps (for profilers)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
+    p.add_argument("--all-workloads", action="store_true",
+                   help="add every workload's layer time and both roofline fractions")
     return p.parse_args()
+
+
+PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp4": 10066.3}
+
+
+def workload_table(stream, steps):
+    """Layer time of every workload (one moe_layer call per step, caches evicted with a 1 GiB read
+    before each), with the algorithmic MFMA and HBM roofline fractions. Tokens, router weight and
+    bias are the seeded inputs; expert weights are seeded device draws of the same shapes (their
+    values do not change the work), quantised by the library for the fp8 / MXFP4 layers."""
+    import torch
+    import moe_inputs as mi
+    import moe_layer_softmax_amd as moe
+    from moe_inputs import gen
+    fmt_of = {mi.FMT_BF16: ("bf16", moe.MOE_BF16), mi.FMT_FP8: ("fp8", moe.MOE_FP8_E4M3),
+              mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4)}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {}
+    for name in ("C2p", "C2d", "C3a", "C3b", "C4p", "C4d", "C5p", "C5d"):
+        wl = mi.WORKLOADS[name]
+        fname, fcode = fmt_of[wl.fmt]
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
+        x, wr = bf(gen.tokens(wl)), bf(gen.router_weight(wl))
+        b = gen.router_bias(wl)
+        bias = None if b is None else torch.from_numpy(b).to("cuda")
+        gen_t = torch.Generator(device="cuda")
+        gen_t.manual_seed(1)
+        shapes = [(wl.E_loc, wl.I, wl.H), (wl.E_loc, wl.I, wl.H), (wl.E_loc, wl.H, wl.I)]
+        if wl.I_s:
+            shapes += [(1, wl.I_s, wl.H), (1, wl.I_s, wl.H), (1, wl.H, wl.I_s)]
+        mats = [torch.randn(s, generator=gen_t, device="cuda") * 0.02 for s in shapes]
+        scales = [None] * len(mats)
+        if fname == "bf16":
+            mats = [m.to(torch.bfloat16) for m in mats]
+            wbytes_expert = 3 * wl.I * wl.H * 2
+        else:
+            qm, qs = [], []
+            for m in mats:
+                G, R, C = m.shape
+                if fname == "fp8":
+                    c = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
+                    s = torch.empty((G, R // 128, C // 128), dtype=torch.float32, device="cuda")
+                else:
+                    c = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
+                    s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
+                moe.moe_quantize(fcode, moe.MOE_F32, G, R, C, 128, m, c, s)
+                qm.append(c)
+                qs.append(s)
+            mats, scales = qm, qs
+            wbytes_expert = sum(int(m[0].numel() * m.element_size()) + int(s[0].numel() * s.element_size())
+                                for m, s in zip(mats[:3], scales[:3]))
+        torch.cuda.synchronize()
+        W = moe.make_weights(wr, *mats[:3], scales=tuple(scales[:3]),
+                             shared=tuple(mats[3:]) if wl.I_s else None,
+                             shared_scales=tuple(scales[3:]) if wl.I_s else (None, None, None))
+        d = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
+                          wl.renormalize, moe.MOE_BF16, fcode, moe.MOE_F32)
+        o = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        ws = torch.empty(moe.moe_layer_workspace_bytes(d), dtype=torch.uint8, device="cuda")
+        call = lambda: moe.moe_layer(d, W, x, bias, o, None, ids, None, ws, stream)
+        with torch.cuda.stream(stream):
+            call()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        with torch.cuda.stream(stream):
+            for a, e in ev:
+                flush.sum()
+                a.record(stream)
+                call()
+                e.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(e) for a, e in ev]))
+        loc = ids[(ids >= wl.e0) & (ids < wl.e0 + wl.E_loc)]
+        R = int(loc.numel())
+        active = int(torch.unique(loc).numel())
+        router_fl = 2.0 * wl.T * wl.H * wl.E
+        expert_fl = 6.0 * R * wl.H * wl.I + 6.0 * wl.T * wl.H * wl.I_s
+        t_mfma = router_fl / PEAK_BF16_TFLOPS / 1e12 + expert_fl / PEAK_TFLOPS[fname] / 1e12
+        nbytes = (active * wbytes_expert + (wbytes_expert * wl.I_s // wl.I if wl.I_s else 0)
+                  + wl.E * wl.H * 2 + wl.T * wl.H * 2 + wl.T * wl.H * 4 + wl.T * wl.k * 8)
+        t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+        t = ms * 1e-3
+        out[name] = {"T": wl.T, "format": fname, "ms": round(ms, 4),
+                     "tokens_per_s": round(wl.T / t, 1), "local_rows_R": R, "active_experts": active,
+                     "tflops": round((router_fl + expert_fl) / t / 1e12, 1),
+                     "frac_mfma": round(t_mfma / t, 4), "compulsory_bytes": nbytes,
+                     "hbm_gbps": round(nbytes / t / 1e9, 1), "frac_hbm": round(t_hbm / t, 4),
+                     "bound": "mfma" if t_mfma > t_hbm else "hbm"}
+        del mats, scales, W, x, wr, o, ids, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 # Source files of the grouped GEMM kernels; HBM counters taken on an older version of them are
@@ -307,6 +402,8 @@ def main():
                             "frac_hbm": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                             "caches": "1 GiB read between steps"}
         del D, flush
+    if args.all_workloads:
+        result["workloads"] = workload_table(stream, max(5, min(args.steps, 20)))
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     print(json.dumps(result), flush=True)
