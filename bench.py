@@ -36,6 +36,8 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--profile-only", action="store_true",
                    help="only the timed moe_layer steps (for profilers)")
+    p.add_argument("--flush", action="store_true",
+                   help="with --profile-only: read a 1 GiB buffer before every step (cold caches)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
     p.add_argument("--all-workloads", action="store_true",
@@ -329,6 +331,15 @@ def main():
     for _ in range(args.warmup):
         L.step(stream)
     torch.cuda.synchronize()
+    if args.profile_only and args.flush:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(args.steps):
+                flush.sum()
+                L.step(stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": wl.name, "steps": args.steps, "flushed": True}))
+        return
     t0 = time.perf_counter()
     for _ in range(args.steps):
         L.step(stream)
