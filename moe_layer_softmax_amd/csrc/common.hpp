@@ -78,6 +78,16 @@ __device__ __forceinline__ void dma_16b_asm(const void* g, const void* lds_regio
                :: "s"(base), "v"(g) : "memory", "m0");
 #endif
 }
+// 4 bytes per lane from global memory straight into LDS (lane i writes lds_region + 4 * i); like
+// dma_16b_asm, invisible to the compiler's wait-count pass.
+__device__ __forceinline__ void dma_4b_asm(const void* g, const void* lds_region) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const unsigned base = __builtin_amdgcn_readfirstlane(
+      static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds_region)));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(base), "v"(g) : "memory", "m0");
+#endif
+}
 // The same load with a scalar base address and a 32-bit per-lane byte offset, and the LDS target
 // given as a wave-uniform byte address for M0. A K loop then advances the scalar base only, so the
 // loads cost no per-lane address arithmetic (vector ALU instructions in the loop take issue cycles

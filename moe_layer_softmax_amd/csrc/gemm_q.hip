@@ -17,7 +17,9 @@
 // full 128 h-columns of the SwiGLU tile: the epilogue can form fp8 1x128 or MXFP4 1x32 blocks of h
 // in registers, with the row amax reduced across 16 lanes by shuffles). K-steps are 128-byte row
 // slices (128 fp8 or 256 fp4 elements) staged through a 3-stage direct-to-LDS ring, with the same
-// bank swizzle, tile scheduler and row gathering as the bf16 kernel.
+// bank swizzle, tile scheduler and row gathering as the bf16 kernel. The block scales of a K-step
+// travel in the same stage as its operands (4-byte direct-to-LDS loads), so the loop has no other
+// global loads: every wait in it is an explicit count of this wave's own loads.
 #include "gemm_common.hpp"
 #include "quant_dev.hpp"
 
@@ -37,8 +39,13 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   constexpr int KE = MX ? 256 : 128;       // elements per K-step
   constexpr int SUB = MX ? 2 : 1;          // 128-element MFMA substeps per K-step
   constexpr int A_INS = BM / (8 * NW), B_INS = BN / (8 * NW);
-  constexpr int INS = A_INS + B_INS;
-  constexpr int STAGE = (BM + BN) * RB;    // bytes per LDS stage
+  constexpr int SINS = MX ? 3 : 1;         // 4-byte scale loads per wave per K-step
+  constexpr int INS = A_INS + B_INS + SINS;
+  constexpr int DATA = (BM + BN) * RB;     // operand bytes per LDS stage
+  // block scales of the K-step follow the operands in the stage: MXFP4 E8M0 [BM rows][8 B] then
+  // [BN rows][8 B]; fp8 fp32 [BM rows] then the two B block scales
+  constexpr int SCALE_BYTES = MX ? (BM + BN) * 8 : 1024;
+  constexpr int STAGE = DATA + SCALE_BYTES; // bytes per LDS stage
   constexpr int NB = 4;                    // B fragments per MFMA batch
   constexpr int FMT_CODE = MX ? 4 : 0;     // f8f6f4 operand format: 0 = fp8 e4m3, 4 = fp4 e2m1
   using Geo = SliceGeo<64>;                // 128-byte rows
@@ -86,54 +93,73 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
     const long long n = b_row(rb, base, sb);
     b_src[j] = base + n * b_row_bytes + ((lane & 7) ^ Geo::swz(rb)) * 16;
   }
+  // ---- scale sources (one 4-byte direct-to-LDS load per lane and instruction) ----
+  // MXFP4: wave w moves A scale rows [32w, 32w + 32) and B scale rows [64w, 64w + 64), 8 bytes
+  //        (one K-step) per row, two lanes per row.
+  // fp8:   waves 0 and 1 move A scale rows [64w, 64w + 64) (one fp32 per row and K-step); wave 2
+  //        the two B block scales (lane i: scale i & 1); wave 3 the same into a spare slot (every
+  //        wave issues the same number of loads, so the wait counts are uniform).
+  const char* s_src[SINS];
+  int s_dst[SINS];
+  long long s_step[SINS];                  // bytes between consecutive K-steps of a source
+  if constexpr (MX) {
+    const int gpr = K / 32;                // scale bytes per row
+    {
+      const int r = wave * 32 + (lane >> 1);
+      s_src[0] = static_cast<const char*>(p.A_scales) + a_src_row(p, t, t.row0 + r) * gpr + (lane & 1) * 4;
+      s_dst[0] = DATA + wave * 256;
+      s_step[0] = 8;
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int rb = (wave * 2 + c) * 32 + (lane >> 1);
+      long long n;
+      const char* sbase = t.Bs;
+      if (SWIGLU) {
+        n = (long long)t.nt * (BN / 2) + (rb % (BN / 2));
+        if (rb >= BN / 2) sbase = t.B2s;
+      } else {
+        n = (long long)t.nt * BN + rb;
+      }
+      if (n >= p.N) n = p.N - 1;
+      s_src[1 + c] = sbase + n * gpr + (lane & 1) * 4;
+      s_dst[1 + c] = DATA + BM * 8 + (wave * 2 + c) * 256;
+      s_step[1 + c] = 8;
+    }
+  } else {
+    const int kb = K / 128;                // fp32 scales per row
+    if (wave < 2) {
+      const int r = wave * 64 + lane;
+      s_src[0] = static_cast<const char*>(p.A_scales) +
+                 (long long)(a_src_row(p, t, t.row0 + r) / p.a_scale_rows) * kb * 4;
+      s_dst[0] = DATA + wave * 256;
+    } else {
+      const char* b0;
+      const char* b1;
+      if (SWIGLU) {                        // 128 h-columns = one block of gate and one of up
+        b0 = t.Bs + (long long)t.nt * kb * 4;
+        b1 = t.B2s + (long long)t.nt * kb * 4;
+      } else {                             // two 128-column blocks
+        b0 = t.Bs + (long long)(t.nt * 2) * kb * 4;
+        b1 = t.Bs + (long long)min(t.nt * 2 + 1, (p.N - 1) / 128) * kb * 4;
+      }
+      s_src[0] = (lane & 1) ? b1 : b0;
+      s_dst[0] = DATA + 512 + (wave - 2) * 256;
+    }
+    s_step[0] = 4;
+  }
+
   auto issue = [&](int kt) {
     if (kt >= nk) return;
     uint8_t* la = ldsq + (kt % S) * STAGE;
     uint8_t* lb = la + BM * RB;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) dma_16b(a_src[j] + (long long)kt * RB, la + (j * NW + wave) * 8 * RB);
+    for (int j = 0; j < A_INS; ++j) dma_16b_asm(a_src[j] + (long long)kt * RB, la + (j * NW + wave) * 8 * RB);
 #pragma unroll
-    for (int j = 0; j < B_INS; ++j) dma_16b(b_src[j] + (long long)kt * RB, lb + (j * NW + wave) * 8 * RB);
+    for (int j = 0; j < B_INS; ++j) dma_16b_asm(b_src[j] + (long long)kt * RB, lb + (j * NW + wave) * 8 * RB);
+#pragma unroll
+    for (int j = 0; j < SINS; ++j) dma_4b_asm(s_src[j] + kt * s_step[j], la + s_dst[j]);
   };
-
-  // ---- scale sources ----
-  // fp8: A scale of each accumulator row (rows (lane/16)*4 + v of fragment i), one per K-step;
-  //      B scales are uniform per 128 columns (gate/up halves, or two 128-column blocks).
-  // MXFP4: E8M0 bytes of each operand row of fragment i / j, 8 per K-step (256 elements).
-  const float* sa_ptr[MX ? 1 : FM * 4];
-  const uint8_t* sa_mx[MX ? FM : 1];
-  const uint8_t* sb_mx[MX ? FN : 1];
-  const float* sb_fp8[2];
-  if constexpr (!MX) {
-    const int kb = K / 128;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int r = t.row0 + wave * TM + i * 16 + (lane >> 4) * 4 + v;
-        sa_ptr[i * 4 + v] = static_cast<const float*>(p.A_scales) + (a_src_row(p, t, r) / p.a_scale_rows) * kb;
-      }
-    if (SWIGLU) {
-      sb_fp8[0] = reinterpret_cast<const float*>(t.Bs) + (long long)t.nt * kb;    // 128 h-columns = one block
-      sb_fp8[1] = reinterpret_cast<const float*>(t.B2s) + (long long)t.nt * kb;
-    } else {
-      sb_fp8[0] = reinterpret_cast<const float*>(t.Bs) + (long long)(t.nt * 2) * kb;
-      sb_fp8[1] = reinterpret_cast<const float*>(t.Bs) + (long long)min(t.nt * 2 + 1, (p.N - 1) / 128) * kb;
-    }
-  } else {
-    const int gpr = K / 32;                  // scale bytes per row
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int r = t.row0 + wave * TM + i * 16 + (lane & 15);
-      sa_mx[i] = static_cast<const uint8_t*>(p.A_scales) + a_src_row(p, t, r) * gpr;
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const char *base, *sb;
-      const long long n = b_row(j * 16 + (lane & 15), base, sb);
-      sb_mx[j] = reinterpret_cast<const uint8_t*>(sb) + n * gpr;
-    }
-  }
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -171,22 +197,29 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
     const uint8_t* la = ldsq + (kt % S) * STAGE;
     const uint8_t* lb = la + BM * RB;
 
-    // scales of this K-step
+    // scales of this K-step, staged with its operands
+    const uint8_t* ls = la + DATA;
     float fs[MX ? 1 : FM * 4][2];
     u32x2 sam[MX ? FM : 1], sbm[MX ? FN : 1];
     if constexpr (!MX) {
-      const float g0 = sb_fp8[0][kt], g1 = sb_fp8[1][kt];
+      const float g0 = reinterpret_cast<const float*>(ls + 512)[0];
+      const float g1 = reinterpret_cast<const float*>(ls + 512)[1];
 #pragma unroll
-      for (int i = 0; i < FM * 4; ++i) {
-        const float a = sa_ptr[i][kt];
-        fs[i][0] = a * g0;
-        fs[i][1] = a * g1;
+      for (int i = 0; i < FM; ++i) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(ls + (wave * TM + i * 16 + q * 4) * 4);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          fs[i * 4 + v][0] = a4[v] * g0;
+          fs[i * 4 + v][1] = a4[v] * g1;
+        }
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) sam[i] = *reinterpret_cast<const u32x2*>(sa_mx[i] + kt * 8);
+      for (int i = 0; i < FM; ++i)
+        sam[i] = *reinterpret_cast<const u32x2*>(ls + (wave * TM + i * 16 + (lane & 15)) * 8);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) sbm[j] = *reinterpret_cast<const u32x2*>(sb_mx[j] + kt * 8);
+      for (int j = 0; j < FN; ++j)
+        sbm[j] = *reinterpret_cast<const u32x2*>(ls + BM * 8 + (j * 16 + (lane & 15)) * 8);
     }
 
 #pragma unroll
@@ -311,7 +344,7 @@ hipError_t run_q(const GemmArgs& a, hipStream_t s) {
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
   Grid g = make_grid(a, BM, SWIGLU ? BN / 2 : BN, 8, 64);
   if (g.total == 0) return hipSuccess;
-  const size_t lds = (size_t)S * (BM + BN) * 128;
+  const size_t lds = (size_t)S * ((BM + BN) * 128 + (FMT == MOE_MXFP4 ? (BM + BN) * 8 : 1024));
   gemm_q_kernel<FMT, EPI><<<dim3(g.blocks), dim3(256), lds, s>>>(a, g.n_tiles, g.x_tiles, g.span,
                                                                   g.total, g.gm);
   return hipGetLastError();
