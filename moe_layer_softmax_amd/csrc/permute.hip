@@ -135,27 +135,49 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int& t
   return res;
 }
 
+// counts, offsets and the base row of every (chunk, expert). One wave per expert (16 waves,
+// experts w, w + 16, ...): lane l sums chunks l, l + 64, ...; then the chunk bases are an in-order
+// scan over chunks, 64 chunks per wave-wide prefix sum.
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ partial, int n_chunks,
                                                          int E_loc, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
   __shared__ int tmp[64];
+  __shared__ int tot_of[kMaxLocal];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int e = w; e < E_loc; e += 16) {
+    int sum = 0;
+    for (int c = lane; c < n_chunks; c += 64) sum += partial[(size_t)c * E_loc + e];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0) tot_of[e] = sum;
+  }
+  __syncthreads();
   const int el = threadIdx.x;
-  int tot = 0;
-  if (el < E_loc)
-    for (int c = 0; c < n_chunks; ++c) tot += partial[(size_t)c * E_loc + el];
+  const int tot = el < E_loc ? tot_of[el] : 0;
   int total;
-  const int off = block_exclusive_scan_1024(el < E_loc ? tot : 0, tmp, total);
+  const int off = block_exclusive_scan_1024(tot, tmp, total);   // ends with a barrier
   if (el < E_loc) {
     counts[el] = tot;
     offsets[el] = off;
-    int run = off;
-    for (int c = 0; c < n_chunks; ++c) {
-      int v = partial[(size_t)c * E_loc + el];
-      partial[(size_t)c * E_loc + el] = run;
-      run += v;
-    }
+    tot_of[el] = off;                                             // each thread rewrites its own
   }
   if (threadIdx.x == 0) offsets[E_loc] = total;
+  __syncthreads();
+  for (int e = w; e < E_loc; e += 16) {
+    int run = tot_of[e];
+    for (int c0 = 0; c0 < n_chunks; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < n_chunks ? partial[(size_t)c * E_loc + e] : 0;
+      int inc = v;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+      }
+      if (c < n_chunks) partial[(size_t)c * E_loc + e] = run + inc - v;
+      run += __shfl(inc, 63, 64);
+    }
+  }
 }
 
 __global__ void __launch_bounds__(256) perm_scatter_kernel(const int32_t* __restrict__ ids,
