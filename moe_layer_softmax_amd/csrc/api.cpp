@@ -458,6 +458,9 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   a.G = d->E_loc;
   a.offsets = offsets;
   a.max_rows = slots;
+  // tile shapes are chosen for the rows this GPU's slice receives under balanced routing; the
+  // grid still covers every slot, so skewed routing only changes the speed
+  a.expected_rows = static_cast<int>(std::min<long long>(slots, ((long long)slots * d->E_loc + d->E - 1) / d->E));
   a.B = w->w_gate;
   a.Bs = w->w_gate_scales;
   a.B2 = w->w_up;
@@ -495,6 +498,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   b.G = d->E_loc;
   b.offsets = offsets;
   b.max_rows = slots;
+  b.expected_rows = a.expected_rows;
   b.B = w->w_down;
   b.Bs = w->w_down_scales;
   b.b_stride = row_bytes(dt, I) * (long long)H;

@@ -754,11 +754,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.dtype == MOE_FP8_E4M3 || a.dtype == MOE_MXFP4) return launch_gemm_q(a, s);
   if (a.dtype == MOE_F32) return run_f32(a, s);
   if (a.dtype == MOE_BF16) {
-    const long long rows = (long long)a.max_rows + a.x_rows;
+    const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;
     const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
     const long long per_group = groups ? rows / groups : rows;
     const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
-    if (per_group >= 512 && n_full >= 256) {
+    if (per_group >= 256 && n_full >= 256) {
       // 256 x 256 tiles, K-steps of 32 through 5 LDS stages of 32 KB. SwiGLU (K = hidden size,
       // long K loops): ping-pong schedule of 8 waves of 128 x 64. Plain store (the down projection,
       // short K): 16 waves of 64 x 64 (measured a few percent faster there than ping-pong).

@@ -27,6 +27,9 @@ namespace moe {
 
 enum { QEPI_STORE_F32 = 0, QEPI_STORE_BF16 = 1, QEPI_SWIGLU_BF16 = 2, QEPI_SWIGLU_Q = 3 };
 
+// m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel
+constexpr int kQStreamGroupM = 8;
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <int FMT, int EPI>
@@ -336,6 +339,302 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Weight-streaming variant for decode-sized groups (fp8 and MXFP4 weights), after the bf16 one in
+// gemm.hip: the weights are the scaled MFMA's first operand and go straight to registers, 128
+// bytes of every row per K-pair (one 128-element step for fp8, two for MXFP4), each load
+// instruction covering 8 rows x 128 contiguous bytes, redistributed to the operand lanes with
+// ds_bpermute; activations and block scales are loaded in the operand layout directly; pairs are
+// double-buffered. For fp8 a lane's 32-byte operand is chunks kq and kq + 4 of the pair (the same
+// chunks of the activation row, so the dot product is unchanged); for MXFP4 step s uses chunk
+// 4 s + kq and scale byte 4 s + kq of the row's 8 scale bytes per pair.
+// Workgroup: 4 waves on 16 * FM rows x 4 adjacent column blocks of one group (SWIGLU: 128 h-columns,
+// wave w on 32 of them = 32 gate + 32 up weight rows; STORE: 256 columns, 64 per wave), so the
+// fp8 1 x 128 blocks of h are complete inside the workgroup (row amax exchanged through LDS) and
+// the MXFP4 1 x 32 groups inside one wave.
+// ------------------------------------------------------------------------------------------------
+template <int FMT, int EPI, int FM>
+__global__ void __launch_bounds__(256)
+gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
+  constexpr bool MX = FMT == MOE_MXFP4;
+  constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
+  constexpr int BM = 16 * FM;
+  constexpr int FMT_CODE = MX ? 4 : 0;
+  __shared__ float amax_x[4][BM];          // fp8 h: per-wave row amax
+
+  const int logical = xcd_remap(blockIdx.x, kQStreamGroupM);
+  if (logical >= total) return;            // uniform per workgroup
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kQStreamGroupM)) return;
+
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int lr = lane & 15, kq = lane >> 4;
+  const int K = p.K;
+  const long long wrow = MX ? K / 2 : K;   // weight row bytes
+  const int np = MX ? K / 256 : K / 128;   // K-pairs (128 bytes of every row)
+  // weight rows of fragment j (SWIGLU: j < 2 gate, else up; 16 rows each) of this wave
+  auto wrow_of = [&](int j, int r, const char*& base, const char*& sbase) -> long long {
+    long long n;
+    base = t.B;
+    sbase = t.Bs;
+    if (SWIGLU) {
+      n = (long long)t.nt * 128 + wave * 32 + (j & 1) * 16 + r;
+      if (j >= 2) { base = t.B2; sbase = t.B2s; }
+    } else {
+      n = (long long)t.nt * 256 + wave * 64 + j * 16 + r;
+    }
+    return n < p.N ? n : p.N - 1;          // columns past N: valid row, never stored
+  };
+  const char* wp[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const char *base, *sb;
+      const long long n = wrow_of(j, h * 8 + (lane >> 3), base, sb);
+      wp[j][h] = base + n * wrow + (lane & 7) * 16;
+    }
+  const char* A = static_cast<const char*>(p.A);
+  const char* ap[FM];
+  long long arow[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    arow[i] = a_src_row(p, t, t.row0 + i * 16 + lr);
+    ap[i] = A + arow[i] * p.a_pitch + kq * 16;
+  }
+  // block scales: MXFP4 E8M0 bytes of the operand rows (8 per pair); fp8 fp32 block scales
+  const uint8_t* wsc[MX ? 4 : 1];
+  const uint8_t* asc[MX ? FM : 1];
+  const float* wsf[MX ? 1 : 2];
+  const float* asf[MX ? 1 : FM];
+  if constexpr (MX) {
+    const int gpr = K / 32;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const char *base, *sb;
+      const long long n = wrow_of(j, lr, base, sb);
+      wsc[j] = reinterpret_cast<const uint8_t*>(sb) + n * gpr;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asc[i] = static_cast<const uint8_t*>(p.A_scales) + arow[i] * gpr;
+  } else {
+    const int kb = K / 128;
+    const char *b0, *s0, *b1, *s1;
+    const long long n0 = wrow_of(0, 0, b0, s0), n1 = wrow_of(SWIGLU ? 2 : 0, 0, b1, s1);
+    wsf[0] = reinterpret_cast<const float*>(s0) + (n0 / 128) * kb;
+    wsf[1] = reinterpret_cast<const float*>(s1) + (n1 / 128) * kb;   // SWIGLU: the up block
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      asf[i] = static_cast<const float*>(p.A_scales) + (arow[i] / p.a_scale_rows) * kb;
+  }
+  const int src0 = ((lr & 7) * 8 + kq) * 4, src1 = src0 + 16;
+  const bool upper = lr >= 8;
+
+  i32x4 wraw[2][4][2];
+  i32x4 av[2][FM][2];
+  u32x2 wsm[2][MX ? 4 : 1], asm_[2][MX ? FM : 1];
+  float wss[2][2], ass[2][MX ? 1 : FM];
+  auto load = [&](int c, int set) {
+    c = c < np ? c : np - 1;
+    const long long off = (long long)c * 128;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) wraw[set][j][h] = *reinterpret_cast<const i32x4*>(wp[j][h] + off);
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) av[set][i][s2] = *reinterpret_cast<const i32x4*>(ap[i] + off + s2 * 64);
+    if constexpr (MX) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wsm[set][j] = *reinterpret_cast<const u32x2*>(wsc[j] + c * 8);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm_[set][i] = *reinterpret_cast<const u32x2*>(asc[i] + c * 8);
+    } else {
+      wss[set][0] = wsf[0][c];
+      wss[set][1] = wsf[1][c];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ass[set][i] = asf[i][c];
+    }
+  };
+  f32x4 acc[4][FM];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{};
+  auto piece = [&](int set, int j, int src) -> i32x4 {
+    i32x4 w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lo = __builtin_amdgcn_ds_bpermute(src, wraw[set][j][0][q]);
+      const int hi = __builtin_amdgcn_ds_bpermute(src, wraw[set][j][1][q]);
+      w[q] = upper ? hi : lo;
+    }
+    return w;
+  };
+  auto compute = [&](int set) {
+    if constexpr (MX) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        i32x8 wf[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const i32x4 w = piece(set, j, s2 ? src1 : src0);
+          wf[j] = i32x8{w[0], w[1], w[2], w[3], 0, 0, 0, 0};
+        }
+        const int sh = 8 * (s2 * 4 + kq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sw = static_cast<int>(((s2 ? wsm[set][j][1] : wsm[set][j][0]) >> (sh - 32 * s2)) & 0xFFu);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            const int sa = static_cast<int>(((s2 ? asm_[set][i][1] : asm_[set][i][0]) >> (sh - 32 * s2)) & 0xFFu);
+            const i32x4 a = av[set][i][s2];
+            acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                wf[j], i32x8{a[0], a[1], a[2], a[3], 0, 0, 0, 0}, acc[j][i], FMT_CODE, FMT_CODE, 0, sw, 0, sa);
+          }
+        }
+      }
+    } else {
+      i32x8 wf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const i32x4 w0 = piece(set, j, src0), w1 = piece(set, j, src1);
+        wf[j] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const i32x4 a0 = av[set][i][0], a1 = av[set][i][1];
+        const i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 tmp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[j], a, f32x4{}, FMT_CODE, FMT_CODE, 0, 127, 0, 127);
+          const float sc = ass[set][i] * wss[set][(SWIGLU && j >= 2) ? 1 : 0];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[j][i][v] = fmaf(tmp[v], sc, acc[j][i][v]);
+        }
+      }
+    }
+  };
+  load(0, 0);
+  int c = 0;
+  for (; c + 1 < np; c += 2) {
+    MOE_SCHED_FENCE();
+    load(c + 1, 1);
+    MOE_SCHED_FENCE();
+    compute(0);
+    MOE_SCHED_FENCE();
+    load(c + 2, 0);
+    MOE_SCHED_FENCE();
+    compute(1);
+  }
+  MOE_SCHED_FENCE();
+  if (c < np) compute(0);                  // odd number of pairs: the last is in set 0
+
+  // ---- epilogue: acc[j][i][v] = weight row j * 16 + kq * 4 + v of the wave, C row row0 + i*16 + lr
+  char* C = static_cast<char*>(p.C);
+  if constexpr (!SWIGLU) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = t.row0 + i * 16 + lr;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long long col = (long long)t.nt * 256 + wave * 64 + j * 16 + kq * 4;
+        if (r >= t.row1 || col >= p.N) continue;
+        char* crow = C + (long long)r * p.c_pitch;
+        if (EPI == QEPI_STORE_F32) {
+          *reinterpret_cast<f32x4*>(crow + col * 4) = acc[j][i];
+        } else {
+          *reinterpret_cast<uint2*>(crow + col * 2) =
+              make_uint2(pack_bf16x2(acc[j][i][0], acc[j][i][1]), pack_bf16x2(acc[j][i][2], acc[j][i][3]));
+        }
+      }
+    }
+  } else {
+    // h[i][jj][v]: h column (jj * 16 + kq * 4 + v) of the wave's 32, C row row0 + i*16 + lr
+    float h[FM][2][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) h[i][jj][v] = silu_fast(acc[jj][i][v]) * acc[jj + 2][i][v];
+    const long long col0 = (long long)t.nt * 128 + wave * 32;   // first h column of the wave
+    if constexpr (EPI == QEPI_SWIGLU_BF16) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = t.row0 + i * 16 + lr;
+        if (r >= t.row1) continue;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          *reinterpret_cast<uint2*>(C + (long long)r * p.c_pitch + (col0 + jj * 16 + kq * 4) * 2) =
+              make_uint2(pack_bf16x2(h[i][jj][0], h[i][jj][1]), pack_bf16x2(h[i][jj][2], h[i][jj][3]));
+      }
+    } else if constexpr (MX) {
+      // one 1 x 32 group per row: the wave's 32 columns; row amax over the 4 lanes of the row
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(h[i][jj][v]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int e = mx_shared_exp(amax);
+        const float mul = ldexpf(1.0f, -e);
+        const int r = t.row0 + i * 16 + lr;
+        if (r >= t.row1) continue;
+        uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          uint32_t b[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) b[v] = e2m1_rne_sat(h[i][jj][v] * mul);
+          const uint16_t two = static_cast<uint16_t>((b[0] | (b[1] << 4)) | ((b[2] | (b[3] << 4)) << 8));
+          *reinterpret_cast<uint16_t*>(crow + (col0 + jj * 16 + kq * 4) / 2) = two;
+        }
+        if (kq == 0)
+          static_cast<uint8_t*>(p.C_scales)[(long long)r * (p.N / 32) + col0 / 32] = static_cast<uint8_t>(e + 127);
+      }
+    } else {
+      // fp8: one 1 x 128 block per row over the workgroup's 128 columns (4 waves)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(h[i][jj][v]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        if (kq == 0) amax_x[wave][i * 16 + lr] = amax;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int rl = i * 16 + lr;
+        const float amax = fmaxf(fmaxf(amax_x[0][rl], amax_x[1][rl]), fmaxf(amax_x[2][rl], amax_x[3][rl]));
+        const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+        const int r = t.row0 + rl;
+        if (r >= t.row1) continue;
+        uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) word |= static_cast<uint32_t>(e4m3_rne_sat(h[i][jj][v] / sc)) << (8 * v);
+          *reinterpret_cast<uint32_t*>(crow + col0 + jj * 16 + kq * 4) = word;
+        }
+        if (wave == 0 && kq == 0)
+          reinterpret_cast<float*>(p.C_scales)[(long long)r * (p.N / 128) + t.nt] = sc;
+      }
+    }
+  }
+}
+
 namespace {
 
 template <int FMT, int EPI>
@@ -350,15 +649,36 @@ hipError_t run_q(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int FMT, int EPI>
+hipError_t run_q_stream(const GemmArgs& a, hipStream_t s) {
+  constexpr int FM = 2;
+  constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
+  Grid g = make_grid(a, 16 * FM, SWIGLU ? 128 : 256, kQStreamGroupM, kQStreamGroupM);
+  if (g.total == 0) return hipSuccess;
+  gemm_q_stream_kernel<FMT, EPI, FM><<<dim3(g.blocks), dim3(256), 0, s>>>(a, g.n_tiles, g.x_tiles,
+                                                                        g.total);
+  return hipGetLastError();
+}
+
+// decode-sized groups (few rows per group on average) stream the weights; others use the tiles
+template <int FMT, int EPI>
+hipError_t run_q_choice(const GemmArgs& a, hipStream_t s) {
+  const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;
+  const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
+  const long long per_group = groups ? rows / groups : rows;
+  if (per_group <= 32 && a.N % 128 == 0) return run_q_stream<FMT, EPI>(a, s);
+  return run_q<FMT, EPI>(a, s);
+}
+
 template <int FMT>
 hipError_t run_q_fmt(const GemmArgs& a, hipStream_t s) {
   if (a.epilogue == MOE_EPI_SWIGLU) {
-    if (a.out_dtype == FMT) return run_q<FMT, QEPI_SWIGLU_Q>(a, s);
-    if (a.out_dtype == MOE_BF16) return run_q<FMT, QEPI_SWIGLU_BF16>(a, s);
+    if (a.out_dtype == FMT) return run_q_choice<FMT, QEPI_SWIGLU_Q>(a, s);
+    if (a.out_dtype == MOE_BF16) return run_q_choice<FMT, QEPI_SWIGLU_BF16>(a, s);
     return hipErrorInvalidValue;
   }
-  if (a.out_dtype == MOE_F32) return run_q<FMT, QEPI_STORE_F32>(a, s);
-  if (a.out_dtype == MOE_BF16) return run_q<FMT, QEPI_STORE_BF16>(a, s);
+  if (a.out_dtype == MOE_F32) return run_q_choice<FMT, QEPI_STORE_F32>(a, s);
+  if (a.out_dtype == MOE_BF16) return run_q_choice<FMT, QEPI_STORE_BF16>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -24,6 +24,8 @@ struct GemmArgs {
   int G;
   const int32_t* offsets;
   int max_rows;         // bound on offsets[G] (sizes the grid)
+  int expected_rows;    // rows the routed groups are expected to hold (tile-shape choice only;
+                        // 0: take max_rows); results never depend on it
   const void* B; const void* Bs; const void* B2; const void* B2s;
   long long b_stride;   // bytes between groups' B (and B2)
   long long bs_stride;  // bytes between groups' scales

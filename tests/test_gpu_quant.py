@@ -18,9 +18,20 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
 @pytest.mark.parametrize("counts", [[0, 37, 130, 1, 9], [300, 140, 0, 513]])
 def test_grouped_gemm_quant(fmt, epi, counts):
+    _quant_case(fmt, epi, counts, 512)
+
+
+# decode-sized groups (the weight-streaming kernel): empty groups, groups of 1-33 rows and one of
+# 40 (a second 32-row tile), and an odd number of 128-byte K-pairs per row
+@pytest.mark.parametrize("fmt", ["fp8", "mx4"])
+@pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
+def test_grouped_gemm_quant_decode(fmt, epi):
+    _quant_case(fmt, epi, [3, 0, 17, 40, 1, 8, 33, 2], 640 if fmt == "fp8" else 768)
+
+
+def _quant_case(fmt, epi, counts, K):
     dfmt, ofmt = FMTS[fmt]
     rng = np.random.default_rng([len(counts), sum(counts)])
-    K = 512
     swiglu = epi.startswith("swiglu")
     N = 256 if swiglu else 384                 # 384: a partial 256-column tile
     G = len(counts)
