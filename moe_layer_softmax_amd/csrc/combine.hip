@@ -10,9 +10,10 @@
 
 namespace moe {
 
-// Workgroup (t, c): token t, columns [c * 1024, c * 1024 + 1024), four per thread. All k rows'
-// loads are issued before the first is added (unconditional: a non-local slot reads row 0 and adds
-// nothing), so one token's latency is one memory round trip.
+// Workgroup (t, c): token t, columns [c * 256 * CPL, (c + 1) * 256 * CPL), CPL per thread (8 for
+// bf16 rows, 4 for fp32: one 16-byte load per row). All k rows' loads are issued before the first
+// is added (unconditional: a non-local slot reads row 0 and adds nothing), so one token's latency
+// is one memory round trip.
 template <bool Y_BF16, bool OUT_BF16>
 __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* __restrict__ y,
                                                       const float* __restrict__ w,
@@ -20,8 +21,9 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
                                                       const void* __restrict__ shared,
                                                       void* __restrict__ out) {
   constexpr int KMAX = 16;
+  constexpr int CPL = Y_BF16 ? 8 : 4;
   const int t = blockIdx.x;
-  const int c0 = blockIdx.y * 1024 + threadIdx.x * 4;
+  const int c0 = (blockIdx.y * 256 + threadIdx.x) * CPL;
   __shared__ int rows[KMAX];
   __shared__ float wts[KMAX];
   if (threadIdx.x < KMAX) {
@@ -30,51 +32,55 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
     wts[threadIdx.x] = in ? w[(size_t)t * k + threadIdx.x] : 0.0f;
   }
   __syncthreads();
-  if (c0 >= H) return;
-  f32x4 v[KMAX];
-#pragma unroll
-  for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
-      const long long r = rows[j] < 0 ? 0 : rows[j];
-      if (Y_BF16) {
-        const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(y) + r * H + c0);
-        v[j] = f32x4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                     __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u)};
-      } else {
-        v[j] = *reinterpret_cast<const f32x4*>(static_cast<const float*>(y) + r * H + c0);
-      }
-    }
-  }
-  f32x4 sh = f32x4{};
-  if (shared) {
+  if (c0 >= H) return;                      // H % 8 == 0: a thread's columns are all in or all out
+  auto load_row = [&](const void* base, long long r, float* v) {
     if (Y_BF16) {
-      const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(shared) + (size_t)t * H + c0);
-      sh = f32x4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xFFFF0000u),
-                 __uint_as_float(b.y << 16), __uint_as_float(b.y & 0xFFFF0000u)};
+      const i32x4 b = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(base) + r * H + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(static_cast<uint32_t>(b[q]) << 16);
+        v[2 * q + 1] = __uint_as_float(static_cast<uint32_t>(b[q]) & 0xFFFF0000u);
+      }
     } else {
-      sh = *reinterpret_cast<const f32x4*>(static_cast<const float*>(shared) + (size_t)t * H + c0);
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + r * H + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = a[q];
     }
-  }
+  };
+  float v[KMAX][CPL];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j)
+    if (j < k) load_row(y, rows[j] < 0 ? 0 : rows[j], v[j]);
+  float sh[CPL];
+  if (shared) load_row(shared, t, sh);
   // fp32 accumulation in slot order j = 0..k-1, the shared row last, one rounding
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = 0.0f;
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
     if (j < k && rows[j] >= 0) {
       const float wj = wts[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += wj * v[j][i];
+      for (int i = 0; i < CPL; ++i) acc[i] += wj * v[j][i];
     }
   }
   if (shared) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += sh[i];
+    for (int i = 0; i < CPL; ++i) acc[i] += sh[i];
   }
   if (OUT_BF16) {
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + (size_t)t * H + c0) =
-        make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
+    uint32_t o[CPL / 2];
+#pragma unroll
+    for (int i = 0; i < CPL / 2; ++i) o[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    uint16_t* dst = static_cast<uint16_t*>(out) + (size_t)t * H + c0;
+    if (CPL == 8) *reinterpret_cast<i32x4*>(dst) = i32x4{(int)o[0], (int)o[1], (int)o[2], (int)o[3]};
+    else *reinterpret_cast<uint2*>(dst) = make_uint2(o[0], o[1]);
   } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + (size_t)t * H + c0) =
-        f32x4{acc[0], acc[1], acc[2], acc[3]};
+    float* dst = static_cast<float*>(out) + (size_t)t * H + c0;
+#pragma unroll
+    for (int q = 0; q < CPL / 4; ++q)
+      *reinterpret_cast<f32x4*>(dst + 4 * q) = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
   }
 }
 
@@ -83,7 +89,8 @@ hipError_t launch_combine(int T, int H, int k, int y_dtype, int out_dtype, const
                           void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const bool yb = y_dtype == MOE_BF16, ob = out_dtype == MOE_BF16;
-  dim3 grid(T, (H + 1023) / 1024), block(256);
+  const int cols_per_wg = 256 * (yb ? 8 : 4);
+  dim3 grid(T, (H + cols_per_wg - 1) / cols_per_wg), block(256);
   if (yb && ob) combine_kernel<true, true><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);
   else if (yb) combine_kernel<true, false><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);
   else if (ob) combine_kernel<false, true><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);

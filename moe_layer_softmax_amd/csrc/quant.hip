@@ -13,13 +13,27 @@
 
 namespace moe {
 
+// 8 consecutive source elements starting at element i (i a multiple of 8), as fp32
 template <bool SRC_BF16>
-__device__ __forceinline__ float load_src(const void* src, size_t i) {
-  if (SRC_BF16) return bf16_to_f32(static_cast<const uint16_t*>(src)[i]);
-  return static_cast<const float*>(src)[i];
+__device__ __forceinline__ void load8(const void* src, size_t i, float* v) {
+  if (SRC_BF16) {
+    const i32x4 w = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(src) + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(static_cast<uint32_t>(w[q]) << 16);
+      v[2 * q + 1] = __uint_as_float(static_cast<uint32_t>(w[q]) & 0xFFFF0000u);
+    }
+  } else {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(src) + i + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { v[q] = a[q]; v[4 + q] = b[q]; }
+  }
 }
 
-// one workgroup per (batch, block of block_rows x 128)
+// One workgroup per (batch, block of block_rows x 128); block_rows is 1 or 128. Each thread holds
+// up to 8 chunks of 8 consecutive elements (16-byte loads) in registers, so the block is read once:
+// amax over the block, then the codes (8 per 8-byte store).
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256) quant_fp8_kernel(int rows, int cols, int block_rows,
                                                         const void* __restrict__ src,
@@ -32,11 +46,17 @@ __global__ void __launch_bounds__(256) quant_fp8_kernel(int rows, int cols, int 
   const size_t mat = (size_t)b * rows * cols;
   const int r0 = bi * block_rows;
   const int r1 = r0 + block_rows < rows ? r0 + block_rows : rows;
-  const int n = (r1 - r0) * 128;
+  const int nch = (r1 - r0) * 16;          // 8-element chunks of the block (<= 2048)
+  float v[8][8];
   float amax = 0.0f;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int r = r0 + i / 128, c = bj * 128 + (i & 127);
-    amax = fmaxf(amax, fabsf(load_src<SRC_BF16>(src, mat + (size_t)r * cols + c)));
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = threadIdx.x + u * 256;
+    if (i < nch) {
+      load8<SRC_BF16>(src, mat + (size_t)(r0 + i / 16) * cols + bj * 128 + (i % 16) * 8, v[u]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[u][e]));
+    }
   }
   __shared__ float red[4];
   amax = wave_max(amax);
@@ -45,39 +65,51 @@ __global__ void __launch_bounds__(256) quant_fp8_kernel(int rows, int cols, int 
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (threadIdx.x == 0) scales[((size_t)b * nbr + bi) * nbc + bj] = s;
-  for (int i = threadIdx.x; i < n; i += 256) {
-    const int r = r0 + i / 128, c = bj * 128 + (i & 127);
-    const size_t idx = mat + (size_t)r * cols + c;
-    codes[idx] = e4m3_rne_sat(load_src<SRC_BF16>(src, idx) / s);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = threadIdx.x + u * 256;
+    if (i < nch) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo |= static_cast<uint32_t>(e4m3_rne_sat(v[u][e] / s)) << (8 * e);
+        hi |= static_cast<uint32_t>(e4m3_rne_sat(v[u][4 + e] / s)) << (8 * e);
+      }
+      *reinterpret_cast<uint2*>(codes + mat + (size_t)(r0 + i / 16) * cols + bj * 128 + (i % 16) * 8) =
+          make_uint2(lo, hi);
+    }
   }
 }
 
-// one thread per 32-element group
+// Four lanes per 32-element group, 8 elements (one 16-byte bf16 load) each: group amax over the
+// four lanes, then each lane packs its 8 codes into one 32-bit word (element 2i in the low nibble
+// of byte i); the first lane writes the E8M0 scale.
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256) quant_mx4_kernel(long long groups, const void* __restrict__ src,
                                                         uint8_t* __restrict__ packed,
                                                         uint8_t* __restrict__ scales) {
-  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (g >= groups) return;
-  float v[32];
+  const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long g = tid >> 2;
+  const int sub = static_cast<int>(tid & 3);
+  const bool live = g < groups;
+  float v[8];
+  if (live) load8<SRC_BF16>(src, (size_t)g * 32 + sub * 8, v);
+  else
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = load_src<SRC_BF16>(src, (size_t)g * 32 + i);
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int e = mx_shared_exp(amax);
-  scales[g] = static_cast<uint8_t>(e + 127);
-  const float mul = ldexpf(1.0f, -e);
-  uint32_t w[4];
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int e8 = mx_shared_exp(amax);
+  const float mul = ldexpf(1.0f, -e8);
+  uint32_t word = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) word |= static_cast<uint32_t>(e2m1_rne_sat(v[q * 8 + i] * mul)) << (4 * i);
-    w[q] = word;
-  }
-  *reinterpret_cast<i32x4*>(packed + (size_t)g * 16) =
-      i32x4{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  for (int e = 0; e < 8; ++e) word |= static_cast<uint32_t>(e2m1_rne_sat(v[e] * mul)) << (4 * e);
+  if (!live) return;
+  *reinterpret_cast<uint32_t*>(packed + (size_t)g * 16 + sub * 4) = word;
+  if (sub == 0) scales[g] = static_cast<uint8_t>(e8 + 127);
 }
 
 hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int block_rows,
@@ -96,7 +128,7 @@ hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const 
                             uint8_t* packed, uint8_t* scales, hipStream_t s) {
   const long long groups = (long long)batch * rows * (cols / 32);
   if (groups == 0) return hipSuccess;
-  dim3 grid(static_cast<unsigned>((groups + 255) / 256));
+  dim3 grid(static_cast<unsigned>((groups * 4 + 255) / 256));
   if (src_dtype == MOE_BF16)
     quant_mx4_kernel<true><<<grid, 256, 0, s>>>(groups, src, packed, scales);
   else
