@@ -152,16 +152,23 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
     s_step[0] = 4;
   }
 
+  // load q of this wave's share of K-step kt (q < A_INS: A rows, then B rows, then scales)
+  auto issue_one = [&](int kt, int q) {
+    uint8_t* la = ldsq + (kt % S) * STAGE;
+    if (q < A_INS) {
+      dma_16b_asm(a_src[q] + (long long)kt * RB, la + (q * NW + wave) * 8 * RB);
+    } else if (q < A_INS + B_INS) {
+      const int j = q - A_INS;
+      dma_16b_asm(b_src[j] + (long long)kt * RB, la + BM * RB + (j * NW + wave) * 8 * RB);
+    } else {
+      const int j = q - A_INS - B_INS;
+      dma_4b_asm(s_src[j] + kt * s_step[j], la + s_dst[j]);
+    }
+  };
   auto issue = [&](int kt) {
     if (kt >= nk) return;
-    uint8_t* la = ldsq + (kt % S) * STAGE;
-    uint8_t* lb = la + BM * RB;
 #pragma unroll
-    for (int j = 0; j < A_INS; ++j) dma_16b_asm(a_src[j] + (long long)kt * RB, la + (j * NW + wave) * 8 * RB);
-#pragma unroll
-    for (int j = 0; j < B_INS; ++j) dma_16b_asm(b_src[j] + (long long)kt * RB, lb + (j * NW + wave) * 8 * RB);
-#pragma unroll
-    for (int j = 0; j < SINS; ++j) dma_4b_asm(s_src[j] + kt * s_step[j], la + s_dst[j]);
+    for (int q = 0; q < INS; ++q) issue_one(kt, q);
   };
 
   f32x4 acc[FM][FN];
@@ -195,8 +202,13 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   else wait_vmem();
   barrier_lds();
 
+  // The loads of step kt + S - 1 (its stage was released by the last barrier) are spread through
+  // the MFMAs of step kt, a few after each batch: issuing them in one block stalls the wave for
+  // as long as the address unit takes to accept them, with the matrix unit idle.
+  constexpr int BATCHES = SUB * (FN / NB);
+  constexpr int PER_BATCH = (INS + BATCHES - 1) / BATCHES;
   for (int kt = 0; kt < nk; ++kt) {
-    issue(kt + S - 1);                     // its stage was released by the last barrier
+    const bool do_load = kt + S - 1 < nk;
     const uint8_t* la = ldsq + (kt % S) * STAGE;
     const uint8_t* lb = la + BM * RB;
 
@@ -253,6 +265,16 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
               for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(tmp[v], fs[i * 4 + v][half], acc[i][j][v]);
             }
           }
+        MOE_SCHED_FENCE();
+        if (do_load) {
+          const int batch = s * (FN / NB) + b0 / NB;
+#pragma unroll
+          for (int u = 0; u < PER_BATCH; ++u) {
+            const int q = batch * PER_BATCH + u;
+            if (q < INS) issue_one(kt + S - 1, q);
+          }
+        }
+        MOE_SCHED_FENCE();
       }
     }
     if (kt + S - 1 < nk) wait_vmem_n<(S - 2) * INS>();   // step kt+1 landed
