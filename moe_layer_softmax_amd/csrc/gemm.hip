@@ -449,9 +449,13 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 // loads where they are written -- left alone, the scheduler sinks each load next to its use).
 // Loads past the end re-read the last pair and rows past the group's end re-read its last row, so
 // every load is unconditional and in bounds. Rows of C beyond 16 * FM per group take further tiles.
+//
+// KS > 1: the workgroup's KS waves split the tile's K pairs into KS contiguous ranges (more loads in
+// flight per CU for the same registers per wave); their fp32 partial sums meet in LDS and wave 0
+// adds them in wave order (deterministic) before the epilogue.
 // ------------------------------------------------------------------------------------------------
-template <int FM, bool SWIGLU, bool OUT_F32>
-__global__ void __launch_bounds__(64)
+template <int FM, int KS, bool SWIGLU, bool OUT_F32>
+__global__ void __launch_bounds__(64 * KS)
 gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
   // tile order: groups of 8 m-tiles with the m-tile fastest, 8 consecutive tiles per XCD, so the
@@ -491,11 +495,14 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   const int src0 = ((lr & 7) * 8 + kq) * 4, src1 = src0 + 16;
   const bool upper = lr >= 8;
 
-  const int np = p.K / 64;                             // pairs of K-steps
+  // this wave's pairs of K-steps: [c0, c0 + np)
+  const int wave = KS > 1 ? (int)(threadIdx.x >> 6) : 0;
+  const int np_all = p.K / 64;
+  const int c0 = np_all * wave / KS, np = np_all * (wave + 1) / KS - c0;
   i32x4 wraw[2][4][2];
   bf16x8 av[2][FM][2];
   auto load = [&](int c, int set) {
-    const long long off = (long long)min(c, np - 1) * 128;
+    const long long off = (long long)(c0 + min(c, np - 1)) * 128;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -533,20 +540,39 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
           acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], av[set][i][s2], acc[j][i], 0, 0, 0);
     }
   };
-  load(0, 0);
-  int c = 0;
-  for (; c + 1 < np; c += 2) {
+  if (np > 0) {                                        // wave-uniform; np = 0 only if K < 64 * KS
+    load(0, 0);
+    int c = 0;
+    for (; c + 1 < np; c += 2) {
+      MOE_SCHED_FENCE();
+      load(c + 1, 1);
+      MOE_SCHED_FENCE();
+      compute(0);
+      MOE_SCHED_FENCE();
+      load(c + 2, 0);
+      MOE_SCHED_FENCE();
+      compute(1);
+    }
     MOE_SCHED_FENCE();
-    load(c + 1, 1);
-    MOE_SCHED_FENCE();
-    compute(0);
-    MOE_SCHED_FENCE();
-    load(c + 2, 0);
-    MOE_SCHED_FENCE();
-    compute(1);
+    if (c < np) compute(0);                            // odd number of pairs: the last is in set 0
   }
-  MOE_SCHED_FENCE();
-  if (c < np) compute(0);                              // odd number of pairs: the last is in set 0
+  if constexpr (KS > 1) {
+    __shared__ f32x4 part[KS - 1][4][FM][64];
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) part[wave - 1][j][i][lane] = acc[j][i];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < KS - 1; ++w)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] += part[w][j][i][lane];
+  }
 
   // acc[j][i][v]: weight row j * 16 + kq * 4 + v of the tile, C row row0 + i * 16 + lr
   char* C = static_cast<char*>(p.C);
@@ -670,6 +696,9 @@ constexpr int kTileSpan = 64;
 constexpr int kPPStages = 5;
 // weight-streaming tiles of 32 rows up to this many rows per group on average, 64 rows above
 constexpr int kStreamRows32 = 24;
+// weight streaming: K pairs (128 bytes of every weight row) per wave at or above which a tile is
+// split over 4 waves (the long-K gate/up projection; a short K loop is dominated by its start-up)
+constexpr int kStreamSplitPairs = 64;
 
 template <int BM, int BN, int WM, int WN, int MI, int BK, int S>
 hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) {
@@ -709,15 +738,15 @@ hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   return hipGetLastError();
 }
 
-template <int FM>
+template <int FM, int KS>
 hipError_t run_bf16_stream(const GemmArgs& a, hipStream_t s) {
   const bool sw = a.epilogue == MOE_EPI_SWIGLU;
   Grid g = make_grid(a, 16 * FM, sw ? 32 : 64, kStreamGroupM, kStreamGroupM);
   if (g.total == 0) return hipSuccess;
-  dim3 grid(g.blocks), block(64);
+  dim3 grid(g.blocks), block(64 * KS);
   const bool f32 = a.out_dtype == MOE_F32;
 #define MOE_RUN(SWI, F32) \
-  gemm_bf16_stream_kernel<FM, SWI, F32><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.total)
+  gemm_bf16_stream_kernel<FM, KS, SWI, F32><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.total)
   if (sw && f32) MOE_RUN(true, true);
   else if (sw) MOE_RUN(true, false);
   else if (f32) MOE_RUN(false, true);
@@ -767,8 +796,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
     // decode-sized groups: stream the weights once per 32 (or 64) rows of each group
-    if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32))
-      return per_group <= kStreamRows32 ? run_bf16_stream<2>(a, s) : run_bf16_stream<4>(a, s);
+    if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32)) {
+      const bool split = a.K / 64 >= kStreamSplitPairs;
+      if (per_group <= kStreamRows32)
+        return split ? run_bf16_stream<2, 4>(a, s) : run_bf16_stream<2, 1>(a, s);
+      return split ? run_bf16_stream<4, 4>(a, s) : run_bf16_stream<4, 1>(a, s);
+    }
     return run_bf16<32, 128, 1, 4, 16, 64, 4>(a, s);
   }
   return hipErrorInvalidValue;

@@ -240,8 +240,9 @@ def test_grouped_gemm_bf16(counts, swiglu, gather):
 
 
 # decode-sized groups (the weight-streaming kernel): groups of 0, 1, 63, 64 and 65 rows (a second
-# 64-row tile), K with an odd number of 64-wide steps (the 2-deep register ring) and the 4-deep one
-@pytest.mark.parametrize("K", [320, 1536])
+# 64-row tile), K of one 64-wide step, an odd number of steps (the 2-deep register ring), and a
+# long K whose 65 steps are split over four waves (16, 16, 16 and 17 steps)
+@pytest.mark.parametrize("K", [64, 320, 1536, 4160])
 @pytest.mark.parametrize("swiglu", [False, True])
 @pytest.mark.parametrize("gather", [False, True])
 def test_grouped_gemm_bf16_decode_groups(K, swiglu, gather):
