@@ -275,6 +275,20 @@ def test_grouped_gemm_bf16_f32_out(counts, K, N):
     assert np.abs(Cg[:R] - ref).max() <= 1e-4 * rms * np.sqrt(K / 256)
 
 
+# more 256 x 256 tiles (459, the last n-tile partial) than CUs: the down projection's persistent
+# kernel gives each workgroup several tiles, priming each next tile's loads behind the stores
+@pytest.mark.parametrize("out_f32", [False, True])
+def test_grouped_gemm_bf16_persistent_tiles(out_f32):
+    Cg, ref, R = _gemm_case([1500, 1300, 0, 2701, 900], K=128, N=4160, swiglu=False, gather=False,
+                            out_f32=out_f32)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if out_f32:
+        assert np.abs(Cg[:R] - ref).max() <= 1e-4 * rms
+    else:
+        assert np.all(np.abs(Cg[:R] - ref) <= 2 ** -8 * np.abs(ref) + 1e-3 * rms)
+    assert np.all(Cg[R:] == 1024.0)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_f32(swiglu):
     Cg, ref, R = _gemm_case([20, 0, 65, 7], K=256, N=128, swiglu=swiglu, gather=True, out_f32=True,
