@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8, MX4 = 0, 1, 2, 3
+F32, BF16, FP8, MX4, MX8 = 0, 1, 2, 3, 4
 SOFTMAX, SIGMOID = 0, 1
 
 
@@ -122,8 +122,19 @@ def quant_mx4(src):
     return packed, scales
 
 
+def quant_mx8(src):
+    """e4m3 codes [rows, cols] and E8M0 scales [rows, cols/32] (MXFP8)."""
+    src = _c(src, np.float32)
+    rows, cols = src.shape
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    lib().oracle_quant_mx8(rows, cols, _p(src), _p(codes), _p(scales))
+    return codes, scales
+
+
 class Mat:
-    """A stack of G [N, K] matrices in one of the formats F32 / FP8 / MX4 (keeps its arrays)."""
+    """A stack of G [N, K] matrices in one of the formats F32 / FP8 / MX4 / MX8 (keeps its
+    arrays)."""
 
     def __init__(self, fmt, q, s=None, bn=128, bk=128):
         self.fmt = fmt
@@ -167,6 +178,9 @@ def quantise_stack(fmt, w):
     if fmt == MX4:
         qs, ss = zip(*(quant_mx4(w[g]) for g in range(G)))
         return Mat(MX4, np.stack(qs), np.stack(ss))
+    if fmt == MX8:
+        qs, ss = zip(*(quant_mx8(w[g]) for g in range(G)))
+        return Mat(MX8, np.stack(qs), np.stack(ss))
     raise ValueError(fmt)
 
 

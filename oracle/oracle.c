@@ -164,6 +164,37 @@ void oracle_quant_mx4(int rows, int cols, const float* src, uint8_t* packed, uin
     }
 }
 
+/* The MX shared exponent of one group: floor(log2(amax)) minus the element format's largest
+ * exponent (2 for e2m1, 8 for e4m3), clamped to the E8M0 range; -127 for an all-zero group. */
+static int mx_shared_exp(float amax, int emax_elem)
+{
+  if (amax == 0.0f) return -127;
+  int ex;
+  frexpf(amax, &ex);                  /* floor(log2(amax)) = ex - 1 */
+  int e = (ex - 1) - emax_elem;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+void oracle_quant_mx8(int rows, int cols, const float* src, uint8_t* codes, uint8_t* scales)
+{
+  int ng = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; ++r)
+    for (int g = 0; g < ng; ++g) {
+      const float* v = src + (size_t)r * cols + (size_t)g * 32;
+      float amax = 0.0f;
+      for (int i = 0; i < 32; ++i)
+        if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+      int e = mx_shared_exp(amax, 8);
+      scales[(size_t)r * ng + g] = (uint8_t)(e + 127);
+      float mul = ldexpf(1.0f, -e);   /* exact power of two */
+      uint8_t* out = codes + (size_t)r * cols + (size_t)g * 32;
+      for (int i = 0; i < 32; ++i) out[i] = oracle_e4m3_encode(v[i] * mul);
+    }
+}
+
 double oracle_mat_at(const oracle_mat* m, int g, int n, int kk)
 {
   size_t row = (size_t)g * m->N + n;
@@ -181,6 +212,11 @@ double oracle_mat_at(const oracle_mat* m, int g, int n, int kk)
     uint8_t nib = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
     uint8_t sc = ((const uint8_t*)m->s)[row * (m->K / 32) + kk / 32];
     return oracle_e2m1_value(nib) * oracle_e8m0_value(sc);
+  }
+  case ORACLE_MX8: {
+    uint8_t c = ((const uint8_t*)m->q)[row * m->K + kk];
+    uint8_t sc = ((const uint8_t*)m->s)[row * (m->K / 32) + kk / 32];
+    return oracle_e4m3_value(c) * oracle_e8m0_value(sc);
   }
   default:
     return NAN;
@@ -338,6 +374,16 @@ static void quantise_h(int act_fmt, int I, double* h)
     oracle_mat m = {ORACLE_MX4, 1, 1, I, 0, 0, pk, sc};
     for (int i = 0; i < I; ++i) h[i] = oracle_mat_at(&m, 0, 0, i);
     free(hf); free(pk); free(sc);
+  } else if (act_fmt == ORACLE_MX8) {
+    /* 1 x 32 groups along the intermediate dimension, decisions on the fp32 value of h */
+    float* hf = (float*)calloc((size_t)I, sizeof(float));
+    uint8_t* cd = (uint8_t*)malloc((size_t)I);
+    uint8_t* sc = (uint8_t*)malloc((size_t)I / 32);
+    for (int i = 0; i < I; ++i) hf[i] = (float)h[i];
+    oracle_quant_mx8(1, I, hf, cd, sc);
+    oracle_mat m = {ORACLE_MX8, 1, 1, I, 0, 0, cd, sc};
+    for (int i = 0; i < I; ++i) h[i] = oracle_mat_at(&m, 0, 0, i);
+    free(hf); free(cd); free(sc);
   }
 }
 

@@ -41,7 +41,8 @@ enum {
   ORACLE_F32 = 0,   /* float values (fp32 and bf16 workloads)                                   */
   ORACLE_BF16 = 1,  /* activation format only: h rounded to bf16 before the down projection      */
   ORACLE_FP8 = 2,   /* e4m3 codes [G,N,K] + fp32 scales [G, ceil(N/bn), ceil(K/bk)]           */
-  ORACLE_MX4 = 3    /* e2m1 codes, 2 per byte, [G,N,K/2] + E8M0 scales [G, N, K/32]            */
+  ORACLE_MX4 = 3,   /* e2m1 codes, 2 per byte, [G,N,K/2] + E8M0 scales [G, N, K/32]            */
+  ORACLE_MX8 = 4    /* e4m3 codes [G,N,K] + E8M0 scales [G, N, K/32] (MXFP8)                    */
 };
 
 /* A stack of G matrices of shape [N, K] (K contiguous) in one of the formats above. */
@@ -70,6 +71,12 @@ void oracle_quant_fp8(int rows, int cols, int bn, int bk, const float* src,
  * element code = e2m1(v * 2^-e). Element 2i sits in bits 0-3 of byte i, element 2i+1 in bits 4-7.
  * cols % 32 == 0. packed: [rows, cols/2]; scales: [rows, cols/32]. */
 void oracle_quant_mx4(int rows, int cols, const float* src, uint8_t* packed, uint8_t* scales);
+/* MXFP8 (E4M3) quantiser: per row, per 32 consecutive columns: shared exponent
+ * e = floor(log2(amax)) - 8 (8 is the largest e4m3 exponent; clamped to [-127, 127], -127 when
+ * amax = 0), E8M0 code e + 127, element code = e4m3(v * 2^-e) rounded to nearest even and
+ * saturated to +-448 (scaled values reach up to 2^9). cols % 32 == 0. codes: [rows, cols];
+ * scales: [rows, cols/32]. */
+void oracle_quant_mx8(int rows, int cols, const float* src, uint8_t* codes, uint8_t* scales);
 
 /* value of element (g, n, kk) of a matrix stack */
 double oracle_mat_at(const oracle_mat* m, int g, int n, int kk);
@@ -101,8 +108,8 @@ typedef struct {
   int scoring, renormalize;
   int act_fmt;            /* format of h, the input of the down projection: ORACLE_F32: as
                              computed; ORACLE_BF16: rounded to bf16; ORACLE_FP8: e4m3 with 1x128
-                             fp32 scales; ORACLE_MX4: MXFP4 (x arrives pre-quantised in `xa` for
-                             both quantised formats)                                               */
+                             fp32 scales; ORACLE_MX4: MXFP4; ORACLE_MX8: MXFP8 (x arrives
+                             pre-quantised in `xa` for the quantised formats)                      */
 } oracle_desc;
 
 /* SwiGLU FFN of one activation row a[H] through matrix g of the gate/up/down stacks:

@@ -136,6 +136,112 @@ def test_mx4_scale_rule_and_roundtrip():
     assert np.all(np.abs(dq[~inside]) == 6 * unit[~inside])
 
 
+def _golden_kv(name):
+    lines = {}
+    for line in open(os.path.join(GOLD, name)):
+        if line.startswith("#") or ":" not in line:
+            continue
+        key, val = line.split(":", 1)
+        lines[key.strip()] = val.split()
+    return lines
+
+
+def test_mx8_hand_example():
+    lines = _golden_kv("mx8_block_example.txt")
+    vals = np.array([float(v) for v in lines["values"]], np.float32)[None]
+    codes, scales = oracle.quant_mx8(vals)
+    assert [int(s) for s in scales[0]] == [int(s) for s in lines["scales"]]
+    assert [int(c) for c in codes[0]] == [int(c, 0) for c in lines["codes"]]
+
+
+def test_mx8_scale_rule_and_codes_match_torch_cast():
+    """Shared exponent: amax in [2^(e+8), 2^(e+9)) gives e. Codes: torch's round-to-nearest-even
+    e4m3 cast of v * 2^-e after clamping to +-448 (torch's cast does not saturate)."""
+    rng = np.random.default_rng(21)
+    for e in range(-30, 30):
+        amax = np.float32(2.0 ** (e + 8) * (1 + rng.random() * 0.999))
+        v = ((rng.random((3, 32)) * 2 - 1) * amax).astype(np.float32)
+        v[1, :8] *= np.float32(1e-3)                 # small elements go subnormal in e4m3
+        v[:, 8 + rng.integers(24)] = amax
+        c, s = oracle.quant_mx8(v)
+        assert np.all(s == e + 127)
+        q = np.clip(v * np.float32(2.0 ** -e), -448, 448).astype(np.float32)
+        ref = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(c, ref), e
+    c, s = oracle.quant_mx8(np.zeros((2, 64), np.float32))
+    assert np.all(s == 0) and not c.any()
+
+
+def test_mx8_roundtrip_and_error_bound():
+    rng = np.random.default_rng(22)
+    # E4M3 grid values times 2^e, with 448 * 2^e present in every group, survive exactly
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)], np.float64)
+    for e in (-9, -1, 0, 4):
+        v = rng.choice(grid, size=(3, 64)) * rng.choice([-1, 1], size=(3, 64))
+        v[:, 0] = 448.0
+        v[:, 40] = -448.0
+        v = (v * 2.0 ** e).astype(np.float32)
+        c, s = oracle.quant_mx8(v)
+        assert np.all(s == e + 127)
+        m = oracle.Mat(oracle.MX8, c[None], s[None])
+        assert np.array_equal(m.dequant()[0], v.astype(np.float64))
+    # error: within the normal E4M3 range at most half a step (2^-4 relative), below the
+    # subnormal threshold at most 2^-10 * 2^e; values above 448 * 2^e saturate
+    v = rng.standard_normal((16, 256)).astype(np.float32) * np.float32(3.0)
+    c, s = oracle.quant_mx8(v)
+    dq = oracle.Mat(oracle.MX8, c[None], s[None]).dequant()[0]
+    unit = np.repeat(2.0 ** (s.astype(np.int32) - 127), 32, axis=1)
+    a = np.abs(v.astype(np.float64))
+    err = np.abs(dq - v)
+    normal = (a >= 2.0 ** -6 * unit) & (a <= 448 * unit)
+    sub = a < 2.0 ** -6 * unit
+    sat = a > 448 * unit
+    assert np.all(err[normal] <= a[normal] * 2.0 ** -4)
+    assert np.all(err[sub] <= 2.0 ** -10 * unit[sub])
+    assert np.all(np.abs(dq[sat]) == 448 * unit[sat]) and np.all(err[sat] < 64 * unit[sat])
+
+
+def test_ffn_quantised_activations_mx8():
+    """h quantised to MXFP8 (1x32 groups along I): equals the dense FFN with h passed through the
+    independent scale rule and torch's e4m3 cast of the clamped quotient."""
+    rng = np.random.default_rng(23)
+    H, I = 64, 128
+    a = rng.standard_normal(H)
+    wg, wu = (rng.standard_normal((I, H)) * 0.1 for _ in range(2))
+    wd = rng.standard_normal((H, I)) * 0.1
+    M = oracle.Mat
+    y = oracle.ffn_row(a, M(oracle.F32, wg.astype(np.float32)), M(oracle.F32, wu.astype(np.float32)),
+                       M(oracle.F32, wd.astype(np.float32)), act_fmt=oracle.MX8)
+    wg32, wu32, wd32 = (w.astype(np.float32).astype(np.float64) for w in (wg, wu, wd))
+    gg, uu = a @ wg32.T, a @ wu32.T
+    h = (gg * expit(gg) * uu).astype(np.float32)
+    hq = np.empty(I)
+    for b in range(0, I, 32):
+        blk = h[b:b + 32]
+        e = int(np.floor(np.log2(np.abs(blk).max()))) - 8
+        q = np.clip(blk * np.float32(2.0 ** -e), -448, 448).astype(np.float32)
+        c = torch.from_numpy(q).to(torch.float8_e4m3fn).float().numpy()
+        hq[b:b + 32] = c.astype(np.float64) * 2.0 ** e
+    assert np.allclose(y, hq @ wd32.T, rtol=1e-12, atol=1e-12)
+
+
+def test_grouped_gemm_mx8_equals_dequantised_matmul():
+    rng = np.random.default_rng(24)
+    K, N, T = 256, 96, 40
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((2, N, K)) * 0.02).astype(np.float32)
+    xc, xs = oracle.quant_mx8(x)
+    xa = oracle.Mat(oracle.MX8, xc[None], xs[None])
+    wm = oracle.quantise_stack(oracle.MX8, w)
+    assert wm.q.shape == (2, N, K) and wm.s.shape == (2, N, K // 32)
+    off = np.array([0, 15, T], np.int32)
+    out = oracle.grouped_gemm(off, xa, wm)
+    xd, wd = xa.dequant()[0], wm.dequant()
+    for g in range(2):
+        ref = xd[off[g]:off[g + 1]] @ wd[g].T
+        assert np.allclose(out[off[g]:off[g + 1]], ref, rtol=0, atol=1e-12)
+
+
 def test_fp8_block_quantiser():
     rng = np.random.default_rng(3)
     w = rng.standard_normal((256, 384)).astype(np.float32) * 0.02
