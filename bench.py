@@ -45,7 +45,7 @@ def parse():
     return p.parse_args()
 
 
-PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp4": 10066.3}
+PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3}
 
 
 def workload_table(stream, steps):
@@ -58,10 +58,10 @@ def workload_table(stream, steps):
     import moe_layer_softmax_amd as moe
     from moe_inputs import gen
     fmt_of = {mi.FMT_BF16: ("bf16", moe.MOE_BF16), mi.FMT_FP8: ("fp8", moe.MOE_FP8_E4M3),
-              mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4)}
+              mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8)}
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     out = {}
-    for name in ("C2p", "C2d", "C3a", "C3b", "C4p", "C4d", "C5p", "C5d"):
+    for name in ("C2p", "C2d", "C3a", "C3b", "C4p", "C4d", "C5p", "C5d", "C2p_mx8", "C2d_mx8"):
         wl = mi.WORKLOADS[name]
         fname, fcode = fmt_of[wl.fmt]
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
@@ -85,6 +85,9 @@ def workload_table(stream, steps):
                 if fname == "fp8":
                     c = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
                     s = torch.empty((G, R // 128, C // 128), dtype=torch.float32, device="cuda")
+                elif fname == "mxfp8":
+                    c = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
+                    s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
                 else:
                     c = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
                     s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")

@@ -7,7 +7,8 @@
  *   w_tj     = softmax over S_t, or sigmoid(L) / sum over S_t of sigmoid(L)
  *   out_t    = sum_{j : e_tj local} w_tj * FFN_{e_tj}(a_t)  [+ FFN_shared(a_t)]
  *   FFN_e(a) = W_down,e ( silu(W_gate,e a) * (W_up,e a) )
- * where a_t is x_t, or x_t after the activation quantiser for the fp8 / MXFP4 expert formats.
+ * where a_t is x_t, or x_t after the activation quantiser for the fp8 / MXFP4 / MXFP8 expert
+ * formats.
  *
  * Passages that define the steps (cited by page title and section):
  *   - "Hosting Qwen on Blackwell", section "Prefillers": top-8 routing over 128 experts makes each
@@ -63,8 +64,11 @@ typedef enum {
   MOE_F32 = 0,        /* fp32                                                                  */
   MOE_BF16 = 1,       /* bf16                                                                  */
   MOE_FP8_E4M3 = 2,   /* OCP e4m3 bytes with fp32 block scales                                 */
-  MOE_MXFP4 = 3       /* OCP e2m1, two per byte (element 2i in bits 0-3 of byte i), E8M0 scale
+  MOE_MXFP4 = 3,      /* OCP e2m1, two per byte (element 2i in bits 0-3 of byte i), E8M0 scale
                          byte per 32 consecutive elements along K                             */
+  MOE_MXFP8 = 4       /* OCP e4m3 bytes with an E8M0 scale byte per 32 consecutive elements
+                         along K (OCP MX v1.0 MXFP8; the MoE GEMM format of "Hosting Qwen on
+                         Blackwell", section "Quantization")                                  */
 } moe_dtype;
 
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_scoring;
@@ -87,7 +91,7 @@ typedef struct {
                            local experts; fp32 keeps it unrounded for the reduction across
                            expert-parallel ranks that follows the layer                        */
   int32_t expert_dtype; /* expert weights and GEMM activations: MOE_F32 (io F32 only),
-                           MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4                                  */
+                           MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8                       */
 } moe_desc;
 
 /* Expert weights of one layer, in expert_dtype:
@@ -96,6 +100,7 @@ typedef struct {
  *                down [E_loc, H/128, I/128].
  *   MXFP4:       packed codes gate/up [E_loc, I, H/2], down [E_loc, H, I/2]; E8M0 scales
  *                gate/up [E_loc, I, H/32], down [E_loc, H, I/32].
+ *   MXFP8:       codes gate/up [E_loc, I, H], down [E_loc, H, I]; E8M0 scales as for MXFP4.
  * The shared expert (sh_*) has the same layouts with E_loc = 1 and I = I_s; NULL when I_s = 0.
  * w_router is [E, H] in io_dtype. Produce quantised weights with moe_quantize. */
 typedef struct {
@@ -131,6 +136,7 @@ size_t moe_route_workspace_bytes(const moe_desc* d);
  *   FP8_E4M3:   e4m3 [T, H] + fp32 a_in_scales [ceil(T/128), H/128] (128x128 blocks);
  *               a_perm_scales receives [T*k, H/128] (the block row of each token).
  *   MXFP4:      packed [T, H/2] + E8M0 [T, H/32]; a_perm_scales receives [T*k, H/32].
+ *   MXFP8:      e4m3 [T, H] + E8M0 [T, H/32]; a_perm_scales receives [T*k, H/32].
  * a_perm: [T*k, row bytes] (R rows written), or NULL to produce only the maps.
  * ws: moe_permute_workspace_bytes(d) bytes of device scratch. */
 moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a_in,
@@ -148,9 +154,10 @@ size_t moe_permute_workspace_bytes(const moe_desc* d);
  * dtype is the format of A and B (see moe_weights for B and its scales; A and its scales follow
  * moe_permute's a_perm). out_dtype: STORE -> MOE_F32 | MOE_BF16; SWIGLU -> MOE_F32 | MOE_BF16, or
  * the next GEMM's input format (MOE_FP8_E4M3: fp32 C_scales [max_rows, N/128] per 1x128 block;
- * MOE_MXFP4: C_scales [max_rows, N/32]). a_scale_rows: 128 when A's fp8 scales are per
- * 128-row block of A (a token-order x), else 1. Rows outside every group are not written.
- * Preconditions: K % 128 == 0 (K % 64 for BF16/F32), N % 64 == 0; dtype F32 needs out F32. */
+ * MOE_MXFP4 and MOE_MXFP8: C_scales [max_rows, N/32]). a_scale_rows: 128 when A's fp8 scales
+ * are per 128-row block of A (a token-order x), else 1. Rows outside every group are not written.
+ * Preconditions: K % 128 == 0 (K % 256 for MXFP4, K % 64 for BF16/F32), N % 64 == 0 (N % 128
+ * for the quantised formats); dtype F32 needs out F32. */
 typedef struct {
   int32_t G;            /* groups (experts)                                                   */
   int32_t max_rows;     /* rows of C (and of A when a_rows == NULL)                           */
@@ -185,8 +192,11 @@ moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const 
  *   MOE_MXFP4:    packed [rows, cols/2], E8M0 scales [rows, cols/32]: per 32 elements
  *                 e = floor(log2(amax)) - 2 clamped to [-127,127] (-127 if amax = 0),
  *                 code = e2m1(v * 2^-e) rounded to nearest even, saturated to +-6 (OCP MX v1.0).
+ *   MOE_MXFP8:    codes [rows, cols], E8M0 scales [rows, cols/32]: per 32 elements
+ *                 e = floor(log2(amax)) - 8 clamped to [-127,127] (-127 if amax = 0),
+ *                 code = e4m3(v * 2^-e) rounded to nearest even, saturated to +-448.
  * Element signs are kept (a value rounding to zero keeps its sign bit). cols % 128 == 0 (FP8) or
- * cols % 32 == 0 (MXFP4). `batch` stacked matrices are quantised independently (weights of
+ * cols % 32 == 0 (MXFP4, MXFP8). `batch` stacked matrices are quantised independently (weights of
  * E_loc experts): src, codes and scales are then [batch, ...] of the shapes above. */
 moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int32_t rows,
                         int32_t cols, int32_t block_rows, const void* src, void* codes,
@@ -198,7 +208,8 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
  * is out_dtype. logits [T,E], topk_ids [T,k], topk_w [T,k] are optional outputs (NULL: kept in the
  * workspace). out is this GPU's partial sum over its local experts plus the shared expert.
  * Intermediate formats: h (the down projection's input) is in the expert format (bf16 for bf16
- * experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for fp8/MXFP4.
+ * experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for
+ * fp8/MXFP4/MXFP8.
  * Requires I_s == 0 or I_s == I. ws: moe_layer_workspace_bytes(d) bytes. */
 moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, const float* bias,
                      void* out, float* logits, int32_t* topk_ids, float* topk_w, void* ws,

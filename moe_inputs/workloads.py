@@ -11,6 +11,8 @@ Shape sources (pages):
   * DeepSeek-V3 with 4-bit MoE weights and 4-bit dispatch ("Driving vLLM WideEP ... on Blackwell
     (Part I)", section on lower-precision operations); block scaling as used for DeepSeek
     (Hosting Qwen on Blackwell, section "Quantization").
+  * The Qwen3-235B slice in MXFP8, the format the Qwen deployment uses for its MoE GEMMs (Hosting
+    Qwen on Blackwell, section "Quantization").
 """
 from dataclasses import dataclass, replace
 
@@ -23,6 +25,7 @@ FMT_F32 = 0      # fp32 values (tiny config)
 FMT_BF16 = 1     # bf16 values
 FMT_FP8 = 2      # OCP e4m3 codes with fp32 scales per 128x128 block (weights, x) / 1x128 (h)
 FMT_MX4 = 3      # OCP e2m1 codes, two per byte, with one E8M0 scale per 32 elements along K
+FMT_MX8 = 4      # OCP e4m3 codes with one E8M0 scale per 32 elements along K (MXFP8)
 
 
 @dataclass(frozen=True)
@@ -68,4 +71,7 @@ WORKLOADS = {
     # same shape, MXFP4 experts and activations
     "C5p": Workload("C5p", 16384, 7168, 256, 0, 32, 2048, 8, 2048, SIGMOID, 1, FMT_BF16, FMT_MX4, 1.2),
     "C5d": Workload("C5d", 64, 7168, 256, 0, 32, 2048, 8, 2048, SIGMOID, 1, FMT_BF16, FMT_MX4, 0.0),
+    # the Qwen3-235B-shaped slice with MXFP8 experts and activations (x and h in MXFP8)
+    "C2p_mx8": Workload("C2p_mx8", 16384, 4096, 128, 0, 32, 1536, 8, 0, SOFTMAX, 1, FMT_BF16, FMT_MX8, 1.1),
+    "C2d_mx8": Workload("C2d_mx8", 64, 4096, 128, 0, 32, 1536, 8, 0, SOFTMAX, 1, FMT_BF16, FMT_MX8, 1.1),
 }

@@ -35,10 +35,13 @@ size_t round_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 
 int io_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
+// block-scaled 8-bit / 4-bit formats (quantised codes + scales)
+bool quantised(int dt) { return dt == MOE_FP8_E4M3 || dt == MOE_MXFP4 || dt == MOE_MXFP8; }
+// MX formats: one E8M0 scale byte per 32 elements along K
+bool mx_format(int dt) { return dt == MOE_MXFP4 || dt == MOE_MXFP8; }
+
 // format of the per-slot expert outputs y inside moe_layer
-int y_dtype_of(const moe_desc* d) {
-  return (d->expert_dtype == MOE_FP8_E4M3 || d->expert_dtype == MOE_MXFP4) ? MOE_BF16 : MOE_F32;
-}
+int y_dtype_of(const moe_desc* d) { return quantised(d->expert_dtype) ? MOE_BF16 : MOE_F32; }
 
 // bytes of one activation row of `cols` elements in expert format dt
 long long row_bytes(int dt, long long cols) {
@@ -47,13 +50,14 @@ long long row_bytes(int dt, long long cols) {
     case MOE_BF16: return cols * 2;
     case MOE_FP8_E4M3: return cols;
     case MOE_MXFP4: return cols / 2;
+    case MOE_MXFP8: return cols;
     default: return 0;
   }
 }
 
 bool valid_io(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 bool valid_expert(int dt) {
-  return dt == MOE_F32 || dt == MOE_BF16 || dt == MOE_FP8_E4M3 || dt == MOE_MXFP4;
+  return dt == MOE_F32 || dt == MOE_BF16 || quantised(dt);
 }
 
 moe_status check_desc(const moe_desc* d) {
@@ -75,12 +79,13 @@ moe_status check_desc(const moe_desc* d) {
 }
 
 // K (and N) granularity of the expert GEMMs: one K-step row slice is 128 bytes for bf16 / fp8 /
-// MXFP4 (64 / 128 / 256 elements), 16 elements for fp32
+// MXFP8 / MXFP4 (64 / 128 / 128 / 256 elements), 16 elements for fp32
 int k_align(int dt) {
   switch (dt) {
     case MOE_F32: return 16;
     case MOE_BF16: return 64;
     case MOE_FP8_E4M3: return 128;
+    case MOE_MXFP8: return 128;
     default: return 256;
   }
 }
@@ -98,7 +103,7 @@ moe_status check_expert_shapes(const moe_desc* d) {
 // bytes between consecutive experts' scale arrays of an [N, K] weight matrix
 long long scale_bytes(int dt, long long N, long long K) {
   if (dt == MOE_FP8_E4M3) return (N / 128) * (K / 128) * 4;
-  if (dt == MOE_MXFP4) return N * (K / 32);
+  if (mx_format(dt)) return N * (K / 32);
   return 0;
 }
 
@@ -142,10 +147,10 @@ LayerWs layer_ws(const moe_desc* d) {
     L.xs = take((T + 127) / 128 * (H / 128) * 4);
     L.h = take(rows * I);
     L.hs = take(rows * (I / 128) * 4);
-  } else if (dt == MOE_MXFP4) {
-    L.xq = take(T * H / 2);
+  } else if (mx_format(dt)) {
+    L.xq = take(row_bytes(dt, H) * T);
     L.xs = take(T * (H / 32));
-    L.h = take(rows * I / 2);
+    L.h = take(row_bytes(dt, I) * rows);
     L.hs = take(rows * (I / 32));
   } else {
     L.h = take(rows * I * io_bytes(d->io_dtype));
@@ -256,12 +261,11 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a
     return MOE_ERR_INVALID_ARG;
   if (!ok_opt(a_perm) || !ok_opt(a_perm_scales) || !ok_opt(ws)) return MOE_ERR_INVALID_ARG;
   const int dt = d->expert_dtype;
-  const bool quant = dt == MOE_FP8_E4M3 || dt == MOE_MXFP4;
+  const bool quant = quantised(dt);
   if (a_perm) {
     if (!ok_ptr(a_in)) return MOE_ERR_INVALID_ARG;
     if (quant && (!ok_ptr(a_in_scales) || !ok_ptr(a_perm_scales))) return MOE_ERR_INVALID_ARG;
-    if (dt == MOE_FP8_E4M3 && d->H % 128) return MOE_ERR_INVALID_ARG;
-    if (dt == MOE_MXFP4 && d->H % 128) return MOE_ERR_INVALID_ARG;
+    if (quant && d->H % 128) return MOE_ERR_INVALID_ARG;
     if (dt == MOE_F32 && d->io_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   }
   if (ws_bytes < permute_ws_bytes(slots, d->E_loc) || (slots > 16 * 1024 && !ws))
@@ -273,7 +277,7 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a
   long long sbytes = 0;
   int sblock = 1;
   if (dt == MOE_FP8_E4M3) { sbytes = (long long)(d->H / 128) * 4; sblock = 128; }
-  if (dt == MOE_MXFP4) sbytes = d->H / 32;
+  if (mx_format(dt)) sbytes = d->H / 32;
   e = launch_gather_rows(slots, d->k, offsets + d->E_loc, row_to_flat, a_in, row_bytes(dt, d->H),
                          a_perm, quant ? a_in_scales : nullptr, sbytes, sblock,
                          quant ? a_perm_scales : nullptr, stream);
@@ -293,7 +297,7 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
     return MOE_ERR_INVALID_ARG;
   if (g->epilogue == MOE_EPI_SWIGLU && !ok_ptr(B2)) return MOE_ERR_INVALID_ARG;
   if (g->K % k_align(g->dtype) || g->N % 64) return MOE_ERR_INVALID_ARG;
-  const bool quant = g->dtype == MOE_FP8_E4M3 || g->dtype == MOE_MXFP4;
+  const bool quant = quantised(g->dtype);
   if (g->dtype == MOE_F32 && g->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (quant) {
     if (!ok_ptr(A_scales) || !ok_ptr(B_scales)) return MOE_ERR_INVALID_ARG;
@@ -368,6 +372,12 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
                                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
                                        stream));
   }
+  if (dst_dtype == MOE_MXFP8) {
+    if (cols % 32) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_mx8(src_dtype, batch, rows, cols, src,
+                                       static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                       stream));
+  }
   return MOE_ERR_INVALID_ARG;
 }
 
@@ -386,7 +396,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   if (st != MOE_OK) return st;
   if (d->I_s != 0 && d->I_s != d->I) return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
-  const bool quant = d->expert_dtype == MOE_FP8_E4M3 || d->expert_dtype == MOE_MXFP4;
+  const bool quant = quantised(d->expert_dtype);
   if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(w->w_router) || !ok_ptr(w->w_gate) ||
       !ok_ptr(w->w_up) || !ok_ptr(w->w_down) || !ok_opt(bias) || !ok_opt(logits) ||
       !ok_opt(topk_ids) || !ok_opt(topk_w) || !ok_ptr(ws))
@@ -423,8 +433,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   if (st != MOE_OK) return st;
 
   // 3. activations for the expert GEMMs: x itself, or x quantised once in token order (fp8 with
-  //    128-token x 128-channel blocks, MXFP4 with 1 x 32 groups) before the rows are dispatched
-  // (quant: expert_dtype is fp8 or MXFP4)
+  //    128-token x 128-channel blocks, MXFP4 / MXFP8 with 1 x 32 groups) before the rows are
+  //    dispatched
   const void* xa = x;
   const void* xs = nullptr;
   if (dt == MOE_FP8_E4M3) {
@@ -437,12 +447,18 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
                                      reinterpret_cast<uint8_t*>(base + L.xs), stream));
     xa = base + L.xq;
     xs = base + L.xs;
+  } else if (dt == MOE_MXFP8) {
+    st = hip_status(launch_quant_mx8(io, 1, T, H, x, reinterpret_cast<uint8_t*>(base + L.xq),
+                                     reinterpret_cast<uint8_t*>(base + L.xs), stream));
+    xa = base + L.xq;
+    xs = base + L.xs;
   }
   if (st != MOE_OK) return st;
 
   // 4. gate/up GEMM with the SwiGLU epilogue; routed rows gather the activations through
   //    row_to_flat / k, shared-expert rows (C rows slots..slots+T) read them in token order. h
-  //    leaves in the down projection's input format (bf16 / fp32, or re-quantised fp8 / MXFP4).
+  //    leaves in the down projection's input format (bf16 / fp32, or re-quantised fp8 / MXFP4 /
+  //    MXFP8).
   GemmArgs a{};
   a.dtype = dt;
   a.epilogue = MOE_EPI_SWIGLU;

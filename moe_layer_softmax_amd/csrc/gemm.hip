@@ -853,7 +853,7 @@ hipError_t launch_gemm_router(const GemmArgs& a, hipStream_t s) {
 // Tile shape choice: the expected rows per group decide between a compute-shaped tile (large
 // groups, MFMA-bound) and a weight-streaming tile (few rows per group, HBM-bound).
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  if (a.dtype == MOE_FP8_E4M3 || a.dtype == MOE_MXFP4) return launch_gemm_q(a, s);
+  if (a.dtype == MOE_FP8_E4M3 || a.dtype == MOE_MXFP4 || a.dtype == MOE_MXFP8) return launch_gemm_q(a, s);
   if (a.dtype == MOE_F32) return run_f32(a, s);
   if (a.dtype == MOE_BF16) {
     const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;
@@ -874,6 +874,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     // decode-sized groups: stream the weights once per 32 (or 64) rows of each group
     if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32)) {
       const bool split = a.K / 64 >= kStreamSplitPairs;
+      // the down projection streams its (short-K) weights once per 64 rows: measured ~5% faster
+      // than 32-row tiles on the 64-token Qwen3-235B-shaped slice, where a few experts get more
+      // than 32 rows and 32-row tiles would read their weights twice
+      if (a.epilogue != MOE_EPI_SWIGLU && !split && per_group <= 64) return run_bf16_stream<4, 1>(a, s);
       if (per_group <= kStreamRows32)
         return split ? run_bf16_stream<2, 4>(a, s) : run_bf16_stream<2, 1>(a, s);
       return split ? run_bf16_stream<4, 4>(a, s) : run_bf16_stream<4, 1>(a, s);

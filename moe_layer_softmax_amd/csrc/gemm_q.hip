@@ -12,9 +12,15 @@
 //     (Part I)", section on lower-precision operations; absmax over 32 elements for MX formats,
 //     "CuTeDSL at Perplexity", Blackwell section). The E8M0 scales go straight into the MFMA's
 //     per-lane scale operands, so the dequantisation happens inside the matrix core.
+//   * MXFP8: OCP e4m3 codes with one E8M0 scale per 32 elements along K (the MXFP8 MoE GEMMs of
+//     "Hosting Qwen on Blackwell", section "Quantization"). The 32-byte fp8 operand of lane group q
+//     (lanes 16q .. 16q + 15) holds K-elements [16q, 16q + 16) in its first 16 bytes and
+//     [64 + 16q, 64 + 16q + 16) in its last 16, and the scale byte of lane group q applies to
+//     K-elements [32q, 32q + 32); so the operand is built from 16-byte chunks q and q + 4 of the
+//     128-element row slice, and lane group q passes the E8M0 scale of group q.
 //
 // Tile: 128 rows x 256 B-rows, 4 waves each owning 32 rows x all 256 B-rows (so a wave holds the
-// full 128 h-columns of the SwiGLU tile: the epilogue can form fp8 1x128 or MXFP4 1x32 blocks of h
+// full 128 h-columns of the SwiGLU tile: the epilogue can form fp8 1x128 or MX 1x32 blocks of h
 // in registers, with the row amax reduced across 16 lanes by shuffles). K-steps are 128-byte row
 // slices (128 fp8 or 256 fp4 elements) staged through a 3-stage direct-to-LDS ring, with the same
 // bank swizzle, tile scheduler and row gathering as the bf16 kernel. The block scales of a K-step
@@ -32,25 +38,34 @@ constexpr int kQStreamGroupM = 8;
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
+// Block scales of a K-step follow its operands in the LDS stage: MXFP4 E8M0 [128 A rows][8 B] then
+// [256 B rows][8 B]; MXFP8 E8M0 [128][4 B] then [256][4 B] and 512 spare bytes (the target of the
+// padding loads that keep every wave's load count equal); fp8 fp32 [128 A rows] then the two B
+// block scales (1 KB).
+template <int FMT>
+constexpr int q_scale_stage_bytes() {
+  return FMT == MOE_MXFP4 ? (128 + 256) * 8 : (FMT == MOE_MXFP8 ? (128 + 256) * 4 + 512 : 1024);
+}
+
 template <int FMT, int EPI>
 __global__ void __launch_bounds__(256)
 gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
-  constexpr bool MX = FMT == MOE_MXFP4;
+  constexpr bool MX4 = FMT == MOE_MXFP4;   // e2m1 elements, E8M0 per 32
+  constexpr bool MX8 = FMT == MOE_MXFP8;   // e4m3 elements, E8M0 per 32
+  constexpr bool MX = MX4 || MX8;          // E8M0 scales go straight into the MFMA
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
   constexpr int BM = 128, BN = 256, NW = 4, TM = 32, FM = 2, FN = 16, S = 3;
   constexpr int RB = 128;                  // bytes per row slice (one K-step)
-  constexpr int KE = MX ? 256 : 128;       // elements per K-step
-  constexpr int SUB = MX ? 2 : 1;          // 128-element MFMA substeps per K-step
+  constexpr int KE = MX4 ? 256 : 128;      // elements per K-step
+  constexpr int SUB = MX4 ? 2 : 1;         // 128-element MFMA substeps per K-step
   constexpr int A_INS = BM / (8 * NW), B_INS = BN / (8 * NW);
-  constexpr int SINS = MX ? 3 : 1;         // 4-byte scale loads per wave per K-step
+  constexpr int SINS = MX4 ? 3 : (MX8 ? 2 : 1);   // 4-byte scale loads per wave per K-step
   constexpr int INS = A_INS + B_INS + SINS;
   constexpr int DATA = (BM + BN) * RB;     // operand bytes per LDS stage
-  // block scales of the K-step follow the operands in the stage: MXFP4 E8M0 [BM rows][8 B] then
-  // [BN rows][8 B]; fp8 fp32 [BM rows] then the two B block scales
-  constexpr int SCALE_BYTES = MX ? (BM + BN) * 8 : 1024;
+  constexpr int SCALE_BYTES = q_scale_stage_bytes<FMT>();
   constexpr int STAGE = DATA + SCALE_BYTES; // bytes per LDS stage
   constexpr int NB = 4;                    // B fragments per MFMA batch
-  constexpr int FMT_CODE = MX ? 4 : 0;     // f8f6f4 operand format: 0 = fp8 e4m3, 4 = fp4 e2m1
+  constexpr int FMT_CODE = MX4 ? 4 : 0;    // f8f6f4 operand format: 0 = fp8 e4m3, 4 = fp4 e2m1
   using Geo = SliceGeo<64>;                // 128-byte rows
   static_assert((S - 2) * INS < 64, "pipeline depth");
 
@@ -64,7 +79,7 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = p.K;
   const int nk = K / KE;
-  const long long b_row_bytes = MX ? K / 2 : K;
+  const long long b_row_bytes = MX4 ? K / 2 : K;
   const int lrow = lane >> 3;
 
   // ---- DMA sources of this lane's rows ----
@@ -99,13 +114,41 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   // ---- scale sources (one 4-byte direct-to-LDS load per lane and instruction) ----
   // MXFP4: wave w moves A scale rows [32w, 32w + 32) and B scale rows [64w, 64w + 64), 8 bytes
   //        (one K-step) per row, two lanes per row.
+  // MXFP8: 4 bytes per row and K-step, one lane per row: wave w's loads c = 0, 1 take 64-row slot
+  //        u = 2w + c: A rows for u < 2, B rows for 2 <= u < 6, and for u >= 6 the A rows again
+  //        into the spare bytes.
   // fp8:   waves 0 and 1 move A scale rows [64w, 64w + 64) (one fp32 per row and K-step); wave 2
   //        the two B block scales (lane i: scale i & 1); wave 3 the same into a spare slot (every
   //        wave issues the same number of loads, so the wait counts are uniform).
   const char* s_src[SINS];
   int s_dst[SINS];
   long long s_step[SINS];                  // bytes between consecutive K-steps of a source
-  if constexpr (MX) {
+  if constexpr (MX8) {
+    const int gpr = K / 32;                // scale bytes per row
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int u = wave * 2 + c;
+      if (u < 2 || u >= 6) {
+        const int r = (u & 1) * 64 + lane;
+        s_src[c] = static_cast<const char*>(p.A_scales) + a_src_row(p, t, t.row0 + r) * gpr;
+        s_dst[c] = u < 2 ? DATA + u * 256 : DATA + (BM + BN) * 4 + (u - 6) * 256;
+      } else {
+        const int rb = (u - 2) * 64 + lane;
+        long long n;
+        const char* sbase = t.Bs;
+        if (SWIGLU) {
+          n = (long long)t.nt * (BN / 2) + (rb % (BN / 2));
+          if (rb >= BN / 2) sbase = t.B2s;
+        } else {
+          n = (long long)t.nt * BN + rb;
+        }
+        if (n >= p.N) n = p.N - 1;
+        s_src[c] = sbase + n * gpr;
+        s_dst[c] = DATA + BM * 4 + (u - 2) * 256;
+      }
+      s_step[c] = 4;
+    }
+  } else if constexpr (MX4) {
     const int gpr = K / 32;                // scale bytes per row
     {
       const int r = wave * 32 + (lane >> 1);
@@ -177,17 +220,19 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{};
 
-  // fragment readers (operand layout of the 16x16x128 f8f6f4 MFMA: lane l holds row/column
-  // l % 16 and the 32 K-elements [32 (l / 16), 32 (l / 16) + 32) of the 128)
+  // fragment readers (operand of the 16x16x128 f8f6f4 MFMA: lane l holds row/column l % 16; for
+  // MXFP4 the 32 K-elements [32 (l / 16), +32) of the 128; for MXFP8 chunks l / 16 and l / 16 + 4,
+  // the hardware's K order; for fp8 with whole-step block scales any K order shared by both
+  // operands gives the same dot product: chunks 2 (l / 16) and 2 (l / 16) + 1)
   const int q = lane >> 4;
   auto read_frag = [&](const uint8_t* base, int r, int s) -> i32x8 {
     i32x8 out;
-    if constexpr (MX) {
+    if constexpr (MX4) {
       const int c = s * 4 + q;                       // 16 bytes = 32 fp4
       const i32x4 v = *reinterpret_cast<const i32x4*>(base + r * RB + ((c ^ Geo::swz(r)) * 16));
       out = i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
     } else {
-      const int c0 = 2 * q, c1 = 2 * q + 1;          // 32 bytes = 32 fp8
+      const int c0 = MX8 ? q : 2 * q, c1 = MX8 ? q + 4 : 2 * q + 1;   // 32 bytes = 32 fp8
       const i32x4 v0 = *reinterpret_cast<const i32x4*>(base + r * RB + ((c0 ^ Geo::swz(r)) * 16));
       const i32x4 v1 = *reinterpret_cast<const i32x4*>(base + r * RB + ((c1 ^ Geo::swz(r)) * 16));
       out = i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
@@ -215,8 +260,16 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
     // scales of this K-step, staged with its operands
     const uint8_t* ls = la + DATA;
     float fs[MX ? 1 : FM * 4][2];
-    u32x2 sam[MX ? FM : 1], sbm[MX ? FN : 1];
-    if constexpr (!MX) {
+    u32x2 sam[MX4 ? FM : 1], sbm[MX4 ? FN : 1];
+    uint32_t sa8[MX8 ? FM : 1], sb8[MX8 ? FN : 1];
+    if constexpr (MX8) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        sa8[i] = *reinterpret_cast<const uint32_t*>(ls + (wave * TM + i * 16 + (lane & 15)) * 4);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        sb8[j] = *reinterpret_cast<const uint32_t*>(ls + BM * 4 + (j * 16 + (lane & 15)) * 4);
+    } else if constexpr (!MX) {
       const float g0 = reinterpret_cast<const float*>(ls + 512)[0];
       const float g1 = reinterpret_cast<const float*>(ls + 512)[1];
 #pragma unroll
@@ -253,8 +306,9 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
           for (int jj = 0; jj < NB; ++jj) {
             const int j = b0 + jj;
             if constexpr (MX) {
-              const int sa = static_cast<int>((sam[i][s] >> (8 * q)) & 0xFFu);
-              const int sb = static_cast<int>((sbm[j][s] >> (8 * q)) & 0xFFu);
+              // lane group q passes the scale of K group q of the (sub)step
+              const int sa = static_cast<int>(((MX4 ? sam[i][s] : sa8[i]) >> (8 * q)) & 0xFFu);
+              const int sb = static_cast<int>(((MX4 ? sbm[j][s] : sb8[j]) >> (8 * q)) & 0xFFu);
               acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                   fa[i], fb[jj], acc[i][j], FMT_CODE, FMT_CODE, 0, sa, 0, sb);
             } else {
@@ -318,6 +372,26 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
             const long long col = (long long)t.nt * (BN / 2) + j * 16 + colw;
             if (col < p.N) reinterpret_cast<uint16_t*>(C + r * p.c_pitch)[col] = f32_to_bf16(h[j]);
           }
+        } else if constexpr (MX8) {
+          // MXFP8 h: four 1 x 32 groups per row (fragments 2g, 2g+1), one code byte per lane
+          uint8_t* crow = reinterpret_cast<uint8_t*>(C + r * p.c_pitch);
+#pragma unroll
+          for (int g = 0; g < HF / 2; ++g) {
+            float amax = fmaxf(fabsf(h[2 * g]), fabsf(h[2 * g + 1]));
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+            const int e = mx_shared_exp<8>(amax);
+            const float mul = ldexpf(1.0f, -e);
+            if (!live) continue;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const long long col = (long long)t.nt * (BN / 2) + (2 * g + hh) * 16 + colw;
+              crow[col] = e4m3_rne_sat(h[2 * g + hh] * mul);
+            }
+            if (colw == 0)
+              reinterpret_cast<uint8_t*>(p.C_scales)[(long long)r * (p.N / 32) + (t.nt * (BN / 2)) / 32 + g] =
+                  static_cast<uint8_t>(e + 127);
+          }
         } else if constexpr (!MX) {
           // fp8 h: one 1 x 128 block per row per tile (the 128 h-columns of this tile)
           float amax = 0.0f;
@@ -369,7 +443,8 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
 // ds_bpermute; activations and block scales are loaded in the operand layout directly; pairs are
 // double-buffered. For fp8 a lane's 32-byte operand is chunks kq and kq + 4 of the pair (the same
 // chunks of the activation row, so the dot product is unchanged); for MXFP4 step s uses chunk
-// 4 s + kq and scale byte 4 s + kq of the row's 8 scale bytes per pair.
+// 4 s + kq and scale byte 4 s + kq of the row's 8 scale bytes per pair; MXFP8 uses the fp8
+// operand (chunks kq and kq + 4, the hardware's K order) and scale byte kq of the pair.
 // Workgroup: 4 waves on 16 * FM rows x 4 adjacent column blocks of one group (SWIGLU: 128 h-columns,
 // wave w on 32 of them = 32 gate + 32 up weight rows; STORE: 256 columns, 64 per wave), so the
 // fp8 1 x 128 blocks of h are complete inside the workgroup (row amax exchanged through LDS) and
@@ -378,10 +453,10 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
 template <int FMT, int EPI, int FM>
 __global__ void __launch_bounds__(256)
 gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
-  constexpr bool MX = FMT == MOE_MXFP4;
+  constexpr bool MX4 = FMT == MOE_MXFP4, MX8 = FMT == MOE_MXFP8, MX = MX4 || MX8;
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
   constexpr int BM = 16 * FM;
-  constexpr int FMT_CODE = MX ? 4 : 0;
+  constexpr int FMT_CODE = MX4 ? 4 : 0;
   __shared__ float amax_x[4][BM];          // fp8 h: per-wave row amax
 
   const int logical = xcd_remap(blockIdx.x, kQStreamGroupM);
@@ -393,8 +468,8 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   const int wave = threadIdx.x >> 6;
   const int lr = lane & 15, kq = lane >> 4;
   const int K = p.K;
-  const long long wrow = MX ? K / 2 : K;   // weight row bytes
-  const int np = MX ? K / 256 : K / 128;   // K-pairs (128 bytes of every row)
+  const long long wrow = MX4 ? K / 2 : K;  // weight row bytes
+  const int np = MX4 ? K / 256 : K / 128;  // K-pairs (128 bytes of every row)
   // weight rows of fragment j (SWIGLU: j < 2 gate, else up; 16 rows each) of this wave
   auto wrow_of = [&](int j, int r, const char*& base, const char*& sbase) -> long long {
     long long n;
@@ -425,7 +500,8 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     arow[i] = a_src_row(p, t, t.row0 + i * 16 + lr);
     ap[i] = A + arow[i] * p.a_pitch + kq * 16;
   }
-  // block scales: MXFP4 E8M0 bytes of the operand rows (8 per pair); fp8 fp32 block scales
+  // block scales: MX E8M0 bytes of the operand rows (8 per pair for MXFP4, 4 for MXFP8); fp8 fp32
+  // block scales
   const uint8_t* wsc[MX ? 4 : 1];
   const uint8_t* asc[MX ? FM : 1];
   const float* wsf[MX ? 1 : 2];
@@ -467,12 +543,18 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) av[set][i][s2] = *reinterpret_cast<const i32x4*>(ap[i] + off + s2 * 64);
-    if constexpr (MX) {
+      for (int s2 = 0; s2 < 2; ++s2)
+        av[set][i][s2] = *reinterpret_cast<const i32x4*>(ap[i] + off + s2 * 64);
+    if constexpr (MX4) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) wsm[set][j] = *reinterpret_cast<const u32x2*>(wsc[j] + c * 8);
 #pragma unroll
       for (int i = 0; i < FM; ++i) asm_[set][i] = *reinterpret_cast<const u32x2*>(asc[i] + c * 8);
+    } else if constexpr (MX8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wsm[set][j][0] = *reinterpret_cast<const uint32_t*>(wsc[j] + c * 4);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm_[set][i][0] = *reinterpret_cast<const uint32_t*>(asc[i] + c * 4);
     } else {
       wss[set][0] = wsf[0][c];
       wss[set][1] = wsf[1][c];
@@ -496,7 +578,26 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     return w;
   };
   auto compute = [&](int set) {
-    if constexpr (MX) {
+    if constexpr (MX8) {
+      i32x8 wf[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const i32x4 w0 = piece(set, j, src0), w1 = piece(set, j, src1);
+        wf[j] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const i32x4 a0 = av[set][i][0], a1 = av[set][i][1];
+        const i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const int sa = static_cast<int>((asm_[set][i][0] >> (8 * kq)) & 0xFFu);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int sw = static_cast<int>((wsm[set][j][0] >> (8 * kq)) & 0xFFu);
+          acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[j], a, acc[j][i], FMT_CODE,
+                                                                      FMT_CODE, 0, sw, 0, sa);
+        }
+      }
+    } else if constexpr (MX4) {
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         i32x8 wf[4];
@@ -594,7 +695,33 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
           *reinterpret_cast<uint2*>(C + (long long)r * p.c_pitch + (col0 + jj * 16 + kq * 4) * 2) =
               make_uint2(pack_bf16x2(h[i][jj][0], h[i][jj][1]), pack_bf16x2(h[i][jj][2], h[i][jj][3]));
       }
-    } else if constexpr (MX) {
+    } else if constexpr (MX8) {
+      // one 1 x 32 group per row: the wave's 32 columns; row amax over the 4 lanes of the row
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        float amax = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(h[i][jj][v]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        const int e = mx_shared_exp<8>(amax);
+        const float mul = ldexpf(1.0f, -e);
+        const int r = t.row0 + i * 16 + lr;
+        if (r >= t.row1) continue;
+        uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) word |= static_cast<uint32_t>(e4m3_rne_sat(h[i][jj][v] * mul)) << (8 * v);
+          *reinterpret_cast<uint32_t*>(crow + col0 + jj * 16 + kq * 4) = word;
+        }
+        if (kq == 0)
+          static_cast<uint8_t*>(p.C_scales)[(long long)r * (p.N / 32) + col0 / 32] = static_cast<uint8_t>(e + 127);
+      }
+    } else if constexpr (MX4) {
       // one 1 x 32 group per row: the wave's 32 columns; row amax over the 4 lanes of the row
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
@@ -665,7 +792,7 @@ hipError_t run_q(const GemmArgs& a, hipStream_t s) {
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
   Grid g = make_grid(a, BM, SWIGLU ? BN / 2 : BN, 8, 64);
   if (g.total == 0) return hipSuccess;
-  const size_t lds = (size_t)S * ((BM + BN) * 128 + (FMT == MOE_MXFP4 ? (BM + BN) * 8 : 1024));
+  const size_t lds = (size_t)S * ((BM + BN) * 128 + q_scale_stage_bytes<FMT>());
   gemm_q_kernel<FMT, EPI><<<dim3(g.blocks), dim3(256), lds, s>>>(a, g.n_tiles, g.x_tiles, g.span,
                                                                   g.total, g.gm);
   return hipGetLastError();
@@ -709,6 +836,7 @@ hipError_t run_q_fmt(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_q(const GemmArgs& a, hipStream_t s) {
   if (a.dtype == MOE_FP8_E4M3) return run_q_fmt<MOE_FP8_E4M3>(a, s);
   if (a.dtype == MOE_MXFP4) return run_q_fmt<MOE_MXFP4>(a, s);
+  if (a.dtype == MOE_MXFP8) return run_q_fmt<MOE_MXFP8>(a, s);
   return hipErrorInvalidValue;
 }
 

@@ -41,7 +41,7 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // the router as a grouped GEMM (one extra group of T rows): a tile shape for N = E and many rows
 hipError_t launch_gemm_router(const GemmArgs& a, hipStream_t s);
-// block-scaled fp8 / MXFP4 grouped GEMM (A and B in a.dtype)
+// block-scaled fp8 / MXFP4 / MXFP8 grouped GEMM (A and B in a.dtype)
 hipError_t launch_gemm_q(const GemmArgs& a, hipStream_t s);
 
 // Top-k selection and weights. With nsplit > 1, logits[t, e] is first formed as the sum of the
@@ -79,5 +79,7 @@ hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int bl
                             const void* src, uint8_t* codes, float* scales, hipStream_t s);
 hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const void* src,
                             uint8_t* packed, uint8_t* scales, hipStream_t s);
+hipError_t launch_quant_mx8(int src_dtype, int batch, int rows, int cols, const void* src,
+                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 }  // namespace moe

@@ -1,4 +1,5 @@
-// quant.hip -- fp8 (e4m3, fp32 block scales) and MXFP4 (e2m1 + E8M0 per 32) quantisers on gfx950.
+// quant.hip -- fp8 (e4m3, fp32 block scales), MXFP4 (e2m1 + E8M0 per 32) and MXFP8 (e4m3 + E8M0 per
+// 32) quantisers on gfx950.
 //
 // Block scaling "as used for models like DeepSeek" ("Hosting Qwen on Blackwell", section
 // "Quantization"); 4-bit weights packed two per byte with per-group scales and activations
@@ -112,6 +113,39 @@ __global__ void __launch_bounds__(256) quant_mx4_kernel(long long groups, const 
   if (sub == 0) scales[g] = static_cast<uint8_t>(e8 + 127);
 }
 
+// MXFP8: four lanes per 32-element group as for MXFP4; each lane writes its 8 codes as one 8-byte
+// store.
+template <bool SRC_BF16>
+__global__ void __launch_bounds__(256) quant_mx8_kernel(long long groups, const void* __restrict__ src,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long g = tid >> 2;
+  const int sub = static_cast<int>(tid & 3);
+  const bool live = g < groups;
+  float v[8];
+  if (live) load8<SRC_BF16>(src, (size_t)g * 32 + sub * 8, v);
+  else
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  const int e8 = mx_shared_exp<8>(amax);
+  const float mul = ldexpf(1.0f, -e8);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    lo |= static_cast<uint32_t>(e4m3_rne_sat(v[e] * mul)) << (8 * e);
+    hi |= static_cast<uint32_t>(e4m3_rne_sat(v[4 + e] * mul)) << (8 * e);
+  }
+  if (!live) return;
+  *reinterpret_cast<uint2*>(codes + (size_t)g * 32 + sub * 8) = make_uint2(lo, hi);
+  if (sub == 0) scales[g] = static_cast<uint8_t>(e8 + 127);
+}
+
 hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int block_rows,
                             const void* src, uint8_t* codes, float* scales, hipStream_t s) {
   if (rows == 0 || batch == 0) return hipSuccess;
@@ -121,6 +155,18 @@ hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int bl
     quant_fp8_kernel<true><<<grid, 256, 0, s>>>(rows, cols, block_rows, src, codes, scales);
   else
     quant_fp8_kernel<false><<<grid, 256, 0, s>>>(rows, cols, block_rows, src, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx8(int src_dtype, int batch, int rows, int cols, const void* src,
+                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const long long groups = (long long)batch * rows * (cols / 32);
+  if (groups == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((groups * 4 + 255) / 256));
+  if (src_dtype == MOE_BF16)
+    quant_mx8_kernel<true><<<grid, 256, 0, s>>>(groups, src, codes, scales);
+  else
+    quant_mx8_kernel<false><<<grid, 256, 0, s>>>(groups, src, codes, scales);
   return hipGetLastError();
 }
 

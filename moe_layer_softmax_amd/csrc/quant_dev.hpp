@@ -46,12 +46,14 @@ __device__ __forceinline__ uint8_t e2m1_rne_sat(float y) {
   return sign | c;
 }
 
-// shared exponent of an MX block: floor(log2(amax)) - 2, clamped to [-127, 127]; -127 for amax = 0
+// shared exponent of an MX block: floor(log2(amax)) minus the element format's largest exponent
+// (2 for e2m1, 8 for e4m3), clamped to [-127, 127]; -127 for amax = 0
+template <int EMAX = 2>
 __device__ __forceinline__ int mx_shared_exp(float amax) {
   if (amax == 0.0f) return -127;
   int ex;
   frexpf(amax, &ex);
-  int e = ex - 1 - 2;
+  int e = ex - 1 - EMAX;
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 

@@ -53,12 +53,13 @@ def rel_err(gpu, ref):
 
 
 def tol_for(fmt):
-    return 6e-2 if fmt in (mi.FMT_FP8, mi.FMT_MX4) else 2e-2
+    return 6e-2 if fmt in (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8) else 2e-2
 
 
 # ---- quantised formats ------------------------------------------------------------------
 
-FMTS = {"fp8": (moe.MOE_FP8_E4M3, oracle.FP8), "mx4": (moe.MOE_MXFP4, oracle.MX4)}
+FMTS = {"fp8": (moe.MOE_FP8_E4M3, oracle.FP8), "mx4": (moe.MOE_MXFP4, oracle.MX4),
+        "mx8": (moe.MOE_MXFP8, oracle.MX8)}
 E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
 
 
@@ -73,6 +74,9 @@ def gpu_quant(fmt, a, block_rows):
         codes = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
         scales = torch.empty((G, (R + block_rows - 1) // block_rows, C // 128), dtype=torch.float32,
                              device="cuda")
+    elif fmt == moe.MOE_MXFP8:
+        codes = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
     else:
         codes = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
         scales = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
@@ -88,6 +92,9 @@ def oracle_quant(ofmt, a, block_rows):
         qs = [oracle.quant_fp8(a[g], block_rows, 128) for g in range(a.shape[0])]
         return oracle.Mat(oracle.FP8, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]),
                           bn=block_rows, bk=128)
+    if ofmt == oracle.MX8:
+        qs = [oracle.quant_mx8(a[g]) for g in range(a.shape[0])]
+        return oracle.Mat(oracle.MX8, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]))
     qs = [oracle.quant_mx4(a[g]) for g in range(a.shape[0])]
     return oracle.Mat(oracle.MX4, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]))
 
@@ -99,6 +106,9 @@ def decode(fmt, codes, scales, cols):
     if fmt == moe.MOE_FP8_E4M3:
         v = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
         return v * np.repeat(scales.astype(np.float64), 128, axis=1)[:, :cols]
+    if fmt == moe.MOE_MXFP8:
+        v = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+        return v * np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)[:, :cols]
     lo, hi = codes & 15, codes >> 4
     v = np.empty((codes.shape[0], cols))
     v[:, 0::2] = E2M1[lo]

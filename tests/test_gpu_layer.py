@@ -17,7 +17,8 @@ from gpu_util import (gamma, gpu_quant, io_torch, oracle_quant, rel_err, routing
 pytestmark = pytest.mark.gpu
 
 _FMT = {mi.FMT_F32: moe.MOE_F32, mi.FMT_BF16: moe.MOE_BF16, mi.FMT_FP8: moe.MOE_FP8_E4M3,
-        mi.FMT_MX4: moe.MOE_MXFP4}
+        mi.FMT_MX4: moe.MOE_MXFP4, mi.FMT_MX8: moe.MOE_MXFP8}
+_QUANT = (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8)
 
 
 def make_inputs(wl, bias_override=None):
@@ -32,8 +33,8 @@ def gpu_layer(wl, x, wr, bias, experts, sh):
     dt = io_torch(wl.io_fmt)
     desc = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
                          wl.renormalize, _FMT[wl.io_fmt], _FMT[wl.fmt])
-    if wl.fmt in (mi.FMT_FP8, mi.FMT_MX4):
-        # expert weights quantised on the GPU (128 x 128 fp8 blocks / MXFP4 groups of 32)
+    if wl.fmt in _QUANT:
+        # expert weights quantised on the GPU (128 x 128 fp8 blocks / MX groups of 32)
         f = _FMT[wl.fmt]
         eq = [gpu_quant(f, a, 128) for a in experts]
         shq = None if sh is None else [gpu_quant(f, a, 128) for a in sh]
@@ -62,12 +63,12 @@ def gpu_layer(wl, x, wr, bias, experts, sh):
 def oracle_layer(wl, x, wr, bias, experts, sh, tok):
     # h enters the down projection in the expert format (bf16 / fp8 1x128 / MXFP4)
     act = {mi.FMT_F32: oracle.F32, mi.FMT_BF16: oracle.BF16, mi.FMT_FP8: oracle.FP8,
-           mi.FMT_MX4: oracle.MX4}[wl.fmt]
+           mi.FMT_MX4: oracle.MX4, mi.FMT_MX8: oracle.MX8}[wl.fmt]
     desc = dict(T=wl.T, H=wl.H, E=wl.E, e0=wl.e0, E_loc=wl.E_loc, I=wl.I, k=wl.k, I_s=wl.I_s,
                 scoring=wl.scoring, renormalize=wl.renormalize, act_fmt=act)
     M = oracle.Mat
-    if wl.fmt in (mi.FMT_FP8, mi.FMT_MX4):
-        # the oracle quantises x (fp8: 128-token x 128-channel blocks; MXFP4: 1 x 32) and the
+    if wl.fmt in _QUANT:
+        # the oracle quantises x (fp8: 128-token x 128-channel blocks; MX: 1 x 32) and the
         # weights with its own quantisers
         xa = oracle_quant(act, x, 128)
         mats = [oracle_quant(act, a, 128) for a in experts]
@@ -114,7 +115,8 @@ def check_layer(wl, n_sample=None, bias_override=None, seed=0):
 
 @pytest.mark.parametrize("name,n_sample", [("C1", None), ("C2d", None), ("C3a", 96),
                                            ("C2p", 48), ("C3b", 64), ("C4d", 64), ("C4p", 48),
-                                           ("C5d", None), ("C5p", 48)])
+                                           ("C5d", None), ("C5p", 48), ("C2d_mx8", None),
+                                           ("C2p_mx8", 48)])
 def test_layer_workloads(name, n_sample):
     check_layer(mi.WORKLOADS[name], n_sample)
 

@@ -1,5 +1,5 @@
-"""Block-scaled fp8 (e4m3, 128x128 fp32 scales) and MXFP4 (e2m1 + E8M0 per 32) grouped GEMMs
-against the oracle. Each side quantises the same float32 inputs with its own quantiser (the codes
+"""Block-scaled fp8 (e4m3, 128x128 fp32 scales), MXFP4 (e2m1 + E8M0 per 32) and MXFP8 (e4m3 + E8M0
+per 32) grouped GEMMs against the oracle. Each side quantises the same float32 inputs with its own quantiser (the codes
 are checked equal in test_gpu_steps); the GPU GEMM runs on its own codes, the oracle dequantises
 its own."""
 import numpy as np
@@ -14,7 +14,7 @@ from gpu_util import FMTS, decode, gpu_quant, oracle_quant, to_dev
 
 pytestmark = pytest.mark.gpu
 
-@pytest.mark.parametrize("fmt", ["fp8", "mx4"])
+@pytest.mark.parametrize("fmt", ["fp8", "mx4", "mx8"])
 @pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
 @pytest.mark.parametrize("counts", [[0, 37, 130, 1, 9], [300, 140, 0, 513]])
 def test_grouped_gemm_quant(fmt, epi, counts):
@@ -23,10 +23,10 @@ def test_grouped_gemm_quant(fmt, epi, counts):
 
 # decode-sized groups (the weight-streaming kernel): empty groups, groups of 1-33 rows and one of
 # 40 (a second 32-row tile), and an odd number of 128-byte K-pairs per row
-@pytest.mark.parametrize("fmt", ["fp8", "mx4"])
+@pytest.mark.parametrize("fmt", ["fp8", "mx4", "mx8"])
 @pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
 def test_grouped_gemm_quant_decode(fmt, epi):
-    _quant_case(fmt, epi, [3, 0, 17, 40, 1, 8, 33, 2], 640 if fmt == "fp8" else 768)
+    _quant_case(fmt, epi, [3, 0, 17, 40, 1, 8, 33, 2], 768 if fmt == "mx4" else 640)
 
 
 def _quant_case(fmt, epi, counts, K):
@@ -53,7 +53,7 @@ def _quant_case(fmt, epi, counts, K):
                           out_dt, kk, a_block)
     C_scales = None
     if epi == "swiglu_q":
-        C = torch.zeros((max_rows, N if fmt == "fp8" else N // 2), dtype=torch.uint8, device="cuda")
+        C = torch.zeros((max_rows, N // 2 if fmt == "mx4" else N), dtype=torch.uint8, device="cuda")
         C_scales = torch.zeros((max_rows, N // 128) if fmt == "fp8" else (max_rows, N // 32),
                                dtype=torch.float32 if fmt == "fp8" else torch.uint8, device="cuda")
     else:
@@ -74,6 +74,11 @@ def _quant_case(fmt, epi, counts, K):
             # within one e4m3 step of the block's scale grid (fp32 vs fp64 h may round differently)
             s = np.repeat(C_scales[:R].cpu().numpy().astype(np.float64), 128, axis=1)
             assert np.all(np.abs(h - ref) <= 2.0 ** -3 * np.abs(ref) + s * 2.0 ** -8)
+        elif fmt == "mx8":
+            # within one e4m3 step (relative 2^-3, saturation above 448 * 2^e included) or one
+            # subnormal step 2^(e-9) of the group's scale
+            unit = np.repeat(2.0 ** (C_scales[:R].cpu().numpy().astype(np.int64) - 127), 32, axis=1)
+            assert np.all(np.abs(h - ref) <= 2.0 ** -3 * np.abs(ref) + unit * 2.0 ** -8)
         else:
             unit = np.repeat(2.0 ** (C_scales[:R].cpu().numpy().astype(np.int64) - 127), 32, axis=1)
             assert np.all(np.abs(h - ref) <= 2.0 * unit + 1e-30)

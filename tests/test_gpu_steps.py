@@ -64,6 +64,28 @@ def test_quantize_mx4_bitexact(rows, cols, src):
         assert np.array_equal(packed[b].cpu().numpy(), p_ref)
 
 
+@pytest.mark.parametrize("rows,cols,src", [(64, 256, "f32"), (333, 4096, "bf16"), (5, 1536, "f32")])
+def test_quantize_mx8_bitexact(rows, cols, src):
+    rng = np.random.default_rng(rows + 7 * cols)
+    a = rng.standard_normal((3, rows, cols)).astype(np.float32)
+    a[1] *= 1e-3
+    a[2, :, :32] = 0.0
+    a[2, 0, 40:72] = np.array([300.0, -1.0, 0.5, 3.0, -250.0, 17.0, -0.0, 0.001] * 4, np.float32)
+    a[2, 1, 64:96] = np.float32(7.5)                 # scaled values saturate at 448
+    if src == "bf16":
+        a = gen.bf16_round(a)
+    t = to_dev(a, torch.float32 if src == "f32" else torch.bfloat16)
+    codes = torch.empty((3, rows, cols), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((3, rows, cols // 32), dtype=torch.uint8, device="cuda")
+    moe.moe_quantize(moe.MOE_MXFP8, moe.MOE_F32 if src == "f32" else moe.MOE_BF16, 3, rows, cols, 1,
+                     t, codes, scales)
+    _sync()
+    for b in range(3):
+        c_ref, s_ref = oracle.quant_mx8(a[b])
+        assert np.array_equal(scales[b].cpu().numpy(), s_ref)
+        assert np.array_equal(codes[b].cpu().numpy(), c_ref)
+
+
 # ---------------------------------------------------------------------------------------------
 # routing
 # ---------------------------------------------------------------------------------------------
