@@ -42,6 +42,8 @@ def parse():
                    help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
     p.add_argument("--all-workloads", action="store_true",
                    help="add every workload's layer time and both roofline fractions")
+    p.add_argument("--no-ep-sweep", action="store_true",
+                   help="skip the decode MoE-GEMM sweep over local expert counts")
     return p.parse_args()
 
 
@@ -137,6 +139,72 @@ def workload_table(stream, steps):
                      "hbm_gbps": round(nbytes / t / 1e9, 1), "frac_hbm": round(t_hbm / t, 4),
                      "bound": "mfma" if t_mfma > t_hbm else "hbm"}
         del mats, scales, W, x, wr, o, ids, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+def ep_sweep(stream, steps):
+    """The decode MoE-GEMM microbenchmark of "Hosting Qwen on Blackwell" (section "MoE GEMM"):
+    every local expert activated by exactly one token, at the Qwen3-235B expert shape (hidden 4096,
+    intermediate 1536, top-8 of 128) for local slices of 8, 16, 32 and 64 experts (expert-parallel
+    degrees 16, 8, 4, 2). E_loc / 8 tokens, token t routed to local experts 8t .. 8t+7. Per slice:
+    the MoE GEMM time (gate/up + down, weights streamed from HBM: caches evicted by a 1 GiB read
+    before each step) and the whole step (dispatch maps, both GEMMs, combine; routing excluded, the
+    routing table is given). Weights are seeded device draws; their values do not change the work."""
+    import torch
+    import moe_layer_softmax_amd as moe
+    H, I, E, k = 4096, 1536, 128, 8
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {}
+    for E_loc in (8, 16, 32, 64):
+        T = E_loc // k
+        gen_t = torch.Generator(device="cuda")
+        gen_t.manual_seed(E_loc)
+        bf = lambda shape: (torch.randn(shape, generator=gen_t, device="cuda") * 0.02).to(torch.bfloat16)
+        wg, wu, wd = bf((E_loc, I, H)), bf((E_loc, I, H)), bf((E_loc, H, I))
+        x = torch.randn((T, H), generator=gen_t, device="cuda").to(torch.bfloat16)
+        ids = (torch.arange(T, device="cuda")[:, None] * k +
+               torch.arange(k, device="cuda")[None, :]).to(torch.int32).contiguous()
+        tw = torch.full((T, k), 1.0 / k, dtype=torch.float32, device="cuda")
+        d = moe.make_desc(T, H, E, 0, E_loc, I, k)
+        ws = torch.empty(max(moe.moe_permute_workspace_bytes(d), 16), dtype=torch.uint8, device="cuda")
+        counts = torch.empty(E_loc, dtype=torch.int32, device="cuda")
+        offsets = torch.empty(E_loc + 1, dtype=torch.int32, device="cuda")
+        s2r = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        r2f = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+        y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+        o = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        g_up = moe.moe_gemm_desc(E_loc, T * k, H, I, moe.MOE_BF16, moe.MOE_EPI_SWIGLU, moe.MOE_BF16, k, 1)
+        g_dn = moe.moe_gemm_desc(E_loc, T * k, I, H, moe.MOE_BF16, moe.MOE_EPI_STORE, moe.MOE_F32, 1, 1)
+        perm = lambda: moe.moe_permute(d, ids, None, None, counts, offsets, s2r, r2f, None, None, ws,
+                                       stream)
+        gemms = lambda: (moe.moe_grouped_gemm(g_up, x, None, r2f, wg, None, wu, None, offsets, h,
+                                              None, stream),
+                         moe.moe_grouped_gemm(g_dn, h, None, None, wd, None, None, None, offsets, y,
+                                              None, stream))
+        comb = lambda: moe.moe_combine(d, moe.MOE_F32, y, tw, s2r, None, o, stream)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        with torch.cuda.stream(stream):
+            perm(); gemms(); comb()
+            for e in ev:
+                flush.sum()
+                e[0].record(stream)
+                perm()
+                e[1].record(stream)
+                gemms()
+                e[2].record(stream)
+                comb()
+                e[3].record(stream)
+        torch.cuda.synchronize()
+        gemm_us = float(np.median([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
+        step_us = float(np.median([e[0].elapsed_time(e[3]) for e in ev])) * 1e3
+        wbytes = E_loc * 3 * I * H * 2
+        out[f"E_loc={E_loc}"] = {"ep_degree": E // E_loc, "tokens": T, "moe_gemm_us": round(gemm_us, 1),
+                                 "step_us": round(step_us, 1), "weight_bytes": wbytes,
+                                 "hbm_gbps": round(wbytes / (gemm_us * 1e-6) / 1e9, 1),
+                                 "frac_hbm": round(wbytes / (gemm_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4)}
+        del wg, wu, wd, x, h, y, o
         torch.cuda.empty_cache()
     return out
 
@@ -416,6 +484,8 @@ def main():
                             "frac_hbm": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
                             "caches": "1 GiB read between steps"}
         del D, flush
+    if not args.no_ep_sweep:
+        result["decode_one_token_per_expert"] = ep_sweep(stream, max(5, min(args.steps, 20)))
     if args.all_workloads:
         result["workloads"] = workload_table(stream, max(5, min(args.steps, 20)))
     if args.cpu_seconds > 0:

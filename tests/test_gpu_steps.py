@@ -319,6 +319,62 @@ def test_grouped_gemm_f32(swiglu):
     assert np.abs(Cg[:R] - ref).max() <= 1e-5 * rms
 
 
+# The decode microbenchmark of "Hosting Qwen on Blackwell" (section "MoE GEMM"): every local
+# expert activated by exactly one token. Qwen3-235B expert shape (hidden 4096, intermediate 1536,
+# top-8 of 128), E_loc / 8 tokens with token t routed to local experts 8t .. 8t+7, run through the
+# public steps (dispatch maps, gate/up GEMM gathering x, down GEMM, combine) and compared with the
+# oracle's dense per-token loop over the chosen experts (h rounded to bf16, as the layer does).
+@pytest.mark.parametrize("E_loc", [8, 16])
+def test_one_token_per_expert_decode(E_loc):
+    H, I, E, k = 4096, 1536, 128, 8
+    T = E_loc // k
+    rng = np.random.default_rng(E_loc)
+    x = gen.bf16_round(rng.standard_normal((T, H)).astype(np.float32))
+    wg, wu = (gen.bf16_round((rng.standard_normal((E_loc, I, H)) * 0.02).astype(np.float32))
+              for _ in range(2))
+    wd = gen.bf16_round((rng.standard_normal((E_loc, H, I)) * 0.02).astype(np.float32))
+    ids_np = (np.arange(T)[:, None] * k + np.arange(k)[None, :]).astype(np.int32)
+    w_np = rng.random((T, k)).astype(np.float32) + 0.1
+    w_np /= w_np.sum(1, keepdims=True)
+    d = moe.make_desc(T, H, E, 0, E_loc, I, k)
+    ws = torch.empty(max(moe.moe_permute_workspace_bytes(d), 16), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(E_loc, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E_loc + 1, dtype=torch.int32, device="cuda")
+    s2r = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    r2f = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d, to_dev(ids_np, torch.int32), None, None, counts, offsets, s2r, r2f, None,
+                    None, ws)
+    h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    g_up = moe.moe_gemm_desc(E_loc, T * k, H, I, moe.MOE_BF16, moe.MOE_EPI_SWIGLU, moe.MOE_BF16, k, 1)
+    g_dn = moe.moe_gemm_desc(E_loc, T * k, I, H, moe.MOE_BF16, moe.MOE_EPI_STORE, moe.MOE_F32, 1, 1)
+    moe.moe_grouped_gemm(g_up, to_dev(x, torch.bfloat16), None, r2f, to_dev(wg, torch.bfloat16),
+                         None, to_dev(wu, torch.bfloat16), None, offsets, h, None)
+    moe.moe_grouped_gemm(g_dn, h, None, None, to_dev(wd, torch.bfloat16), None, None, None, offsets,
+                         y, None)
+    moe.moe_combine(d, moe.MOE_F32, y, to_dev(w_np, torch.float32), s2r, None, out)
+    _sync()
+    c_ref, off_ref, s2r_ref, r2f_ref = oracle.permute(ids_np, 0, E_loc)
+    assert np.array_equal(counts.cpu().numpy(), np.ones(E_loc, np.int32))
+    assert np.array_equal(offsets.cpu().numpy(), off_ref)
+    assert np.array_equal(s2r.cpu().numpy(), s2r_ref)
+    assert np.array_equal(r2f.cpu().numpy()[:E_loc], r2f_ref)
+    M = oracle.Mat
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(k):
+            e = ids_np[t, j]
+            ref[t] += np.float64(w_np[t, j]) * oracle.ffn_row(
+                x[t], M(oracle.F32, wg[e]), M(oracle.F32, wu[e]), M(oracle.F32, wd[e]),
+                act_fmt=oracle.BF16)
+    err, rms = rel_err(out.cpu().numpy(), ref)
+    # the bar of bf16 layers; in fact only fp32 accumulation (and a rare bf16 rounding of h that
+    # the fp32 and fp64 sums put on different sides of a rounding boundary) differs here
+    assert err <= 2e-2, err
+    assert err <= 2e-3, err
+
+
 # ---------------------------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------------------------
