@@ -98,6 +98,54 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t, int
     }
 }
 
+// fp32 STORE epilogue of 32 x 32 fragments with one 16-byte store per lane and 4 rows: in a quad
+// of lanes (4 consecutive columns) each lane holds 4 consecutive rows of its column for entries
+// 4g .. 4g + 3; two cross-lane exchanges (lane ^ 1, then lane ^ 2, as DPP quad permutations)
+// transpose the 4 x 4 block so lane q holds row (q & 1) * 2 + (q >> 1) of the block, 4 columns.
+// Stores are non-temporal (C is read by the next kernel from HBM anyway). Returns true when every
+// row and column of the wave's block is inside the tile: the wave then issued exactly
+// FM * FN * 4 store instructions (callers count them in their vmcnt waits).
+template <int FM, int FN, int TM, int TN, int BN, class AccAt>
+__device__ __forceinline__ bool store_tile_f32x4(const GemmArgs& p, const Tile& t, int wm, int wn,
+                                                 AccAt acc_at) {
+  const int lane = lane_id();
+  const int q = lane & 3;
+  const bool odd = q & 1, hi = q & 2;
+  auto dpp = [](float x, auto ctrl) -> float {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  using swap1 = std::integral_constant<int, 0xB1>;     // quad_perm [1, 0, 3, 2]: lane ^ 1
+  using swap2 = std::integral_constant<int, 0x4E>;     // quad_perm [2, 3, 0, 1]: lane ^ 2
+  const int row_in = (lane / 32) * 4 + (q & 1) * 2 + (q >> 1);
+  const long long col0 = (long long)t.nt * BN + wn * TN + ((lane % 32) & ~3);
+  const int rbase = t.row0 + wm * TM;
+  const bool full = rbase + TM <= t.row1 && (long long)t.nt * BN + wn * TN + TN <= p.N;
+  char* C = static_cast<char*>(p.C);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float a0 = acc_at(i, j, 4 * g), a1 = acc_at(i, j, 4 * g + 1);
+        const float a2 = acc_at(i, j, 4 * g + 2), a3 = acc_at(i, j, 4 * g + 3);
+        // step 1: even lanes keep rows 0, 1 and take the partner column's rows 0, 1; odd lanes
+        // keep rows 2, 3 and take the partner's rows 2, 3
+        const float r0 = dpp(odd ? a0 : a2, swap1{}), r1 = dpp(odd ? a1 : a3, swap1{});
+        const float x0 = odd ? r0 : a0, x1 = odd ? a2 : r0;
+        const float x2 = odd ? r1 : a1, x3 = odd ? a3 : r1;
+        // step 2: lanes 0, 1 keep their first row (x0, x1) and take the other column pair's;
+        // lanes 2, 3 keep their second row (x2, x3)
+        const float s0 = dpp(hi ? x0 : x2, swap2{}), s1 = dpp(hi ? x1 : x3, swap2{});
+        const f32x4 v = hi ? f32x4{s0, s1, x2, x3} : f32x4{x0, x1, s0, s1};
+        const int r = rbase + i * 32 + g * 8 + row_in;
+        const long long col = col0 + j * 32;
+        if (full || (r < t.row1 && col < p.N))
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (long long)r * p.c_pitch + col * 4));
+      }
+  return full;
+}
+
 // Per-wave direct-to-LDS load plan of one BM x BN tile. Slot j of A moves tile rows
 // (j * NW + wave) * RPI ... + RPI - 1 of a K-slice (RPI rows per wave-wide instruction, lanes on
 // 16-byte chunks, swizzled), likewise slot j of B (SWIGLU: the B rows of each wave column are TN/2
@@ -377,9 +425,9 @@ __device__ __forceinline__ void phase_barrier() {
 #endif
 }
 
-template <bool SWIGLU, bool OUT_F32, int S>
+template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST>
 __global__ void __launch_bounds__(512)
-gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
+gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm, int nphys) {
   constexpr int BM = 256, BN = 256, WN = 4, MI = 32, BK = 32;
   constexpr int NW = 8, TM = 128, TN = 64, FM = TM / MI, FN = TN / MI, MK = 16, KS = BK / MK;
   using Geo = SliceGeo<BK>;
@@ -392,10 +440,20 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 
   extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
 
-  const int logical = xcd_remap(blockIdx.x, span);
-  if (logical >= total) return;
+  // PERSIST: one workgroup per CU slot takes the tiles of workgroup positions b, b + gridDim.x, ...
+  // (as in gemm_bf16_pipe_kernel): the next tile's first S - 1 K-steps are loaded while the
+  // finished tile's stores drain.
+  int phys = blockIdx.x;
+  auto next_tile = [&](Tile& tt) -> bool {
+    for (; phys < nphys; phys += gridDim.x) {
+      const int logical = xcd_remap(phys, span);
+      if (logical < total && resolve_tile(p, BM, n_tiles, x_tiles, logical, tt, gm)) return true;
+      if (!PERSIST) break;
+    }
+    return false;
+  };
   Tile t;
-  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
+  if (!next_tile(t)) return;
 
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -411,10 +469,25 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
     lp.template issue<decltype(wide_tag)::value>((long long)kt * Geo::kRowBytes, lds + (kt % S) * STAGE,
                                                  lds0 + (kt % S) * (STAGE * 2), wave);
   };
-  // this wave's share of step kt + 1 has landed (steps up to kt + S - 1 may have been issued)
-  auto wait_next = [&](int kt) {
-    if (kt + S - 1 < nk) wait_vmem_n<(S - 2) * INS>();
-    else wait_vmem();
+  // Store instructions of the epilogue of a wave whose block lies inside the tile: 16-byte stores
+  // for fp32 STORE (4 per 32 x 32 fragment), otherwise 2-column stores (8 per fragment pair row
+  // group, see store_tile).
+  constexpr bool F32X4 = !SWIGLU && OUT_F32;
+  constexpr int NST = F32X4 ? FM * FN * 4 : FM * (SWIGLU ? FN / 2 : FN) * 8;
+  // stores left in flight must fit the vmcnt counter (6 bits) with the loads
+  constexpr bool OVERLAP = PERSIST && (S - 2) * INS + NST < 64;
+  constexpr int NPEND = OVERLAP ? NST : 0;
+  // this wave's share of step kt + 1 has landed (steps up to kt + S - 1 may have been issued).
+  // pend: the wave issued NST stores after the first S - 1 steps of this tile (the previous
+  // tile's epilogue, see tile_loop); vmcnt retires in issue order, so while those stores are
+  // younger than step kt + 1 (kt + 1 <= S - 2) they are left in flight by counting them too.
+  auto wait_next = [&](int kt, bool pend) {
+    if (kt + S - 1 < nk) {
+      if (OVERLAP && pend && kt <= S - 3) wait_vmem_n<(S - 2) * INS + NPEND>();
+      else wait_vmem_n<(S - 2) * INS>();
+    } else {
+      wait_vmem();
+    }
   };
 
   // Fragment reads: every fragment row is (32-row block) + lane % 32, and the swizzle only depends
@@ -444,13 +517,23 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-  // The K loop, instantiated for the 32-bit-offset and the 64-bit-address load forms.
-  auto k_loop = [&](auto wide_tag) {
-    // prologue: steps 0 .. S-2 in flight; step 0 published by b0
+  auto prime = [&](auto wide_tag) {
 #pragma unroll
     for (int q = 0; q < S - 1; ++q) issue(q, wide_tag);
-    if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
-    else wait_vmem();
+  };
+  // The K loop, instantiated for the 32-bit-offset and the 64-bit-address load forms.
+  // On return every wave has finished its LDS reads of the tile: group 0 leaves through its last
+  // barrier, which group 1 passes right after its last memory phase.
+  auto k_loop = [&](auto wide_tag, bool primed, bool pend) {
+    // prologue: steps 0 .. S-2 in flight (issued here unless already primed); step 0 published by
+    // b0. Stores issued after the primed steps are left in flight (pend), others are waited for.
+    if (!primed) prime(wide_tag);
+    if (nk >= S - 1) {
+      if (OVERLAP && pend) wait_vmem_n<(S - 2) * INS + NPEND>();
+      else wait_vmem_n<(S - 2) * INS>();
+    } else {
+      wait_vmem();
+    }
     phase_barrier();                                   // b0
     if (grp == 1) phase_barrier();                     // b1 (group 1 starts one phase later)
 
@@ -458,7 +541,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
       // memory phase
       read_step(kt % S);
       issue(kt + S - 1, wide_tag);
-      if (grp == 1) wait_next(kt);
+      if (grp == 1) wait_next(kt, pend);
       wait_lgkm();
       phase_barrier();
       // compute phase
@@ -469,15 +552,61 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-      if (grp == 0) wait_next(kt);
+      if (grp == 0) wait_next(kt, pend);
       if (grp == 0 || kt + 1 < nk) phase_barrier();
     }
   };
-  if (lp.wide) k_loop(std::true_type{});
-  else k_loop(std::false_type{});
-
-  store_tile<MI, FM, FN, TM, TN, BN, SWIGLU, OUT_F32>(p, t, wm, wn,
-                                                      [&](int i, int j, int v) { return acc[i][j][v]; });
+  // The workgroup's tiles, in one address form. Returns false (with the next tile in t, not yet
+  // loaded) when that tile needs the 64-bit form and this loop runs the 32-bit one. The two forms
+  // run as consecutive loops rather than one loop choosing per tile: a loop body holding both K
+  // loops needs more registers than a wave has at this occupancy.
+  //
+  // Between tiles the next tile's first S - 1 K-steps are issued before the finished tile's
+  // stores, and a wave whose stores all went out (its block lies inside the tile) does not wait
+  // for them before the next tile's MFMAs: the stores drain behind the first K-steps.
+  auto tile_loop = [&](auto wide_tag, bool primed) -> bool {
+    bool pend = false;
+    for (;;) {
+      k_loop(wide_tag, primed, pend);
+      // next tile and its load plan (their loads find nothing else in flight), then its first
+      // K-steps if it uses this loop's address form
+      Tile tn;
+      bool more = false, next_primed = false;
+      if constexpr (PERSIST) {
+        phys += gridDim.x;
+        more = next_tile(tn);
+        if (more) {
+          lp.init(p, tn, wave, lane);
+          if (decltype(wide_tag)::value || !lp.wide) {   // lp.wide is wave-uniform (a ballot)
+            prime(wide_tag);
+            next_primed = true;
+          }
+        }
+      }
+      bool full;
+      if constexpr (F32X4) {
+        full = store_tile_f32x4<FM, FN, TM, TN, BN>(p, t, wm, wn,
+                                                    [&](int i, int j, int v) { return acc[i][j][v]; });
+      } else {
+        full = t.row0 + wm * TM + TM <= t.row1 &&
+               (long long)t.nt * (SWIGLU ? BN / 2 : BN) + wn * (SWIGLU ? TN / 2 : TN) +
+                       (SWIGLU ? TN / 2 : TN) <= p.N;
+        store_tile<MI, FM, FN, TM, TN, BN, SWIGLU, OUT_F32, OUT_F32>(
+            p, t, wm, wn, [&](int i, int j, int v) { return acc[i][j][v]; });
+      }
+      if (!more) return true;
+      t = tn;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      if (!next_primed) return false;                  // the next tile needs the 64-bit form
+      primed = true;
+      pend = OVERLAP && full;
+    }
+  };
+  if (!lp.wide && tile_loop(std::false_type{}, false)) return;
+  tile_loop(std::true_type{}, false);                  // the 64-bit form serves every later tile
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -792,17 +921,22 @@ hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) 
   return hipGetLastError();
 }
 
-template <int S>
+template <int S, bool PERSIST = false>
 hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   const bool sw = a.epilogue == MOE_EPI_SWIGLU;
   Grid g = make_grid(a, 256, sw ? 128 : 256, gm, span);
   if (g.total == 0) return hipSuccess;
-  dim3 grid(g.blocks), block(512);
+  unsigned blocks = g.blocks;
+  if (PERSIST) {
+    const unsigned slots = persistent_slots();          // a multiple of the XCD count
+    if (slots > 0 && slots < blocks) blocks = slots;
+  }
+  dim3 grid(blocks), block(512);
   const bool f32 = a.out_dtype == MOE_F32;
   const size_t lds_bytes = (size_t)S * (256 + 256) * 32 * sizeof(uint16_t);
 #define MOE_RUN(SWI, F32)                                                                        \
-  gemm_bf16_pp_kernel<SWI, F32, S><<<grid, block, lds_bytes, s>>>(a, g.n_tiles, g.x_tiles, g.span, \
-                                                                  g.total, g.gm)
+  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST><<<grid, block, lds_bytes, s>>>(                     \
+      a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm, (int)g.blocks)
   if (sw && f32) MOE_RUN(true, true);
   else if (sw) MOE_RUN(true, false);
   else if (f32) MOE_RUN(false, true);
@@ -861,14 +995,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const long long per_group = groups ? rows / groups : rows;
     const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
     if (per_group >= 256 && n_full >= 256) {
-      // 256 x 256 tiles, K-steps of 32 through 5 LDS stages of 32 KB. SwiGLU (K = hidden size,
-      // long K loops): ping-pong schedule of 8 waves of 128 x 64. Plain store (the down projection,
-      // short K): 16 waves of 64 x 64 (measured a few percent faster there than ping-pong), one
-      // persistent workgroup per CU so each tile's set-up and first loads overlap the previous
-      // tile's stores (per-tile timestamps: set-up, first loads and the fp32 stores took ~20% of a
-      // 256 x 256 x 1536 tile when every tile was its own workgroup).
-      if (a.epilogue == MOE_EPI_SWIGLU) return run_bf16_pp<kPPStages>(a, s, kTileGroupM, kTileSpan);
-      return run_bf16<256, 256, 4, 4, 32, 32, 5, true>(a, s, kTileGroupM, kTileSpan);
+      // 256 x 256 tiles, K-steps of 32 through 5 LDS stages of 32 KB, ping-pong schedule of 8
+      // waves of 128 x 64, one persistent workgroup per CU: each tile's first loads are issued
+      // before the previous tile's stores, which drain behind its first K-steps (measured with the
+      // down projection's fp32 stores removed: the stores, waited for at every tile start, took
+      // a quarter of its time).
+      return run_bf16_pp<kPPStages, true>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
     // decode-sized groups: stream the weights once per 32 (or 64) rows of each group
