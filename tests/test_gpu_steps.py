@@ -311,6 +311,22 @@ def test_grouped_gemm_bf16_persistent_tiles(out_f32):
     assert np.all(Cg[R:] == 1024.0)
 
 
+# more 256 x 256 tiles than CUs with K-steps to spare (K >= 5 steps of 32) and no row gather:
+# consecutive tiles of a workgroup chain (the next tile's first K-steps are issued from the
+# current K loop, groups resolved from the LDS table); K = 192 is the shortest chained loop, the
+# extra rows of an empty group and a partial last n-tile included
+@pytest.mark.parametrize("K,out_f32", [(1536, True), (1536, False), (192, True), (448, False)])
+def test_grouped_gemm_bf16_chained_tiles(K, out_f32):
+    Cg, ref, R = _gemm_case([1500, 1300, 0, 2701, 900, 5], K=K, N=4160, swiglu=False, gather=False,
+                            out_f32=out_f32, seed=K)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if out_f32:
+        assert np.abs(Cg[:R] - ref).max() <= 1e-4 * rms * np.sqrt(K / 256)
+    else:
+        assert np.all(np.abs(Cg[:R] - ref) <= 2 ** -8 * np.abs(ref) + 1e-3 * rms)
+    assert np.all(Cg[R:] == 1024.0)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_f32(swiglu):
     Cg, ref, R = _gemm_case([20, 0, 65, 7], K=256, N=128, swiglu=swiglu, gather=True, out_f32=True,
