@@ -158,6 +158,34 @@ def test_layer_k_equals_E_sigmoid_ragged():
     check_layer(_small(T=37, E=16, k=3, e0=4, E_loc=12, I_s=256))
 
 
+def test_layer_mx8_single_token_full_shape():
+    # one token at the full MXFP8 shape: one row per chosen expert (weight streaming)
+    check_layer(mi.WORKLOADS["C2p_mx8"].with_tokens(1))
+
+
+@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8])
+def test_layer_quantised_single_token_with_shared(fmt):
+    # one token, sigmoid routing, shared expert as a one-row extra group
+    check_layer(_small(T=1, fmt=fmt, H=512, I=256, I_s=256, scoring=mi.SIGMOID))
+
+
+@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8])
+def test_layer_quantised_all_tokens_one_expert(fmt):
+    # every token's top choice is expert 3 (one large group on the tile kernels, the rest small)
+    wl = _small(T=700, fmt=fmt, H=512, I=256)
+    bias = np.zeros(16, np.float32)
+    bias[3] = 30.0
+    check_layer(wl, bias_override=bias)
+
+
+@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8])
+def test_layer_quantised_no_local_rows_with_shared(fmt):
+    wl = _small(e0=8, I_s=256, fmt=fmt, H=512, I=256)
+    bias = np.zeros(16, np.float32)
+    bias[8:] = -100.0
+    check_layer(wl, bias_override=bias)
+
+
 def test_layer_deterministic():
     wl = mi.WORKLOADS["C3a"]
     x, wr, bias, experts, sh = make_inputs(wl)
