@@ -425,11 +425,7 @@ __device__ __forceinline__ void phase_barrier() {
 #endif
 }
 
-// XT (persistent, A not gathered): the workgroup keeps the groups' row offsets and m-tile prefix
-// in LDS (built once), so a tile resolves without global loads; the next tile is resolved at the
-// start of the current one and the K loop's last iterations issue the next tile's first S - 1
-// K-steps into the stages they free, so consecutive tiles run back to back.
-template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST, bool XT = false>
+template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST>
 __global__ void __launch_bounds__(512)
 gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm, int nphys) {
   constexpr int BM = 256, BN = 256, WN = 4, MI = 32, BK = 32;
@@ -443,69 +439,6 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
 
   extern __shared__ __attribute__((aligned(1024))) uint16_t lds[];
-  static_assert(!XT || PERSIST, "cross-tile loads need the persistent schedule");
-
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);
-  // XT: group table after the stages: tbl[g] = offsets[g] (g <= G), tbl[G + 1 + g] = routed
-  // m-tiles before group g (g <= G)
-  int* const tbl = reinterpret_cast<int*>(lds + S * STAGE);
-  if constexpr (XT) {
-    if (wave == 0) {
-      int base = 0;
-      for (int g0 = 0; g0 <= p.G; g0 += 64) {
-        const int g = g0 + lane;
-        int o = 0, tiles = 0;
-        if (g <= p.G) o = p.offsets[g];
-        if (g < p.G) tiles = (p.offsets[g + 1] - o + BM - 1) / BM;
-        int inc = tiles;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const int v = __shfl_up(inc, d, 64);
-          if (lane >= d) inc += v;
-        }
-        if (g <= p.G) {
-          tbl[g] = o;
-          tbl[p.G + 1 + g] = base + inc - tiles;
-        }
-        base += __shfl(inc, 63, 64);
-      }
-    }
-    __syncthreads();
-  }
-  // routed m-tile mt -> group rows from the LDS table (the wave-uniform first group whose tile
-  // prefix passes mt)
-  auto resolve_lds = [&](int logical, Tile& tt) -> bool {
-    const int per_group = gm * n_tiles;
-    const int grp_i = logical / per_group;
-    const int within = logical - grp_i * per_group;
-    const int mt = grp_i * gm + within % gm;
-    tt.nt = within / gm;
-    if (mt < x_tiles) {
-      tt.extra = true;
-      tt.row0 = p.x_row0 + mt * BM;
-      tt.row1 = min(tt.row0 + BM, p.x_row0 + p.x_rows);
-      tt.B = static_cast<const char*>(p.xB);
-      tt.B2 = static_cast<const char*>(p.xB2);
-      return true;
-    }
-    const int m = mt - x_tiles;
-    for (int g0 = 0; g0 < p.G; g0 += 64) {
-      const int g = g0 + lane;
-      const int hi = g < p.G ? tbl[p.G + 2 + g] : 0x7FFFFFFF;
-      const unsigned long long hit = __ballot(g < p.G && hi > m);
-      if (hit) {
-        const int gg = uniform(g0 + __builtin_ctzll(hit));
-        tt.extra = false;
-        tt.row0 = uniform(tbl[gg] + (m - tbl[p.G + 1 + gg]) * BM);
-        tt.row1 = uniform(min(tt.row0 + BM, tbl[gg + 1]));
-        tt.B = static_cast<const char*>(p.B) + gg * p.b_stride;
-        tt.B2 = p.B2 ? static_cast<const char*>(p.B2) + gg * p.b_stride : nullptr;
-        return true;
-      }
-    }
-    return false;
-  };
 
   // PERSIST: one workgroup per CU slot takes the tiles of workgroup positions b, b + gridDim.x, ...
   // (as in gemm_bf16_pipe_kernel): the next tile's first S - 1 K-steps are loaded while the
@@ -514,11 +447,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   auto next_tile = [&](Tile& tt) -> bool {
     for (; phys < nphys; phys += gridDim.x) {
       const int logical = xcd_remap(phys, span);
-      if constexpr (XT) {
-        if (logical < total && resolve_lds(logical, tt)) return true;
-      } else {
-        if (logical < total && resolve_tile(p, BM, n_tiles, x_tiles, logical, tt, gm)) return true;
-      }
+      if (logical < total && resolve_tile(p, BM, n_tiles, x_tiles, logical, tt, gm)) return true;
       if (!PERSIST) break;
     }
     return false;
@@ -526,29 +455,19 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   Tile t;
   if (!next_tile(t)) return;
 
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
   const int grp = wave >> 2;                           // wave-uniform (scalar branches below)
   const int wm = grp, wn = wave & (WN - 1);
   const int nk = p.K / BK;
 
   LoadPlan<Geo, BM, BN, TN, NW, SWIGLU> lp;
   lp.init(p, t, wave, lane);
-  // XT: the next tile, its load plan, and whether its K-steps follow this tile's in the K loop
-  Tile tx;
-  LoadPlan<Geo, BM, BN, TN, NW, SWIGLU> lpx;
-  bool more_x = false, chain_x = false;
-  // stage of K-step kt of the current tile: (stg0 + kt) % S; stg0 advances by nk per chained tile
-  int stg0 = 0;
   const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds));
-  // K-step kt of the current tile, or (XT) step kt - nk of the next one when the tiles chain
   auto issue = [&](int kt, auto wide_tag) {
-    constexpr bool W = decltype(wide_tag)::value;
-    const int st = (stg0 + kt) % S;
-    if (kt < nk) {
-      lp.template issue<W>((long long)kt * Geo::kRowBytes, lds + st * STAGE, lds0 + st * (STAGE * 2), wave);
-    } else if (XT && chain_x) {
-      lpx.template issue<W>((long long)(kt - nk) * Geo::kRowBytes, lds + st * STAGE,
-                            lds0 + st * (STAGE * 2), wave);
-    }
+    if (kt >= nk) return;
+    lp.template issue<decltype(wide_tag)::value>((long long)kt * Geo::kRowBytes, lds + (kt % S) * STAGE,
+                                                 lds0 + (kt % S) * (STAGE * 2), wave);
   };
   // Store instructions of the epilogue of a wave whose block lies inside the tile: 16-byte stores
   // for fp32 STORE (4 per 32 x 32 fragment), otherwise 2-column stores (8 per fragment pair row
@@ -563,7 +482,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   // tile's epilogue, see tile_loop); vmcnt retires in issue order, so while those stores are
   // younger than step kt + 1 (kt + 1 <= S - 2) they are left in flight by counting them too.
   auto wait_next = [&](int kt, bool pend) {
-    if (kt + S - 1 < nk || (XT && chain_x && nk >= S - 1)) {
+    if (kt + S - 1 < nk) {
       if (OVERLAP && pend && kt <= S - 3) wait_vmem_n<(S - 2) * INS + NPEND>();
       else wait_vmem_n<(S - 2) * INS>();
     } else {
@@ -617,11 +536,10 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
     }
     phase_barrier();                                   // b0
     if (grp == 1) phase_barrier();                     // b1 (group 1 starts one phase later)
-    if constexpr (XT) chain_x = false;
 
     for (int kt = 0; kt < nk; ++kt) {
       // memory phase
-      read_step((stg0 + kt) % S);
+      read_step(kt % S);
       issue(kt + S - 1, wide_tag);
       if (grp == 1) wait_next(kt, pend);
       wait_lgkm();
@@ -634,19 +552,6 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-      if constexpr (XT) {
-        // the next tile, resolved from the LDS table while this step's MFMAs run (its first
-        // K-steps are issued from step nk - S + 1 on; the host launches XT only when nk >= S)
-        if (kt == 0) {
-          phys += gridDim.x;
-          more_x = next_tile(tx);
-          if (more_x) {
-            lpx.init(p, tx, wave, lane);
-            // the 64-bit form serves any tile; the 32-bit one only tiles that fit it
-            chain_x = decltype(wide_tag)::value || !lpx.wide;   // wave-uniform (a ballot)
-          }
-        }
-      }
       if (grp == 0) wait_next(kt, pend);
       if (grp == 0 || kt + 1 < nk) phase_barrier();
     }
@@ -664,17 +569,10 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
     for (;;) {
       k_loop(wide_tag, primed, pend);
       // next tile and its load plan (their loads find nothing else in flight), then its first
-      // K-steps if it uses this loop's address form (XT: both already done inside the K loop)
+      // K-steps if it uses this loop's address form
       Tile tn;
       bool more = false, next_primed = false;
-      if constexpr (XT) {
-        more = more_x;
-        next_primed = chain_x;
-        if (more) {
-          tn = tx;
-          lp = lpx;
-        }
-      } else if constexpr (PERSIST) {
+      if constexpr (PERSIST) {
         phys += gridDim.x;
         more = next_tile(tn);
         if (more) {
@@ -702,10 +600,6 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-      // XT: every wave moves the stage base on, chained or not (the address form is chosen per
-      // wave, so in one workgroup some waves may have issued their share of the next tile's
-      // first K-steps and others not: all must agree where each step lives)
-      if constexpr (XT) stg0 = (stg0 + nk) % S;
       if (!next_primed) return false;                  // the next tile needs the 64-bit form
       primed = true;
       pend = OVERLAP && full;
@@ -978,7 +872,10 @@ namespace {
 // (12 distinct slices per 32 tiles).
 constexpr int kTileGroupM = 8;
 constexpr int kTileSpan = 64;
-constexpr int kPPStages = 5;
+// LDS stages of the persistent ping-pong kernel. Measured on the 16384-token Qwen3-235B slice
+// (same box, gate/up / down): 3 stages 2.52 / 1.61 ms, 4 stages 2.54 / 1.63 ms, 5 stages 2.60-2.63 /
+// 1.65-1.67 ms -- fewer loads in flight per CU run faster here.
+constexpr int kPPStages = 3;
 // weight-streaming tiles of 32 rows up to this many rows per group on average, 64 rows above
 constexpr int kStreamRows32 = 24;
 // weight streaming: K pairs (128 bytes of every weight row) per wave at or above which a tile is
@@ -1027,7 +924,7 @@ hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) 
   return hipGetLastError();
 }
 
-template <int S, bool PERSIST = false, bool XT = false>
+template <int S, bool PERSIST = false>
 hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   const bool sw = a.epilogue == MOE_EPI_SWIGLU;
   Grid g = make_grid(a, 256, sw ? 128 : 256, gm, span);
@@ -1039,11 +936,9 @@ hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   }
   dim3 grid(blocks), block(512);
   const bool f32 = a.out_dtype == MOE_F32;
-  // XT: the group table (offsets and m-tile prefix, 2 (G + 1) ints) follows the stages
-  const size_t lds_bytes = (size_t)S * (256 + 256) * 32 * sizeof(uint16_t) +
-                           (XT ? (size_t)(2 * a.G + 2) * sizeof(int) : 0);
+  const size_t lds_bytes = (size_t)S * (256 + 256) * 32 * sizeof(uint16_t);
 #define MOE_RUN(SWI, F32)                                                                        \
-  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST, XT><<<grid, block, lds_bytes, s>>>(                 \
+  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST><<<grid, block, lds_bytes, s>>>(                     \
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm, (int)g.blocks)
   if (sw && f32) MOE_RUN(true, true);
   else if (sw) MOE_RUN(true, false);
@@ -1103,15 +998,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const long long per_group = groups ? rows / groups : rows;
     const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
     if (per_group >= 256 && n_full >= 256) {
-      // 256 x 256 tiles, K-steps of 32 through 5 LDS stages of 32 KB, ping-pong schedule of 8
+      // 256 x 256 tiles, K-steps of 32 through 3 LDS stages of 32 KB, ping-pong schedule of 8
       // waves of 128 x 64, one persistent workgroup per CU: each tile's first loads are issued
       // before the previous tile's stores, which drain behind its first K-steps (measured with the
       // down projection's fp32 stores removed: the stores, waited for at every tile start, took
       // a quarter of its time).
-      // Without a row gather (the down projection) consecutive tiles chain: 4 stages, the group
-      // table in LDS, the next tile's first K-steps issued from the current K loop.
-      if (!a.a_rows && a.G >= 1 && a.offsets && a.K / 32 >= 5 && a.G <= 1024)
-        return run_bf16_pp<4, true, true>(a, s, kTileGroupM, kTileSpan);
       return run_bf16_pp<kPPStages, true>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);

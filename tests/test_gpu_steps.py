@@ -311,12 +311,12 @@ def test_grouped_gemm_bf16_persistent_tiles(out_f32):
     assert np.all(Cg[R:] == 1024.0)
 
 
-# more 256 x 256 tiles than CUs with K-steps to spare (K >= 5 steps of 32) and no row gather:
-# consecutive tiles of a workgroup chain (the next tile's first K-steps are issued from the
-# current K loop, groups resolved from the LDS table); K = 192 is the shortest chained loop, the
-# extra rows of an empty group and a partial last n-tile included
-@pytest.mark.parametrize("K,out_f32", [(1536, True), (1536, False), (192, True), (448, False)])
-def test_grouped_gemm_bf16_chained_tiles(K, out_f32):
+# more 256 x 256 tiles than CUs, no row gather, several K lengths (2 to 48 K-steps of 32) and a
+# partial last n-tile: each persistent workgroup runs several tiles, issuing a tile's first
+# K-steps before the previous tile's stores and leaving those stores in flight
+@pytest.mark.parametrize("K,out_f32", [(1536, True), (1536, False), (192, True), (448, False),
+                                       (64, True)])
+def test_grouped_gemm_bf16_many_tiles(K, out_f32):
     Cg, ref, R = _gemm_case([1500, 1300, 0, 2701, 900, 5], K=K, N=4160, swiglu=False, gather=False,
                             out_f32=out_f32, seed=K)
     rms = np.sqrt(np.mean(ref ** 2))
