@@ -9,6 +9,7 @@ Recipe (every draw is float32 from numpy's PCG64 `default_rng`, seeded by a tupl
                     W_up   [I, H]        rng([seed, 1, e, 1])     N(0, 1) * 0.02
                     W_down [H, I]        rng([seed, 1, e, 2])     N(0, 1) * 0.02
   * shared expert   same three shapes    rng([seed, 2, 0, m])
+  * shared gate     w_sg [H]             rng([seed, 2, 1, 0])     N(0, 1) * 0.02 (gated workloads)
   * tokens          x [T, H]             rng([seed, 3, T])        N(0, 1)
   * router bias     log of the Zipf(s) pmf over experts (expert e has rank e + 1), or none.
 
@@ -103,6 +104,11 @@ def shared_weights(wl: Workload):
     if wl.I_s == 0:
         return None
     return tuple(shared_weight(wl, w) for w in range(3))
+
+
+def shared_gate_vector(wl: Workload):
+    """Gate vector of the shared expert [H], in the io format (same rounding as the router)."""
+    return _io_round(wl, _normal((wl.seed, 2, 1, 0), (wl.H,), 0.02))
 
 
 def tokens(wl: Workload):

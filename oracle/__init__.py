@@ -237,16 +237,29 @@ def grouped_gemm(offsets, A, B, B2=None, a_rows=None, a_row_div=1, bias=None):
     return out
 
 
-def combine(y, w, slot_to_row, shared=None):
+def combine(y, w, slot_to_row, shared=None, shared_w=None):
     y = _c(y, np.float32)
     w = _c(w, np.float32)
     s2r = _c(slot_to_row, np.int32)
     T, k = s2r.shape
     H = y.shape[1]
     sh = None if shared is None else _c(shared, np.float32)
+    sw = None if shared_w is None else _c(shared_w, np.float32)
     out = np.empty((T, H), np.float64)
-    lib().oracle_combine(T, H, k, _p(y), _p(w), _p(s2r), _p(sh), _p(out))
+    lib().oracle_combine(T, H, k, _p(y), _p(w), _p(s2r), _p(sh), _p(sw), _p(out))
     return out
+
+
+def shared_gate(x, w_sg, tok=None):
+    """Gate of the shared expert per token: 1 / (1 + exp(-(x_t . w_sg))), double [n]."""
+    x = _c(x, np.float32)
+    g_w = _c(w_sg, np.float32)
+    T, H = x.shape
+    t = None if tok is None else _c(tok, np.int32)
+    n = T if t is None else len(t)
+    g = np.empty(n, np.float64)
+    lib().oracle_shared_gate(T, H, _p(x), _p(g_w), n, _p(t), _p(g))
+    return g
 
 
 # ---- the layer -------------------------------------------------------------------------
@@ -260,11 +273,12 @@ def ffn_row(a, gate, up, down, g=0, act_fmt=F32):
     return y
 
 
-def moe_layer(desc, x, w_r, bias, xa, gate, up, down, shared=None, tok=None):
+def moe_layer(desc, x, w_r, bias, xa, gate, up, down, shared=None, tok=None, shared_gate=None):
     """Run the layer for all tokens (tok None) or a subset of token indices.
 
     desc: dict with T, H, E, e0, E_loc, I, k, I_s, scoring, renormalize, act_fmt.
-    x: float32 [T, H] unquantised input (router input); xa: Mat [1, T, H] fed to the experts.
+    x: float32 [T, H] unquantised input (router and shared-gate input); xa: Mat [1, T, H] fed to
+    the experts; shared_gate: float32 [H] gate vector of the shared expert, or None (ungated).
     Returns dict(out, logits64, logits32, ids, w)."""
     x = _c(x, np.float32)
     w_r = _c(w_r, np.float32)
@@ -281,9 +295,10 @@ def moe_layer(desc, x, w_r, bias, xa, gate, up, down, shared=None, tok=None):
     w = np.empty((n, k), np.float64)
     null = ctypes.c_void_p(None)
     sg, su, sd = (shared if shared is not None else (None, None, None))
+    gv = None if shared_gate is None else _c(shared_gate, np.float32)
     lib().oracle_moe_layer(ctypes.byref(d), _p(x), _p(w_r), _p(b), xa.ref, gate.ref, up.ref,
                            down.ref, sg.ref if sg else null, su.ref if su else null,
-                           sd.ref if sd else null, n, _p(t), _p(out), _p(L64), _p(L32),
+                           sd.ref if sd else null, _p(gv), n, _p(t), _p(out), _p(L64), _p(L32),
                            _p(ids), _p(w))
     return dict(out=out, logits64=L64, logits32=L32, ids=ids, w=w)
 

@@ -267,6 +267,23 @@ void oracle_logits(int T, int H, int E, const float* x, const float* w_r, const 
     }
 }
 
+/* Gate of the shared expert for token t: one logit z = x_t . w_sg (double), then the logistic
+ * function 1 / (1 + exp(-z)). */
+static double shared_gate_row(int H, const float* x, const float* w_sg, int t)
+{
+  double z = 0.0;
+  for (int h = 0; h < H; ++h) z += (double)x[(size_t)t * H + h] * (double)w_sg[h];
+  return 1.0 / (1.0 + exp(-z));
+}
+
+void oracle_shared_gate(int T, int H, const float* x, const float* w_sg, int n_tok,
+                        const int32_t* tok, double* g)
+{
+  int n = tok ? n_tok : T;
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < n; ++i) g[i] = shared_gate_row(H, x, w_sg, tok ? tok[i] : i);
+}
+
 /* Selection of the k largest fp32 logits: repeatedly take the largest remaining value, the lowest
  * index among equal values (C comparison treats +0 and -0 as equal). This equals a full sort by
  * (value descending, index ascending) cut after k entries. */
@@ -415,8 +432,9 @@ void oracle_ffn_row(const oracle_desc* d, int I, const double* a, const oracle_m
 void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, const float* bias,
                       const oracle_mat* xa, const oracle_mat* gate, const oracle_mat* up,
                       const oracle_mat* down, const oracle_mat* sh_gate, const oracle_mat* sh_up,
-                      const oracle_mat* sh_down, int n_tok, const int32_t* tok, double* out,
-                      double* logits64, float* logits32, int32_t* ids, double* w)
+                      const oracle_mat* sh_down, const float* w_sg, int n_tok,
+                      const int32_t* tok, double* out, double* logits64, float* logits32,
+                      int32_t* ids, double* w)
 {
   int n = tok ? n_tok : d->T;
   int H = d->H, E = d->E, k = d->k;
@@ -445,8 +463,9 @@ void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, co
       for (int c = 0; c < H; ++c) o[c] += wt[j] * y[c];
     }
     if (d->I_s > 0) {
+      double gs = w_sg ? shared_gate_row(H, x, w_sg, t) : 1.0;
       oracle_ffn_row(d, d->I_s, a, sh_gate, sh_up, sh_down, 0, y);
-      for (int c = 0; c < H; ++c) o[c] += y[c];
+      for (int c = 0; c < H; ++c) o[c] += gs * y[c];
     }
     if (logits64) memcpy(logits64 + (size_t)i * E, L64, sizeof(double) * (size_t)E);
     if (logits32) memcpy(logits32 + (size_t)i * E, L32, sizeof(float) * (size_t)E);
@@ -496,7 +515,7 @@ void oracle_grouped_gemm(int G, const int32_t* offsets, const oracle_mat* A, con
 }
 
 void oracle_combine(int T, int H, int k, const float* y, const float* w, const int32_t* slot_to_row,
-                    const float* shared, double* out)
+                    const float* shared, const float* shared_w, double* out)
 {
 #pragma omp parallel for schedule(static)
   for (int t = 0; t < T; ++t) {
@@ -507,7 +526,9 @@ void oracle_combine(int T, int H, int k, const float* y, const float* w, const i
       if (r < 0) continue;
       for (int c = 0; c < H; ++c) o[c] += (double)w[t * k + j] * (double)y[(size_t)r * H + c];
     }
-    if (shared)
-      for (int c = 0; c < H; ++c) o[c] += (double)shared[(size_t)t * H + c];
+    if (shared) {
+      double gs = shared_w ? (double)shared_w[t] : 1.0;
+      for (int c = 0; c < H; ++c) o[c] += gs * (double)shared[(size_t)t * H + c];
+    }
   }
 }

@@ -117,17 +117,27 @@ typedef struct {
 void oracle_ffn_row(const oracle_desc* d, int I, const double* a, const oracle_mat* gate,
                     const oracle_mat* up, const oracle_mat* down, int g, double* y);
 
+/* Gate of the shared expert, for n_tok tokens (tok = NULL: all T in order):
+ *   g[i] = 1 / (1 + exp(-(x_t . w_sg))), t = tok[i], the dot over the H columns in double.
+ * [P1], introduction: the layer adapts to the newer models' additional gate terms, whose form
+ * the pages leave open; read as one learned projection of the unquantised token, through the
+ * logistic function, scaling the always-active shared expert's output. */
+void oracle_shared_gate(int T, int H, const float* x, const float* w_sg, int n_tok,
+                        const int32_t* tok, double* g);
+
 /* The layer for n_tok tokens (tok = NULL: all T in order):
  *   logits from the unquantised x and w_r (double, rounded to fp32 for the selection),
  *   top-k, then out[t] = sum_j w_tj * FFN_{e_tj}(a_t) over local slots (j ascending)
- *                        + FFN_shared(a_t) if I_s > 0,
- * where a_t is row t of `xa` (x itself, or x after the activation quantiser).
+ *                        + g_t * FFN_shared(a_t) if I_s > 0,
+ * where a_t is row t of `xa` (x itself, or x after the activation quantiser), and g_t is
+ * oracle_shared_gate's value for token t if w_sg != NULL, else 1.
  * Optional outputs (NULL to skip): logits64 [n,E], logits32 [n,E], ids [n,k], w [n,k]. */
 void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, const float* bias,
                       const oracle_mat* xa, const oracle_mat* gate, const oracle_mat* up,
                       const oracle_mat* down, const oracle_mat* sh_gate, const oracle_mat* sh_up,
-                      const oracle_mat* sh_down, int n_tok, const int32_t* tok, double* out,
-                      double* logits64, float* logits32, int32_t* ids, double* w);
+                      const oracle_mat* sh_down, const float* w_sg, int n_tok,
+                      const int32_t* tok, double* out, double* logits64, float* logits32,
+                      int32_t* ids, double* w);
 
 /* ---- the grouped GEMM and the combine on their own ---------------------------------------------- */
 /* For each group g and row r in [offsets[g], offsets[g+1]): with a(r) = a_rows ? a_rows[r] / div : r,
@@ -139,9 +149,10 @@ void oracle_grouped_gemm(int G, const int32_t* offsets, const oracle_mat* A, con
                          const float* bias, double* out);
 
 /* out[t, :] = sum_{j ascending, slot_to_row[t,j] >= 0} w[t,j] * y[slot_to_row[t,j], :]
- *             (+ shared[t, :] if shared != NULL); y, shared float; out double [T, H]. */
+ *             (+ g_t * shared[t, :] if shared != NULL, g_t = shared_w[t], or 1 if shared_w is
+ *             NULL); y, shared, shared_w float; out double [T, H]. */
 void oracle_combine(int T, int H, int k, const float* y, const float* w, const int32_t* slot_to_row,
-                    const float* shared, double* out);
+                    const float* shared, const float* shared_w, double* out);
 
 int oracle_num_threads(void);
 

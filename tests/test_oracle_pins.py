@@ -426,11 +426,11 @@ def _tiny(T=12, H=64, E=4, I=32, k=2, e0=0, E_loc=4, I_s=0, scoring=0, seed=0, s
     return desc, x, wr, g, u, d, sh
 
 
-def _run(desc, x, wr, g, u, d, sh, bias=None, tok=None):
+def _run(desc, x, wr, g, u, d, sh, bias=None, tok=None, shared_gate=None):
     M = oracle.Mat
     shared = None if sh is None else tuple(M(oracle.F32, s) for s in sh)
     return oracle.moe_layer(desc, x, wr, bias, M(oracle.F32, x), M(oracle.F32, g), M(oracle.F32, u),
-                            M(oracle.F32, d), shared, tok)
+                            M(oracle.F32, d), shared, tok, shared_gate=shared_gate)
 
 
 def test_single_expert_is_dense_ffn():
@@ -607,6 +607,59 @@ def test_combine_matches_gather_formula_and_layer():
     shy = np.stack([oracle.ffn_row(x[t], *(M(oracle.F32, s) for s in shw)) for t in range(8)])
     comb = oracle.combine(ys, full["w"].astype(np.float32), s2r, shy.astype(np.float32))
     assert np.allclose(comb, full["out"], rtol=1e-5, atol=1e-5)
+
+
+def test_shared_gate_closed_forms():
+    # logistic function at z = +-ln 3 (3/4 and 1/4) and z = 0 (1/2), reached through one-hot rows
+    H = 16
+    x = np.zeros((4, H), np.float32)
+    x[0, 3], x[1, 3], x[3, 5] = 1.0, -1.0, 2.0
+    w = np.zeros(H, np.float32)
+    w[3] = np.float32(np.log(3.0))
+    w[5] = np.float32(-np.log(3.0) / 2)
+    g = oracle.shared_gate(x, w)
+    assert np.allclose(g, [0.75, 0.25, 0.5, 0.25], rtol=0, atol=1e-7)
+    # a zero gate vector halves the shared expert for every token, exactly
+    rng = np.random.default_rng(21)
+    xr = rng.standard_normal((7, 40)).astype(np.float32)
+    assert np.array_equal(oracle.shared_gate(xr, np.zeros(40, np.float32)), np.full(7, 0.5))
+    # g(x) + g(-x) = 1, strictly increasing in the logit, subset of tokens = rows of the full call
+    wr = (rng.standard_normal(40) * 0.3).astype(np.float32)
+    gp, gm = oracle.shared_gate(xr, wr), oracle.shared_gate(-xr, wr)
+    assert np.allclose(gp + gm, 1.0, rtol=0, atol=1e-15)
+    z = xr.astype(np.float64) @ wr.astype(np.float64)
+    assert np.all(np.diff(gp[np.argsort(z)]) > 0)
+    tok = np.array([6, 0, 3], np.int32)
+    assert np.array_equal(oracle.shared_gate(xr, wr, tok), gp[tok])
+
+
+def test_gated_shared_expert_scales_only_the_shared_term():
+    desc, x, wr, g, u, d, sh = _tiny(T=9, E=6, E_loc=3, e0=2, k=2, I_s=8)
+    routed = _run(dict(desc, I_s=0), x, wr, g, u, d, None)["out"]
+    ungated = _run(desc, x, wr, g, u, d, sh)["out"]
+    # zero gate vector: exactly half of the shared expert's output is added to the routed sum
+    half = _run(desc, x, wr, g, u, d, sh, shared_gate=np.zeros(desc["H"], np.float32))["out"]
+    assert np.allclose(half, routed + 0.5 * (ungated - routed), rtol=0, atol=1e-12)
+    # any gate vector: per token, a single factor in (0, 1) on the shared term, equal to the gate
+    gv = (np.random.default_rng(22).standard_normal(desc["H"]) * 0.5).astype(np.float32)
+    gated = _run(desc, x, wr, g, u, d, sh, shared_gate=gv)["out"]
+    sh_term = ungated - routed
+    ratio = (gated - routed) / sh_term
+    gt = oracle.shared_gate(x, gv)
+    assert np.all((gt > 0) & (gt < 1)) and gt.std() > 0.05
+    assert np.allclose(ratio, gt[:, None], rtol=0, atol=1e-9)
+    # the combine step applies the same per-token factor to the shared rows
+    rng = np.random.default_rng(23)
+    T, k, H, R = 5, 2, 8, 7
+    y = rng.standard_normal((R, H)).astype(np.float32)
+    w = rng.random((T, k)).astype(np.float32)
+    s2r = rng.integers(-1, R, size=(T, k)).astype(np.int32)
+    shr = rng.standard_normal((T, H)).astype(np.float32)
+    sw = rng.random(T).astype(np.float32)
+    wm = np.where(s2r >= 0, w.astype(np.float64), 0.0)
+    ref = (np.einsum("tj,tjh->th", wm, y.astype(np.float64)[np.maximum(s2r, 0)])
+           + sw.astype(np.float64)[:, None] * shr)
+    assert np.allclose(oracle.combine(y, w, s2r, shr, sw), ref, rtol=0, atol=1e-12)
 
 
 def test_bf16_rounding_matches_torch():
