@@ -63,7 +63,8 @@ def workload_table(stream, steps):
               mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8)}
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     out = {}
-    for name in ("C2p", "C2d", "C3a", "C3b", "C4p", "C4d", "C5p", "C5d", "C2p_mx8", "C2d_mx8"):
+    for name in ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
+                 "C2p_mx8", "C2d_mx8"):
         wl = mi.WORKLOADS[name]
         fname, fcode = fmt_of[wl.fmt]
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
@@ -100,9 +101,12 @@ def workload_table(stream, steps):
             wbytes_expert = sum(int(m[0].numel() * m.element_size()) + int(s[0].numel() * s.element_size())
                                 for m, s in zip(mats[:3], scales[:3]))
         torch.cuda.synchronize()
+        sgate = (torch.randn(wl.H, generator=gen_t, device="cuda") * 0.02).to(torch.bfloat16) \
+            if wl.gated else None
         W = moe.make_weights(wr, *mats[:3], scales=tuple(scales[:3]),
                              shared=tuple(mats[3:]) if wl.I_s else None,
-                             shared_scales=tuple(scales[3:]) if wl.I_s else (None, None, None))
+                             shared_scales=tuple(scales[3:]) if wl.I_s else (None, None, None),
+                             shared_gate=sgate)
         d = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
                           wl.renormalize, moe.MOE_BF16, fcode, moe.MOE_F32)
         o = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")

@@ -5,8 +5,9 @@
  *   logits_t = W_r x_t + bias                      router over all E experts (fp32)
  *   S_t      = the k largest logits (lowest expert index first among equal values)
  *   w_tj     = softmax over S_t, or sigmoid(L) / sum over S_t of sigmoid(L)
- *   out_t    = sum_{j : e_tj local} w_tj * FFN_{e_tj}(a_t)  [+ FFN_shared(a_t)]
+ *   out_t    = sum_{j : e_tj local} w_tj * FFN_{e_tj}(a_t)  [+ g_t * FFN_shared(a_t)]
  *   FFN_e(a) = W_down,e ( silu(W_gate,e a) * (W_up,e a) )
+ *   g_t      = 1 / (1 + exp(-(w_sg . x_t))) for a gated shared expert, else 1
  * where a_t is x_t, or x_t after the activation quantiser for the fp8 / MXFP4 / MXFP8 expert
  * formats.
  *
@@ -20,6 +21,8 @@
  *     per expert from the routing table, gives each token a unique index within its expert's list,
  *     copies tokens into (optionally padded) expert buffers, and the combine accumulates weighted
  *     rows in registers using those positions and the offsets the dispatch computed.
+ *     Introduction: the layer adapts to the newer models' additional gate terms (their form is
+ *     not given; read here as the per-token logistic gate g_t of the shared expert above).
  *   - "How we served a 397B MoE model with 4.7x speedup on TPU v7", architectural constraints
  *     section: 512 experts, top-10, one always-active shared expert; "Three collectives become two":
  *     routing indices (int) and weights (float) as two arrays of shape [T, k].
@@ -102,7 +105,9 @@ typedef struct {
  *                gate/up [E_loc, I, H/32], down [E_loc, H, I/32].
  *   MXFP8:       codes gate/up [E_loc, I, H], down [E_loc, H, I]; E8M0 scales as for MXFP4.
  * The shared expert (sh_*) has the same layouts with E_loc = 1 and I = I_s; NULL when I_s = 0.
- * w_router is [E, H] in io_dtype. Produce quantised weights with moe_quantize. */
+ * w_router is [E, H] in io_dtype. w_shared_gate is the shared expert's gate vector w_sg [H] in
+ * io_dtype, or NULL for an ungated shared expert (g_t = 1); ignored when I_s = 0. Produce
+ * quantised weights with moe_quantize. */
 typedef struct {
   const void* w_router;
   const void* w_gate;  const void* w_gate_scales;
@@ -111,6 +116,7 @@ typedef struct {
   const void* sh_gate; const void* sh_gate_scales;
   const void* sh_up;   const void* sh_up_scales;
   const void* sh_down; const void* sh_down_scales;
+  const void* w_shared_gate;
 } moe_weights;
 
 /* ---- routing (router logits, scores, top-k, renormalisation) ---------------------------------
@@ -176,12 +182,23 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
 
 /* ---- combine (weighted un-permute) -------------------------------------------------------------
  * out[t, :] = sum_{j ascending, slot_to_row[t,j] >= 0} topk_w[t,j] * y[slot_to_row[t,j], :]
- *             (+ shared[t, :] if shared != NULL), accumulated in fp32, rounded once to out_dtype.
- * y: [T*k, H] and shared: [T, H] (or NULL) in y_dtype (MOE_F32 or MOE_BF16); out: [T, H] in
- * d->out_dtype. A token with no local expert and no shared expert gets zeros. */
+ *             (+ g_t * shared[t, :] if shared != NULL, g_t = shared_w[t], or 1 when shared_w is
+ *             NULL), accumulated in fp32, rounded once to out_dtype.
+ * y: [T*k, H] and shared: [T, H] (or NULL) in y_dtype (MOE_F32 or MOE_BF16); shared_w: [T] fp32
+ * (or NULL; must be NULL when shared is); out: [T, H] in d->out_dtype. A token with no local
+ * expert and no shared expert gets zeros. Pointers: 16-byte aligned. */
 moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const float* topk_w,
-                       const int32_t* slot_to_row, const void* shared, void* out,
-                       hipStream_t stream);
+                       const int32_t* slot_to_row, const void* shared, const float* shared_w,
+                       void* out, hipStream_t stream);
+
+/* ---- gate of the shared expert -------------------------------------------------------------------
+ * shared_w[t] = 1 / (1 + exp(-(x_t . w_shared_gate))), the dot accumulated in fp32 over the H
+ * columns of the unquantised token ("Hosting Qwen on Blackwell", introduction: the newer models'
+ * additional gate terms; this per-token logistic gate of the shared expert is the reading taken).
+ * x [T, H] and w_shared_gate [H] in d->io_dtype; shared_w [T] fp32, the combine's per-token factor
+ * of the shared rows. Pointers: 16-byte aligned. */
+moe_status moe_shared_gate(const moe_desc* d, const void* x, const void* w_shared_gate,
+                           float* shared_w, hipStream_t stream);
 
 /* ---- activation / weight quantiser -------------------------------------------------------------
  * src [rows, cols] (src_dtype MOE_F32 or MOE_BF16) -> dst_dtype:
@@ -206,7 +223,8 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
  * Routing, dispatch, expert GEMMs (gate/up with the SwiGLU epilogue, then down), shared expert and
  * combine, all enqueued on `stream` with no host synchronisation. x [T, H] is io_dtype, out [T, H]
  * is out_dtype. logits [T,E], topk_ids [T,k], topk_w [T,k] are optional outputs (NULL: kept in the
- * workspace). out is this GPU's partial sum over its local experts plus the shared expert.
+ * workspace). out is this GPU's partial sum over its local experts plus the shared expert (times
+ * its gate g_t when w->w_shared_gate is given).
  * Intermediate formats: h (the down projection's input) is in the expert format (bf16 for bf16
  * experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for
  * fp8/MXFP4/MXFP8.

@@ -45,6 +45,7 @@ class Workload:
     fmt: int          # expert path format
     zipf_s: float     # Zipf exponent of the per-expert router bias (0 = no bias)
     seed: int = 0
+    gated: int = 0    # 1: the shared expert is scaled by a per-token logistic gate
 
     @property
     def desc(self):
@@ -65,6 +66,11 @@ WORKLOADS = {
     # Qwen3.5-397B-shaped, EP=8 slice (64 of 512), top-10, shared expert, bf16
     "C3a": Workload("C3a", 1024, 4096, 512, 0, 64, 1024, 10, 1024, SOFTMAX, 1, FMT_BF16, FMT_BF16, 0.0),
     "C3b": Workload("C3b", 8192, 4096, 512, 0, 64, 1024, 10, 1024, SOFTMAX, 1, FMT_BF16, FMT_BF16, 0.0),
+    # the same slices with the shared expert behind its per-token logistic gate
+    "C3a_g": Workload("C3a_g", 1024, 4096, 512, 0, 64, 1024, 10, 1024, SOFTMAX, 1, FMT_BF16, FMT_BF16,
+                      0.0, gated=1),
+    "C3b_g": Workload("C3b_g", 8192, 4096, 512, 0, 64, 1024, 10, 1024, SOFTMAX, 1, FMT_BF16, FMT_BF16,
+                      0.0, gated=1),
     # DeepSeek-V3-shaped slice (32 of 256), fp8 e4m3 with 128x128 fp32 block scales, sigmoid
     "C4p": Workload("C4p", 4096, 7168, 256, 0, 32, 2048, 8, 2048, SIGMOID, 1, FMT_BF16, FMT_FP8, 0.0),
     "C4d": Workload("C4d", 256, 7168, 256, 0, 32, 2048, 8, 2048, SIGMOID, 1, FMT_BF16, FMT_FP8, 0.0),

@@ -47,7 +47,7 @@ class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_router", "w_gate", "w_gate_scales", "w_up", "w_up_scales", "w_down",
                  "w_down_scales", "sh_gate", "sh_gate_scales", "sh_up", "sh_up_scales",
-                 "sh_down", "sh_down_scales")]
+                 "sh_down", "sh_down_scales", "w_shared_gate")]
 
 
 _P = ctypes.c_void_p
@@ -63,14 +63,15 @@ _lib.moe_permute_workspace_bytes.argtypes = [_D]
 _lib.moe_permute_workspace_bytes.restype = ctypes.c_size_t
 _lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(moe_gemm_desc), _P, _P, _P, _P, _P, _P, _P, _P,
                                   _P, _P, _P]
-_lib.moe_combine.argtypes = [_D, ctypes.c_int32, _P, _P, _P, _P, _P, _P]
+_lib.moe_combine.argtypes = [_D, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]
+_lib.moe_shared_gate.argtypes = [_D, _P, _P, _P, _P]
 _lib.moe_quantize.argtypes = [ctypes.c_int32] * 6 + [_P, _P, _P, _P]
 _lib.moe_layer.argtypes = [_D, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P, _P, _P,
                            ctypes.c_size_t, _P]
 _lib.moe_layer_workspace_bytes.argtypes = [_D]
 _lib.moe_layer_workspace_bytes.restype = ctypes.c_size_t
-for _f in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_quantize",
-           "moe_layer"):
+for _f in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_shared_gate",
+           "moe_quantize", "moe_layer"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -133,9 +134,15 @@ def moe_grouped_gemm(g, A, A_scales, a_rows, B, B_scales, B2, B2_scales, group_o
                                  _ptr(C), _ptr(C_scales), _stream(stream)), "moe_grouped_gemm")
 
 
-def moe_combine(d, y_dtype, y, topk_w, slot_to_row, shared, out, stream=None):
+def moe_combine(d, y_dtype, y, topk_w, slot_to_row, shared, out, stream=None, shared_w=None):
     _check(_lib.moe_combine(ctypes.byref(d), y_dtype, _ptr(y), _ptr(topk_w), _ptr(slot_to_row),
-                            _ptr(shared), _ptr(out), _stream(stream)), "moe_combine")
+                            _ptr(shared), _ptr(shared_w), _ptr(out), _stream(stream)),
+           "moe_combine")
+
+
+def moe_shared_gate(d, x, w_shared_gate, shared_w, stream=None):
+    _check(_lib.moe_shared_gate(ctypes.byref(d), _ptr(x), _ptr(w_shared_gate), _ptr(shared_w),
+                                _stream(stream)), "moe_shared_gate")
 
 
 def moe_quantize(dst_dtype, src_dtype, batch, rows, cols, block_rows, src, codes, scales,
@@ -145,13 +152,13 @@ def moe_quantize(dst_dtype, src_dtype, batch, rows, cols, block_rows, src, codes
 
 
 def make_weights(w_router, w_gate, w_up, w_down, scales=(None, None, None), shared=None,
-                 shared_scales=(None, None, None)):
+                 shared_scales=(None, None, None), shared_gate=None):
     sh = shared if shared is not None else (None, None, None)
-    keep = [w_router, w_gate, w_up, w_down, *scales, *sh, *shared_scales]
+    keep = [w_router, w_gate, w_up, w_down, *scales, *sh, *shared_scales, shared_gate]
     w = moe_weights(*(_p.value if _p is not None else None for _p in (
         _ptr(w_router), _ptr(w_gate), _ptr(scales[0]), _ptr(w_up), _ptr(scales[1]), _ptr(w_down),
         _ptr(scales[2]), _ptr(sh[0]), _ptr(shared_scales[0]), _ptr(sh[1]),
-        _ptr(shared_scales[1]), _ptr(sh[2]), _ptr(shared_scales[2]))))
+        _ptr(shared_scales[1]), _ptr(sh[2]), _ptr(shared_scales[2]), _ptr(shared_gate))))
     w._keep = keep          # keep the tensors alive as long as the struct
     return w
 

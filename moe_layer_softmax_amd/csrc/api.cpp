@@ -122,7 +122,7 @@ size_t route_ws(const moe_desc* d) { return router_fast(d) ? router_ws_bytes(d->
 
 // ---- layer workspace layout (identical in the size query and in moe_layer) ----------------------
 struct LayerWs {
-  size_t logits, ids, w, rpart, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, y, total;
+  size_t logits, ids, w, rpart, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, y, sw, total;
 };
 
 LayerWs layer_ws(const moe_desc* d) {
@@ -156,6 +156,7 @@ LayerWs layer_ws(const moe_desc* d) {
     L.h = take(rows * I * io_bytes(d->io_dtype));
   }
   L.y = take(rows * H * io_bytes(y_dtype_of(d)));
+  L.sw = take(d->I_s ? T * 4 : 0);
   L.total = o;
   return L;
 }
@@ -341,16 +342,28 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
 }
 
 moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const float* topk_w,
-                       const int32_t* slot_to_row, const void* shared, void* out,
-                       hipStream_t stream) {
+                       const int32_t* slot_to_row, const void* shared, const float* shared_w,
+                       void* out, hipStream_t stream) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
   if (!valid_io(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (shared_w && !shared) return MOE_ERR_INVALID_ARG;
   if (d->T == 0) return MOE_OK;
-  if (!ok_ptr(y) || !ok_ptr(topk_w) || !ok_ptr(slot_to_row) || !ok_ptr(out) || !ok_opt(shared))
+  if (!ok_ptr(y) || !ok_ptr(topk_w) || !ok_ptr(slot_to_row) || !ok_ptr(out) || !ok_opt(shared) ||
+      !ok_opt(shared_w))
     return MOE_ERR_INVALID_ARG;
   return hip_status(launch_combine(d->T, d->H, d->k, y_dtype, d->out_dtype, y, topk_w, slot_to_row,
-                                   shared, out, stream));
+                                   shared, shared_w, out, stream));
+}
+
+moe_status moe_shared_gate(const moe_desc* d, const void* x, const void* w_shared_gate,
+                           float* shared_w, hipStream_t stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return MOE_OK;
+  if (!ok_ptr(x) || !ok_ptr(w_shared_gate) || !ok_ptr(shared_w)) return MOE_ERR_INVALID_ARG;
+  return hip_status(launch_shared_gate(d->T, d->H, d->io_dtype, x, w_shared_gate, shared_w,
+                                       stream));
 }
 
 moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int32_t rows,
@@ -404,7 +417,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   if (quant && (!ok_ptr(w->w_gate_scales) || !ok_ptr(w->w_up_scales) ||
                 !ok_ptr(w->w_down_scales)))
     return MOE_ERR_INVALID_ARG;
-  if (d->I_s && (!ok_ptr(w->sh_gate) || !ok_ptr(w->sh_up) || !ok_ptr(w->sh_down)))
+  if (d->I_s && (!ok_ptr(w->sh_gate) || !ok_ptr(w->sh_up) || !ok_ptr(w->sh_down) ||
+                 !ok_opt(w->w_shared_gate)))
     return MOE_ERR_INVALID_ARG;
   if (d->I_s && quant && (!ok_ptr(w->sh_gate_scales) || !ok_ptr(w->sh_up_scales) ||
                           !ok_ptr(w->sh_down_scales)))
@@ -531,10 +545,16 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   st = hip_status(launch_gemm(b, stream));
   if (st != MOE_OK) return st;
 
-  // 6. combine (+ shared expert rows)
+  // 6. combine (+ shared expert rows, times their per-token gate when the layer has one)
   const void* shared = d->I_s ? base + L.y + (size_t)slots * H * io_bytes(ydt) : nullptr;
-  return hip_status(launch_combine(T, H, k, ydt, d->out_dtype, base + L.y, tw, s2r, shared, out,
-                                   stream));
+  float* sw = nullptr;
+  if (d->I_s && w->w_shared_gate) {
+    sw = reinterpret_cast<float*>(base + L.sw);
+    st = hip_status(launch_shared_gate(T, H, io, x, w->w_shared_gate, sw, stream));
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_combine(T, H, k, ydt, d->out_dtype, base + L.y, tw, s2r, shared, sw,
+                                   out, stream));
 }
 
 }  // extern "C"

@@ -4,7 +4,8 @@
 // weighted accumulation in registers that reads the routing information and the positions the
 // dispatch computed, writing the final tokens to the output buffer. Here a token's k rows (found
 // through slot_to_row) are read with 16-byte (fp32) or 8-byte (bf16) loads per lane, accumulated in
-// fp32 in slot order j = 0..k-1, the shared expert row added last, and the sum rounded once.
+// fp32 in slot order j = 0..k-1, the shared expert row added last (times its per-token gate when
+// one is given), and the sum rounded once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,6 +20,7 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot_to_row,
                                                       const void* __restrict__ shared,
+                                                      const float* __restrict__ shared_w,
                                                       void* __restrict__ out) {
   constexpr int KMAX = 16;
   constexpr int CPL = Y_BF16 ? 8 : 4;
@@ -66,8 +68,9 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
     }
   }
   if (shared) {
+    const float gs = shared_w ? shared_w[t] : 1.0f;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) acc[i] += sh[i];
+    for (int i = 0; i < CPL; ++i) acc[i] += gs * sh[i];
   }
   if (OUT_BF16) {
     uint32_t o[CPL / 2];
@@ -86,15 +89,16 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
 
 hipError_t launch_combine(int T, int H, int k, int y_dtype, int out_dtype, const void* y,
                           const float* w, const int32_t* slot_to_row, const void* shared,
-                          void* out, hipStream_t s) {
+                          const float* shared_w, void* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const bool yb = y_dtype == MOE_BF16, ob = out_dtype == MOE_BF16;
   const int cols_per_wg = 256 * (yb ? 8 : 4);
   dim3 grid(T, (H + cols_per_wg - 1) / cols_per_wg), block(256);
-  if (yb && ob) combine_kernel<true, true><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);
-  else if (yb) combine_kernel<true, false><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);
-  else if (ob) combine_kernel<false, true><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);
-  else combine_kernel<false, false><<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, out);
+  auto k_ = combine_kernel<false, false>;
+  if (yb && ob) k_ = combine_kernel<true, true>;
+  else if (yb) k_ = combine_kernel<true, false>;
+  else if (ob) k_ = combine_kernel<false, true>;
+  k_<<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, shared_w, out);
   return hipGetLastError();
 }
 

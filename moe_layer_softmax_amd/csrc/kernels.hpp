@@ -72,8 +72,11 @@ hipError_t launch_gather_rows(long long max_rows, int k, const int32_t* offsets_
                               int scale_rows_per_block, void* dst_scales, hipStream_t s);
 
 hipError_t launch_combine(int T, int H, int k, int y_dtype, int out_dtype, const void* y, const float* w,
-                          const int32_t* slot_to_row, const void* shared, void* out,
-                          hipStream_t s);
+                          const int32_t* slot_to_row, const void* shared, const float* shared_w,
+                          void* out, hipStream_t s);
+// g[t] = 1 / (1 + exp(-(x_t . w_sg))), fp32 accumulation; x [T, H], w_sg [H] in io_dtype; H % 8 == 0.
+hipError_t launch_shared_gate(int T, int H, int io_dtype, const void* x, const void* w_sg, float* g,
+                              hipStream_t s);
 
 hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int block_rows,
                             const void* src, uint8_t* codes, float* scales, hipStream_t s);

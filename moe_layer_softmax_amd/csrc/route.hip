@@ -287,4 +287,48 @@ hipError_t launch_router(int T, int H, int E, const void* x, const void* w_route
   return hipGetLastError();
 }
 
+// Gate of the shared expert ("Hosting Qwen on Blackwell", introduction: the layer adapts to the
+// newer models' additional gate terms; read as g_t = 1 / (1 + exp(-(x_t . w_sg))) on the
+// unquantised token). One wave per token, four tokens per workgroup: each lane loads 16 bytes of
+// x_t and of w_sg per step (8 bf16 or 4 fp32 columns), accumulates in fp32, and the wave sums
+// the lanes. x and w_sg are read once; H % 8 == 0.
+template <bool BF16>
+__global__ void __launch_bounds__(256) shared_gate_kernel(int T, int H, const void* __restrict__ x,
+                                                          const void* __restrict__ wsg,
+                                                          float* __restrict__ g) {
+  constexpr int CPL = BF16 ? 8 : 4;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;                                   // whole waves leave together
+  float acc = 0.0f;
+  for (int c = lane * CPL; c < H; c += 64 * CPL) {
+    if (BF16) {
+      const i32x4 a = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(x) + (size_t)t * H + c);
+      const i32x4 b = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(wsg) + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t ua = static_cast<uint32_t>(a[q]), ub = static_cast<uint32_t>(b[q]);
+        acc = fmaf(__uint_as_float(ua << 16), __uint_as_float(ub << 16), acc);
+        acc = fmaf(__uint_as_float(ua & 0xFFFF0000u), __uint_as_float(ub & 0xFFFF0000u), acc);
+      }
+    } else {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + (size_t)t * H + c);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(static_cast<const float*>(wsg) + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = fmaf(a[q], b[q], acc);
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) g[t] = 1.0f / (1.0f + expf(-acc));
+}
+
+hipError_t launch_shared_gate(int T, int H, int io_dtype, const void* x, const void* w_sg, float* g,
+                              hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4), block(256);
+  if (io_dtype == MOE_BF16) shared_gate_kernel<true><<<grid, block, 0, s>>>(T, H, x, w_sg, g);
+  else shared_gate_kernel<false><<<grid, block, 0, s>>>(T, H, x, w_sg, g);
+  return hipGetLastError();
+}
+
 }  // namespace moe

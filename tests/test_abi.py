@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(LIB)
     names = _declared()
     assert {"moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_layer",
-            "moe_quantize"} <= set(names)
+            "moe_quantize", "moe_shared_gate"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -96,8 +96,13 @@ def test_null_and_misaligned_pointers_are_rejected():
     assert lib.moe_route(ctypes.byref(d), ok, ok, None, None, ok, ok, None, 0, None) == m.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(d), bad, ok, None, ok, ok, ok, None, 0, None) == m.MOE_ERR_INVALID_ARG
     assert lib.moe_route(ctypes.byref(d), ok, ok, None, ok, ok, ok, bad, 64, None) == m.MOE_ERR_INVALID_ARG
-    assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, ok, ok, ok, None, bad, None) == m.MOE_ERR_INVALID_ARG
-    assert lib.moe_combine(ctypes.byref(d), 9, ok, ok, ok, None, ok, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, ok, ok, ok, None, None, bad, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(d), 9, ok, ok, ok, None, None, ok, None) == m.MOE_ERR_INVALID_ARG
+    # a gate for shared rows that are not there
+    assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, ok, ok, ok, None, ok, ok, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, ok, ok, ok, ok, bad, ok, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_shared_gate(ctypes.byref(d), ok, None, ok, None) == m.MOE_ERR_INVALID_ARG
+    assert lib.moe_shared_gate(ctypes.byref(d), ok, ok, bad, None) == m.MOE_ERR_INVALID_ARG
     g = m.moe_gemm_desc(2, 64, 256, 128, m.MOE_BF16, m.MOE_EPI_SWIGLU, m.MOE_BF16, 1, 1)
     # SWIGLU needs B2
     assert lib.moe_grouped_gemm(ctypes.byref(g), ok, None, None, ok, None, None, None, ok, ok,
@@ -114,7 +119,7 @@ def test_workspace_too_small_and_unsupported():
     d = _desc(T=4096, k=8, E=64, E_loc=16)                 # 32768 slots: needs the scan workspace
     st = lib.moe_permute(ctypes.byref(d), ok, None, None, ok, ok, ok, ok, None, None, ok, 16, None)
     assert st == m.MOE_ERR_WORKSPACE
-    w = m.moe_weights(*([4096] * 13))
+    w = m.moe_weights(*([4096] * 14))
     d2 = _desc()
     st = lib.moe_layer(ctypes.byref(d2), ctypes.byref(w), ok, None, ok, None, None, None, ok, 10,
                        None)
@@ -133,8 +138,9 @@ def test_zero_tokens_is_a_no_op():
     import moe_layer_softmax_amd as m
     lib = m.lib()
     d = _desc(T=0)
-    w = m.moe_weights(*([4096] * 13))
+    w = m.moe_weights(*([4096] * 14))
     assert lib.moe_route(ctypes.byref(d), None, None, None, None, None, None, None, 0, None) == m.MOE_OK
-    assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, None, None, None, None, None, None) == m.MOE_OK
+    assert lib.moe_combine(ctypes.byref(d), m.MOE_F32, None, None, None, None, None, None, None) == m.MOE_OK
+    assert lib.moe_shared_gate(ctypes.byref(d), None, None, None, None) == m.MOE_OK
     assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), None, None, None, None, None, None,
                          None, 0, None) == m.MOE_OK

@@ -29,7 +29,7 @@ def make_inputs(wl, bias_override=None):
     return x, wr, bias, (g, u, d), sh
 
 
-def gpu_layer(wl, x, wr, bias, experts, sh):
+def gpu_layer(wl, x, wr, bias, experts, sh, sgate=None):
     dt = io_torch(wl.io_fmt)
     desc = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
                          wl.renormalize, _FMT[wl.io_fmt], _FMT[wl.fmt])
@@ -42,11 +42,13 @@ def gpu_layer(wl, x, wr, bias, experts, sh):
                                    scales=tuple(s for _, s in eq),
                                    shared=None if shq is None else tuple(c for c, _ in shq),
                                    shared_scales=(None, None, None) if shq is None
-                                   else tuple(s for _, s in shq))
+                                   else tuple(s for _, s in shq),
+                                   shared_gate=None if sgate is None else to_dev(sgate, dt))
     else:
         ew = [to_dev(a, dt) for a in experts]
         shw = None if sh is None else [to_dev(a, dt) for a in sh]
-        weights = moe.make_weights(to_dev(wr, dt), *ew, shared=shw)
+        weights = moe.make_weights(to_dev(wr, dt), *ew, shared=shw,
+                                   shared_gate=None if sgate is None else to_dev(sgate, dt))
     out = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
     logits = torch.empty((wl.T, wl.E), dtype=torch.float32, device="cuda")
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
@@ -60,7 +62,7 @@ def gpu_layer(wl, x, wr, bias, experts, sh):
             (desc, weights, xb, bt, out, logits, ids, w, ws))
 
 
-def oracle_layer(wl, x, wr, bias, experts, sh, tok):
+def oracle_layer(wl, x, wr, bias, experts, sh, tok, sgate=None):
     # h enters the down projection in the expert format (bf16 / fp8 1x128 / MXFP4)
     act = {mi.FMT_F32: oracle.F32, mi.FMT_BF16: oracle.BF16, mi.FMT_FP8: oracle.FP8,
            mi.FMT_MX4: oracle.MX4, mi.FMT_MX8: oracle.MX8}[wl.fmt]
@@ -77,14 +79,16 @@ def oracle_layer(wl, x, wr, bias, experts, sh, tok):
         xa = M(oracle.F32, x)
         mats = [M(oracle.F32, a) for a in experts]
         shared = None if sh is None else tuple(M(oracle.F32, a) for a in sh)
-    return oracle.moe_layer(desc, x, wr, bias, xa, *mats, shared, tok)
+    return oracle.moe_layer(desc, x, wr, bias, xa, *mats, shared, tok, shared_gate=sgate)
 
 
-def check_layer(wl, n_sample=None, bias_override=None, seed=0):
+def check_layer(wl, n_sample=None, bias_override=None, seed=0, gated=None):
+    gated = bool(wl.gated) if gated is None else gated
     print(f"[layer] {wl.name} T={wl.T} H={wl.H} E={wl.E} E_loc={wl.E_loc} I={wl.I} k={wl.k} "
-          f"I_s={wl.I_s}", flush=True)
+          f"I_s={wl.I_s} gated={gated}", flush=True)
     x, wr, bias, experts, sh = make_inputs(wl, bias_override)
-    out, lg, ids, w, _ = gpu_layer(wl, x, wr, bias, experts, sh)
+    sgate = gen.shared_gate_vector(wl) if gated else None
+    out, lg, ids, w, _ = gpu_layer(wl, x, wr, bias, experts, sh, sgate)
     T = wl.T
     if n_sample is None or n_sample >= T:
         tok = np.arange(T, dtype=np.int32)
@@ -92,7 +96,7 @@ def check_layer(wl, n_sample=None, bias_override=None, seed=0):
         rng = np.random.default_rng([seed, T])
         tok = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample, replace=False)]))
         tok = tok.astype(np.int32)
-    ref = oracle_layer(wl, x, wr, bias, experts, sh, tok)
+    ref = oracle_layer(wl, x, wr, bias, experts, sh, tok, sgate)
     # logits inside the fp32 accumulation bound
     L64, absdot = oracle.logits(x, wr, bias, tok=tok)
     bound = gamma(wl.H + 1) * absdot
@@ -119,6 +123,14 @@ def check_layer(wl, n_sample=None, bias_override=None, seed=0):
                                            ("C2p_mx8", 48)])
 def test_layer_workloads(name, n_sample):
     check_layer(mi.WORKLOADS[name], n_sample)
+
+
+# the shared expert scaled by its per-token logistic gate: bf16 (Qwen3.5-397B slice), fp8 and MXFP4
+# (DeepSeek-V3 slice), at a prefill and a decode size
+@pytest.mark.parametrize("name,n_sample", [("C3a_g", 96), ("C3b_g", 48), ("C4p", 48),
+                                           ("C5d", None)])
+def test_layer_gated_shared_expert(name, n_sample):
+    check_layer(mi.WORKLOADS[name], n_sample, gated=True)
 
 
 def _small(**kw):

@@ -395,11 +395,13 @@ def test_one_token_per_expert_decode(E_loc):
 # combine
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("T,k,H,shared,io,out_bf16", [(64, 2, 256, False, "f32", False),
-                                                      (300, 8, 4096, False, "bf16", False),
-                                                      (77, 10, 1024, True, "bf16", True),
-                                                      (5, 16, 7168, True, "f32", True)])
-def test_combine(T, k, H, shared, io, out_bf16):
+@pytest.mark.parametrize("T,k,H,shared,io,out_bf16,gated", [(64, 2, 256, False, "f32", False, False),
+                                                            (300, 8, 4096, False, "bf16", False, False),
+                                                            (77, 10, 1024, True, "bf16", True, False),
+                                                            (5, 16, 7168, True, "f32", True, False),
+                                                            (77, 10, 1024, True, "bf16", False, True),
+                                                            (33, 8, 7168, True, "f32", True, True)])
+def test_combine(T, k, H, shared, io, out_bf16, gated):
     rng = np.random.default_rng(T * k)
     R = T * k
     rnd = (lambda a: a) if io == "f32" else gen.bf16_round
@@ -410,14 +412,16 @@ def test_combine(T, k, H, shared, io, out_bf16):
     s2r[rng.random((T, k)) < 0.3] = -1
     s2r[0, :] = -1                                        # a token with no local expert
     sh = rnd(rng.standard_normal((T, H)).astype(np.float32)) if shared else None
+    sw = rng.random(T).astype(np.float32) if gated else None
     ydt = moe.MOE_F32 if io == "f32" else moe.MOE_BF16
     d = moe.make_desc(T, H, 64, 0, 8, 64, k, 0, 0, 1, ydt, ydt,
                       out_dtype=moe.MOE_BF16 if out_bf16 else moe.MOE_F32)
     out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
     moe.moe_combine(d, ydt, to_dev(y, tdt), to_dev(w, torch.float32), to_dev(s2r, torch.int32),
-                    None if sh is None else to_dev(sh, tdt), out)
+                    None if sh is None else to_dev(sh, tdt), out,
+                    shared_w=None if sw is None else to_dev(sw, torch.float32))
     _sync()
-    ref = oracle.combine(y, w, s2r, sh)
+    ref = oracle.combine(y, w, s2r, sh, sw)
     og = out.float().cpu().numpy()
     rms = np.sqrt(np.mean(ref ** 2))
     if not out_bf16:
@@ -426,3 +430,25 @@ def test_combine(T, k, H, shared, io, out_bf16):
         assert np.all(np.abs(og - ref) <= 2 ** -8 * np.abs(ref) + 1e-5 * rms)
     if not shared:
         assert not og[0].any()
+
+
+# shared-expert gate: bf16 and fp32 tokens, hidden sizes of the workloads and a ragged one (H not a
+# multiple of the 512 columns a wave covers per step), 1 to 4099 tokens (a partial last workgroup)
+@pytest.mark.parametrize("T,H,io", [(1, 4096, "bf16"), (5, 7168, "bf16"), (4099, 4096, "bf16"),
+                                    (3, 4160, "bf16"), (130, 272, "f32"), (7, 7168, "f32")])
+def test_shared_gate(T, H, io):
+    rng = np.random.default_rng([T, H])
+    rnd = (lambda a: a) if io == "f32" else gen.bf16_round
+    tdt = torch.float32 if io == "f32" else torch.bfloat16
+    x = rnd(rng.standard_normal((T, H)).astype(np.float32))
+    wg = rnd((rng.standard_normal(H) * 0.02).astype(np.float32))
+    d = moe.make_desc(T, H, 64, 0, 8, 64, 2, 64, 0, 1, moe.MOE_F32 if io == "f32" else moe.MOE_BF16)
+    g = torch.full((T,), -1.0, dtype=torch.float32, device="cuda")
+    moe.moe_shared_gate(d, to_dev(x, tdt), to_dev(wg, tdt), g)
+    _sync()
+    ref = oracle.shared_gate(x, wg)
+    # fp32 accumulation of H products (bounded by gamma_H * sum |x w|), then the logistic
+    # function, whose slope is at most 1/4, plus a few ulps of the fp32 exponential and division
+    absdot = np.abs(x.astype(np.float64)) @ np.abs(wg.astype(np.float64))
+    bound = 0.25 * gamma(H) * absdot + 4e-7
+    assert np.all(np.abs(g.cpu().numpy() - ref) <= bound)
