@@ -213,11 +213,10 @@ def ep_sweep(stream, steps):
     return out
 
 
-# Source files of the grouped GEMM kernels; HBM counters taken on an older version of them are
-# not reported.
+# Source files that define the bf16 grouped GEMM kernels' device code; HBM counters taken on an
+# older version of them are not reported.
 GEMM_SOURCES = ["moe_layer_softmax_amd/csrc/gemm.hip", "moe_layer_softmax_amd/csrc/gemm_common.hpp",
-                "moe_layer_softmax_amd/csrc/common.hpp", "moe_layer_softmax_amd/csrc/kernels.hpp",
-                "moe_layer_softmax_amd/csrc/quant_dev.hpp", "include/moe.h"]
+                "moe_layer_softmax_amd/csrc/common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_traffic.json")
 
 
