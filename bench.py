@@ -42,6 +42,8 @@ def parse():
                    help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
     p.add_argument("--all-workloads", action="store_true",
                    help="add every workload's layer time and both roofline fractions")
+    p.add_argument("--workloads", default=None,
+                   help="comma-separated names: the workload table for these only")
     p.add_argument("--no-ep-sweep", action="store_true",
                    help="skip the decode MoE-GEMM sweep over local expert counts")
     return p.parse_args()
@@ -50,7 +52,7 @@ def parse():
 PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3}
 
 
-def workload_table(stream, steps):
+def workload_table(stream, steps, names=None):
     """Layer time of every workload (one moe_layer call per step, caches evicted with a 1 GiB read
     before each), with the algorithmic MFMA and HBM roofline fractions. Tokens, router weight and
     bias are the seeded inputs; expert weights are seeded device draws of the same shapes (their
@@ -63,8 +65,8 @@ def workload_table(stream, steps):
               mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8)}
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     out = {}
-    for name in ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
-                 "C2p_mx8", "C2d_mx8"):
+    for name in names or ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
+                          "C2p_mx8", "C2d_mx8"):
         wl = mi.WORKLOADS[name]
         fname, fcode = fmt_of[wl.fmt]
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
@@ -489,8 +491,9 @@ def main():
         del D, flush
     if not args.no_ep_sweep:
         result["decode_one_token_per_expert"] = ep_sweep(stream, max(5, min(args.steps, 20)))
-    if args.all_workloads:
-        result["workloads"] = workload_table(stream, max(5, min(args.steps, 20)))
+    if args.all_workloads or args.workloads:
+        names = args.workloads.split(",") if args.workloads else None
+        result["workloads"] = workload_table(stream, max(5, min(args.steps, 20)), names)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(L, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -196,8 +196,8 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   }
 
   // load q of this wave's share of K-step kt (q < A_INS: A rows, then B rows, then scales)
-  auto issue_one = [&](int kt, int q) {
-    uint8_t* la = ldsq + (kt % S) * STAGE;
+  auto issue_one = [&](int kt, int q, int stage) {
+    uint8_t* la = ldsq + stage * STAGE;
     if (q < A_INS) {
       dma_16b_asm(a_src[q] + (long long)kt * RB, la + (q * NW + wave) * 8 * RB);
     } else if (q < A_INS + B_INS) {
@@ -211,7 +211,7 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   auto issue = [&](int kt) {
     if (kt >= nk) return;
 #pragma unroll
-    for (int q = 0; q < INS; ++q) issue_one(kt, q);
+    for (int q = 0; q < INS; ++q) issue_one(kt, q, kt % S);
   };
 
   f32x4 acc[FM][FN];
@@ -253,7 +253,10 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
   constexpr int BATCHES = SUB * (FN / NB);
   constexpr int PER_BATCH = (INS + BATCHES - 1) / BATCHES;
   for (int kt = 0; kt < nk; ++kt) {
-    const bool do_load = kt + S - 1 < nk;
+    // step kt + S - 1 goes into the stage the last barrier released; past the end the last step
+    // loads itself again there, unread: no branch in the loop, so nothing can move the MFMAs out
+    // of their place between the loads
+    const int kn = kt + S - 1 < nk ? kt + S - 1 : nk - 1;
     const uint8_t* la = ldsq + (kt % S) * STAGE;
     const uint8_t* lb = la + BM * RB;
 
@@ -320,21 +323,21 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
             }
           }
         MOE_SCHED_FENCE();
-        if (do_load) {
+        {
           const int batch = s * (FN / NB) + b0 / NB;
 #pragma unroll
           for (int u = 0; u < PER_BATCH; ++u) {
             const int q = batch * PER_BATCH + u;
-            if (q < INS) issue_one(kt + S - 1, q);
+            if (q < INS) issue_one(kn, q, (kt + S - 1) % S);
           }
         }
         MOE_SCHED_FENCE();
       }
     }
-    if (kt + S - 1 < nk) wait_vmem_n<(S - 2) * INS>();   // step kt+1 landed
-    else wait_vmem();
+    wait_vmem_n<(S - 2) * INS>();          // step kt+1 landed (only step kt+2's loads remain)
     barrier_lds();
   }
+  wait_vmem();                             // the unread tail loads, before the stores
 
   // ---- epilogue ----
   char* C = static_cast<char*>(p.C);
@@ -784,6 +787,371 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Wide-tile variant for prefill-sized groups in the MX formats: 256 x 256 tiles, 4 waves in a 2 x 2
+// arrangement, each owning 128 rows x 128 B-rows as 4 x 4 fragments of 32 x 32 (256 accumulator
+// registers), on v_mfma_scale_f32_32x32x64_f8f6f4: measured on the MI355X with one wave per SIMD
+// it issues at the full fp8 and fp4 rates, while the 16 x 16 x 128 form loses ~20% there and runs
+// fp4 only at the fp8 rate. A wave reads (128 + 128) x 128 bytes of fragments per 128-byte K-step
+// (half the LDS bytes per flop of the 32-row wave tile above). The E8M0 scales go to the MFMA
+// directly, so the accumulators never leave the matrix core's registers (fp8's fp32 block scales
+// would need a vector FMA per MFMA on them; fp8 keeps the 32-row kernel).
+// Operand layout of the 32 x 32 x 64 MFMA (measured): lane l holds row l % 32; lane half
+// h = l / 32 holds, for fp8, K-elements [16h, 16h + 16) in bytes 0-15 and [32 + 16h, +16) in bytes
+// 16-31, for fp4 K-elements [32h, 32h + 32) in bytes 0-15, and passes the E8M0 scale of K-elements
+// [32h, 32h + 32). A 128-byte K-step is SUB = 2 (fp8) or 4 (fp4) substeps of 64 elements.
+// Schedule: two LDS stages of 64 KB of operands plus the step's scales. Fragments of the next
+// substep are read while the current one's MFMAs run. At the start of a step's last substep a
+// wave waits for the next step's loads and the workgroup meets at a barrier; the wave then reads
+// the next step's first fragments and issues the loads of the step after it into the stage just
+// released, both while the last substep's MFMAs run, so the loads have a whole step to land.
+// SwiGLU: wave column wn holds gate rows [64 wn, 64 wn + 64) and the up rows of the same h-columns,
+// so gate and up of one h-column meet in one lane and a 1 x 32 MX group of h is one fragment row.
+// ------------------------------------------------------------------------------------------------
+template <int FMT>
+constexpr int qw_scale_stage_bytes() {
+  return FMT == MOE_MXFP4 ? 4096 : 2048;   // E8M0 [256 A rows + 256 B rows][8 or 4 bytes]
+}
+constexpr int kQWideBM = 256, kQWideBN = 256, kQWideStages = 2;
+
+template <int FMT>
+constexpr size_t qw_lds_bytes() {
+  return (size_t)kQWideStages * ((kQWideBM + kQWideBN) * 128 + qw_scale_stage_bytes<FMT>());
+}
+
+template <int FMT, int EPI>
+__global__ void __launch_bounds__(256)
+gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
+  constexpr bool MX4 = FMT == MOE_MXFP4, MX8 = FMT == MOE_MXFP8;
+  static_assert(MX4 || MX8, "E8M0-scaled formats only");
+  constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
+  constexpr int BM = kQWideBM, BN = kQWideBN, NW = 4, FM = 4, FN = 4, S = kQWideStages;
+  constexpr int RB = 128;                  // bytes per row slice (one K-step)
+  constexpr int KE = MX4 ? 256 : 128;      // elements per K-step
+  constexpr int SUB = MX4 ? 4 : 2;         // 64-element MFMA substeps per K-step
+  constexpr int A_INS = BM / (8 * NW), B_INS = BN / (8 * NW);
+  constexpr int SINS = MX4 ? 4 : 2;        // 4-byte scale loads per wave per K-step
+  constexpr int INS = A_INS + B_INS + SINS;
+  constexpr int DATA = (BM + BN) * RB;
+  constexpr int STAGE = DATA + qw_scale_stage_bytes<FMT>();
+  constexpr int SRB = MX4 ? 8 : 4;         // E8M0 bytes per row and K-step
+  constexpr int FMT_CODE = MX4 ? 4 : 0;
+  using Geo = SliceGeo<64>;
+  using SW = typename std::conditional<MX4, u32x2, uint32_t>::type;   // a row's scales of a step
+  static_assert(INS < 64, "vmcnt range");
+  static_assert(SUB % 2 == 0, "fragment sets alternate by substep parity");
+
+  extern __shared__ __attribute__((aligned(1024))) uint8_t ldsw[];
+
+  const int logical = xcd_remap(blockIdx.x, span);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int K = p.K;
+  const int nk = K / KE;
+  const long long b_row_bytes = MX4 ? K / 2 : K;
+  const int lrow = lane >> 3;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  // B row (and matrices) behind tile B-row rb: SWIGLU rows [0, 128) gate, [128, 256) up
+  auto b_row = [&](int rb, const char*& base, const char*& sbase) -> long long {
+    long long n;
+    base = t.B;
+    sbase = t.Bs;
+    if (SWIGLU) {
+      n = (long long)t.nt * (BN / 2) + (rb % (BN / 2));
+      if (rb >= BN / 2) { base = t.B2; sbase = t.B2s; }
+    } else {
+      n = (long long)t.nt * BN + rb;
+    }
+    return n < p.N ? n : p.N - 1;
+  };
+  // first tile B-row of this wave's fragment j
+  auto frag_brow = [&](int j) -> int {
+    if (SWIGLU) return j < FN / 2 ? wn * 64 + j * 32 : BN / 2 + wn * 64 + (j - FN / 2) * 32;
+    return wn * 128 + j * 32;
+  };
+
+  // ---- DMA sources: 8 A and 8 B instructions of 8 rows x 128 bytes per wave ----
+  const char* a_src[A_INS];
+#pragma unroll
+  for (int j = 0; j < A_INS; ++j) {
+    const int r = (j * NW + wave) * 8 + lrow;
+    a_src[j] = static_cast<const char*>(p.A) + a_src_row(p, t, t.row0 + r) * p.a_pitch +
+               ((lane & 7) ^ Geo::swz(r)) * 16;
+  }
+  const char* b_src[B_INS];
+#pragma unroll
+  for (int j = 0; j < B_INS; ++j) {
+    const int rb = (j * NW + wave) * 8 + lrow;
+    const char *base, *sb;
+    const long long n = b_row(rb, base, sb);
+    b_src[j] = base + n * b_row_bytes + ((lane & 7) ^ Geo::swz(rb)) * 16;
+  }
+  // ---- scale sources (4-byte direct-to-LDS loads) ----
+  // MXFP8: one lane per row, 64 rows per load: load c of wave w is slot u = 2w + c: A rows
+  //        [64u, 64u + 64) for u < 4, B rows [64 (u - 4), +64) for u >= 4.
+  // MXFP4: two lanes per row (8 bytes per K-step), 32 rows per load: slot u = 4w + c: A rows for
+  //        u < 8, B rows for u >= 8.
+  const char* s_src[SINS];
+  int s_dst[SINS];
+  {
+    const int gpr = K / 32;                // scale bytes per row
+    constexpr int RPL = MX4 ? 32 : 64;     // rows per load
+    constexpr int ASLOTS = BM / RPL;
+#pragma unroll
+    for (int c = 0; c < SINS; ++c) {
+      const int u = wave * SINS + c;
+      const int part = MX4 ? (lane & 1) * 4 : 0;
+      const int rr = MX4 ? (lane >> 1) : lane;
+      if (u < ASLOTS) {
+        const int r = u * RPL + rr;
+        s_src[c] = static_cast<const char*>(p.A_scales) + a_src_row(p, t, t.row0 + r) * gpr + part;
+        s_dst[c] = DATA + u * 256;
+      } else {
+        const int rb = (u - ASLOTS) * RPL + rr;
+        const char *base, *sbase;
+        const long long n = b_row(rb, base, sbase);
+        s_src[c] = sbase + n * gpr + part;
+        s_dst[c] = DATA + BM * SRB + (u - ASLOTS) * 256;
+      }
+    }
+  }
+
+  // load qi of this wave's share of K-step kt into LDS stage `stage`
+  auto issue_one = [&](int kt, int qi, int stage) {
+    uint8_t* la = ldsw + stage * STAGE;
+    if (qi < A_INS) {
+      dma_16b_asm(a_src[qi] + (long long)kt * RB, la + (qi * NW + wave) * 8 * RB);
+    } else if (qi < A_INS + B_INS) {
+      const int j = qi - A_INS;
+      dma_16b_asm(b_src[j] + (long long)kt * RB, la + BM * RB + (j * NW + wave) * 8 * RB);
+    } else {
+      const int j = qi - A_INS - B_INS;
+      dma_4b_asm(s_src[j] + (long long)kt * SRB, la + s_dst[j]);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+  // fragment (32 rows from tile row r0) of substep sub of the step in stage base
+  auto read_frag = [&](const uint8_t* base, int r0, int sub) -> i32x8 {
+    const int r = r0 + l32;
+    if constexpr (MX4) {
+      const int c = sub * 2 + h;                     // 16 bytes = 32 fp4
+      const i32x4 v = *reinterpret_cast<const i32x4*>(base + r * RB + ((c ^ Geo::swz(r)) * 16));
+      return i32x8{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+    } else {
+      const int c0 = sub * 4 + h, c1 = sub * 4 + 2 + h;
+      const i32x4 v0 = *reinterpret_cast<const i32x4*>(base + r * RB + ((c0 ^ Geo::swz(r)) * 16));
+      const i32x4 v1 = *reinterpret_cast<const i32x4*>(base + r * RB + ((c1 ^ Geo::swz(r)) * 16));
+      return i32x8{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+  };
+  // fragment sets alternate by substep parity; scale words (a row's E8M0 bytes of a step) are
+  // [current step, next step]
+  i32x8 fa[2][FM], fb[2][FN];
+  SW sa[2][FM], sb[2][FN];
+  auto stage_ptr = [&](int kt) -> const uint8_t* { return ldsw + (kt % S) * STAGE; };
+  auto read_scales = [&](const uint8_t* la, int sset) {
+    const uint8_t* ls = la + DATA;
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj)
+      sb[sset][jj] = *reinterpret_cast<const SW*>(ls + BM * SRB + (frag_brow(jj) + l32) * SRB);
+#pragma unroll
+    for (int ii = 0; ii < FM; ++ii)
+      sa[sset][ii] = *reinterpret_cast<const SW*>(ls + (wm * 128 + ii * 32 + l32) * SRB);
+  };
+  auto scale_byte = [&](const SW& w, int sub) -> int {   // byte 2 sub + h of the step's scales
+    if constexpr (MX4) return static_cast<int>((w[sub >> 1] >> (16 * (sub & 1) + 8 * h)) & 0xFFu);
+    else return static_cast<int>((w >> (16 * sub + 8 * h)) & 0xFFu);
+  };
+
+  // prologue: steps 0 and 1 in flight, wait for step 0, read its first fragments
+#pragma unroll
+  for (int qi = 0; qi < INS; ++qi) issue_one(0, qi, 0);
+#pragma unroll
+  for (int qi = 0; qi < INS; ++qi) issue_one(nk > 1 ? 1 : 0, qi, 1);
+  wait_vmem_n<INS>();
+  barrier_lds();
+  read_scales(stage_ptr(0), 0);
+#pragma unroll
+  for (int ii = 0; ii < FM; ++ii) fa[0][ii] = read_frag(stage_ptr(0), wm * 128 + ii * 32, 0);
+#pragma unroll
+  for (int jj = 0; jj < FN; ++jj) fb[0][jj] = read_frag(stage_ptr(0) + BM * RB, frag_brow(jj), 0);
+
+  // Each substep runs its 16 MFMAs in four rows (A fragment i against the four B fragments). The
+  // fragments of the next substep are read one row at a time, each read placed between two
+  // MFMAs: a burst of reads would hold up the in-order issue of the MFMAs behind it while the
+  // LDS queue drains. In the last substep the loads of step kt + 2 go out after each row.
+  constexpr int DS_PER_ROW = MX4 ? 2 : 4;  // ds_read_b128 of one A and one B fragment
+  constexpr int PER_BATCH = (INS + FM - 1) / FM;
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int sub = 0; sub < SUB; ++sub) {
+      const int cur = sub & 1;
+      const bool last = sub == SUB - 1;
+      if (last) {
+        // step kt + 1 landed and every wave is done with stage kt % S: the next step's first
+        // fragments come from stage (kt + 1) % S, and step kt + 2 goes into stage kt % S (past the
+        // end: the last step again, unread, which keeps the loop free of branches)
+        wait_vmem();
+        wait_lgkm();
+        barrier_lds();
+      }
+      const int rk = last ? (kt + 1 < nk ? kt + 1 : kt) : kt;   // step and substep read next
+      const int rs = last ? 0 : sub + 1;
+      const uint8_t* la = stage_ptr(rk);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (last && i == 0) read_scales(la, 1);
+        fa[cur ^ 1][i] = read_frag(la, wm * 128 + i * 32, rs);
+        fb[cur ^ 1][i] = read_frag(la + BM * RB, frag_brow(i), rs);
+#pragma unroll
+        for (int jj = 0; jj < FN; ++jj) {
+          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              fa[cur][i], fb[cur][jj], acc[i][jj], FMT_CODE, FMT_CODE, 0, scale_byte(sa[0][i], sub), 0,
+              scale_byte(sb[0][jj], sub));
+        }
+        if (last && i == 0) MOE_SCHED_GROUP(0x100, 2 * FN);   // the scale reads first
+#pragma unroll
+        for (int m = 0; m < FN; ++m) {
+          MOE_SCHED_GROUP(0x008, 1);                          // one MFMA
+          if (m < DS_PER_ROW) MOE_SCHED_GROUP(0x100, 1);      // one fragment read
+        }
+        MOE_SCHED_FENCE();
+        if (last) {
+          const int kn = kt + 2 < nk ? kt + 2 : nk - 1;
+#pragma unroll
+          for (int u = 0; u < PER_BATCH; ++u) {
+            const int qi = i * PER_BATCH + u;
+            if (qi < INS) issue_one(kn, qi, kt % S);
+          }
+          MOE_SCHED_FENCE();
+        }
+      }
+    }
+    // the next step's scale words become the current ones
+#pragma unroll
+    for (int i = 0; i < FM; ++i) sa[0][i] = sa[1][i];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) sb[0][j] = sb[1][j];
+  }
+  wait_vmem();                             // the unread tail loads, before the stores
+  wait_lgkm();
+
+  // ---- epilogue ----
+  // A lane holds column l32 of rows 8 g + 4 h + v (g, v = 0..3) of fragment (i, j), entry 4 g + v.
+  // A 4 x 4 transpose inside each quad of lanes (two DPP exchanges) gives quad lane qq row
+  // 8 g + 4 h + rt and 4 adjacent columns, so every store writes 4 values (16 bytes fp32, 8 bf16,
+  // 4 MXFP8 codes, 2 MXFP4 bytes).
+  char* C = static_cast<char*>(p.C);
+  const int rbase = t.row0 + wm * 128;
+  const int qq = lane & 3;
+  const bool odd = qq & 1, hi = qq & 2;
+  const int rt = (qq & 1) * 2 + (qq >> 1);
+  auto dpp = [](float x, auto ctrl) -> float {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                      0xF, 0xF, false));
+  };
+  using swap1 = std::integral_constant<int, 0xB1>;     // quad_perm [1, 0, 3, 2]: lane ^ 1
+  using swap2 = std::integral_constant<int, 0x4E>;     // quad_perm [2, 3, 0, 1]: lane ^ 2
+  auto quad_t = [&](const float (&a)[4]) -> f32x4 {
+    const float r0 = dpp(odd ? a[0] : a[2], swap1{}), r1 = dpp(odd ? a[1] : a[3], swap1{});
+    const float x0 = odd ? r0 : a[0], x1 = odd ? a[2] : r0;
+    const float x2 = odd ? r1 : a[1], x3 = odd ? a[3] : r1;
+    const float s0 = dpp(hi ? x0 : x2, swap2{}), s1 = dpp(hi ? x1 : x3, swap2{});
+    return hi ? f32x4{s0, s1, x2, x3} : f32x4{x0, x1, s0, s1};
+  };
+  if constexpr (!SWIGLU || EPI == QEPI_SWIGLU_BF16) {
+    constexpr int JN = SWIGLU ? FN / 2 : FN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < JN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float a[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            a[v] = SWIGLU ? silu_fast(acc[i][j][4 * g + v]) * acc[i][j + FN / 2][4 * g + v]
+                          : acc[i][j][4 * g + v];
+          const f32x4 v4 = quad_t(a);
+          const int r = rbase + i * 32 + g * 8 + h * 4 + rt;
+          const long long col = SWIGLU ? (long long)t.nt * (BN / 2) + wn * 64 + j * 32 + (l32 & ~3)
+                                       : (long long)t.nt * BN + wn * 128 + j * 32 + (l32 & ~3);
+          if (r >= t.row1 || col >= p.N) continue;         // N % 128 == 0: 4 columns all in or out
+          char* dst = C + (long long)r * p.c_pitch;
+          if (EPI == QEPI_STORE_F32) {
+            *reinterpret_cast<f32x4*>(dst + col * 4) = v4;
+          } else {
+            *reinterpret_cast<uint2*>(dst + col * 2) =
+                make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
+          }
+        }
+  } else {
+    // h re-quantised to 1 x 32 MX groups, one fragment row each: the group amax is reduced over
+    // the lanes holding the row after the transpose (DPP inside 16-lane rows, then one exchange
+    // between the two), the codes are formed by the hardware conversions (fp8: operands clamped to +-448 first, which
+    // makes its round-to-nearest-even saturating; fp4: saturating itself) on the values times
+    // 2^-e, as the element rule prescribes
+    constexpr int HF = FN / 2;             // h fragments: 2 x 32 = 64 columns per wave
+    using ror4 = std::integral_constant<int, 0x124>;    // row_ror:4 inside a 16-lane row
+    using ror8 = std::integral_constant<int, 0x128>;    // row_ror:8
+    const long long col0 = (long long)t.nt * (BN / 2) + wn * 64;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // after the transpose a lane holds 4 columns of its row; the row's other 28 columns are in
+        // the lanes 4, 8, ... apart (same quad position), 16 of them across the two 16-lane rows
+        f32x4 hv[HF];
+        int ex[HF];
+#pragma unroll
+        for (int j = 0; j < HF; ++j) {
+          float a[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) a[v] = silu_fast(acc[i][j][4 * g + v]) * acc[i][j + HF][4 * g + v];
+          hv[j] = quad_t(a);
+          float am = fmaxf(fmaxf(fabsf(hv[j][0]), fabsf(hv[j][1])), fmaxf(fabsf(hv[j][2]), fabsf(hv[j][3])));
+          am = fmaxf(am, dpp(am, ror4{}));
+          am = fmaxf(am, dpp(am, ror8{}));
+          am = fmaxf(am, __shfl_xor(am, 16, 64));
+          ex[j] = mx_shared_exp<MX8 ? 8 : 2>(am);
+        }
+        const int r = rbase + i * 32 + g * 8 + h * 4 + rt;
+        const bool live = r < t.row1;
+        uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
+#pragma unroll
+        for (int j = 0; j < HF; ++j) {
+          const f32x4 v4 = hv[j];
+          const float mul = ldexpf(1.0f, -ex[j]);
+          const long long col = col0 + j * 32 + (l32 & ~3);
+          if constexpr (MX8) {
+            auto cl = [&](float x) { return fminf(fmaxf(x * mul, -448.0f), 448.0f); };
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(v4[0]), cl(v4[1]), 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(v4[2]), cl(v4[3]), w, true);
+            if (live) *reinterpret_cast<uint32_t*>(crow + col) = static_cast<uint32_t>(w);
+          } else {
+            uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v4[0] * mul, v4[1] * mul, 1.0f, 0);
+            w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v4[2] * mul, v4[3] * mul, 1.0f, 1);
+            if (live) *reinterpret_cast<uint16_t*>(crow + col / 2) = static_cast<uint16_t>(w);
+          }
+        }
+        if (live && l32 < 4)
+          *reinterpret_cast<uint16_t*>(static_cast<uint8_t*>(p.C_scales) + (long long)r * (p.N / 32) + col0 / 32) =
+              static_cast<uint16_t>((ex[0] + 127) | ((ex[1] + 127) << 8));
+      }
+  }
+}
+
 namespace {
 
 template <int FMT, int EPI>
@@ -809,13 +1177,27 @@ hipError_t run_q_stream(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// decode-sized groups (few rows per group on average) stream the weights; others use the tiles
+template <int FMT, int EPI>
+hipError_t run_q_wide(const GemmArgs& a, hipStream_t s) {
+  constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
+  Grid g = make_grid(a, kQWideBM, SWIGLU ? kQWideBN / 2 : kQWideBN, 8, 64);
+  if (g.total == 0) return hipSuccess;
+  gemm_q_wide_kernel<FMT, EPI><<<dim3(g.blocks), dim3(256), qw_lds_bytes<FMT>(), s>>>(
+      a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm);
+  return hipGetLastError();
+}
+
+// decode-sized groups (few rows per group on average) stream the weights; prefill-sized groups
+// (a full 256-row tile or more per group) of the MX formats use the wide tiles; others the
+// 128-row tiles
 template <int FMT, int EPI>
 hipError_t run_q_choice(const GemmArgs& a, hipStream_t s) {
   const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;
   const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
   const long long per_group = groups ? rows / groups : rows;
   if (per_group <= 32 && a.N % 128 == 0) return run_q_stream<FMT, EPI>(a, s);
+  if constexpr (FMT == MOE_MXFP4 || FMT == MOE_MXFP8)
+    if (per_group >= kQWideBM) return run_q_wide<FMT, EPI>(a, s);
   return run_q<FMT, EPI>(a, s);
 }
 

@@ -29,6 +29,16 @@ def test_grouped_gemm_quant_decode(fmt, epi):
     _quant_case(fmt, epi, [3, 0, 17, 40, 1, 8, 33, 2], 768 if fmt == "mx4" else 640)
 
 
+# prefill-sized groups (256 rows or more per group on average): the 256 x 256 tiles of the MX formats
+# (fp8 keeps the 128-row tiles), with an empty group, a one-row group, ragged last m-tiles and, for
+# the stores, a partial last 256-column tile; 2 to 12 K-steps
+@pytest.mark.parametrize("fmt", ["fp8", "mx4", "mx8"])
+@pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
+@pytest.mark.parametrize("K", [512, 1536])
+def test_grouped_gemm_quant_prefill_groups(fmt, epi, K):
+    _quant_case(fmt, epi, [700, 0, 1, 513, 300], K)
+
+
 def _quant_case(fmt, epi, counts, K):
     dfmt, ofmt = FMTS[fmt]
     rng = np.random.default_rng([len(counts), sum(counts)])
