@@ -808,16 +808,12 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 // SwiGLU: wave column wn holds gate rows [64 wn, 64 wn + 64) and the up rows of the same h-columns,
 // so gate and up of one h-column meet in one lane and a 1 x 32 MX group of h is one fragment row.
 // ------------------------------------------------------------------------------------------------
-template <int FMT>
-constexpr int qw_scale_stage_bytes() {
-  return FMT == MOE_MXFP4 ? 4096 : 2048;   // E8M0 [256 A rows + 256 B rows][8 or 4 bytes]
-}
 constexpr int kQWideBM = 256, kQWideBN = 256, kQWideStages = 2;
-
-template <int FMT>
-constexpr size_t qw_lds_bytes() {
-  return (size_t)kQWideStages * ((kQWideBM + kQWideBN) * 128 + qw_scale_stage_bytes<FMT>());
-}
+// E8M0 scales travel in chunks of 16 bytes per row (4 K-steps of MXFP8, 2 of MXFP4), each lane
+// loading one row's 16 bytes: per K-step that is a quarter (half) of the 4-byte loads' requests,
+// which otherwise are as many as the operand loads'. Two chunk slots of [256 A + 256 B rows][16 B].
+constexpr int kQWideScaleSlot = (kQWideBM + kQWideBN) * 16;
+constexpr size_t kQWideLds = (size_t)kQWideStages * (kQWideBM + kQWideBN) * 128 + 2 * kQWideScaleSlot;
 
 template <int FMT, int EPI>
 __global__ void __launch_bounds__(256)
@@ -830,15 +826,17 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
   constexpr int KE = MX4 ? 256 : 128;      // elements per K-step
   constexpr int SUB = MX4 ? 4 : 2;         // 64-element MFMA substeps per K-step
   constexpr int A_INS = BM / (8 * NW), B_INS = BN / (8 * NW);
-  constexpr int SINS = MX4 ? 4 : 2;        // 4-byte scale loads per wave per K-step
-  constexpr int INS = A_INS + B_INS + SINS;
+  constexpr int INS = A_INS + B_INS;       // operand loads per wave per K-step
+  constexpr int SCH = 2;                   // scale chunk loads per wave (512 rows / 4 waves / 64)
   constexpr int DATA = (BM + BN) * RB;
-  constexpr int STAGE = DATA + qw_scale_stage_bytes<FMT>();
+  constexpr int STAGE = DATA;
+  constexpr int SC_BASE = S * DATA;        // the two scale chunk slots
   constexpr int SRB = MX4 ? 8 : 4;         // E8M0 bytes per row and K-step
+  constexpr int CH = 16 / SRB;             // K-steps per scale chunk
   constexpr int FMT_CODE = MX4 ? 4 : 0;
   using Geo = SliceGeo<64>;
   using SW = typename std::conditional<MX4, u32x2, uint32_t>::type;   // a row's scales of a step
-  static_assert(INS < 64, "vmcnt range");
+  static_assert(INS + SCH < 64, "vmcnt range");
   static_assert(SUB % 2 == 0, "fragment sets alternate by substep parity");
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t ldsw[];
@@ -891,47 +889,38 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
     const long long n = b_row(rb, base, sb);
     b_src[j] = base + n * b_row_bytes + ((lane & 7) ^ Geo::swz(rb)) * 16;
   }
-  // ---- scale sources (4-byte direct-to-LDS loads) ----
-  // MXFP8: one lane per row, 64 rows per load: load c of wave w is slot u = 2w + c: A rows
-  //        [64u, 64u + 64) for u < 4, B rows [64 (u - 4), +64) for u >= 4.
-  // MXFP4: two lanes per row (8 bytes per K-step), 32 rows per load: slot u = 4w + c: A rows for
-  //        u < 8, B rows for u >= 8.
-  const char* s_src[SINS];
-  int s_dst[SINS];
+  // ---- scale chunk sources: load c of wave w moves rows of slot u = 2w + c, A rows
+  //      [64u, 64u + 64) for u < 4, B rows [64 (u - 4), +64) for u >= 4, 16 bytes per lane ----
+  const char* s_src[SCH];
   {
     const int gpr = K / 32;                // scale bytes per row
-    constexpr int RPL = MX4 ? 32 : 64;     // rows per load
-    constexpr int ASLOTS = BM / RPL;
 #pragma unroll
-    for (int c = 0; c < SINS; ++c) {
-      const int u = wave * SINS + c;
-      const int part = MX4 ? (lane & 1) * 4 : 0;
-      const int rr = MX4 ? (lane >> 1) : lane;
-      if (u < ASLOTS) {
-        const int r = u * RPL + rr;
-        s_src[c] = static_cast<const char*>(p.A_scales) + a_src_row(p, t, t.row0 + r) * gpr + part;
-        s_dst[c] = DATA + u * 256;
+    for (int c = 0; c < SCH; ++c) {
+      const int u = wave * SCH + c;
+      if (u < 4) {
+        s_src[c] = static_cast<const char*>(p.A_scales) + a_src_row(p, t, t.row0 + u * 64 + lane) * gpr;
       } else {
-        const int rb = (u - ASLOTS) * RPL + rr;
         const char *base, *sbase;
-        const long long n = b_row(rb, base, sbase);
-        s_src[c] = sbase + n * gpr + part;
-        s_dst[c] = DATA + BM * SRB + (u - ASLOTS) * 256;
+        const long long n = b_row((u - 4) * 64 + lane, base, sbase);
+        s_src[c] = sbase + n * gpr;
       }
     }
   }
+  const int nch = nk / CH;                 // scale chunks (K % 512 == 0)
+  auto issue_scales = [&](int ch, int slot) {
+#pragma unroll
+    for (int c = 0; c < SCH; ++c)
+      dma_16b_asm(s_src[c] + (long long)ch * 16, ldsw + SC_BASE + slot * kQWideScaleSlot + (wave * SCH + c) * 64 * 16);
+  };
 
   // load qi of this wave's share of K-step kt into LDS stage `stage`
   auto issue_one = [&](int kt, int qi, int stage) {
     uint8_t* la = ldsw + stage * STAGE;
     if (qi < A_INS) {
       dma_16b_asm(a_src[qi] + (long long)kt * RB, la + (qi * NW + wave) * 8 * RB);
-    } else if (qi < A_INS + B_INS) {
+    } else {
       const int j = qi - A_INS;
       dma_16b_asm(b_src[j] + (long long)kt * RB, la + BM * RB + (j * NW + wave) * 8 * RB);
-    } else {
-      const int j = qi - A_INS - B_INS;
-      dma_4b_asm(s_src[j] + (long long)kt * SRB, la + s_dst[j]);
     }
   };
 
@@ -960,28 +949,31 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
   i32x8 fa[2][FM], fb[2][FN];
   SW sa[2][FM], sb[2][FN];
   auto stage_ptr = [&](int kt) -> const uint8_t* { return ldsw + (kt % S) * STAGE; };
-  auto read_scales = [&](const uint8_t* la, int sset) {
-    const uint8_t* ls = la + DATA;
+  // scale words of K-step kt (a row's E8M0 bytes of the step) into set sset
+  auto read_scales = [&](int kt, int sset) {
+    const uint8_t* ls = ldsw + SC_BASE + ((kt / CH) & 1) * kQWideScaleSlot + (kt % CH) * SRB;
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj)
-      sb[sset][jj] = *reinterpret_cast<const SW*>(ls + BM * SRB + (frag_brow(jj) + l32) * SRB);
+      sb[sset][jj] = *reinterpret_cast<const SW*>(ls + (BM + frag_brow(jj) + l32) * 16);
 #pragma unroll
     for (int ii = 0; ii < FM; ++ii)
-      sa[sset][ii] = *reinterpret_cast<const SW*>(ls + (wm * 128 + ii * 32 + l32) * SRB);
+      sa[sset][ii] = *reinterpret_cast<const SW*>(ls + (wm * 128 + ii * 32 + l32) * 16);
   };
   auto scale_byte = [&](const SW& w, int sub) -> int {   // byte 2 sub + h of the step's scales
     if constexpr (MX4) return static_cast<int>((w[sub >> 1] >> (16 * (sub & 1) + 8 * h)) & 0xFFu);
     else return static_cast<int>((w >> (16 * sub + 8 * h)) & 0xFFu);
   };
 
-  // prologue: steps 0 and 1 in flight, wait for step 0, read its first fragments
+  // prologue: scale chunk 0, steps 0 and 1, scale chunk 1 in flight; wait for the first two
+  issue_scales(0, 0);
 #pragma unroll
   for (int qi = 0; qi < INS; ++qi) issue_one(0, qi, 0);
 #pragma unroll
   for (int qi = 0; qi < INS; ++qi) issue_one(nk > 1 ? 1 : 0, qi, 1);
-  wait_vmem_n<INS>();
+  issue_scales(nch > 1 ? 1 : 0, 1);
+  wait_vmem_n<INS + SCH>();
   barrier_lds();
-  read_scales(stage_ptr(0), 0);
+  read_scales(0, 0);
 #pragma unroll
   for (int ii = 0; ii < FM; ++ii) fa[0][ii] = read_frag(stage_ptr(0), wm * 128 + ii * 32, 0);
 #pragma unroll
@@ -1005,13 +997,16 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
         wait_vmem();
         wait_lgkm();
         barrier_lds();
+        // the scale chunk after the next one goes into the slot of the chunk just finished
+        const int nc = (kt + 1) / CH + 1;
+        if ((kt + 1) % CH == 0) issue_scales(nc < nch ? nc : nch - 1, nc & 1);
       }
       const int rk = last ? (kt + 1 < nk ? kt + 1 : kt) : kt;   // step and substep read next
       const int rs = last ? 0 : sub + 1;
       const uint8_t* la = stage_ptr(rk);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        if (last && i == 0) read_scales(la, 1);
+        if (last && i == 0) read_scales(rk, 1);
         fa[cur ^ 1][i] = read_frag(la, wm * 128 + i * 32, rs);
         fb[cur ^ 1][i] = read_frag(la + BM * RB, frag_brow(i), rs);
 #pragma unroll
@@ -1182,14 +1177,14 @@ hipError_t run_q_wide(const GemmArgs& a, hipStream_t s) {
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
   Grid g = make_grid(a, kQWideBM, SWIGLU ? kQWideBN / 2 : kQWideBN, 8, 64);
   if (g.total == 0) return hipSuccess;
-  gemm_q_wide_kernel<FMT, EPI><<<dim3(g.blocks), dim3(256), qw_lds_bytes<FMT>(), s>>>(
+  gemm_q_wide_kernel<FMT, EPI><<<dim3(g.blocks), dim3(256), kQWideLds, s>>>(
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm);
   return hipGetLastError();
 }
 
 // decode-sized groups (few rows per group on average) stream the weights; prefill-sized groups
-// (a full 256-row tile or more per group) of the MX formats use the wide tiles; others the
-// 128-row tiles
+// (a full 256-row tile or more per group) of the MX formats with K % 512 == 0 (whole scale
+// chunks) use the wide tiles; others the 128-row tiles
 template <int FMT, int EPI>
 hipError_t run_q_choice(const GemmArgs& a, hipStream_t s) {
   const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;
@@ -1197,7 +1192,7 @@ hipError_t run_q_choice(const GemmArgs& a, hipStream_t s) {
   const long long per_group = groups ? rows / groups : rows;
   if (per_group <= 32 && a.N % 128 == 0) return run_q_stream<FMT, EPI>(a, s);
   if constexpr (FMT == MOE_MXFP4 || FMT == MOE_MXFP8)
-    if (per_group >= kQWideBM) return run_q_wide<FMT, EPI>(a, s);
+    if (per_group >= kQWideBM && a.K % 512 == 0) return run_q_wide<FMT, EPI>(a, s);
   return run_q<FMT, EPI>(a, s);
 }
 
