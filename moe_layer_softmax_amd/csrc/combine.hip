@@ -12,17 +12,17 @@
 namespace moe {
 
 // Workgroup (t, c): token t, columns [c * 256 * CPL, (c + 1) * 256 * CPL), CPL per thread (8 for
-// bf16 rows, 4 for fp32: one 16-byte load per row). All k rows' loads are issued before the first
-// is added (unconditional: a non-local slot reads row 0 and adds nothing), so one token's latency
-// is one memory round trip.
-template <bool Y_BF16, bool OUT_BF16>
+// bf16 rows, 4 for fp32: one 16-byte load per row). All KMAX rows' loads are issued before the
+// first is added (unconditional: a non-local slot, and a slot j >= k, reads row 0 and adds
+// nothing), so one token's latency is one memory round trip. KMAX (8 or 16) bounds k: the k rows' values are held in registers, and
+// with KMAX = 8 twice as many waves fit on a CU to keep loads in flight.
+template <bool Y_BF16, bool OUT_BF16, int KMAX>
 __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* __restrict__ y,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ slot_to_row,
                                                       const void* __restrict__ shared,
                                                       const float* __restrict__ shared_w,
                                                       void* __restrict__ out) {
-  constexpr int KMAX = 16;
   constexpr int CPL = Y_BF16 ? 8 : 4;
   const int t = blockIdx.x;
   const int c0 = (blockIdx.y * 256 + threadIdx.x) * CPL;
@@ -35,26 +35,29 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
   }
   __syncthreads();
   if (c0 >= H) return;                      // H % 8 == 0: a thread's columns are all in or all out
-  auto load_row = [&](const void* base, long long r, float* v) {
+  // raw 16-byte row pieces (bf16 values are widened only when added, which keeps the registers
+  // per row at four)
+  auto load_raw = [&](const void* base, long long r) -> i32x4 {
+    if (Y_BF16) return *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(base) + r * H + c0);
+    return *reinterpret_cast<const i32x4*>(static_cast<const float*>(base) + r * H + c0);
+  };
+  auto widen = [&](const i32x4& b, float* v) {
     if (Y_BF16) {
-      const i32x4 b = *reinterpret_cast<const i32x4*>(static_cast<const uint16_t*>(base) + r * H + c0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[2 * q] = __uint_as_float(static_cast<uint32_t>(b[q]) << 16);
         v[2 * q + 1] = __uint_as_float(static_cast<uint32_t>(b[q]) & 0xFFFF0000u);
       }
     } else {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + r * H + c0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = a[q];
+      for (int q = 0; q < 4; ++q) v[q] = __int_as_float(b[q]);
     }
   };
-  float v[KMAX][CPL];
+  i32x4 raw[KMAX];                          // y holds T * k >= 1 rows, so row 0 exists
 #pragma unroll
-  for (int j = 0; j < KMAX; ++j)
-    if (j < k) load_row(y, rows[j] < 0 ? 0 : rows[j], v[j]);
-  float sh[CPL];
-  if (shared) load_row(shared, t, sh);
+  for (int j = 0; j < KMAX; ++j) raw[j] = load_raw(y, rows[j] < 0 ? 0 : rows[j]);
+  i32x4 sh_raw = {};
+  if (shared) sh_raw = load_raw(shared, t);
   // fp32 accumulation in slot order j = 0..k-1, the shared row last, one rounding
   float acc[CPL];
 #pragma unroll
@@ -63,10 +66,14 @@ __global__ void __launch_bounds__(256) combine_kernel(int H, int k, const void* 
   for (int j = 0; j < KMAX; ++j) {
     if (j < k && rows[j] >= 0) {
       const float wj = wts[j];
+      float v[CPL];
+      widen(raw[j], v);
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) acc[i] += wj * v[j][i];
+      for (int i = 0; i < CPL; ++i) acc[i] += wj * v[i];
     }
   }
+  float sh[CPL];
+  widen(sh_raw, sh);
   if (shared) {
     const float gs = shared_w ? shared_w[t] : 1.0f;
 #pragma unroll
@@ -94,10 +101,17 @@ hipError_t launch_combine(int T, int H, int k, int y_dtype, int out_dtype, const
   const bool yb = y_dtype == MOE_BF16, ob = out_dtype == MOE_BF16;
   const int cols_per_wg = 256 * (yb ? 8 : 4);
   dim3 grid(T, (H + cols_per_wg - 1) / cols_per_wg), block(256);
-  auto k_ = combine_kernel<false, false>;
-  if (yb && ob) k_ = combine_kernel<true, true>;
-  else if (yb) k_ = combine_kernel<true, false>;
-  else if (ob) k_ = combine_kernel<false, true>;
+  auto k_ = combine_kernel<false, false, 16>;
+  if (k <= 8) {
+    k_ = combine_kernel<false, false, 8>;
+    if (yb && ob) k_ = combine_kernel<true, true, 8>;
+    else if (yb) k_ = combine_kernel<true, false, 8>;
+    else if (ob) k_ = combine_kernel<false, true, 8>;
+  } else {
+    if (yb && ob) k_ = combine_kernel<true, true, 16>;
+    else if (yb) k_ = combine_kernel<true, false, 16>;
+    else if (ob) k_ = combine_kernel<false, true, 16>;
+  }
   k_<<<grid, block, 0, s>>>(H, k, y, w, slot_to_row, shared, shared_w, out);
   return hipGetLastError();
 }
