@@ -132,6 +132,15 @@ moe_status moe_route(const moe_desc* d, const void* x, const void* w_router, con
                      hipStream_t stream);
 size_t moe_route_workspace_bytes(const moe_desc* d);
 
+/* ---- routing blob --------------------------------------------------------------------------------
+ * The routing result as one 32-bit array [2][P], P = T*k rounded up to a multiple of 4 (so that
+ * each plane starts 16-byte aligned): plane 0 holds topk_ids, plane 1 the bits of topk_w. This is
+ * the stacked, bitcast form in which one all-gather moves indices and weights together ("How we
+ * served a 397B MoE model with 4.7x speedup on TPU v7", section "Three collectives become two").
+ * Pass topk_ids = blob and topk_w = (float*)(blob + P) to moe_route or moe_layer, and the same
+ * planes to moe_permute and moe_combine. Returns P (0 for an invalid descriptor). */
+int64_t moe_routing_blob_plane(const moe_desc* d);
+
 /* ---- dispatch (count, offsets, unique row per local slot, copy) ------------------------------
  * counts[E_loc]: local slots per expert. offsets[E_loc+1]: exclusive prefix sum, offsets[E_loc] = R.
  * slot_to_row[T,k]: row of slot (t,j) in the expert-contiguous buffer, -1 if e_tj is not local.

@@ -65,6 +65,8 @@ _lib.moe_grouped_gemm.argtypes = [ctypes.POINTER(moe_gemm_desc), _P, _P, _P, _P,
                                   _P, _P, _P]
 _lib.moe_combine.argtypes = [_D, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_shared_gate.argtypes = [_D, _P, _P, _P, _P]
+_lib.moe_routing_blob_plane.argtypes = [_D]
+_lib.moe_routing_blob_plane.restype = ctypes.c_int64
 _lib.moe_quantize.argtypes = [ctypes.c_int32] * 6 + [_P, _P, _P, _P]
 _lib.moe_layer.argtypes = [_D, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P, _P, _P,
                            ctypes.c_size_t, _P]
@@ -138,6 +140,10 @@ def moe_combine(d, y_dtype, y, topk_w, slot_to_row, shared, out, stream=None, sh
     _check(_lib.moe_combine(ctypes.byref(d), y_dtype, _ptr(y), _ptr(topk_w), _ptr(slot_to_row),
                             _ptr(shared), _ptr(shared_w), _ptr(out), _stream(stream)),
            "moe_combine")
+
+
+def moe_routing_blob_plane(d):
+    return _lib.moe_routing_blob_plane(ctypes.byref(d))
 
 
 def moe_shared_gate(d, x, w_shared_gate, shared_w, stream=None):

@@ -356,6 +356,11 @@ moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const 
                                    shared, shared_w, out, stream));
 }
 
+int64_t moe_routing_blob_plane(const moe_desc* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return ((int64_t)d->T * d->k + 3) / 4 * 4;
+}
+
 moe_status moe_shared_gate(const moe_desc* d, const void* x, const void* w_shared_gate,
                            float* shared_w, hipStream_t stream) {
   moe_status st = check_desc(d);

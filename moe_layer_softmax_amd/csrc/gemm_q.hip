@@ -716,9 +716,8 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
         uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) word |= static_cast<uint32_t>(e4m3_rne_sat(h[i][jj][v] * mul)) << (8 * v);
+          const uint32_t word = e4m3x4_rne_sat(h[i][jj][0] * mul, h[i][jj][1] * mul, h[i][jj][2] * mul,
+                                               h[i][jj][3] * mul);
           *reinterpret_cast<uint32_t*>(crow + col0 + jj * 16 + kq * 4) = word;
         }
         if (kq == 0)
@@ -775,9 +774,8 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
         uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) word |= static_cast<uint32_t>(e4m3_rne_sat(h[i][jj][v] / sc)) << (8 * v);
+          const uint32_t word = e4m3x4_rne_sat(h[i][jj][0] / sc, h[i][jj][1] / sc, h[i][jj][2] / sc,
+                                               h[i][jj][3] / sc);
           *reinterpret_cast<uint32_t*>(crow + col0 + jj * 16 + kq * 4) = word;
         }
         if (wave == 0 && kq == 0)

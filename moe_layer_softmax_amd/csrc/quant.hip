@@ -70,12 +70,8 @@ __global__ void __launch_bounds__(256) quant_fp8_kernel(int rows, int cols, int 
   for (int u = 0; u < 8; ++u) {
     const int i = threadIdx.x + u * 256;
     if (i < nch) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo |= static_cast<uint32_t>(e4m3_rne_sat(v[u][e] / s)) << (8 * e);
-        hi |= static_cast<uint32_t>(e4m3_rne_sat(v[u][4 + e] / s)) << (8 * e);
-      }
+      const uint32_t lo = e4m3x4_rne_sat(v[u][0] / s, v[u][1] / s, v[u][2] / s, v[u][3] / s);
+      const uint32_t hi = e4m3x4_rne_sat(v[u][4] / s, v[u][5] / s, v[u][6] / s, v[u][7] / s);
       *reinterpret_cast<uint2*>(codes + mat + (size_t)(r0 + i / 16) * cols + bj * 128 + (i % 16) * 8) =
           make_uint2(lo, hi);
     }
@@ -105,9 +101,10 @@ __global__ void __launch_bounds__(256) quant_mx4_kernel(long long groups, const 
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int e8 = mx_shared_exp(amax);
   const float mul = ldexpf(1.0f, -e8);
-  uint32_t word = 0;
+  float y[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) word |= static_cast<uint32_t>(e2m1_rne_sat(v[e] * mul)) << (4 * e);
+  for (int e = 0; e < 8; ++e) y[e] = v[e] * mul;
+  const uint32_t word = e2m1x8_rne_sat(y);
   if (!live) return;
   *reinterpret_cast<uint32_t*>(packed + (size_t)g * 16 + sub * 4) = word;
   if (sub == 0) scales[g] = static_cast<uint8_t>(e8 + 127);
@@ -135,12 +132,8 @@ __global__ void __launch_bounds__(256) quant_mx8_kernel(long long groups, const 
   amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
   const int e8 = mx_shared_exp<8>(amax);
   const float mul = ldexpf(1.0f, -e8);
-  uint32_t lo = 0, hi = 0;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    lo |= static_cast<uint32_t>(e4m3_rne_sat(v[e] * mul)) << (8 * e);
-    hi |= static_cast<uint32_t>(e4m3_rne_sat(v[4 + e] * mul)) << (8 * e);
-  }
+  const uint32_t lo = e4m3x4_rne_sat(v[0] * mul, v[1] * mul, v[2] * mul, v[3] * mul);
+  const uint32_t hi = e4m3x4_rne_sat(v[4] * mul, v[5] * mul, v[6] * mul, v[7] * mul);
   if (!live) return;
   *reinterpret_cast<uint2*>(codes + (size_t)g * 32 + sub * 8) = make_uint2(lo, hi);
   if (sub == 0) scales[g] = static_cast<uint8_t>(e8 + 127);

@@ -46,6 +46,26 @@ __device__ __forceinline__ uint8_t e2m1_rne_sat(float y) {
   return sign | c;
 }
 
+// Four fp32 values -> four e4m3 codes (value i in byte i) by the hardware conversion. Clamping the
+// operands to +-448 first makes its round-to-nearest-even saturate as e4m3_rne_sat does; the two
+// agree bit for bit (checked on the MI355X over every grid value, every tie and its neighbours,
+// subnormals, +-0 and 440-620, at scales 2^-30 .. 2^30).
+__device__ __forceinline__ uint32_t e4m3x4_rne_sat(float a, float b, float c, float d) {
+  auto cl = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// Eight fp32 values -> eight e2m1 codes (value i in bits 4i .. 4i + 3) by the hardware conversion
+// with a unit scale, which saturates itself and agrees with e2m1_rne_sat bit for bit (same check).
+__device__ __forceinline__ uint32_t e2m1x8_rne_sat(const float* v) {
+  uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+}
+
 // shared exponent of an MX block: floor(log2(amax)) minus the element format's largest exponent
 // (2 for e2m1, 8 for e4m3), clamped to [-127, 127]; -127 for amax = 0
 template <int EMAX = 2>

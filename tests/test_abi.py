@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     lib = ctypes.CDLL(LIB)
     names = _declared()
     assert {"moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_layer",
-            "moe_quantize", "moe_shared_gate"} <= set(names)
+            "moe_quantize", "moe_shared_gate", "moe_routing_blob_plane"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -144,3 +144,10 @@ def test_zero_tokens_is_a_no_op():
     assert lib.moe_shared_gate(ctypes.byref(d), None, None, None, None) == m.MOE_OK
     assert lib.moe_layer(ctypes.byref(d), ctypes.byref(w), None, None, None, None, None, None,
                          None, 0, None) == m.MOE_OK
+
+
+def test_routing_blob_plane():
+    import moe_layer_softmax_amd as m
+    for T, k, P in ((1, 8, 8), (3, 2, 8), (5, 3, 16), (0, 4, 0), (16384, 8, 131072), (7, 10, 72)):
+        assert m.moe_routing_blob_plane(_desc(T=T, k=k, E=16, E_loc=16)) == P
+    assert m.moe_routing_blob_plane(_desc(T=-1)) == 0

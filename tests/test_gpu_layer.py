@@ -204,3 +204,42 @@ def test_layer_deterministic():
     a = gpu_layer(wl, x, wr, bias, experts, sh)[0]
     b = gpu_layer(wl, x, wr, bias, experts, sh)[0]
     assert np.array_equal(a, b)
+
+
+# the routing result as one stacked 32-bit blob: ids in plane 0, weight bits in plane 1 (T * k = 21 is
+# not a multiple of 4, so plane 1 starts at the padded offset); the layer writes the same ids and
+# weight bits into the blob as into separate arrays, and permute / combine read the planes
+def test_layer_routing_blob():
+    wl = _small(T=7, k=3, I_s=256)
+    x, wr, bias, experts, sh = make_inputs(wl)
+    out, lg, ids, w, (desc, weights, xb, bt, o_dev, l_dev, i_dev, w_dev, ws) = gpu_layer(
+        wl, x, wr, bias, experts, sh)
+    P = moe.moe_routing_blob_plane(desc)
+    assert P == 24
+    blob = torch.full((2 * P,), -7, dtype=torch.int32, device="cuda")
+    out2 = torch.empty_like(o_dev)
+    moe.moe_layer(desc, weights, xb, bt, out2, None, blob[:P], blob[P:].view(torch.float32), ws)
+    torch.cuda.synchronize()
+    b = blob.cpu().numpy()
+    assert np.array_equal(b[:wl.T * wl.k].reshape(wl.T, wl.k), ids)
+    assert np.array_equal(b[P:P + wl.T * wl.k].view(np.float32).reshape(wl.T, wl.k), w)
+    assert np.all(b[wl.T * wl.k:P] == -7)                       # padding untouched
+    assert np.array_equal(out2.cpu().numpy(), out)
+    # permute and combine from the planes: the same maps and the same combine as from the arrays
+    k, T, H = wl.k, wl.T, wl.H
+    counts = torch.empty(wl.E_loc, dtype=torch.int32, device="cuda")
+    offs = torch.empty(wl.E_loc + 1, dtype=torch.int32, device="cuda")
+    s2r = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    r2f = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    pws = torch.empty(max(moe.moe_permute_workspace_bytes(desc), 16), dtype=torch.uint8, device="cuda")
+    moe.moe_permute(desc, blob[:P], None, None, counts, offs, s2r, r2f, None, None, pws)
+    ref = oracle.permute(ids, wl.e0, wl.E_loc)
+    torch.cuda.synchronize()
+    assert np.array_equal(s2r.cpu().numpy(), ref[2])
+    y = torch.randn((T * k, H), device="cuda")
+    c1 = torch.empty((T, H), device="cuda")
+    c2 = torch.empty((T, H), device="cuda")
+    moe.moe_combine(desc, moe.MOE_F32, y, blob[P:].view(torch.float32), s2r, None, c1)
+    moe.moe_combine(desc, moe.MOE_F32, y, w_dev, s2r, None, c2)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, c2)
