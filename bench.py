@@ -427,6 +427,18 @@ def main():
         print(json.dumps({"workload": wl.name, "ms_per_step": ms_per_step}))
         return
 
+    # per-call spread of the same layer (HIP events around each call on its stream), outside the
+    # timed region above
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(5, min(args.steps, 50)))]
+    with torch.cuda.stream(stream):
+        for a, b in ev:
+            a.record(stream)
+            L.step(stream)
+            b.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
     steps_ms, R, counts = step_breakdown(L, stream, max(5, min(args.steps, 20)))
     flops_gu = 4.0 * R * wl.H * wl.I
     achieved = flops_gu / (steps_ms["gemm_gate_up"] * 1e-3) / 1e12
@@ -461,6 +473,9 @@ def main():
                      "flops_per_launch": flops_gu,
                      "avg_launch_ms": round(steps_ms["gemm_gate_up"], 4)},
         "steps_ms": {k: round(v, 4) for k, v in steps_ms.items()},
+        "layer_call_ms": {"p10": round(float(np.percentile(call_ms, 10)), 4),
+                          "median": round(float(np.median(call_ms)), 4),
+                          "p90": round(float(np.percentile(call_ms, 90)), 4), "calls": len(call_ms)},
     }
     if not args.no_decode:
         dwl = mi.WORKLOADS[args.decode_workload]
@@ -479,7 +494,8 @@ def main():
                 D.step(stream)
                 b.record(stream)
         torch.cuda.synchronize()
-        dms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        dcall = np.array([a.elapsed_time(b) for a, b in ev])
+        dms = float(np.median(dcall))
         _, dR, dcounts = step_breakdown(D, stream, 5)
         dbytes = compulsory_bytes(dwl, dcounts)
         result["decode"] = {"workload": f"same layer, {dwl.T} tokens", "ms": round(dms, 4),
@@ -487,7 +503,9 @@ def main():
                             "compulsory_bytes": dbytes,
                             "hbm_gbps": round(dbytes / (dms * 1e-3) / 1e9, 1),
                             "frac_hbm": round(dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-                            "caches": "1 GiB read between steps"}
+                            "caches": "1 GiB read between steps",
+                            "ms_p10": round(float(np.percentile(dcall, 10)), 4),
+                            "ms_p90": round(float(np.percentile(dcall, 90)), 4)}
         del D, flush
     if not args.no_ep_sweep:
         result["decode_one_token_per_expert"] = ep_sweep(stream, max(5, min(args.steps, 20)))
