@@ -127,7 +127,8 @@ def workload_table(stream, steps, names=None):
                 call()
                 e.record(stream)
         torch.cuda.synchronize()
-        ms = float(np.median([a.elapsed_time(e) for a, e in ev]))
+        call_ms = np.array([a.elapsed_time(e) for a, e in ev])
+        ms = float(np.median(call_ms))
         loc = ids[(ids >= wl.e0) & (ids < wl.e0 + wl.E_loc)]
         R = int(loc.numel())
         active = int(torch.unique(loc).numel())
@@ -139,6 +140,8 @@ def workload_table(stream, steps, names=None):
         t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
         t = ms * 1e-3
         out[name] = {"T": wl.T, "format": fname, "ms": round(ms, 4),
+                     "ms_p10": round(float(np.percentile(call_ms, 10)), 4),
+                     "ms_p90": round(float(np.percentile(call_ms, 90)), 4),
                      "tokens_per_s": round(wl.T / t, 1), "local_rows_R": R, "active_experts": active,
                      "tflops": round((router_fl + expert_fl) / t / 1e12, 1),
                      "frac_mfma": round(t_mfma / t, 4), "compulsory_bytes": nbytes,
