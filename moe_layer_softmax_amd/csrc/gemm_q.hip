@@ -947,19 +947,22 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
   i32x8 fa[2][FM], fb[2][FN];
   SW sa[2][FM], sb[2][FN];
   auto stage_ptr = [&](int kt) -> const uint8_t* { return ldsw + (kt % S) * STAGE; };
-  // scale words of K-step kt (a row's E8M0 bytes of the step) into set sset
+  // scale words of K-step kt (a row's E8M0 bytes of the step) into set sset. Substep sub of lane
+  // half h needs byte 2 sub + h; the words are shifted right by 8 h once here, so that the MFMA's
+  // op_sel picks byte 2 sub (MXFP8) or 2 (sub & 1) of word sub / 2 (MXFP4) for every lane with no
+  // per-MFMA extraction
   auto read_scales = [&](int kt, int sset) {
     const uint8_t* ls = ldsw + SC_BASE + ((kt / CH) & 1) * kQWideScaleSlot + (kt % CH) * SRB;
 #pragma unroll
     for (int jj = 0; jj < FN; ++jj)
-      sb[sset][jj] = *reinterpret_cast<const SW*>(ls + (BM + frag_brow(jj) + l32) * 16);
+      sb[sset][jj] = *reinterpret_cast<const SW*>(ls + (BM + frag_brow(jj) + l32) * 16) >> (8 * h);
 #pragma unroll
     for (int ii = 0; ii < FM; ++ii)
-      sa[sset][ii] = *reinterpret_cast<const SW*>(ls + (wm * 128 + ii * 32 + l32) * 16);
+      sa[sset][ii] = *reinterpret_cast<const SW*>(ls + (wm * 128 + ii * 32 + l32) * 16) >> (8 * h);
   };
-  auto scale_byte = [&](const SW& w, int sub) -> int {   // byte 2 sub + h of the step's scales
-    if constexpr (MX4) return static_cast<int>((w[sub >> 1] >> (16 * (sub & 1) + 8 * h)) & 0xFFu);
-    else return static_cast<int>((w >> (16 * sub + 8 * h)) & 0xFFu);
+  auto scale_word = [&](const SW& w, int sub) -> int {
+    if constexpr (MX4) return static_cast<int>(w[sub >> 1]);
+    else return static_cast<int>(w);
   };
 
   // prologue: scale chunk 0, steps 0 and 1, scale chunk 1 in flight; wait for the first two
@@ -1009,9 +1012,13 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
         fb[cur ^ 1][i] = read_frag(la + BM * RB, frag_brow(i), rs);
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) {
-          acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              fa[cur][i], fb[cur][jj], acc[i][jj], FMT_CODE, FMT_CODE, 0, scale_byte(sa[0][i], sub), 0,
-              scale_byte(sb[0][jj], sub));
+          const int wa = scale_word(sa[0][i], sub), wb = scale_word(sb[0][jj], sub);
+          if ((MX4 ? (sub & 1) : sub) == 0)   // op_sel byte 0 or 2 (resolved at compile time)
+            acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa[cur][i], fb[cur][jj], acc[i][jj], FMT_CODE, FMT_CODE, 0, wa, 0, wb);
+          else
+            acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fa[cur][i], fb[cur][jj], acc[i][jj], FMT_CODE, FMT_CODE, 2, wa, 2, wb);
         }
         if (last && i == 0) MOE_SCHED_GROUP(0x100, 2 * FN);   // the scale reads first
 #pragma unroll
