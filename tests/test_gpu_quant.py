@@ -10,7 +10,7 @@ import moe_layer_softmax_amd as moe
 import oracle
 from moe_inputs import gen
 
-from gpu_util import FMTS, decode, gpu_quant, oracle_quant, to_dev
+from gpu_util import FMTS, decode, gamma, gpu_quant, oracle_quant, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +37,14 @@ def test_grouped_gemm_quant_decode(fmt, epi):
 @pytest.mark.parametrize("K", [512, 1536])
 def test_grouped_gemm_quant_prefill_groups(fmt, epi, K):
     _quant_case(fmt, epi, [700, 0, 1, 513, 300], K)
+
+
+# decode-sized groups with fewer 128-byte K-pairs than the streaming kernel's four K-split waves
+# (K = 256: two of the four waves get no K-pair and contribute zeros)
+@pytest.mark.parametrize("fmt", ["fp8", "mx8"])
+@pytest.mark.parametrize("epi", ["store_f32", "store_bf16", "swiglu_bf16", "swiglu_q"])
+def test_grouped_gemm_quant_decode_short_k(fmt, epi):
+    _quant_case(fmt, epi, [5, 0, 31, 2], 256)
 
 
 def _quant_case(fmt, epi, counts, K):
@@ -80,18 +88,35 @@ def _quant_case(fmt, epi, counts, K):
     rms = np.sqrt(np.mean(ref ** 2)) if R else 1.0
     if epi == "swiglu_q":
         h = decode(dfmt, C[:R], C_scales[:R], N)
+        # h itself comes from fp32 accumulations: |dg|, |du| <= gamma_K sum|a b| (the bound used
+        # for the router logits), so |dh| <= |silu'(g)| |dg| |u| + |silu(g)| |du| with |silu'| < 1.1;
+        # a code is then within the quantisation bounds below of the fp32 h, not of the exact one
+        Ad = np.abs(A.dequant()[0])
+        g_ref = oracle.grouped_gemm(off, A, oracle_quant(ofmt, B, 128), None, a_rows=a_rows, a_row_div=kk)
+        u_ref = oracle.grouped_gemm(off, A, oracle_quant(ofmt, B2, 128), None, a_rows=a_rows, a_row_div=kk)
+        Bd, B2d = np.abs(oracle_quant(ofmt, B, 128).dequant()), np.abs(oracle_quant(ofmt, B2, 128).dequant())
+        dg = np.zeros_like(ref)
+        du = np.zeros_like(ref)
+        for gi in range(G):
+            rows = slice(int(off[gi]), int(off[gi + 1]))
+            Ar = Ad[a_rows[rows] // kk]
+            dg[rows] = gamma(K) * (Ar @ Bd[gi].T)
+            du[rows] = gamma(K) * (Ar @ B2d[gi].T)
+        silu = g_ref / (1.0 + np.exp(-g_ref))
+        dh = 1.1 * dg * np.abs(u_ref) + np.abs(silu) * du
+        ref_abs = np.abs(ref) + dh
         if fmt == "fp8":
             # within one e4m3 step of the block's scale grid (fp32 vs fp64 h may round differently)
             s = np.repeat(C_scales[:R].cpu().numpy().astype(np.float64), 128, axis=1)
-            assert np.all(np.abs(h - ref) <= 2.0 ** -3 * np.abs(ref) + s * 2.0 ** -8)
+            assert np.all(np.abs(h - ref) <= 2.0 ** -3 * ref_abs + s * 2.0 ** -8 + dh)
         elif fmt == "mx8":
             # within one e4m3 step (relative 2^-3, saturation above 448 * 2^e included) or one
             # subnormal step 2^(e-9) of the group's scale
             unit = np.repeat(2.0 ** (C_scales[:R].cpu().numpy().astype(np.int64) - 127), 32, axis=1)
-            assert np.all(np.abs(h - ref) <= 2.0 ** -3 * np.abs(ref) + unit * 2.0 ** -8)
+            assert np.all(np.abs(h - ref) <= 2.0 ** -3 * ref_abs + unit * 2.0 ** -8 + dh)
         else:
             unit = np.repeat(2.0 ** (C_scales[:R].cpu().numpy().astype(np.int64) - 127), 32, axis=1)
-            assert np.all(np.abs(h - ref) <= 2.0 * unit + 1e-30)
+            assert np.all(np.abs(h - ref) <= 2.0 * unit + dh + 1e-30)
     else:
         Cg = C.float().cpu().numpy()
         err = np.abs(Cg[:R] - ref)
