@@ -393,8 +393,9 @@ def cpu_baseline(L, target_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; the whole-job value for N=1 is the one-GPU throughput.",
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the layer is one GPU's "
+              "expert slice and has no multi-GPU path; the whole-job value for N=1 is the one-GPU "
+              "throughput.",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
