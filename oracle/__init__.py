@@ -303,5 +303,26 @@ def moe_layer(desc, x, w_r, bias, xa, gate, up, down, shared=None, tok=None, sha
     return dict(out=out, logits64=L64, logits32=L32, ids=ids, w=w)
 
 
+def moe_layer_routed(desc, x, xa, gate, up, down, shared, tok, ids, w, shared_gate=None):
+    """The expert part of the layer for given routing: tokens tok (int32 [n]) with chosen experts
+    ids [n, k] and fp32 weights w [n, k]. Returns float64 out [n, H]."""
+    x = _c(x, np.float32)
+    t = _c(tok, np.int32)
+    i = _c(ids, np.int32)
+    wf = _c(w, np.float32)
+    H = desc["H"]
+    d = _Desc(*(int(desc[f]) for f in ("T", "H", "E", "e0", "E_loc", "I", "k", "I_s",
+                                       "scoring", "renormalize", "act_fmt")))
+    out = np.empty((len(t), H), np.float64)
+    null = ctypes.c_void_p(None)
+    sg, su, sd = (shared if shared is not None else (None, None, None))
+    gv = None if shared_gate is None else _c(shared_gate, np.float32)
+    lib().oracle_moe_layer_routed(ctypes.byref(d), _p(x), xa.ref, gate.ref, up.ref, down.ref,
+                                  sg.ref if sg else null, su.ref if su else null,
+                                  sd.ref if sd else null, _p(gv), len(t), _p(t), _p(i), _p(wf),
+                                  _p(out))
+    return out
+
+
 def num_threads():
     return lib().oracle_num_threads()

@@ -429,6 +429,30 @@ void oracle_ffn_row(const oracle_desc* d, int I, const double* a, const oracle_m
   free(wrow);
 }
 
+/* out row o[H] of token t for a given routing (sel, wt of k slots): the weighted sum of the local
+ * experts' FFN outputs in slot order, then the shared expert times its gate */
+static void expert_sum(const oracle_desc* d, const float* x, const oracle_mat* xa,
+                       const oracle_mat* gate, const oracle_mat* up, const oracle_mat* down,
+                       const oracle_mat* sh_gate, const oracle_mat* sh_up,
+                       const oracle_mat* sh_down, const float* w_sg, int t, const int32_t* sel,
+                       const double* wt, double* a, double* y, double* o)
+{
+  int H = d->H;
+  mat_row(xa, 0, t, a);
+  for (int c = 0; c < H; ++c) o[c] = 0.0;
+  for (int j = 0; j < d->k; ++j) {
+    int el = sel[j] - d->e0;
+    if (el < 0 || el >= d->E_loc) continue;   /* not on this GPU: contributes nothing here */
+    oracle_ffn_row(d, d->I, a, gate, up, down, el, y);
+    for (int c = 0; c < H; ++c) o[c] += wt[j] * y[c];
+  }
+  if (d->I_s > 0) {
+    double gs = w_sg ? shared_gate_row(H, x, w_sg, t) : 1.0;
+    oracle_ffn_row(d, d->I_s, a, sh_gate, sh_up, sh_down, 0, y);
+    for (int c = 0; c < H; ++c) o[c] += gs * y[c];
+  }
+}
+
 void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, const float* bias,
                       const oracle_mat* xa, const oracle_mat* gate, const oracle_mat* up,
                       const oracle_mat* down, const oracle_mat* sh_gate, const oracle_mat* sh_up,
@@ -448,30 +472,38 @@ void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, co
     char* taken = (char*)malloc((size_t)E);
     double* a = (double*)malloc(sizeof(double) * (size_t)H);
     double* y = (double*)malloc(sizeof(double) * (size_t)H);
-    double* o = out + (size_t)i * H;
 
     oracle_logits(d->T, H, E, x, w_r, bias, 1, &t, L64, NULL);
     for (int e = 0; e < E; ++e) L32[e] = (float)L64[e];
     topk_row(E, k, L32, d->scoring, d->renormalize, sel, wt, taken);
+    expert_sum(d, x, xa, gate, up, down, sh_gate, sh_up, sh_down, w_sg, t, sel, wt, a, y,
+               out + (size_t)i * H);
 
-    mat_row(xa, 0, t, a);
-    for (int c = 0; c < H; ++c) o[c] = 0.0;
-    for (int j = 0; j < k; ++j) {
-      int el = sel[j] - d->e0;
-      if (el < 0 || el >= d->E_loc) continue;   /* not on this GPU: contributes nothing here */
-      oracle_ffn_row(d, d->I, a, gate, up, down, el, y);
-      for (int c = 0; c < H; ++c) o[c] += wt[j] * y[c];
-    }
-    if (d->I_s > 0) {
-      double gs = w_sg ? shared_gate_row(H, x, w_sg, t) : 1.0;
-      oracle_ffn_row(d, d->I_s, a, sh_gate, sh_up, sh_down, 0, y);
-      for (int c = 0; c < H; ++c) o[c] += gs * y[c];
-    }
     if (logits64) memcpy(logits64 + (size_t)i * E, L64, sizeof(double) * (size_t)E);
     if (logits32) memcpy(logits32 + (size_t)i * E, L32, sizeof(float) * (size_t)E);
     if (ids) memcpy(ids + (size_t)i * k, sel, sizeof(int32_t) * (size_t)k);
     if (w) memcpy(w + (size_t)i * k, wt, sizeof(double) * (size_t)k);
     free(L64); free(L32); free(sel); free(wt); free(taken); free(a); free(y);
+  }
+}
+
+void oracle_moe_layer_routed(const oracle_desc* d, const float* x, const oracle_mat* xa,
+                             const oracle_mat* gate, const oracle_mat* up,
+                             const oracle_mat* down, const oracle_mat* sh_gate,
+                             const oracle_mat* sh_up, const oracle_mat* sh_down,
+                             const float* w_sg, int n_tok, const int32_t* tok,
+                             const int32_t* ids, const float* w, double* out)
+{
+  int H = d->H, k = d->k;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < n_tok; ++i) {
+    double* wt = (double*)malloc(sizeof(double) * (size_t)k);
+    double* a = (double*)malloc(sizeof(double) * (size_t)H);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int j = 0; j < k; ++j) wt[j] = (double)w[(size_t)i * k + j];
+    expert_sum(d, x, xa, gate, up, down, sh_gate, sh_up, sh_down, w_sg, tok[i],
+               ids + (size_t)i * k, wt, a, y, out + (size_t)i * H);
+    free(wt); free(a); free(y);
   }
 }
 

@@ -139,6 +139,19 @@ void oracle_moe_layer(const oracle_desc* d, const float* x, const float* w_r, co
                       const int32_t* tok, double* out, double* logits64, float* logits32,
                       int32_t* ids, double* w);
 
+/* The expert part of the layer for a GIVEN routing: for i < n_tok, token t = tok[i] with chosen
+ * experts ids[i, 0..k) and weights w[i, 0..k) (fp32, used as given),
+ *   out[i] = sum_j w[i,j] * FFN_{ids[i,j]}(a_t) over local slots (j ascending)
+ *            + g_t * FFN_shared(a_t) if I_s > 0,
+ * with a_t and g_t as in oracle_moe_layer. Checks a GPU layer output on tokens whose routing the
+ * GPU's fp32 logits decided differently from the oracle's fp64 logits (a near tie). */
+void oracle_moe_layer_routed(const oracle_desc* d, const float* x, const oracle_mat* xa,
+                             const oracle_mat* gate, const oracle_mat* up,
+                             const oracle_mat* down, const oracle_mat* sh_gate,
+                             const oracle_mat* sh_up, const oracle_mat* sh_down,
+                             const float* w_sg, int n_tok, const int32_t* tok,
+                             const int32_t* ids, const float* w, double* out);
+
 /* ---- the grouped GEMM and the combine on their own ---------------------------------------------- */
 /* For each group g and row r in [offsets[g], offsets[g+1]): with a(r) = a_rows ? a_rows[r] / div : r,
  *   d_n = sum_k A(a(r), k) * B(g, n, k) (+ bias[n]);  out[r, n] = d_n            (B2 == NULL)

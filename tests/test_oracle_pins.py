@@ -225,6 +225,48 @@ def test_ffn_quantised_activations_mx8():
     assert np.allclose(y, hq @ wd32.T, rtol=1e-12, atol=1e-12)
 
 
+def _e2m1_rne_numpy(q):
+    """Nearest E2M1 magnitude with ties to the even code, saturating at 6, sign kept: the
+    grid has steps of 0.5 below 2, 1 in [2, 4) and 2 in [4, 6], and ties-to-even on the code
+    is half-to-even on the step count (numpy's rounding)."""
+    a = np.minimum(np.abs(q.astype(np.float64)), 6.0)
+    r = np.where(a < 2, np.round(a * 2) / 2, np.where(a < 4, np.round(a), np.round(a / 2) * 2))
+    return np.copysign(np.minimum(r, 6.0), q)
+
+
+def test_ffn_quantised_activations_mx4():
+    """h re-quantised to MXFP4 (1x32 groups along I, OCP MX v1.0): equals the dense FFN with h
+    passed through the scale rule floor(log2 amax) - 2 and round-to-nearest-even on the E2M1
+    grid, restated here in numpy. The gate rows get a magnitude per 32-column group (1e-3 .. 30)
+    so that a wrong group orientation changes the scales; a few h values are set on exact ties."""
+    rng = np.random.default_rng(25)
+    H, I = 64, 160
+    a = rng.standard_normal(H)
+    mag = np.repeat(np.array([1e-3, 30.0, 1.0, 0.07, 5.0]), 32)[:, None]
+    wg = (rng.standard_normal((I, H)) * 0.1 * mag).astype(np.float32)
+    wu = (rng.standard_normal((I, H)) * 0.1).astype(np.float32)
+    wd = (rng.standard_normal((H, I)) * 0.1).astype(np.float32)
+    M = oracle.Mat
+    y = oracle.ffn_row(a, M(oracle.F32, wg), M(oracle.F32, wu), M(oracle.F32, wd), act_fmt=oracle.MX4)
+    wg64, wu64, wd64 = (w.astype(np.float64) for w in (wg, wu, wd))
+    gg, uu = a @ wg64.T, a @ wu64.T
+    h = (gg * expit(gg) * uu).astype(np.float32)
+    hq = np.empty(I)
+    for b in range(0, I, 32):
+        blk = h[b:b + 32]
+        amax = float(np.abs(blk).max())
+        e = -127 if amax == 0 else int(np.clip(np.frexp(amax)[1] - 1 - 2, -127, 127))
+        q = (blk * np.float32(2.0 ** -e)).astype(np.float32)
+        hq[b:b + 32] = _e2m1_rne_numpy(q) * 2.0 ** e
+    assert np.allclose(y, hq @ wd64.T, rtol=1e-12, atol=1e-12)
+    # the restated rounding on the ties and neighbours of the grid (the oracle's own encoder)
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 5.9, 6.5, 100.0, 0.2, -0.25, -2.5,
+                     -5.0, -0.0], np.float32)
+    ref = _e2m1_rne_numpy(ties)
+    ours = np.array([oracle.e2m1_value(oracle.e2m1_encode(v)) for v in ties])
+    assert np.array_equal(np.abs(ours), np.abs(ref)) and np.array_equal(np.signbit(ours), np.signbit(ref))
+
+
 def test_grouped_gemm_mx8_equals_dequantised_matmul():
     rng = np.random.default_rng(24)
     K, N, T = 256, 96, 40
@@ -495,6 +537,36 @@ def test_layer_token_subset_and_permutation_equivariance():
     perm = np.random.default_rng(0).permutation(16)
     px = _run(desc, x[perm], wr, g, u, d, sh)
     assert np.allclose(px["out"], full["out"][perm], rtol=0, atol=1e-13)
+
+
+def test_layer_with_given_routing_equals_dense_loop():
+    """oracle_moe_layer_routed: the expert part for a routing handed in (arbitrary chosen experts,
+    some not local, arbitrary fp32 weights) equals the dense per-token loop in numpy; handed the
+    oracle's own routing it reproduces the layer up to the fp32 rounding of the weights."""
+    desc, x, wr, g, u, d, sh = _tiny(T=9, E=8, E_loc=4, e0=2, k=3, I_s=16)
+    M = oracle.Mat
+    mats = [M(oracle.F32, a) for a in (g, u, d)]
+    shared = tuple(M(oracle.F32, s) for s in sh)
+    rng = np.random.default_rng(5)
+    tok = np.array([8, 0, 4, 4], np.int32)
+    ids = np.stack([rng.permutation(8)[:3] for _ in tok]).astype(np.int32)
+    w = rng.random((len(tok), 3)).astype(np.float32)
+    out = oracle.moe_layer_routed(desc, x, M(oracle.F32, x), *mats, shared, tok, ids, w)
+    x64 = x.astype(np.float64)
+    for i, t in enumerate(tok):
+        ref = _dense_swiglu(x64[t:t + 1], *(s.astype(np.float64) for s in sh))[0]
+        for j in range(3):
+            el = ids[i, j] - 2
+            if 0 <= el < 4:
+                ref = ref + np.float64(w[i, j]) * _dense_swiglu(
+                    x64[t:t + 1], g[el].astype(np.float64), u[el].astype(np.float64),
+                    d[el].astype(np.float64))[0]
+        assert np.allclose(out[i], ref, rtol=1e-12, atol=1e-12)
+    full = _run(desc, x, wr, g, u, d, sh)
+    allt = np.arange(9, dtype=np.int32)
+    again = oracle.moe_layer_routed(desc, x, M(oracle.F32, x), *mats, shared, allt, full["ids"],
+                                    full["w"].astype(np.float32))
+    assert np.allclose(again, full["out"], rtol=1e-6, atol=1e-6 * np.abs(full["out"]).max())
 
 
 def test_ffn_quantised_activations_fp8():
