@@ -41,7 +41,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
     p.add_argument("--all-workloads", action="store_true",
-                   help="add every workload's layer time and both roofline fractions")
+                   help="(default) add every workload's layer time and both roofline fractions")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the table of every workload's layer time and roofline fractions")
     p.add_argument("--workloads", default=None,
                    help="comma-separated names: the workload table for these only")
     p.add_argument("--no-ep-sweep", action="store_true",
@@ -367,6 +369,17 @@ def layer_flops(wl, R):
     return 2.0 * wl.T * wl.H * wl.E + 6.0 * R * wl.H * wl.I + 6.0 * wl.T * wl.H * wl.I_s
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(L, target_s):
     import oracle
     wl = L.wl
@@ -386,6 +399,7 @@ def cpu_baseline(L, target_s):
             break
         n = int(min(wl.T, max(n * 2, n * target_s / max(dt, 1e-3) * 0.9)))
     return dict(value=n / dt, unit="tokens/s", cores=oracle.num_threads(), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"{n} random tokens of the same {wl.T}-token layer (routing, all local "
                        f"experts of each token, combine), fp64, {dt:.1f} s")
 
@@ -474,6 +488,9 @@ def main():
                      "traffic": None if traffic is None else round(sum(traffic)),
                      "traffic_read_bytes": None if traffic is None else round(traffic[0]),
                      "traffic_write_bytes": None if traffic is None else round(traffic[1]),
+                     "traffic_source": "committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary "
+                                       "(profiles/gate_up_traffic.json) of the same kernel "
+                                       "sources, not this run",
                      "flops_per_launch": flops_gu,
                      "avg_launch_ms": round(steps_ms["gemm_gate_up"], 4)},
         "steps_ms": {k: round(v, 4) for k, v in steps_ms.items()},
@@ -529,7 +546,7 @@ def main():
         del D, flush
     if not args.no_ep_sweep:
         result["decode_one_token_per_expert"] = ep_sweep(stream, max(5, min(args.steps, 20)))
-    if args.all_workloads or args.workloads:
+    if not args.no_workloads or args.workloads:
         names = args.workloads.split(",") if args.workloads else None
         result["workloads"] = workload_table(stream, max(5, min(args.steps, 20)), names)
     if args.cpu_seconds > 0:

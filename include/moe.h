@@ -86,7 +86,10 @@ typedef struct {
   int32_t E_loc;        /* local experts, e0 + E_loc <= E                                      */
   int32_t I;            /* expert intermediate size                                            */
   int32_t k;            /* experts per token, 1 <= k <= min(E, 16)                             */
-  int32_t I_s;          /* shared expert intermediate size, 0 = no shared expert               */
+  int32_t I_s;          /* shared expert intermediate size, 0 = no shared expert; any multiple
+                           of the expert format's K granularity (64 bf16 / fp32, 128 fp8 and
+                           MXFP8, 256 MXFP4). I_s == I runs the shared expert inside the routed
+                           experts' GEMM launches, other sizes in launches of their own        */
   int32_t scoring;      /* moe_scoring                                                         */
   int32_t renormalize;  /* 1: weights renormalised over the k chosen experts                   */
   int32_t io_dtype;     /* x and the router weight: MOE_F32 or MOE_BF16                        */
@@ -120,6 +123,11 @@ typedef struct {
 } moe_weights;
 
 /* ---- routing (router logits, scores, top-k, renormalisation) ---------------------------------
+ * Defining passages: "How we served a 397B MoE model with 4.7x speedup on TPU v7", section on the
+ * architectural constraints (top-10 of 512 experts) and "Three collectives become two" (the
+ * routing result is an int index array and a float weight array, both [T, k]); "Hosting Qwen on
+ * Blackwell", section "Prefillers" (top-8 of 128). The router function itself (softmax or sigmoid
+ * with renormalisation) is not on the pages; it is the layer configuration's.
  * If x != NULL: logits[T,E] = x . w_router^T + bias (fp32 accumulation) are written, then used.
  * If x == NULL: logits[T,E] (fp32) are read as given and w_router is ignored.
  * topk_ids[T,k] (int32, global ids, rank order: topk_ids[t,0] is the largest logit; equal values
@@ -142,6 +150,11 @@ size_t moe_route_workspace_bytes(const moe_desc* d);
 int64_t moe_routing_blob_plane(const moe_desc* d);
 
 /* ---- dispatch (count, offsets, unique row per local slot, copy) ------------------------------
+ * Defining passage: "CuTeDSL at Perplexity", section "MoE dispatch and combine", local kernel:
+ * count the tokens of each expert, give each token a unique index within its expert, copy the
+ * tokens into the expert buffers; "Hosting Qwen on Blackwell", section "Expert parallel": the
+ * dispatch prepares the tokens routed to this rank's experts as the MoE GEMM's input. The order
+ * inside an expert is fixed here (ascending flat slot) where the pages use atomic counters.
  * counts[E_loc]: local slots per expert. offsets[E_loc+1]: exclusive prefix sum, offsets[E_loc] = R.
  * slot_to_row[T,k]: row of slot (t,j) in the expert-contiguous buffer, -1 if e_tj is not local.
  * row_to_flat[T*k]: flat slot t*k+j of each row (entries >= R untouched).
@@ -161,6 +174,11 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a
 size_t moe_permute_workspace_bytes(const moe_desc* d);
 
 /* ---- grouped GEMM ------------------------------------------------------------------------------
+ * Defining passages: "Hosting Qwen on Blackwell", sections "Prefillers" (every expert's tokens
+ * form one dense GEMM problem) and "MoE GEMM" (the grouped expert GEMM, decode-limited by loading
+ * the weights); "Driving vLLM WideEP and Large-Scale Serving Toward Maturity on Blackwell
+ * (Part I)", section on lower-precision operations (4-bit weights with per-group scales,
+ * dequantised inside the GEMM). SwiGLU (silu(gate) * up) is the layer configuration's.
  * For every group g with rows [group_offsets[g], group_offsets[g+1]) (device array, ascending,
  * group_offsets[G] <= max_rows):
  *   STORE:  C[r, :N]  = A[a(r), :K] . B[g]^T                       (B[g]: [N, K])
@@ -190,6 +208,10 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
                             void* C, void* C_scales, hipStream_t stream);
 
 /* ---- combine (weighted un-permute) -------------------------------------------------------------
+ * Defining passages: "CuTeDSL at Perplexity", section "MoE dispatch and combine": the combine
+ * accumulates each token's weighted expert rows using the routing information and the offsets
+ * the dispatch computed; "Hosting Qwen on Blackwell", section "Expert parallel": the local
+ * contributions are summed first, before the cross-rank reduction (outside this library).
  * out[t, :] = sum_{j ascending, slot_to_row[t,j] >= 0} topk_w[t,j] * y[slot_to_row[t,j], :]
  *             (+ g_t * shared[t, :] if shared != NULL, g_t = shared_w[t], or 1 when shared_w is
  *             NULL), accumulated in fp32, rounded once to out_dtype.
@@ -210,6 +232,11 @@ moe_status moe_shared_gate(const moe_desc* d, const void* x, const void* w_share
                            float* shared_w, hipStream_t stream);
 
 /* ---- activation / weight quantiser -------------------------------------------------------------
+ * Defining passages: "Hosting Qwen on Blackwell", section "Quantization" (block scaling as used for
+ * DeepSeek-style models; MXFP8 for the MoE GEMMs); "CuTeDSL at Perplexity", section "Blackwell"
+ * (scales from the absolute maximum of each small element group); "Driving vLLM WideEP and
+ * Large-Scale Serving Toward Maturity on Blackwell (Part I)", lower-precision operations
+ * (activations quantised before dispatch). The number formats are OCP 8-bit FP and OCP MX v1.0.
  * src [rows, cols] (src_dtype MOE_F32 or MOE_BF16) -> dst_dtype:
  *   MOE_FP8_E4M3: codes [rows, cols]; one fp32 scale per block_rows x 128 block
  *                 (scales [ceil(rows/block_rows), cols/128]): s = amax/448 (1 if amax = 0),
@@ -229,6 +256,12 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
                         void* scales, hipStream_t stream);
 
 /* ---- the whole layer ---------------------------------------------------------------------------
+ * Defining passages: the steps above in the pages' order, route -> dispatch -> MoE GEMM ->
+ * combine ("Hosting Qwen on Blackwell", section "Expert parallel"; "CuTeDSL at Perplexity",
+ * section "MoE dispatch and combine"), plus the always-active shared expert of "How we served a
+ * 397B MoE model with 4.7x speedup on TPU v7" (architectural constraints). The decode or prefill
+ * kernel variants are chosen inside from the table sizes, as "CuTeDSL at Perplexity" chooses its
+ * dispatch kernels (section on grid synchronisation).
  * Routing, dispatch, expert GEMMs (gate/up with the SwiGLU epilogue, then down), shared expert and
  * combine, all enqueued on `stream` with no host synchronisation. x [T, H] is io_dtype, out [T, H]
  * is out_dtype. logits [T,E], topk_ids [T,k], topk_w [T,k] are optional outputs (NULL: kept in the
@@ -237,7 +270,7 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
  * Intermediate formats: h (the down projection's input) is in the expert format (bf16 for bf16
  * experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for
  * fp8/MXFP4/MXFP8.
- * Requires I_s == 0 or I_s == I. ws: moe_layer_workspace_bytes(d) bytes. */
+ * ws: moe_layer_workspace_bytes(d) bytes. */
 moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, const float* bias,
                      void* out, float* logits, int32_t* topk_ids, float* topk_w, void* ws,
                      size_t ws_bytes, hipStream_t stream);

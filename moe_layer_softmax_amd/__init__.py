@@ -178,3 +178,4 @@ def moe_layer(d, weights, x, bias, out, logits, topk_ids, topk_w, ws, stream=Non
     _check(_lib.moe_layer(ctypes.byref(d), ctypes.byref(weights), _ptr(x), _ptr(bias), _ptr(out),
                           _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes,
                           _stream(stream)), "moe_layer")
+

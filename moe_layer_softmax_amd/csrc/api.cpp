@@ -96,7 +96,7 @@ moe_status check_expert_shapes(const moe_desc* d) {
   if (dt != MOE_F32 && d->io_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   const int align = k_align(dt);
   if (d->H % align || d->I % align || (d->I_s && d->I_s % align)) return MOE_ERR_INVALID_ARG;
-  if (d->I % 64 || d->H % 64) return MOE_ERR_INVALID_ARG;
+  if (d->I % 64 || d->H % 64 || d->I_s % 64) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -122,14 +122,22 @@ size_t route_ws(const moe_desc* d) { return router_fast(d) ? router_ws_bytes(d->
 
 // ---- layer workspace layout (identical in the size query and in moe_layer) ----------------------
 struct LayerWs {
-  size_t logits, ids, w, rpart, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, y, sw, total;
+  size_t logits, ids, w, rpart, counts, offsets, s2r, r2f, perm, xq, xs, h, hs, hsh, hshs, y, sw,
+      total;
 };
+
+// The shared expert runs as an extra group inside the routed experts' GEMM launches when its
+// intermediate size equals theirs (one N for all groups); otherwise in launches of its own, with
+// its h in a separate [T, I_s] buffer.
+bool shared_fused(const moe_desc* d) { return d->I_s > 0 && d->I_s == d->I; }
+bool shared_apart(const moe_desc* d) { return d->I_s > 0 && d->I_s != d->I; }
 
 LayerWs layer_ws(const moe_desc* d) {
   LayerWs L{};
   const size_t T = d->T, k = d->k, E = d->E, H = d->H, I = d->I;
   const size_t slots = T * k;
-  const size_t rows = slots + (d->I_s ? T : 0);
+  const size_t rows = slots + (shared_fused(d) ? T : 0);
+  const size_t Is = shared_apart(d) ? d->I_s : 0;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o += round_up(bytes); return at; };
   L.logits = take(T * E * 4);
@@ -147,15 +155,21 @@ LayerWs layer_ws(const moe_desc* d) {
     L.xs = take((T + 127) / 128 * (H / 128) * 4);
     L.h = take(rows * I);
     L.hs = take(rows * (I / 128) * 4);
+    L.hsh = take(T * Is);
+    L.hshs = take(T * (Is / 128) * 4);
   } else if (mx_format(dt)) {
     L.xq = take(row_bytes(dt, H) * T);
     L.xs = take(T * (H / 32));
     L.h = take(row_bytes(dt, I) * rows);
     L.hs = take(rows * (I / 32));
+    L.hsh = take(row_bytes(dt, Is) * T);
+    L.hshs = take(T * (Is / 32));
   } else {
     L.h = take(rows * I * io_bytes(d->io_dtype));
+    L.hsh = take(T * Is * io_bytes(d->io_dtype));
   }
-  L.y = take(rows * H * io_bytes(y_dtype_of(d)));
+  // y: routed rows, then (with a shared expert) its T rows
+  L.y = take((slots + (d->I_s ? T : 0)) * H * io_bytes(y_dtype_of(d)));
   L.sw = take(d->I_s ? T * 4 : 0);
   L.total = o;
   return L;
@@ -412,7 +426,6 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   if (!w) return MOE_ERR_INVALID_ARG;
   st = check_expert_shapes(d);
   if (st != MOE_OK) return st;
-  if (d->I_s != 0 && d->I_s != d->I) return MOE_ERR_UNSUPPORTED;
   if (d->T == 0) return MOE_OK;
   const bool quant = quantised(d->expert_dtype);
   if (!ok_ptr(x) || !ok_ptr(out) || !ok_ptr(w->w_router) || !ok_ptr(w->w_gate) ||
@@ -502,7 +515,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   a.B2s = w->w_up_scales;
   a.b_stride = row_bytes(dt, H) * (long long)I;
   a.bs_stride = scale_bytes(dt, I, H);
-  if (d->I_s) {
+  if (shared_fused(d)) {
     a.x_rows = T;
     a.x_row0 = slots;
     a.x_a_off = slots;
@@ -516,6 +529,31 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   a.c_pitch = quant ? row_bytes(dt, I) : (long long)I * io_bytes(io);
   st = hip_status(launch_gemm(a, stream));
   if (st != MOE_OK) return st;
+  const long long hsh_pitch = quant ? row_bytes(dt, d->I_s) : (long long)d->I_s * io_bytes(io);
+  if (shared_apart(d)) {
+    // the shared expert alone: no routed groups, one extra group of T rows in token order
+    GemmArgs sa = a;
+    sa.N = d->I_s;
+    sa.a_rows = nullptr;
+    sa.a_row_div = 1;
+    sa.G = 0;
+    sa.offsets = nullptr;
+    sa.max_rows = 0;
+    sa.expected_rows = 0;
+    sa.B = sa.B2 = sa.Bs = sa.B2s = nullptr;
+    sa.x_rows = T;
+    sa.x_row0 = 0;
+    sa.x_a_off = 0;
+    sa.xB = w->sh_gate;
+    sa.xBs = w->sh_gate_scales;
+    sa.xB2 = w->sh_up;
+    sa.xB2s = w->sh_up_scales;
+    sa.C = base + L.hsh;
+    sa.C_scales = quant ? base + L.hshs : nullptr;
+    sa.c_pitch = hsh_pitch;
+    st = hip_status(launch_gemm(sa, stream));
+    if (st != MOE_OK) return st;
+  }
 
   // 5. down GEMM: y rows = h rows
   const int ydt = y_dtype_of(d);
@@ -538,7 +576,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   b.Bs = w->w_down_scales;
   b.b_stride = row_bytes(dt, I) * (long long)H;
   b.bs_stride = scale_bytes(dt, H, I);
-  if (d->I_s) {
+  if (shared_fused(d)) {
     b.x_rows = T;
     b.x_row0 = slots;
     b.x_a_off = 0;
@@ -549,6 +587,26 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   b.c_pitch = (long long)H * io_bytes(ydt);
   st = hip_status(launch_gemm(b, stream));
   if (st != MOE_OK) return st;
+  if (shared_apart(d)) {
+    // shared rows of y (rows slots .. slots + T) from the shared h [T, I_s]
+    GemmArgs sb = b;
+    sb.K = d->I_s;
+    sb.A = base + L.hsh;
+    sb.A_scales = quant ? base + L.hshs : nullptr;
+    sb.a_pitch = hsh_pitch;
+    sb.G = 0;
+    sb.offsets = nullptr;
+    sb.max_rows = 0;
+    sb.expected_rows = 0;
+    sb.B = sb.Bs = nullptr;
+    sb.x_rows = T;
+    sb.x_row0 = slots;
+    sb.x_a_off = slots;
+    sb.xB = w->sh_down;
+    sb.xBs = w->sh_down_scales;
+    st = hip_status(launch_gemm(sb, stream));
+    if (st != MOE_OK) return st;
+  }
 
   // 6. combine (+ shared expert rows, times their per-token gate when the layer has one)
   const void* shared = d->I_s ? base + L.y + (size_t)slots * H * io_bytes(ydt) : nullptr;

@@ -6,8 +6,11 @@
 // quantised to 4 bits before dispatch ("Driving vLLM WideEP ... on Blackwell (Part I)", section on
 // lower-precision operations); absmax over 32 elements for the MX formats ("CuTeDSL at
 // Perplexity", Blackwell section). Element formats and the MX scale rule follow the OCP 8-bit FP
-// and OCP MX v1.0 specifications. The conversions are written out in integer/compare form so the
-// codes are exactly round-to-nearest-even, independent of any hardware conversion mode.
+// and OCP MX v1.0 specifications. Codes come from gfx950's packed conversions (v_cvt_pk_fp8_f32 on
+// operands clamped to +-448, v_cvt_scalef32_pk_fp4_f32 with a unit scale), which round to nearest
+// even in the default rounding mode; quant_dev.hpp also keeps the integer/compare encoders they were
+// checked against bit for bit, and the GPU tests compare the codes with the oracle's on every grid
+// value, tie, neighbour, subnormal, +-0 and the 440..620 saturation range.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_dev.hpp"

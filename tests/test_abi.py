@@ -128,10 +128,10 @@ def test_workspace_too_small_and_unsupported():
     st = lib.moe_layer(ctypes.byref(d3), ctypes.byref(w), ok, None, ok, None, None, None, ok,
                        1 << 40, None)
     assert st == m.MOE_ERR_UNSUPPORTED
-    d4 = _desc(I_s=256)                                    # shared size must equal I here
+    d4 = _desc(I_s=96)                                     # shared size off the 64-column grid
     st = lib.moe_layer(ctypes.byref(d4), ctypes.byref(w), ok, None, ok, None, None, None, ok,
                        1 << 40, None)
-    assert st == m.MOE_ERR_UNSUPPORTED
+    assert st == m.MOE_ERR_INVALID_ARG
 
 
 def test_zero_tokens_is_a_no_op():

@@ -47,11 +47,29 @@ def test_grouped_gemm_quant_decode_short_k(fmt, epi):
     _quant_case(fmt, epi, [5, 0, 31, 2], 256)
 
 
-def _quant_case(fmt, epi, counts, K):
+# narrow and short shapes: 128 h-columns (fewer than one 256-row B tile of gate + up) on the wide
+# MX tiles (one group of 700 rows), the 128-row tiles (groups of ~175) and the streaming kernel;
+# stores with one and two K-steps on the 128-row tiles
+@pytest.mark.parametrize("fmt", ["fp8", "mx4", "mx8"])
+@pytest.mark.parametrize("epi,counts,K,N", [("swiglu_q", [700], 512, 128),
+                                            ("swiglu_bf16", [700], 512, 128),
+                                            ("swiglu_q", [175, 170, 180, 176], 512, 128),
+                                            ("swiglu_q", [5, 30, 1], 512, 128),
+                                            ("store_bf16", [700], 128, 512),
+                                            ("store_bf16", [175, 170, 180, 176], 256, 512),
+                                            ("store_f32", [700], 128, 512)])
+def test_grouped_gemm_quant_narrow_shapes(fmt, epi, counts, K, N):
+    if fmt == "mx4" and K % 256:
+        pytest.skip("MXFP4 K-steps are 256 elements")
+    _quant_case(fmt, epi, counts, K, N)
+
+
+def _quant_case(fmt, epi, counts, K, N=None):
     dfmt, ofmt = FMTS[fmt]
     rng = np.random.default_rng([len(counts), sum(counts)])
     swiglu = epi.startswith("swiglu")
-    N = 256 if swiglu else 384                 # 384: a partial 256-column tile
+    if N is None:
+        N = 256 if swiglu else 384             # 384: a partial 256-column tile
     G = len(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     R = int(off[-1])

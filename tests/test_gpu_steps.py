@@ -9,7 +9,7 @@ import moe_layer_softmax_amd as moe
 import oracle
 from moe_inputs import gen
 
-from gpu_util import (gamma, rel_err, routing_consistent, to_dev, topk_numpy)
+from gpu_util import (gamma, gpu_quant, rel_err, routing_consistent, to_dev, topk_numpy)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,6 +84,67 @@ def test_quantize_mx8_bitexact(rows, cols, src):
         c_ref, s_ref = oracle.quant_mx8(a[b])
         assert np.array_equal(scales[b].cpu().numpy(), s_ref)
         assert np.array_equal(codes[b].cpu().numpy(), c_ref)
+
+
+def _edge_values(grid):
+    """Every grid value with both signs, the midpoints of neighbouring grid values (exact ties),
+    the fp32 neighbours of each midpoint and of each grid value, and +-0."""
+    g = np.unique(np.concatenate([grid, -grid])).astype(np.float32)
+    mids = ((g[1:].astype(np.float64) + g[:-1]) / 2).astype(np.float32)
+    vals = [g, mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf)),
+            np.nextafter(g, np.float32(np.inf)), np.nextafter(g, np.float32(-np.inf)),
+            np.array([0.0, -0.0], np.float32)]
+    return np.concatenate(vals).astype(np.float32)
+
+
+def _pack_groups(vals, group, anchor):
+    """Rows of `group`-element blocks, each block led by `anchor` (which fixes a unit scale) and
+    filled with test values; the last block is padded with zeros."""
+    per = group - 1
+    n = (len(vals) + per - 1) // per
+    v = np.zeros(n * per, np.float32)
+    v[:len(vals)] = vals
+    blocks = np.concatenate([np.full((n, 1), anchor, np.float32), v.reshape(n, per)], axis=1)
+    return blocks.reshape(-1)
+
+
+# The quantisers on the values where rounding decisions are made: every e4m3 / e2m1 grid value,
+# every tie between neighbours, their fp32 neighbours, subnormals, +-0 and the saturation range
+# 440..620. Blocks are led by the value that makes the scale exactly 1 (448 for fp8's amax / 448
+# and for MXFP8's floor(log2 amax) - 8; 6 for MXFP4's floor(log2 amax) - 2), so every test value
+# is itself the quotient that is rounded; a second set runs with the natural scales.
+@pytest.mark.parametrize("fmt", ["fp8", "mx8", "mx4"])
+def test_quantize_edge_values_bitexact(fmt):
+    if fmt == "mx4":
+        grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float32)
+        anchor, group, cols = 6.0, 32, 256
+    else:
+        codes = np.arange(0x7F, dtype=np.uint8)                  # every finite non-negative e4m3
+        grid = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+        anchor, group, cols = 448.0, (128 if fmt == "fp8" else 32), 256
+    vals = _edge_values(grid)
+    sat = np.linspace(440.0, 620.0, 361, dtype=np.float32)      # around and beyond the maximum
+    if fmt == "mx4":
+        sat = sat / np.float32(448.0 / 6.0)
+    vals = np.concatenate([vals, sat, -sat])
+    flat = _pack_groups(vals, group, anchor)
+    flat = np.concatenate([flat, np.zeros((-len(flat)) % cols, np.float32)])
+    a_unit = flat.reshape(-1, cols)
+    # the same values without the anchors: block scales follow from each block's own maximum
+    free = np.concatenate([vals, np.zeros((-len(vals)) % cols, np.float32)]).reshape(-1, cols)
+    dfmt = {"fp8": moe.MOE_FP8_E4M3, "mx8": moe.MOE_MXFP8, "mx4": moe.MOE_MXFP4}[fmt]
+    for a in (a_unit, free):
+        rows = a.shape[0]
+        block_rows = 1
+        q, sc = gpu_quant(dfmt, a, block_rows)
+        if fmt == "fp8":
+            c_ref, s_ref = oracle.quant_fp8(a, block_rows, 128)
+        elif fmt == "mx8":
+            c_ref, s_ref = oracle.quant_mx8(a)
+        else:
+            c_ref, s_ref = oracle.quant_mx4(a)
+        assert np.array_equal(sc[0].cpu().numpy(), s_ref), rows
+        assert np.array_equal(q[0].cpu().numpy(), c_ref), rows
 
 
 # ---------------------------------------------------------------------------------------------
@@ -192,6 +253,75 @@ def test_permute_bitexact(T, E, k, e0, E_loc, hot):
     assert np.all(r2f_g[R:] == -7)                      # rows >= R untouched
     ap = a_perm.float().cpu().numpy()
     assert np.array_equal(ap[:R], x[r_ref // k])         # bytes of the gathered rows
+
+
+# the quantised row copy of the dispatch: codes and scales of x (quantised in token order) moved to
+# expert-contiguous rows. fp8 carries the 128x128 block scale row of each token (T not a multiple
+# of 128: a partial last block), MXFP4 / MXFP8 the E8M0 row of the token. Tables up to 16384 slots
+# take the one-workgroup dispatch, larger ones the split count / scan / scatter kernels. The
+# permuted rows then feed the grouped GEMM (per-row scales, no gather), which must give the same
+# bytes as the GEMM gathering the rows of x itself.
+@pytest.mark.parametrize("fmt", ["fp8", "mx4", "mx8"])
+@pytest.mark.parametrize("T,E,k,E_loc", [(333, 64, 8, 16), (2500, 128, 8, 32)])
+def test_permute_quantised_rows(fmt, T, E, k, E_loc):
+    from gpu_util import FMTS, oracle_quant
+    dfmt, ofmt = FMTS[fmt]
+    H = 512
+    rng = np.random.default_rng([T, E, dfmt])
+    x = gen.bf16_round(rng.standard_normal((T, H)).astype(np.float32))
+    x[:, 64:128] *= 40.0                                   # distinct block / group scales
+    ids_np = gen.random_topk_ids(T, E, k, seed=T, hot=[0, 1], hot_frac=0.3)
+    blk = 128 if fmt == "fp8" else 1
+    xq, xs = gpu_quant(dfmt, x, blk)
+    xq, xs = xq[0], xs[0]
+    ref_q = oracle_quant(ofmt, x, blk)
+    assert np.array_equal(xq.cpu().numpy(), ref_q.q[0]) and np.array_equal(xs.cpu().numpy(), ref_q.s[0])
+    d = moe.make_desc(T, H, E, 0, E_loc, 256, k, 0, 1, 1, moe.MOE_BF16, dfmt)
+    ws = torch.empty(max(moe.moe_permute_workspace_bytes(d), 16), dtype=torch.uint8, device="cuda")
+    counts = torch.empty(E_loc, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E_loc + 1, dtype=torch.int32, device="cuda")
+    s2r = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    r2f = torch.full((T * k,), -7, dtype=torch.int32, device="cuda")
+    rb = H // 2 if fmt == "mx4" else H
+    a_perm = torch.full((T * k, rb), 0xA5, dtype=torch.uint8, device="cuda")
+    if fmt == "fp8":
+        a_ps = torch.full((T * k, H // 128), -3.0, dtype=torch.float32, device="cuda")
+    else:
+        a_ps = torch.full((T * k, H // 32), 0xA5, dtype=torch.uint8, device="cuda")
+    moe.moe_permute(d, to_dev(ids_np, torch.int32), xq, xs, counts, offsets, s2r, r2f, a_perm,
+                    a_ps, ws)
+    _sync()
+    c_ref, o_ref, s_ref, r_ref = oracle.permute(ids_np, 0, E_loc)
+    R = len(r_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(r2f.cpu().numpy()[:R], r_ref)
+    tok_of_row = r_ref // k
+    ap, ps = a_perm.cpu().numpy(), a_ps.cpu().numpy()
+    assert np.array_equal(ap[:R], ref_q.q[0][tok_of_row])
+    if fmt == "fp8":
+        assert np.array_equal(ps[:R], ref_q.s[0][tok_of_row // 128])
+    else:
+        assert np.array_equal(ps[:R], ref_q.s[0][tok_of_row])
+    assert np.all(ap[R:] == 0xA5)                           # rows past R untouched
+    # the permuted rows as the GEMM input (one scale row per row) against the gathering GEMM
+    N = 256
+    B = (rng.standard_normal((E_loc, N, H)) * 0.05).astype(np.float32)
+    bq, bs = gpu_quant(dfmt, B, 128)
+    outs = []
+    for gather in (False, True):
+        g = moe.moe_gemm_desc(E_loc, T * k, H, N, dfmt, moe.MOE_EPI_STORE, moe.MOE_F32,
+                              k if gather else 1, blk if gather else 1)
+        C = torch.full((T * k, N), 1024.0, dtype=torch.float32, device="cuda")
+        if gather:
+            moe.moe_grouped_gemm(g, xq, xs, r2f, bq, bs, None, None, offsets, C, None)
+        else:
+            moe.moe_grouped_gemm(g, a_perm, a_ps, None, bq, bs, None, None, offsets, C, None)
+        _sync()
+        outs.append(C.cpu().numpy())
+    assert np.array_equal(outs[0][:R], outs[1][:R])
+    ref = oracle.grouped_gemm(o_ref, ref_q, oracle_quant(ofmt, B, 128), a_rows=r_ref, a_row_div=k)
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.abs(outs[0][:R] - ref).max() <= 2e-3 * rms
 
 
 def test_permute_no_local_rows():
@@ -340,7 +470,7 @@ def test_grouped_gemm_f32(swiglu):
 # top-8 of 128), E_loc / 8 tokens with token t routed to local experts 8t .. 8t+7, run through the
 # public steps (dispatch maps, gate/up GEMM gathering x, down GEMM, combine) and compared with the
 # oracle's dense per-token loop over the chosen experts (h rounded to bf16, as the layer does).
-@pytest.mark.parametrize("E_loc", [8, 16])
+@pytest.mark.parametrize("E_loc", [8, 16, 32, 64])
 def test_one_token_per_expert_decode(E_loc):
     H, I, E, k = 4096, 1536, 128, 8
     T = E_loc // k
