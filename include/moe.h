@@ -276,6 +276,22 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
                      size_t ws_bytes, hipStream_t stream);
 size_t moe_layer_workspace_bytes(const moe_desc* d);
 
+/* ---- the whole layer without a caller workspace --------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): moe_layer with the workspace taken from a fixed device
+ * array of MOE_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the process ends.
+ * Arguments and results are those of moe_layer (inputs and outputs are still the caller's). Layers
+ * whose moe_layer_workspace_bytes(d) exceeds MOE_NOALLOC_SCRATCH_BYTES (decode-sized layers fit;
+ * e.g. 64 tokens of the Qwen3-235B slice need ~10 MiB) return MOE_ERR_WORKSPACE before anything is
+ * launched. No device memory is allocated or freed. Every call on one GPU uses that GPU's array:
+ * calls that overlap on one GPU (several streams, or host threads) race and must be ordered by the
+ * caller. The array keeps the last call's contents; the layer writes every workspace byte it reads
+ * within the call, so nothing needs clearing between calls. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_layer_noalloc(const moe_desc* d, const moe_weights* w, const void* x,
+                             const float* bias, void* out, float* logits, int32_t* topk_ids,
+                             float* topk_w, hipStream_t stream);
+
 const char* moe_status_str(moe_status s);
 int32_t moe_last_hip_error(void);     /* hipError_t of the calling thread's last failed launch */
 

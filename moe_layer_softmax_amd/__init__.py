@@ -70,6 +70,7 @@ _lib.moe_routing_blob_plane.restype = ctypes.c_int64
 _lib.moe_quantize.argtypes = [ctypes.c_int32] * 6 + [_P, _P, _P, _P]
 _lib.moe_layer.argtypes = [_D, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P, _P, _P,
                            ctypes.c_size_t, _P]
+_lib.moe_layer_noalloc.argtypes = [_D, ctypes.POINTER(moe_weights), _P, _P, _P, _P, _P, _P, _P]
 _lib.moe_layer_workspace_bytes.argtypes = [_D]
 _lib.moe_layer_workspace_bytes.restype = ctypes.c_size_t
 for _f in ("moe_route", "moe_permute", "moe_grouped_gemm", "moe_combine", "moe_shared_gate",
@@ -179,3 +180,12 @@ def moe_layer(d, weights, x, bias, out, logits, topk_ids, topk_w, ws, stream=Non
                           _ptr(logits), _ptr(topk_ids), _ptr(topk_w), _ptr(ws), nbytes,
                           _stream(stream)), "moe_layer")
 
+
+# bytes of the library's per-GPU scratch array behind moe_layer_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_layer_noalloc(d, weights, x, bias, out, logits, topk_ids, topk_w, stream=None):
+    _check(_lib.moe_layer_noalloc(ctypes.byref(d), ctypes.byref(weights), _ptr(x), _ptr(bias),
+                                  _ptr(out), _ptr(logits), _ptr(topk_ids), _ptr(topk_w),
+                                  _stream(stream)), "moe_layer_noalloc")

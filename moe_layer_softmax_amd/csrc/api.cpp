@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
@@ -220,6 +221,33 @@ moe_status run_route(const moe_desc* d, const void* x, const void* w_router, con
   }
   return hip_status(launch_topk(d->T, d->E, d->k, d->scoring, d->renormalize, logits, partial, ns,
                                 ns > 1 ? bias : nullptr, ids, w, s));
+}
+
+// Device scratch of the allocation-free layer entry point: one array per GPU the library runs on,
+// kept until the process ends. Its name in host code is only a stand-in for the device symbol;
+// host code uses the device address obtained once per device with hipGetSymbolAddress.
+__device__ __align__(256) static unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of the current device's scratch array (looked up on the device's first call)
+moe_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (!ptr) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -618,6 +646,20 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   }
   return hip_status(launch_combine(T, H, k, ydt, d->out_dtype, base + L.y, tw, s2r, shared, sw,
                                    out, stream));
+}
+
+moe_status moe_layer_noalloc(const moe_desc* d, const moe_weights* w, const void* x,
+                             const float* bias, void* out, float* logits, int32_t* topk_ids,
+                             float* topk_w, hipStream_t stream) {
+  moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->T == 0) return moe_layer(d, w, x, bias, out, logits, topk_ids, topk_w, nullptr, 0, stream);
+  if (layer_ws(d).total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != MOE_OK) return st;
+  return moe_layer(d, w, x, bias, out, logits, topk_ids, topk_w, ws, MOE_NOALLOC_SCRATCH_BYTES,
+                   stream);
 }
 
 }  // extern "C"
