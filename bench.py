@@ -54,23 +54,22 @@ def parse():
 PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3}
 
 
-def workload_table(stream, steps, names=None):
-    """Layer time of every workload (one moe_layer call per step, caches evicted with a 1 GiB read
-    before each), with the algorithmic MFMA and HBM roofline fractions. Tokens, router weight and
-    bias are the seeded inputs; expert weights are seeded device draws of the same shapes (their
-    values do not change the work), quantised by the library for the fp8 / MXFP4 layers."""
-    import torch
-    import moe_inputs as mi
-    import moe_layer_softmax_amd as moe
-    from moe_inputs import gen
-    fmt_of = {mi.FMT_BF16: ("bf16", moe.MOE_BF16), mi.FMT_FP8: ("fp8", moe.MOE_FP8_E4M3),
-              mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8)}
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    out = {}
-    for name in names or ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
-                          "C2p_mx8", "C2d_mx8"):
-        wl = mi.WORKLOADS[name]
+class TableLayer:
+    """One workload's layer call for the workload table and the profiler runs: tokens, router
+    weight and bias are the seeded inputs; expert weights are seeded device draws of the same
+    shapes (their values do not change the work), quantised by the library for the fp8 / MXFP4 /
+    MXFP8 layers."""
+
+    def __init__(self, wl, stream):
+        import torch
+        import moe_inputs as mi
+        import moe_layer_softmax_amd as moe
+        from moe_inputs import gen
+        fmt_of = {mi.FMT_BF16: ("bf16", moe.MOE_BF16), mi.FMT_FP8: ("fp8", moe.MOE_FP8_E4M3),
+                  mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8)}
+        self.wl = wl
         fname, fcode = fmt_of[wl.fmt]
+        self.fname = fname
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(torch.bfloat16)
         x, wr = bf(gen.tokens(wl)), bf(gen.router_weight(wl))
         b = gen.router_bias(wl)
@@ -84,7 +83,7 @@ def workload_table(stream, steps, names=None):
         scales = [None] * len(mats)
         if fname == "bf16":
             mats = [m.to(torch.bfloat16) for m in mats]
-            wbytes_expert = 3 * wl.I * wl.H * 2
+            self.wbytes_expert = 3 * wl.I * wl.H * 2
         else:
             qm, qs = [], []
             for m in mats:
@@ -102,8 +101,9 @@ def workload_table(stream, steps, names=None):
                 qm.append(c)
                 qs.append(s)
             mats, scales = qm, qs
-            wbytes_expert = sum(int(m[0].numel() * m.element_size()) + int(s[0].numel() * s.element_size())
-                                for m, s in zip(mats[:3], scales[:3]))
+            self.wbytes_expert = sum(int(m[0].numel() * m.element_size()) +
+                                     int(s[0].numel() * s.element_size())
+                                     for m, s in zip(mats[:3], scales[:3]))
         torch.cuda.synchronize()
         sgate = (torch.randn(wl.H, generator=gen_t, device="cuda") * 0.02).to(torch.bfloat16) \
             if wl.gated else None
@@ -114,9 +114,24 @@ def workload_table(stream, steps, names=None):
         d = moe.make_desc(wl.T, wl.H, wl.E, wl.e0, wl.E_loc, wl.I, wl.k, wl.I_s, wl.scoring,
                           wl.renormalize, moe.MOE_BF16, fcode, moe.MOE_F32)
         o = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
-        ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+        self.ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
         ws = torch.empty(moe.moe_layer_workspace_bytes(d), dtype=torch.uint8, device="cuda")
-        call = lambda: moe.moe_layer(d, W, x, bias, o, None, ids, None, ws, stream)
+        self._keep = (mats, scales, W, x, wr, bias, o, ws)
+        self.call = lambda: moe.moe_layer(d, W, x, bias, o, None, self.ids, None, ws, stream)
+
+
+def workload_table(stream, steps, names=None):
+    """Layer time of every workload (one moe_layer call per step, caches evicted with a 1 GiB read
+    before each), with the algorithmic MFMA and HBM roofline fractions."""
+    import torch
+    import moe_inputs as mi
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    out = {}
+    for name in names or ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
+                          "C2p_mx8", "C2d_mx8"):
+        wl = mi.WORKLOADS[name]
+        tl = TableLayer(wl, stream)
+        fname, wbytes_expert, ids, call = tl.fname, tl.wbytes_expert, tl.ids, tl.call
         with torch.cuda.stream(stream):
             call()
         torch.cuda.synchronize()
@@ -149,7 +164,7 @@ def workload_table(stream, steps, names=None):
                      "frac_mfma": round(t_mfma / t, 4), "compulsory_bytes": nbytes,
                      "hbm_gbps": round(nbytes / t / 1e9, 1), "frac_hbm": round(t_hbm / t, 4),
                      "bound": "mfma" if t_mfma > t_hbm else "hbm"}
-        del mats, scales, W, x, wr, o, ids, ws
+        del tl, ids, call
         torch.cuda.empty_cache()
     return out
 
@@ -419,8 +434,23 @@ def main():
     import moe_inputs as mi
 
     wl = mi.WORKLOADS[args.workload]
-    L = Layer(wl)
     stream = torch.cuda.Stream()
+    if args.profile_only and (wl.fmt != mi.FMT_BF16 or wl.I_s or wl.gated):
+        # quantised layers and layers with a shared expert: the workload table's set-up, the same
+        # calls as in the table
+        tl = TableLayer(wl, stream)
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda") if args.flush else None
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                tl.call()
+            for _ in range(args.steps):
+                if flush is not None:
+                    flush.sum()
+                tl.call()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": wl.name, "steps": args.steps, "flushed": bool(args.flush)}))
+        return
+    L = Layer(wl)
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         L.step(stream)
