@@ -11,7 +11,12 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_q.hip", "combine.hip", "quant.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_q.hip", "gemm_fp8.hip", "combine.hip",
+           "quant.hip"]
+# gemm_fp8.hip rescales every MFMA result with the vector ALU: its MFMAs are compiled in the form
+# whose accumulators live in ordinary VGPRs (the default puts them in the MFMA-only registers,
+# from which each result would need extra moves)
+EXTRA = {"gemm_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # Packed fp32 VALU ops are disabled for all device code (the compiler otherwise forms
 # v_pk_{add,mul,fma}_f32 from ordinary float code).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -20,7 +25,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 
 def _compile(src):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(SRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(SRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -26,6 +26,8 @@
 // bank swizzle, tile scheduler and row gathering as the bf16 kernel. The block scales of a K-step
 // travel in the same stage as its operands (4-byte direct-to-LDS loads), so the loop has no other
 // global loads: every wait in it is an explicit count of this wave's own loads.
+#include <algorithm>
+
 #include "gemm_common.hpp"
 #include "quant_dev.hpp"
 
@@ -1177,7 +1179,10 @@ gemm_q_wide_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, in
               static_cast<uint16_t>((ex[0] + 127) | ((ex[1] + 127) << 8));
       }
   }
+
 }
+// fp8 tile kernel (gemm_fp8.hip): false if the operands do not fit its 32-bit offsets
+bool launch_fp8_tile(const GemmArgs& a, int epi, hipStream_t s, hipError_t* err);
 
 namespace {
 
@@ -1230,6 +1235,10 @@ hipError_t run_q_choice(const GemmArgs& a, hipStream_t s) {
   if (per_group <= 32 && a.N % 128 == 0) return run_q_stream<FMT, EPI>(a, s);
   if constexpr (FMT == MOE_MXFP4 || FMT == MOE_MXFP8)
     if (per_group >= kQWideBM && a.K % 512 == 0) return run_q_wide<FMT, EPI>(a, s);
+  if constexpr (FMT == MOE_FP8_E4M3) {
+    hipError_t e;
+    if (launch_fp8_tile(a, EPI, s, &e)) return e;
+  }
   return run_q<FMT, EPI>(a, s);
 }
 
