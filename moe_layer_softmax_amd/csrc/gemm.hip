@@ -19,6 +19,8 @@
 //   * Epilogues: STORE (optional per-column bias, fp32 or bf16 out) and SWIGLU, where each wave
 //     holds matching gate and up columns so h = silu(g) * u is formed in registers.
 #include <atomic>
+#include <cstdlib>
+#include <mutex>
 #include <type_traits>
 
 #include "gemm_common.hpp"
@@ -618,7 +620,9 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 // fragment gives each lane four consecutive output columns of one C row. Both operands go from
 // global memory straight into registers -- every weight byte is used by this wave only, so no LDS
 // staging is needed. K advances in pairs of 32-wide steps (128 bytes of every row):
-//   * weights: one load instruction covers 8 rows x 128 contiguous bytes (measured on MI355X: a
+//   * weights: non-temporal loads (each weight byte is read once per layer; on MI355X a plain-load
+//     stream of a row-major weight matrix reaches ~5.9 TB/s, the same stream with non-temporal
+//     loads ~6.1 TB/s); one load instruction covers 8 rows x 128 contiguous bytes (measured: a
 //     weight stream read as 16 rows x 64 bytes per instruction, the MFMA operand's own shape,
 //     reaches ~4.8 TB/s; 8 rows x 128 bytes reaches ~5.8 TB/s). Cross-lane permutes (ds_bpermute,
 //     no LDS storage) then move each 16-byte piece to the lane that holds it in the MFMA operand;
@@ -685,7 +689,8 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) wraw[set][j][h] = *reinterpret_cast<const i32x4*>(wp[j][h] + off);
+      for (int h = 0; h < 2; ++h)
+        wraw[set][j][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp[j][h] + off));
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -989,6 +994,26 @@ hipError_t launch_gemm_router(const GemmArgs& a, hipStream_t s) {
 
 // Tile shape choice: the expected rows per group decide between a compute-shaped tile (large
 // groups, MFMA-bound) and a weight-streaming tile (few rows per group, HBM-bound).
+// MOE_FORCE_VARIANT="<swiglu>,<store>" (each one of 2x1, 2x4, 4x1, 4x4, or "-" for the default)
+// forces the bf16 weight-streaming kernel's tile rows (16 x FM) and K split (KS) wherever the
+// streaming kernel is chosen: a tuning and testing switch; every variant computes the same result.
+// Read once per process.
+static int forced_stream_variant(bool swiglu) {
+  static int v[2] = {-1, -1};
+  static std::once_flag once;
+  std::call_once(once, [] {
+    const char* e = std::getenv("MOE_FORCE_VARIANT");
+    if (!e) return;
+    for (int which = 0; which < 2 && *e; ++which) {
+      if (e[0] >= '1' && e[0] <= '9' && e[1] == 'x' && e[2] >= '1' && e[2] <= '9')
+        v[which] = (e[0] - '0') * 10 + (e[2] - '0');
+      while (*e && *e != ',') ++e;
+      if (*e == ',') ++e;
+    }
+  });
+  return v[swiglu ? 0 : 1];
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.dtype == MOE_FP8_E4M3 || a.dtype == MOE_MXFP4 || a.dtype == MOE_MXFP8) return launch_gemm_q(a, s);
   if (a.dtype == MOE_F32) return run_f32(a, s);
@@ -1009,6 +1034,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     // decode-sized groups: stream the weights once per 32 (or 64) rows of each group
     if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32)) {
       const bool split = a.K / 64 >= kStreamSplitPairs;
+      switch (forced_stream_variant(a.epilogue == MOE_EPI_SWIGLU)) {
+        case 21: return run_bf16_stream<2, 1>(a, s);
+        case 24: return run_bf16_stream<2, 4>(a, s);
+        case 41: return run_bf16_stream<4, 1>(a, s);
+        case 44: return run_bf16_stream<4, 4>(a, s);
+        default: break;
+      }
       // the down projection streams its (short-K) weights once per 64 rows: measured ~5% faster
       // than 32-row tiles on the 64-token Qwen3-235B-shaped slice, where a few experts get more
       // than 32 rows and 32-row tiles would read their weights twice

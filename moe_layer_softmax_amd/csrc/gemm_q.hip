@@ -551,7 +551,8 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) wraw[set][j][h] = *reinterpret_cast<const i32x4*>(wp[j][h] + off);
+      for (int h = 0; h < 2; ++h)
+        wraw[set][j][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp[j][h] + off));
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
