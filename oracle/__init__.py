@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8, MX4, MX8 = 0, 1, 2, 3, 4
+F32, BF16, FP8, MX4, MX8, NV4 = 0, 1, 2, 3, 4, 5
 SOFTMAX, SIGMOID = 0, 1
 
 
@@ -34,7 +34,7 @@ _lib = None
 class _Mat(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int), ("G", ctypes.c_int), ("N", ctypes.c_int),
                 ("K", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
-                ("q", ctypes.c_void_p), ("s", ctypes.c_void_p)]
+                ("q", ctypes.c_void_p), ("s", ctypes.c_void_p), ("r", ctypes.c_void_p)]
 
 
 class _Desc(ctypes.Structure):
@@ -132,11 +132,23 @@ def quant_mx8(src):
     return codes, scales
 
 
-class Mat:
-    """A stack of G [N, K] matrices in one of the formats F32 / FP8 / MX4 / MX8 (keeps its
-    arrays)."""
+def quant_nv4(src):
+    """NVFP4: packed e2m1 [rows, cols/2], e4m3 block scales [rows, cols/16] (one per 16
+    elements), fp32 row scales [rows]."""
+    src = _c(src, np.float32)
+    rows, cols = src.shape
+    packed = np.empty((rows, cols // 2), np.uint8)
+    bscales = np.empty((rows, cols // 16), np.uint8)
+    rscales = np.empty(rows, np.float32)
+    lib().oracle_quant_nv4(rows, cols, _p(src), _p(packed), _p(bscales), _p(rscales))
+    return packed, bscales, rscales
 
-    def __init__(self, fmt, q, s=None, bn=128, bk=128):
+
+class Mat:
+    """A stack of G [N, K] matrices in one of the formats F32 / FP8 / MX4 / MX8 / NV4 (keeps its
+    arrays). NV4 takes its fp32 row scales [G, N] as r."""
+
+    def __init__(self, fmt, q, s=None, bn=128, bk=128, r=None):
         self.fmt = fmt
         if fmt == F32:
             q = _c(q, np.float32)
@@ -146,10 +158,13 @@ class Mat:
             q = q[None]
         self.q = q
         self.s = None if s is None else np.ascontiguousarray(s)
+        self.r = None if r is None else _c(r, np.float32)
+        if fmt == NV4 and self.r is None:
+            raise ValueError("NV4 needs its row scales")
         G, N, Kq = q.shape
-        K = Kq * 2 if fmt == MX4 else Kq
+        K = Kq * 2 if fmt in (MX4, NV4) else Kq
         self.G, self.N, self.K, self.bn, self.bk = G, N, K, bn, bk
-        self._c = _Mat(fmt, G, N, K, bn, bk, _p(self.q), _p(self.s))
+        self._c = _Mat(fmt, G, N, K, bn, bk, _p(self.q), _p(self.s), _p(self.r))
 
     @property
     def ref(self):
@@ -178,6 +193,9 @@ def quantise_stack(fmt, w):
     if fmt == MX4:
         qs, ss = zip(*(quant_mx4(w[g]) for g in range(G)))
         return Mat(MX4, np.stack(qs), np.stack(ss))
+    if fmt == NV4:
+        qs, ss, rs = zip(*(quant_nv4(w[g]) for g in range(G)))
+        return Mat(NV4, np.stack(qs), np.stack(ss), r=np.stack(rs))
     if fmt == MX8:
         qs, ss = zip(*(quant_mx8(w[g]) for g in range(G)))
         return Mat(MX8, np.stack(qs), np.stack(ss))

@@ -195,6 +195,47 @@ void oracle_quant_mx8(int rows, int cols, const float* src, uint8_t* codes, uint
     }
 }
 
+/* NVFP4: two levels of scale. The row scale g maps the row's absolute maximum onto the largest
+ * product of the two formats (6 * 448), so each 16-element block's own scale (its absolute maximum
+ * over 6, relative to g) uses the full e4m3 range; elements are then e2m1 codes of v / (s * g). */
+void oracle_quant_nv4(int rows, int cols, const float* src, uint8_t* packed, uint8_t* bscales,
+                      float* rscales)
+{
+  int nb = cols / 16;
+#pragma omp parallel for schedule(static)
+  for (int r = 0; r < rows; ++r) {
+    const float* row = src + (size_t)r * cols;
+    float amax = 0.0f;
+    for (int c = 0; c < cols; ++c)
+      if (fabsf(row[c]) > amax) amax = fabsf(row[c]);
+    float g = amax / 2688.0f;                          /* fp32 division */
+    if (!(g > 0.0f)) g = 1.0f;                         /* amax = 0 (or below 2688 * 2^-149) */
+    float d6 = 6.0f * g;                               /* fp32 product  */
+    rscales[r] = g;
+    for (int b = 0; b < nb; ++b) {
+      const float* v = row + (size_t)b * 16;
+      float bamax = 0.0f;
+      for (int i = 0; i < 16; ++i)
+        if (fabsf(v[i]) > bamax) bamax = fabsf(v[i]);
+      uint8_t sc = oracle_e4m3_encode(bamax / d6);
+      bscales[(size_t)r * nb + b] = sc;
+      float d = (float)oracle_e4m3_value(sc) * g;      /* exact e4m3 value times g, fp32 product */
+      uint8_t* out = packed + (size_t)r * (cols / 2) + (size_t)b * 8;
+      for (int i = 0; i < 8; ++i) {
+        uint8_t lo, hi;
+        if (d == 0.0f) {
+          lo = signbit(v[2 * i]) ? 0x8 : 0x0;
+          hi = signbit(v[2 * i + 1]) ? 0x8 : 0x0;
+        } else {
+          lo = oracle_e2m1_encode(v[2 * i] / d);
+          hi = oracle_e2m1_encode(v[2 * i + 1] / d);
+        }
+        out[i] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+  }
+}
+
 double oracle_mat_at(const oracle_mat* m, int g, int n, int kk)
 {
   size_t row = (size_t)g * m->N + n;
@@ -217,6 +258,13 @@ double oracle_mat_at(const oracle_mat* m, int g, int n, int kk)
     uint8_t c = ((const uint8_t*)m->q)[row * m->K + kk];
     uint8_t sc = ((const uint8_t*)m->s)[row * (m->K / 32) + kk / 32];
     return oracle_e4m3_value(c) * oracle_e8m0_value(sc);
+  }
+  case ORACLE_NV4: {
+    uint8_t b = ((const uint8_t*)m->q)[row * (m->K / 2) + kk / 2];
+    uint8_t nib = (kk & 1) ? (uint8_t)(b >> 4) : (uint8_t)(b & 15);
+    uint8_t sc = ((const uint8_t*)m->s)[row * (m->K / 16) + kk / 16];
+    double gr = (double)((const float*)m->r)[row];
+    return oracle_e2m1_value(nib) * oracle_e4m3_value(sc) * gr;   /* exact in double */
   }
   default:
     return NAN;
@@ -366,8 +414,8 @@ int oracle_permute(int T, int k, int e0, int E_loc, const int32_t* ids, int32_t*
 
 static void quantise_h(int act_fmt, int I, double* h)
 {
-  if (act_fmt == ORACLE_BF16) {
-    /* the down projection of a bf16 layer reads h as a bf16 tensor (rounded from fp32) */
+  if (act_fmt == ORACLE_BF16 || act_fmt == ORACLE_NV4) {
+    /* the down projection of a bf16 or NVFP4 layer reads h as a bf16 tensor (rounded from fp32) */
     for (int i = 0; i < I; ++i) h[i] = (double)oracle_bf16_round((float)h[i]);
   } else if (act_fmt == ORACLE_FP8) {
     /* 1 x 128 blocks along the intermediate dimension */
@@ -388,7 +436,7 @@ static void quantise_h(int act_fmt, int I, double* h)
     uint8_t* sc = (uint8_t*)malloc((size_t)I / 32);
     for (int i = 0; i < I; ++i) hf[i] = (float)h[i];
     oracle_quant_mx4(1, I, hf, pk, sc);
-    oracle_mat m = {ORACLE_MX4, 1, 1, I, 0, 0, pk, sc};
+    oracle_mat m = {ORACLE_MX4, 1, 1, I, 0, 0, pk, sc, NULL};
     for (int i = 0; i < I; ++i) h[i] = oracle_mat_at(&m, 0, 0, i);
     free(hf); free(pk); free(sc);
   } else if (act_fmt == ORACLE_MX8) {
@@ -398,7 +446,7 @@ static void quantise_h(int act_fmt, int I, double* h)
     uint8_t* sc = (uint8_t*)malloc((size_t)I / 32);
     for (int i = 0; i < I; ++i) hf[i] = (float)h[i];
     oracle_quant_mx8(1, I, hf, cd, sc);
-    oracle_mat m = {ORACLE_MX8, 1, 1, I, 0, 0, cd, sc};
+    oracle_mat m = {ORACLE_MX8, 1, 1, I, 0, 0, cd, sc, NULL};
     for (int i = 0; i < I; ++i) h[i] = oracle_mat_at(&m, 0, 0, i);
     free(hf); free(cd); free(sc);
   }

@@ -23,7 +23,10 @@
  *        per-group scales; activations quantised before dispatch).
  * The router function (softmax / sigmoid), SwiGLU, e4m3, e2m1 and E8M0 are not named on the pages;
  * they come from the workload definitions. e4m3 and e2m1/E8M0 follow the OCP 8-bit floating point
- * specification and the OCP Microscaling (MX) v1.0 specification.
+ * specification and the OCP Microscaling (MX) v1.0 specification. NVFP4 (e2m1 elements, one e4m3
+ * scale per 16 along K: [P3] "Blackwell" section for the 16-element absmax groups, [P4] for 4-bit
+ * weights with FP8 per-group scales) takes its second-level fp32 scale from NVIDIA's published
+ * NVFP4 recipe (per tensor there; one per row here, see oracle_quant_nv4).
  */
 #ifndef MOE_ORACLE_H
 #define MOE_ORACLE_H
@@ -42,7 +45,10 @@ enum {
   ORACLE_BF16 = 1,  /* activation format only: h rounded to bf16 before the down projection      */
   ORACLE_FP8 = 2,   /* e4m3 codes [G,N,K] + fp32 scales [G, ceil(N/bn), ceil(K/bk)]           */
   ORACLE_MX4 = 3,   /* e2m1 codes, 2 per byte, [G,N,K/2] + E8M0 scales [G, N, K/32]            */
-  ORACLE_MX8 = 4    /* e4m3 codes [G,N,K] + E8M0 scales [G, N, K/32] (MXFP8)                    */
+  ORACLE_MX8 = 4,   /* e4m3 codes [G,N,K] + E8M0 scales [G, N, K/32] (MXFP8)                    */
+  ORACLE_NV4 = 5    /* NVFP4: e2m1 codes, 2 per byte, [G,N,K/2] + e4m3 block scales [G, N, K/16]
+                       + fp32 row scales [G, N] (as an activation format: x arrives in NVFP4,
+                       h is rounded to bf16)                                                    */
 };
 
 /* A stack of G matrices of shape [N, K] (K contiguous) in one of the formats above. */
@@ -51,7 +57,8 @@ typedef struct {
   int G, N, K;
   int bn, bk;             /* fp8 block shape (rows x cols); ignored otherwise                     */
   const void* q;          /* float values, e4m3 codes, or packed e2m1 codes                       */
-  const void* s;          /* NULL, fp32 block scales, or E8M0 scale bytes                         */
+  const void* s;          /* NULL, fp32 block scales, E8M0 scale bytes or e4m3 scale bytes (NV4)   */
+  const void* r;          /* NV4: fp32 row scales [G, N]; NULL otherwise                          */
 } oracle_mat;
 
 /* ---- number formats ------------------------------------------------------------------------ */
@@ -77,6 +84,17 @@ void oracle_quant_mx4(int rows, int cols, const float* src, uint8_t* packed, uin
  * saturated to +-448 (scaled values reach up to 2^9). cols % 32 == 0. codes: [rows, cols];
  * scales: [rows, cols/32]. */
 void oracle_quant_mx8(int rows, int cols, const float* src, uint8_t* codes, uint8_t* scales);
+/* NVFP4 quantiser, per row (cols % 16 == 0), every step an fp32 operation:
+ *   g  = amax_row / 2688 (2688 = 6 * 448, so the largest block scale lands on e4m3's largest
+ *        value; g = 1 when that quotient is 0, i.e. amax_row = 0), d6 = 6 * g;
+ *   per 16 consecutive columns: scale code c_b = e4m3(bamax / d6) (nearest even, saturated),
+ *        s = value of c_b, d = s * g;
+ *   element code = e2m1(v / d) (nearest even, saturated to +-6); when d = 0 the codes are
+ *        zeros that keep the element's sign.
+ * The value of an element is e2m1(code) * s * g. packed: [rows, cols/2] (element 2i in bits 0-3
+ * of byte i); bscales: [rows, cols/16] e4m3 codes; rscales: [rows] fp32 g. */
+void oracle_quant_nv4(int rows, int cols, const float* src, uint8_t* packed, uint8_t* bscales,
+                      float* rscales);
 
 /* value of element (g, n, kk) of a matrix stack */
 double oracle_mat_at(const oracle_mat* m, int g, int n, int kk);
@@ -108,8 +126,8 @@ typedef struct {
   int scoring, renormalize;
   int act_fmt;            /* format of h, the input of the down projection: ORACLE_F32: as
                              computed; ORACLE_BF16: rounded to bf16; ORACLE_FP8: e4m3 with 1x128
-                             fp32 scales; ORACLE_MX4: MXFP4; ORACLE_MX8: MXFP8 (x arrives
-                             pre-quantised in `xa` for the quantised formats)                      */
+                             fp32 scales; ORACLE_MX4: MXFP4; ORACLE_MX8: MXFP8; ORACLE_NV4: rounded
+                             to bf16 (x arrives pre-quantised in `xa` for the quantised formats) */
 } oracle_desc;
 
 /* SwiGLU FFN of one activation row a[H] through matrix g of the gate/up/down stacks:

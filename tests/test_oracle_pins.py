@@ -757,3 +757,184 @@ def test_ffn_bf16_activation_rounds_h():
     gg, uu = a @ wg.astype(np.float64).T, a @ wu.astype(np.float64).T
     h = torch.from_numpy((gg * expit(gg) * uu).astype(np.float32)).to(torch.bfloat16).double().numpy()
     assert np.allclose(y, h @ wd.astype(np.float64).T, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------
+# NVFP4: e2m1 elements, e4m3 scale per 16 along K, fp32 row scale
+# ------------------------------------------------------------------------------------------
+
+_E2M1_MAG = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+
+
+def _e2m1_decode_numpy(nib):
+    nib = nib.astype(np.int64)
+    return np.where(nib & 8, -1.0, 1.0) * _E2M1_MAG[nib & 7]
+
+
+def _e4m3_decode_torch(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def _nv4_decode_numpy(packed, bscales, rscales):
+    """Element values e2m1 * s * g from the stored codes, with a numpy nibble table and torch's
+    e4m3 decoding (no oracle code involved)."""
+    lo, hi = packed & 15, packed >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*packed.shape[:-1], packed.shape[-1] * 2)
+    s = np.repeat(_e4m3_decode_torch(bscales), 16, axis=-1)
+    return _e2m1_decode_numpy(nib) * s * rscales.astype(np.float64)[..., None]
+
+
+def test_nv4_hand_example():
+    lines = _golden_kv("nv4_block_example.txt")
+    for r in (0, 1):
+        v = np.array([float(a) for a in lines[f"values{r}"]], np.float32)[None]
+        p, b, rs = oracle.quant_nv4(v)
+        assert rs[0] == np.float32(float(lines[f"rscale{r}"][0]))
+        assert [int(c) for c in b[0]] == [int(c, 0) for c in lines[f"scales{r}"]]
+        assert [int(c) for c in p[0]] == [int(c, 0) for c in lines[f"bytes{r}"]]
+    rows = [np.array([float(a) for a in lines[f"values{r}"]], np.float32) for r in (0, 1)]
+    p, b, rs = oracle.quant_nv4(np.stack(rows))
+    m = oracle.Mat(oracle.NV4, p[None], b[None], r=rs[None])
+    deq = lines["deq"]
+    for i in range(0, len(deq), 3):
+        assert m.at(0, int(deq[i]), int(deq[i + 1])) == float(deq[i + 2])
+
+
+def test_nv4_scale_rules_and_codes_restated():
+    """Row scale g = amax / 2688 (fp32), block scale code = e4m3 (torch's nearest-even cast of
+    the clamped fp32 quotient bamax / (6 g)), element = nearest-even e2m1 of v / (s g), all
+    restated in numpy/torch. Blocks get magnitudes from 1e-6 to 1e3 so the block scales cover
+    e4m3's subnormal and normal ranges and the 16-element grouping matters."""
+    rng = np.random.default_rng(41)
+    rows, cols = 24, 256
+    mag = 10.0 ** rng.uniform(-6, 3, size=(rows, cols // 16))
+    v = (rng.standard_normal((rows, cols)) * np.repeat(mag, 16, axis=1)).astype(np.float32)
+    v[3] = 0.0
+    v[5, :16] = 0.0
+    p, b, rs = oracle.quant_nv4(v)
+    amax = np.abs(v).max(axis=1)
+    g = np.where(amax > 0, amax / np.float32(2688), np.float32(1)).astype(np.float32)
+    assert np.array_equal(rs, g)
+    d6 = (np.float32(6) * g).astype(np.float32)
+    bamax = np.abs(v).reshape(rows, cols // 16, 16).max(axis=2)
+    q = np.minimum((bamax / d6[:, None]).astype(np.float32), np.float32(448))
+    ref_b = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(b, ref_b)
+    s = _e4m3_decode_torch(b).astype(np.float32)
+    d = np.repeat((s * g[:, None]).astype(np.float32), 16, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ref = np.where(d > 0, _e2m1_rne_numpy((v / np.where(d > 0, d, 1)).astype(np.float32)), 0.0)
+    lo, hi = p & 15, p >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(rows, cols)
+    ours = _e2m1_decode_numpy(nib)
+    assert np.array_equal(ours, ref)
+    assert np.array_equal(np.signbit(ours), np.signbit(v))     # zeros keep the element's sign
+
+
+def test_nv4_roundtrip_and_error_bound():
+    rng = np.random.default_rng(42)
+    # values on the grid: g = 2^-k (row amax 2688 * 2^-k), block maxima 6 * s * g with s on the
+    # e4m3 grid, elements e2m1 * s * g: quantise and decode without loss
+    e4 = np.array([oracle.e4m3_value(c) for c in range(1, 0x7F)], np.float64)
+    for k in (0, 5, 12):
+        g = 2.0 ** -k
+        v = np.empty((3, 128))
+        for r in range(3):
+            top = rng.integers(8)                               # the block holding 6 * 448 * g
+            for blk in range(8):
+                sb = 448.0 if blk == top else rng.choice(e4)
+                el = rng.choice(_E2M1_MAG, 16) * rng.choice([-1, 1], 16)
+                el[rng.integers(16)] = 6.0
+                v[r, blk * 16:(blk + 1) * 16] = el * sb * g
+        v = v.astype(np.float32)
+        assert np.array_equal(v.astype(np.float64), v)          # exact in fp32
+        p, b, rs = oracle.quant_nv4(v)
+        m = oracle.Mat(oracle.NV4, p[None], b[None], r=rs[None])
+        assert np.all(rs == np.float32(g))
+        assert np.array_equal(m.dequant()[0], v.astype(np.float64))
+    # random rows: the decoded value equals the numpy decode of the stored codes; inside the e2m1
+    # range the error is at most half the grid step (0.25, 0.5, 1 times d below 2, 4, 6); above
+    # it (the block scale rounded down by up to 2^-4) the value saturates at 6 d
+    v = (rng.standard_normal((32, 512)) * 0.05).astype(np.float32)
+    p, b, rs = oracle.quant_nv4(v)
+    m = oracle.Mat(oracle.NV4, p[None], b[None], r=rs[None])
+    dq = m.dequant()[0]
+    assert np.array_equal(dq, _nv4_decode_numpy(p, b, rs))
+    d = np.repeat(_e4m3_decode_torch(b), 16, axis=1) * rs.astype(np.float64)[:, None]
+    a = np.abs(v.astype(np.float64)) / d
+    err = np.abs(dq - v) / d
+    half = np.where(a < 2, 0.25, np.where(a < 4, 0.5, 1.0))
+    inside = a <= 6
+    assert np.all(err[inside] <= half[inside] * (1 + 1e-6))
+    assert np.all(np.abs(dq[~inside]) == 6 * d[~inside]) and np.all(a[~inside] <= 6 * (1 + 2.0 ** -4) * (1 + 1e-6))
+    # per block the error stays below d <= (bamax / 6)(1 + 2^-4) (block scales in e4m3's
+    # normal range here, where its rounding is within 2^-4)
+    blk_err = np.abs(dq - v).reshape(32, 32, 16).max(axis=2)
+    bamax = np.abs(v.astype(np.float64)).reshape(32, 32, 16).max(axis=2)
+    assert np.all(_e4m3_decode_torch(b) >= 2.0 ** -6)
+    assert np.all(blk_err <= bamax / 6 * (1 + 2.0 ** -4) * (1 + 1e-6))
+
+
+def test_grouped_gemm_nv4_equals_dequantised_matmul():
+    """NVFP4 weights and activations in the oracle's grouped GEMM: the numpy product of the
+    independently decoded operands."""
+    rng = np.random.default_rng(43)
+    K, N, T = 256, 96, 40
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((2, N, K)) * 0.02).astype(np.float32)
+    xp, xb, xr = oracle.quant_nv4(x)
+    xa = oracle.Mat(oracle.NV4, xp[None], xb[None], r=xr[None])
+    wm = oracle.quantise_stack(oracle.NV4, w)
+    assert wm.q.shape == (2, N, K // 2) and wm.s.shape == (2, N, K // 16) and wm.r.shape == (2, N)
+    off = np.array([0, 15, T], np.int32)
+    out = oracle.grouped_gemm(off, xa, wm)
+    xd = _nv4_decode_numpy(xp, xb, xr)
+    wd = _nv4_decode_numpy(wm.q, wm.s, wm.r)
+    for g in range(2):
+        ref = xd[off[g]:off[g + 1]] @ wd[g].T
+        assert np.allclose(out[off[g]:off[g + 1]], ref, rtol=0, atol=1e-12)
+
+
+def test_ffn_nv4_rounds_h_to_bf16():
+    """An NVFP4 layer keeps h in bf16: the FFN with act_fmt NV4 equals the dense FFN with h
+    rounded by torch's bf16 cast."""
+    rng = np.random.default_rng(44)
+    H, I = 64, 96
+    a = rng.standard_normal(H)
+    wg, wu = ((rng.standard_normal((I, H)) * 0.2).astype(np.float32) for _ in range(2))
+    wd = (rng.standard_normal((H, I)) * 0.2).astype(np.float32)
+    M = oracle.Mat
+    y = oracle.ffn_row(a, M(oracle.F32, wg), M(oracle.F32, wu), M(oracle.F32, wd), act_fmt=oracle.NV4)
+    gg, uu = a @ wg.astype(np.float64).T, a @ wu.astype(np.float64).T
+    h = torch.from_numpy((gg * expit(gg) * uu).astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.allclose(y, h @ wd.astype(np.float64).T, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_nv4_equals_dense_loop_on_decoded_operands():
+    """The NVFP4 layer for a given routing: per token, the weighted sum over its local experts of
+    the dense SwiGLU FFN on the numpy-decoded x row and weights, with h rounded to bf16."""
+    rng = np.random.default_rng(45)
+    T, H, I, E_loc, k = 6, 64, 48, 3, 2
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    g, u = ((rng.standard_normal((E_loc, I, H)) * 0.15).astype(np.float32) for _ in range(2))
+    d = (rng.standard_normal((E_loc, H, I)) * 0.15).astype(np.float32)
+    mats = [oracle.quantise_stack(oracle.NV4, w) for w in (g, u, d)]
+    xp, xb, xr = oracle.quant_nv4(x)
+    xa = oracle.Mat(oracle.NV4, xp[None], xb[None], r=xr[None])
+    desc = dict(T=T, H=H, E=5, e0=1, E_loc=E_loc, I=I, k=k, I_s=0, scoring=0, renormalize=1,
+                act_fmt=oracle.NV4)
+    tok = np.arange(T, dtype=np.int32)
+    ids = np.array([[1, 2], [3, 0], [4, 1], [2, 3], [0, 4], [3, 3]], np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    out = oracle.moe_layer_routed(desc, x, xa, *mats, None, tok, ids, w)
+    xd = _nv4_decode_numpy(xp, xb, xr)
+    gd, ud, dd = (_nv4_decode_numpy(m.q, m.s, m.r) for m in mats)
+    for t in range(T):
+        ref = np.zeros(H)
+        for j in range(k):
+            el = ids[t, j] - 1
+            if 0 <= el < E_loc:
+                gg, uu = gd[el] @ xd[t], ud[el] @ xd[t]
+                h = torch.from_numpy((gg * expit(gg) * uu).astype(np.float32)).to(torch.bfloat16).double().numpy()
+                ref += np.float64(w[t, j]) * (dd[el] @ h)
+        assert np.allclose(out[t], ref, rtol=1e-12, atol=1e-12)
