@@ -51,14 +51,16 @@ def parse():
     return p.parse_args()
 
 
-PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3}
+# NVFP4 runs its products (exact in bf16) on the bf16 MFMA, so its MFMA roofline is bf16's
+PEAK_TFLOPS = {"bf16": PEAK_BF16_TFLOPS, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3,
+               "nvfp4": PEAK_BF16_TFLOPS}
 
 
 class TableLayer:
     """One workload's layer call for the workload table and the profiler runs: tokens, router
     weight and bias are the seeded inputs; expert weights are seeded device draws of the same
     shapes (their values do not change the work), quantised by the library for the fp8 / MXFP4 /
-    MXFP8 layers."""
+    MXFP8 / NVFP4 layers."""
 
     def __init__(self, wl, stream):
         import torch
@@ -66,7 +68,8 @@ class TableLayer:
         import moe_layer_softmax_amd as moe
         from moe_inputs import gen
         fmt_of = {mi.FMT_BF16: ("bf16", moe.MOE_BF16), mi.FMT_FP8: ("fp8", moe.MOE_FP8_E4M3),
-                  mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8)}
+                  mi.FMT_MX4: ("mxfp4", moe.MOE_MXFP4), mi.FMT_MX8: ("mxfp8", moe.MOE_MXFP8),
+                  mi.FMT_NV4: ("nvfp4", moe.MOE_NVFP4)}
         self.wl = wl
         fname, fcode = fmt_of[wl.fmt]
         self.fname = fname
@@ -94,6 +97,10 @@ class TableLayer:
                 elif fname == "mxfp8":
                     c = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
                     s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
+                elif fname == "nvfp4":
+                    # per matrix: e4m3 block scales [R, C/16], then fp32 row scales [R]
+                    c = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
+                    s = torch.empty((G, R * (C // 16) + 4 * R), dtype=torch.uint8, device="cuda")
                 else:
                     c = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
                     s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
@@ -128,7 +135,7 @@ def workload_table(stream, steps, names=None):
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     out = {}
     for name in names or ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
-                          "C2p_mx8", "C2d_mx8"):
+                          "C2p_mx8", "C2d_mx8", "C5p_nv4", "C5d_nv4"):
         wl = mi.WORKLOADS[name]
         tl = TableLayer(wl, stream)
         fname, wbytes_expert, ids, call = tl.fname, tl.wbytes_expert, tl.ids, tl.call

@@ -69,9 +69,15 @@ typedef enum {
   MOE_FP8_E4M3 = 2,   /* OCP e4m3 bytes with fp32 block scales                                 */
   MOE_MXFP4 = 3,      /* OCP e2m1, two per byte (element 2i in bits 0-3 of byte i), E8M0 scale
                          byte per 32 consecutive elements along K                             */
-  MOE_MXFP8 = 4       /* OCP e4m3 bytes with an E8M0 scale byte per 32 consecutive elements
+  MOE_MXFP8 = 4,      /* OCP e4m3 bytes with an E8M0 scale byte per 32 consecutive elements
                          along K (OCP MX v1.0 MXFP8; the MoE GEMM format of "Hosting Qwen on
                          Blackwell", section "Quantization")                                  */
+  MOE_NVFP4 = 5       /* NVFP4: OCP e2m1, two per byte as MXFP4, with an e4m3 scale per 16
+                         consecutive elements along K ("CuTeDSL at Perplexity", section
+                         "Blackwell": 16-element absmax groups; "Driving vLLM WideEP ... (Part
+                         I)", lower-precision operations: 4-bit weights with FP8 per-group
+                         scales) and an fp32 scale per row (NVFP4's second level, per tensor in
+                         NVIDIA's recipe, per row here). Element value: e2m1 * s_block * g_row */
 } moe_dtype;
 
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_scoring;
@@ -88,8 +94,9 @@ typedef struct {
   int32_t k;            /* experts per token, 1 <= k <= min(E, 16)                             */
   int32_t I_s;          /* shared expert intermediate size, 0 = no shared expert; any multiple
                            of the expert format's K granularity (64 bf16 / fp32, 128 fp8 and
-                           MXFP8, 256 MXFP4). I_s == I runs the shared expert inside the routed
-                           experts' GEMM launches, other sizes in launches of their own        */
+                           MXFP8, 256 MXFP4 and NVFP4). I_s == I runs the shared expert inside
+                           the routed experts' GEMM launches, other sizes in launches of their
+                           own                                                                 */
   int32_t scoring;      /* moe_scoring                                                         */
   int32_t renormalize;  /* 1: weights renormalised over the k chosen experts                   */
   int32_t io_dtype;     /* x and the router weight: MOE_F32 or MOE_BF16                        */
@@ -97,7 +104,7 @@ typedef struct {
                            local experts; fp32 keeps it unrounded for the reduction across
                            expert-parallel ranks that follows the layer                        */
   int32_t expert_dtype; /* expert weights and GEMM activations: MOE_F32 (io F32 only),
-                           MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8                       */
+                           MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8, MOE_NVFP4              */
 } moe_desc;
 
 /* Expert weights of one layer, in expert_dtype:
@@ -107,6 +114,9 @@ typedef struct {
  *   MXFP4:       packed codes gate/up [E_loc, I, H/2], down [E_loc, H, I/2]; E8M0 scales
  *                gate/up [E_loc, I, H/32], down [E_loc, H, I/32].
  *   MXFP8:       codes gate/up [E_loc, I, H], down [E_loc, H, I]; E8M0 scales as for MXFP4.
+ *   NVFP4:       packed codes as for MXFP4; *_scales: one record per expert (E_loc records back to
+ *                back) of an [N, K] matrix: e4m3 block scales [N, K/16], then fp32 row scales [N]
+ *                (N*K/16 + 4*N bytes; gate/up N = I, K = H; down N = H, K = I).
  * The shared expert (sh_*) has the same layouts with E_loc = 1 and I = I_s; NULL when I_s = 0.
  * w_router is [E, H] in io_dtype. w_shared_gate is the shared expert's gate vector w_sg [H] in
  * io_dtype, or NULL for an ungated shared expert (g_t = 1); ignored when I_s = 0. Produce
@@ -165,6 +175,10 @@ int64_t moe_routing_blob_plane(const moe_desc* d);
  *               a_perm_scales receives [T*k, H/128] (the block row of each token).
  *   MXFP4:      packed [T, H/2] + E8M0 [T, H/32]; a_perm_scales receives [T*k, H/32].
  *   MXFP8:      e4m3 [T, H] + E8M0 [T, H/32]; a_perm_scales receives [T*k, H/32].
+ *   NVFP4:      packed [T, H/2] + one scale record (e4m3 [T, H/16], then fp32 [T]); the copy
+ *               dequantises: a_perm receives the block values e2m1 * s_block as bf16 [T*k, H]
+ *               (exact) and a_perm_scales the fp32 row scales [T*k], the grouped GEMM's A and
+ *               A_scales. H % 64 == 0.
  * a_perm: [T*k, row bytes] (R rows written), or NULL to produce only the maps.
  * ws: moe_permute_workspace_bytes(d) bytes of device scratch. */
 moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a_in,
@@ -189,8 +203,12 @@ size_t moe_permute_workspace_bytes(const moe_desc* d);
  * the next GEMM's input format (MOE_FP8_E4M3: fp32 C_scales [max_rows, N/128] per 1x128 block;
  * MOE_MXFP4 and MOE_MXFP8: C_scales [max_rows, N/32]). a_scale_rows: 128 when A's fp8 scales
  * are per 128-row block of A (a token-order x), else 1. Rows outside every group are not written.
- * Preconditions: K % 128 == 0 (K % 256 for MXFP4, K % 64 for BF16/F32), N % 64 == 0 (N % 128
- * for the quantised formats); dtype F32 needs out F32. */
+ * NVFP4: B and B2 as in moe_weights (B_scales / B2_scales: one scale record per group); A holds
+ * bf16 block values [rows, K] (as moe_permute writes them) and A_scales fp32 row scales [rows of
+ * A] (NULL: 1); every product q * s is exact in bf16 and runs on the bf16 MFMA, the row scales
+ * multiply the result; out_dtype MOE_F32 or MOE_BF16.
+ * Preconditions: K % 128 == 0 (K % 256 for MXFP4 and NVFP4, K % 64 for BF16/F32), N % 64 == 0
+ * (N % 128 for the quantised formats); dtype F32 needs out F32. */
 typedef struct {
   int32_t G;            /* groups (experts)                                                   */
   int32_t max_rows;     /* rows of C (and of A when a_rows == NULL)                           */
@@ -248,8 +266,13 @@ moe_status moe_shared_gate(const moe_desc* d, const void* x, const void* w_share
  *   MOE_MXFP8:    codes [rows, cols], E8M0 scales [rows, cols/32]: per 32 elements
  *                 e = floor(log2(amax)) - 8 clamped to [-127,127] (-127 if amax = 0),
  *                 code = e4m3(v * 2^-e) rounded to nearest even, saturated to +-448.
- * Element signs are kept (a value rounding to zero keeps its sign bit). cols % 128 == 0 (FP8) or
- * cols % 32 == 0 (MXFP4, MXFP8). `batch` stacked matrices are quantised independently (weights of
+ *   MOE_NVFP4:    packed [rows, cols/2]; scales: one record per matrix (e4m3 block scales
+ *                 [rows, cols/16], then fp32 row scales [rows]). Per row g = amax/2688 (1 if
+ *                 that is 0); per 16 elements the scale code c = e4m3(bamax / (6 g)) (nearest
+ *                 even, saturated), s its value, d = s * g; code = e2m1(v / d) (nearest even,
+ *                 saturated to +-6; signed zeros when d = 0). Each step one IEEE fp32 operation.
+ * Element signs are kept (a value rounding to zero keeps its sign bit). cols % 128 == 0 (FP8),
+ * cols % 32 == 0 (MXFP4, MXFP8) or cols % 64 == 0 (NVFP4). `batch` stacked matrices are quantised independently (weights of
  * E_loc experts): src, codes and scales are then [batch, ...] of the shapes above. */
 moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int32_t rows,
                         int32_t cols, int32_t block_rows, const void* src, void* codes,
@@ -268,8 +291,9 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
  * workspace). out is this GPU's partial sum over its local experts plus the shared expert (times
  * its gate g_t when w->w_shared_gate is given).
  * Intermediate formats: h (the down projection's input) is in the expert format (bf16 for bf16
- * experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for
- * fp8/MXFP4/MXFP8.
+ * and NVFP4 experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for
+ * fp8/MXFP4/MXFP8/NVFP4. NVFP4 layers quantise x per token (moe_quantize's rule) and run the
+ * GEMMs on its block values with the row scales applied after each dot product.
  * ws: moe_layer_workspace_bytes(d) bytes. */
 moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, const float* bias,
                      void* out, float* logits, int32_t* topk_ids, float* topk_w, void* ws,

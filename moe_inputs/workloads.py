@@ -13,6 +13,9 @@ Shape sources (pages):
     (Hosting Qwen on Blackwell, section "Quantization").
   * The Qwen3-235B slice in MXFP8, the format the Qwen deployment uses for its MoE GEMMs (Hosting
     Qwen on Blackwell, section "Quantization").
+  * The DeepSeek-V3 slice in NVFP4, the 4-bit format with FP8 per-group scales over 16 elements of
+    the DeepSeek deployment ("Driving vLLM WideEP ... (Part I)", lower-precision operations;
+    "CuTeDSL at Perplexity", section "Blackwell").
 """
 from dataclasses import dataclass, replace
 
@@ -26,6 +29,7 @@ FMT_BF16 = 1     # bf16 values
 FMT_FP8 = 2      # OCP e4m3 codes with fp32 scales per 128x128 block (weights, x) / 1x128 (h)
 FMT_MX4 = 3      # OCP e2m1 codes, two per byte, with one E8M0 scale per 32 elements along K
 FMT_MX8 = 4      # OCP e4m3 codes with one E8M0 scale per 32 elements along K (MXFP8)
+FMT_NV4 = 5      # NVFP4: OCP e2m1 codes with one e4m3 scale per 16 along K and an fp32 scale per row
 
 
 @dataclass(frozen=True)
@@ -80,4 +84,8 @@ WORKLOADS = {
     # the Qwen3-235B-shaped slice with MXFP8 experts and activations (x and h in MXFP8)
     "C2p_mx8": Workload("C2p_mx8", 16384, 4096, 128, 0, 32, 1536, 8, 0, SOFTMAX, 1, FMT_BF16, FMT_MX8, 1.1),
     "C2d_mx8": Workload("C2d_mx8", 64, 4096, 128, 0, 32, 1536, 8, 0, SOFTMAX, 1, FMT_BF16, FMT_MX8, 1.1),
+    # the DeepSeek-V3-shaped slice with NVFP4 experts and activations (h in bf16)
+    "C5p_nv4": Workload("C5p_nv4", 16384, 7168, 256, 0, 32, 2048, 8, 2048, SIGMOID, 1, FMT_BF16, FMT_NV4,
+                        1.2),
+    "C5d_nv4": Workload("C5d_nv4", 64, 7168, 256, 0, 32, 2048, 8, 2048, SIGMOID, 1, FMT_BF16, FMT_NV4, 0.0),
 }

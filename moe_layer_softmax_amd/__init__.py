@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 # enums of include/moe.h
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8 = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8, MOE_NVFP4 = range(6)
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_EPI_STORE, MOE_EPI_SWIGLU = 0, 1
 

@@ -11,8 +11,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_q.hip", "gemm_fp8.hip", "combine.hip",
-           "quant.hip"]
+SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_q.hip", "gemm_fp8.hip",
+           "gemm_nv4.hip", "combine.hip", "quant.hip"]
 # gemm_fp8.hip rescales every MFMA result with the vector ALU: its MFMAs are compiled in the form
 # whose accumulators live in ordinary VGPRs (the default puts them in the MFMA-only registers,
 # from which each result would need extra moves)

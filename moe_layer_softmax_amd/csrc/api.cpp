@@ -37,9 +37,16 @@ size_t round_up(size_t v, size_t a = 256) { return (v + a - 1) / a * a; }
 int io_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 // block-scaled 8-bit / 4-bit formats (quantised codes + scales)
-bool quantised(int dt) { return dt == MOE_FP8_E4M3 || dt == MOE_MXFP4 || dt == MOE_MXFP8; }
+bool quantised(int dt) {
+  return dt == MOE_FP8_E4M3 || dt == MOE_MXFP4 || dt == MOE_MXFP8 || dt == MOE_NVFP4;
+}
 // MX formats: one E8M0 scale byte per 32 elements along K
 bool mx_format(int dt) { return dt == MOE_MXFP4 || dt == MOE_MXFP8; }
+// formats whose layer re-quantises h into the expert format (NVFP4 keeps h in bf16)
+bool h_quantised(int dt) { return dt == MOE_FP8_E4M3 || mx_format(dt); }
+// bytes of one row of `cols` elements of a GEMM's A operand: NVFP4 activations enter the GEMM as
+// their bf16 block values
+long long a_row_bytes(int dt, long long cols);
 
 // format of the per-slot expert outputs y inside moe_layer
 int y_dtype_of(const moe_desc* d) { return quantised(d->expert_dtype) ? MOE_BF16 : MOE_F32; }
@@ -52,9 +59,12 @@ long long row_bytes(int dt, long long cols) {
     case MOE_FP8_E4M3: return cols;
     case MOE_MXFP4: return cols / 2;
     case MOE_MXFP8: return cols;
+    case MOE_NVFP4: return cols / 2;
     default: return 0;
   }
 }
+
+long long a_row_bytes(int dt, long long cols) { return dt == MOE_NVFP4 ? cols * 2 : row_bytes(dt, cols); }
 
 bool valid_io(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 bool valid_expert(int dt) {
@@ -101,10 +111,12 @@ moe_status check_expert_shapes(const moe_desc* d) {
   return MOE_OK;
 }
 
-// bytes between consecutive experts' scale arrays of an [N, K] weight matrix
+// bytes between consecutive experts' scale arrays of an [N, K] weight matrix (NVFP4: the record of
+// e4m3 block scales [N, K/16] followed by fp32 row scales [N])
 long long scale_bytes(int dt, long long N, long long K) {
   if (dt == MOE_FP8_E4M3) return (N / 128) * (K / 128) * 4;
   if (mx_format(dt)) return N * (K / 32);
+  if (dt == MOE_NVFP4) return N * (K / 16) + N * 4;
   return 0;
 }
 
@@ -165,6 +177,12 @@ LayerWs layer_ws(const moe_desc* d) {
     L.hs = take(rows * (I / 32));
     L.hsh = take(row_bytes(dt, Is) * T);
     L.hshs = take(T * (Is / 32));
+  } else if (dt == MOE_NVFP4) {
+    // x as its bf16 block values and fp32 row scales; h in bf16
+    L.xq = take(T * H * 2);
+    L.xs = take(T * 4);
+    L.h = take(rows * I * 2);
+    L.hsh = take(T * Is * 2);
   } else {
     L.h = take(rows * I * io_bytes(d->io_dtype));
     L.hsh = take(T * Is * io_bytes(d->io_dtype));
@@ -308,7 +326,7 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a
   if (a_perm) {
     if (!ok_ptr(a_in)) return MOE_ERR_INVALID_ARG;
     if (quant && (!ok_ptr(a_in_scales) || !ok_ptr(a_perm_scales))) return MOE_ERR_INVALID_ARG;
-    if (quant && d->H % 128) return MOE_ERR_INVALID_ARG;
+    if (quant && d->H % (dt == MOE_NVFP4 ? 64 : 128)) return MOE_ERR_INVALID_ARG;
     if (dt == MOE_F32 && d->io_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
   }
   if (ws_bytes < permute_ws_bytes(slots, d->E_loc) || (slots > 16 * 1024 && !ws))
@@ -317,6 +335,12 @@ moe_status moe_permute(const moe_desc* d, const int32_t* topk_ids, const void* a
   hipError_t e = launch_permute_maps(d->T, d->k, d->e0, d->E_loc, topk_ids, counts, offsets,
                                      slot_to_row, row_to_flat, ws, stream);
   if (e != hipSuccess || !a_perm) return hip_status(e);
+  if (dt == MOE_NVFP4)
+    return hip_status(launch_gather_nv4(slots, d->k, d->T, d->H, offsets + d->E_loc, row_to_flat,
+                                        static_cast<const uint8_t*>(a_in),
+                                        static_cast<const uint8_t*>(a_in_scales),
+                                        static_cast<uint16_t*>(a_perm),
+                                        static_cast<float*>(a_perm_scales), stream));
   long long sbytes = 0;
   int sblock = 1;
   if (dt == MOE_FP8_E4M3) { sbytes = (long long)(d->H / 128) * 4; sblock = 128; }
@@ -342,7 +366,12 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
   if (g->K % k_align(g->dtype) || g->N % 64) return MOE_ERR_INVALID_ARG;
   const bool quant = quantised(g->dtype);
   if (g->dtype == MOE_F32 && g->out_dtype != MOE_F32) return MOE_ERR_UNSUPPORTED;
-  if (quant) {
+  if (g->dtype == MOE_NVFP4) {
+    if (!ok_opt(A_scales) || !ok_ptr(B_scales)) return MOE_ERR_INVALID_ARG;
+    if (g->epilogue == MOE_EPI_SWIGLU && !ok_ptr(B2_scales)) return MOE_ERR_INVALID_ARG;
+    if (g->N % 128) return MOE_ERR_INVALID_ARG;
+    if (g->out_dtype != MOE_F32 && g->out_dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  } else if (quant) {
     if (!ok_ptr(A_scales) || !ok_ptr(B_scales)) return MOE_ERR_INVALID_ARG;
     if (g->epilogue == MOE_EPI_SWIGLU && !ok_ptr(B2_scales)) return MOE_ERR_INVALID_ARG;
     if (g->N % 128) return MOE_ERR_INVALID_ARG;
@@ -363,7 +392,7 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
   a.N = g->N;
   a.A = A;
   a.A_scales = A_scales;
-  a.a_pitch = row_bytes(g->dtype, g->K);
+  a.a_pitch = a_row_bytes(g->dtype, g->K);
   a.a_scale_rows = g->a_scale_rows;
   a.a_rows = a_rows;
   a.a_row_div = g->a_row_div;
@@ -438,6 +467,12 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
                                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
                                        stream));
   }
+  if (dst_dtype == MOE_NVFP4) {
+    if (cols % 64) return MOE_ERR_INVALID_ARG;
+    return hip_status(launch_quant_nv4(src_dtype, batch, rows, cols, src,
+                                       static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                       nullptr, false, stream));
+  }
   return MOE_ERR_INVALID_ARG;
 }
 
@@ -482,6 +517,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   const int T = d->T, k = d->k, H = d->H, I = d->I;
   const int slots = T * k;
   const int io = d->io_dtype, dt = d->expert_dtype;
+  const bool hq = h_quantised(dt);
 
   // 1. route
   st = run_route(d, x, w->w_router, bias, lg, reinterpret_cast<float*>(base + L.rpart), ids, tw,
@@ -512,22 +548,28 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
                                      reinterpret_cast<uint8_t*>(base + L.xs), stream));
     xa = base + L.xq;
     xs = base + L.xs;
+  } else if (dt == MOE_NVFP4) {
+    // NVFP4 per token, kept as the bf16 block values the GEMM consumes plus the row scales
+    st = hip_status(launch_quant_nv4(io, 1, T, H, x, reinterpret_cast<uint8_t*>(base + L.xq),
+                                     nullptr, reinterpret_cast<float*>(base + L.xs), true, stream));
+    xa = base + L.xq;
+    xs = base + L.xs;
   }
   if (st != MOE_OK) return st;
 
   // 4. gate/up GEMM with the SwiGLU epilogue; routed rows gather the activations through
   //    row_to_flat / k, shared-expert rows (C rows slots..slots+T) read them in token order. h
   //    leaves in the down projection's input format (bf16 / fp32, or re-quantised fp8 / MXFP4 /
-  //    MXFP8).
+  //    MXFP8; bf16 for NVFP4).
   GemmArgs a{};
   a.dtype = dt;
   a.epilogue = MOE_EPI_SWIGLU;
-  a.out_dtype = dt == MOE_BF16 ? MOE_BF16 : dt;
+  a.out_dtype = hq ? dt : (dt == MOE_F32 ? MOE_F32 : MOE_BF16);
   a.K = H;
   a.N = I;
   a.A = xa;
   a.A_scales = xs;
-  a.a_pitch = row_bytes(dt, H);
+  a.a_pitch = a_row_bytes(dt, H);
   a.a_scale_rows = dt == MOE_FP8_E4M3 ? 128 : 1;
   a.a_rows = r2f;
   a.a_row_div = k;
@@ -553,11 +595,11 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
     a.xB2s = w->sh_up_scales;
   }
   a.C = base + L.h;
-  a.C_scales = quant ? base + L.hs : nullptr;
-  a.c_pitch = quant ? row_bytes(dt, I) : (long long)I * io_bytes(io);
+  a.C_scales = hq ? base + L.hs : nullptr;
+  a.c_pitch = hq ? row_bytes(dt, I) : (long long)I * io_bytes(io);
   st = hip_status(launch_gemm(a, stream));
   if (st != MOE_OK) return st;
-  const long long hsh_pitch = quant ? row_bytes(dt, d->I_s) : (long long)d->I_s * io_bytes(io);
+  const long long hsh_pitch = hq ? row_bytes(dt, d->I_s) : (long long)d->I_s * io_bytes(io);
   if (shared_apart(d)) {
     // the shared expert alone: no routed groups, one extra group of T rows in token order
     GemmArgs sa = a;
@@ -577,7 +619,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
     sa.xB2 = w->sh_up;
     sa.xB2s = w->sh_up_scales;
     sa.C = base + L.hsh;
-    sa.C_scales = quant ? base + L.hshs : nullptr;
+    sa.C_scales = hq ? base + L.hshs : nullptr;
     sa.c_pitch = hsh_pitch;
     st = hip_status(launch_gemm(sa, stream));
     if (st != MOE_OK) return st;
@@ -592,8 +634,8 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   b.K = I;
   b.N = H;
   b.A = base + L.h;
-  b.A_scales = quant ? base + L.hs : nullptr;
-  b.a_pitch = quant ? row_bytes(dt, I) : (long long)I * io_bytes(io);
+  b.A_scales = hq ? base + L.hs : nullptr;
+  b.a_pitch = hq ? row_bytes(dt, I) : (long long)I * io_bytes(io);
   b.a_scale_rows = 1;
   b.a_row_div = 1;
   b.G = d->E_loc;
@@ -620,7 +662,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
     GemmArgs sb = b;
     sb.K = d->I_s;
     sb.A = base + L.hsh;
-    sb.A_scales = quant ? base + L.hshs : nullptr;
+    sb.A_scales = hq ? base + L.hshs : nullptr;
     sb.a_pitch = hsh_pitch;
     sb.G = 0;
     sb.offsets = nullptr;

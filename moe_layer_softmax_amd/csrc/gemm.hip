@@ -31,75 +31,6 @@ namespace moe {
 // m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel
 constexpr int kStreamGroupM = 8;
 
-// Write one wave's accumulators (FM x FN fragments of MI x MI, the wave's TM x TN block of the
-// BM x BN tile at wave position (wm, wn)). SWIGLU: fragment j < FN/2 holds gate columns and
-// j + FN/2 the matching up columns; h = silu(g) * u is stored. STORE: optional per-column bias.
-// Rows past the tile's end and columns past N are skipped.
-//
-// In both MFMA layouts a lane holds one column and, for accumulator entries 2u and 2u + 1, two
-// consecutive rows; the neighbouring lane (lane ^ 1) holds the next column for the same rows. One
-// cross-lane swap (DPP) per pair gives the even lane both columns of the first row and the odd lane
-// both columns of the second, so every store writes two adjacent values (4 bytes bf16, 8 fp32).
-// STREAM: fp32 stores are non-temporal (a large C that the next kernel reads from HBM anyway, e.g.
-// the down projection's y, is not left occupying L2; measured ~3% faster down projection).
-template <int MI, int FM, int FN, int TM, int TN, int BN, bool SWIGLU, bool OUT_F32,
-          bool STREAM = false, class AccAt>
-__device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t, int wm, int wn,
-                                           AccAt acc_at) {
-  constexpr int VPF = (MI == 32) ? 16 : 4;
-  const int lane = lane_id();
-  const bool odd = lane & 1;
-  auto row_of = [&](int v) -> int {
-    if constexpr (MI == 32) return (v / 4) * 8 + (lane / 32) * 4 + (v % 4);
-    else return (lane / 16) * 4 + v;
-  };
-  auto swap_pair = [](float x) -> float {   // value of lane ^ 1 (quad_perm [1, 0, 3, 2])
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  };
-  const int colw = (lane % MI) & ~1;                   // even column of this lane's pair
-  char* C = static_cast<char*>(p.C);
-  auto put = [&](int r, long long col, float lo, float hi) {
-    if (r >= t.row1 || col >= p.N) return;
-    char* crow = C + (long long)r * p.c_pitch;
-    if (col + 1 < p.N) {
-      if (OUT_F32 && STREAM) __builtin_nontemporal_store(f32x2{lo, hi}, reinterpret_cast<f32x2*>(crow + col * 4));
-      else if (OUT_F32) *reinterpret_cast<float2*>(crow + col * 4) = make_float2(lo, hi);
-      else *reinterpret_cast<uint32_t*>(crow + col * 2) = pack_bf16x2(lo, hi);
-    } else {
-      if (OUT_F32) reinterpret_cast<float*>(crow)[col] = lo;
-      else reinterpret_cast<uint16_t*>(crow)[col] = f32_to_bf16(lo);
-    }
-  };
-  constexpr int JN = SWIGLU ? FN / 2 : FN;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < JN; ++j) {
-      const long long col = SWIGLU ? (long long)t.nt * (BN / 2) + wn * (TN / 2) + j * MI + colw
-                                   : (long long)t.nt * BN + wn * TN + j * MI + colw;
-      float b0 = 0.0f, b1 = 0.0f;
-      if (!SWIGLU && p.bias) {
-        b0 = p.bias[min(col, (long long)p.N - 1)];
-        b1 = p.bias[min(col + 1, (long long)p.N - 1)];
-      }
-#pragma unroll
-      for (int u = 0; u < VPF / 2; ++u) {
-        float a, b;                                    // rows row_of(2u), row_of(2u + 1)
-        if (SWIGLU) {
-          a = silu_fast(acc_at(i, j, 2 * u)) * acc_at(i, j + FN / 2, 2 * u);
-          b = silu_fast(acc_at(i, j, 2 * u + 1)) * acc_at(i, j + FN / 2, 2 * u + 1);
-        } else {
-          a = acc_at(i, j, 2 * u);
-          b = acc_at(i, j, 2 * u + 1);
-        }
-        const float recv = swap_pair(odd ? a : b);
-        const float lo = odd ? recv : a, hi = odd ? b : recv;
-        const int r = t.row0 + wm * TM + i * MI + row_of(odd ? 2 * u + 1 : 2 * u);
-        put(r, col, lo + b0, hi + b1);
-      }
-    }
-}
-
 // fp32 STORE epilogue of 32 x 32 fragments with one 16-byte store per lane and 4 rows: in a quad
 // of lanes (4 consecutive columns) each lane holds 4 consecutive rows of its column for entries
 // 4g .. 4g + 3; two cross-lane exchanges (lane ^ 1, then lane ^ 2, as DPP quad permutations)
@@ -216,17 +147,6 @@ struct LoadPlan {
     }
   }
 };
-
-// A lane's byte offset of its MFMA fragment row inside a stage region for substep s: fragments
-// cover MI-row blocks starting at multiples of 16 rows, where the chunk swizzle repeats, so the
-// offset depends on the lane only (the block adds an immediate).
-template <class Geo, int MI, int MK>
-__device__ __forceinline__ unsigned frag_lane_off(int s, int lane) {
-  constexpr int BK = Geo::kRowBytes / 2;
-  const int r = lane % MI;
-  const int cidx = s * (MK / 8) + lane / MI;
-  return (r * BK + ((cidx ^ Geo::swz(r)) * 8)) * 2;
-}
 
 template <int BM, int BN, int WM, int WN, int MI, int BK, int S, bool SWIGLU, bool OUT_F32,
           bool PERSIST>
@@ -1016,6 +936,7 @@ static int forced_stream_variant(bool swiglu) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.dtype == MOE_FP8_E4M3 || a.dtype == MOE_MXFP4 || a.dtype == MOE_MXFP8) return launch_gemm_q(a, s);
+  if (a.dtype == MOE_NVFP4) return launch_gemm_nv4(a, s);
   if (a.dtype == MOE_F32) return run_f32(a, s);
   if (a.dtype == MOE_BF16) {
     const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;

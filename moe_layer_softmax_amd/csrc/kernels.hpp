@@ -84,5 +84,20 @@ hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const 
                             uint8_t* packed, uint8_t* scales, hipStream_t s);
 hipError_t launch_quant_mx8(int src_dtype, int batch, int rows, int cols, const void* src,
                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+// NVFP4: dequant = false: packed [batch*rows, cols/2] + per-matrix scale records (e4m3 [rows,
+// cols/16] then fp32 [rows]) in `scales`; dequant = true: bf16 block values [batch*rows, cols] in
+// `out` and fp32 row scales in `row_scale`. cols % 64 == 0.
+hipError_t launch_quant_nv4(int src_dtype, int batch, int rows, int cols, const void* src,
+                            uint8_t* out, uint8_t* scales, float* row_scale, bool dequant,
+                            hipStream_t s);
+// a_perm[r] = bf16 block values of packed NVFP4 row row_to_flat[r] / k (scales: one record of T
+// rows), a_perm_scales[r] = its row scale; rows r < *offsets_end. cols % 64 == 0.
+hipError_t launch_gather_nv4(long long max_rows, int k, int T, int cols, const int32_t* offsets_end,
+                             const int32_t* row_to_flat, const uint8_t* packed,
+                             const uint8_t* scales, uint16_t* dst, float* dst_scales,
+                             hipStream_t s);
+// NVFP4 weights (B) with bf16 block-value activations (A) and fp32 row scales (A_scales, may be
+// null); K % 256 == 0, N % 128 == 0
+hipError_t launch_gemm_nv4(const GemmArgs& a, hipStream_t s);
 
 }  // namespace moe

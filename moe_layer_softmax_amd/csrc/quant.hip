@@ -1,11 +1,11 @@
-// quant.hip -- fp8 (e4m3, fp32 block scales), MXFP4 (e2m1 + E8M0 per 32) and MXFP8 (e4m3 + E8M0 per
-// 32) quantisers on gfx950.
+// quant.hip -- fp8 (e4m3, fp32 block scales), MXFP4 (e2m1 + E8M0 per 32), MXFP8 (e4m3 + E8M0 per
+// 32) and NVFP4 (e2m1 + e4m3 per 16 + fp32 per row) quantisers on gfx950.
 //
 // Block scaling "as used for models like DeepSeek" ("Hosting Qwen on Blackwell", section
 // "Quantization"); 4-bit weights packed two per byte with per-group scales and activations
 // quantised to 4 bits before dispatch ("Driving vLLM WideEP ... on Blackwell (Part I)", section on
-// lower-precision operations); absmax over 32 elements for the MX formats ("CuTeDSL at
-// Perplexity", Blackwell section). Element formats and the MX scale rule follow the OCP 8-bit FP
+// lower-precision operations); absmax over 32 elements for the MX formats and over 16 for NVFP4
+// ("CuTeDSL at Perplexity", Blackwell section). Element formats and the MX scale rule follow the OCP 8-bit FP
 // and OCP MX v1.0 specifications. Codes come from gfx950's packed conversions (v_cvt_pk_fp8_f32 on
 // operands clamped to +-448, v_cvt_scalef32_pk_fp4_f32 with a unit scale), which round to nearest
 // even in the default rounding mode; quant_dev.hpp also keeps the integer/compare encoders they were
@@ -142,6 +142,92 @@ __global__ void __launch_bounds__(256) quant_mx8_kernel(long long groups, const 
   if (sub == 0) scales[g] = static_cast<uint8_t>(e8 + 127);
 }
 
+// NVFP4, one wave per row (four rows per workgroup): the row's absolute maximum gives the row scale
+// g = amax / 2688 (1 when that is 0); then per 16-element block (two neighbouring lanes of 8
+// elements each) the e4m3 block scale code of bamax / (6 g), s its value, d = s * g, and the e2m1
+// codes of v / d (signed zeros when d = 0). Every step is one IEEE fp32 operation, taken in the
+// same order as the definition, so the codes are exact decisions. The row is read twice (the
+// second pass finds it in L2).
+//   DEQ = false: packed codes [rows, cols/2]; scale record per matrix of `rows` rows: e4m3 block
+//                scales [rows, cols/16], then fp32 row scales [rows].
+//   DEQ = true:  the block values q * s as bf16 [rows, cols] (exact) and the row scales g [rows]
+//                (the layer's activation operand).
+template <bool SRC_BF16, bool DEQ>
+__global__ void __launch_bounds__(256) quant_nv4_kernel(long long total_rows, int rows, int cols,
+                                                        const void* __restrict__ src,
+                                                        uint8_t* __restrict__ out,
+                                                        uint8_t* __restrict__ scales,
+                                                        float* __restrict__ row_scale) {
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= total_rows) return;                   // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const int nch = cols / 8;                        // 8-element chunks; cols % 64 == 0
+  const size_t base = (size_t)row * cols;
+  float amax = 0.0f;
+  for (int c = lane; c < nch; c += 64) {
+    float v[8];
+    load8<SRC_BF16>(src, base + (size_t)c * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+  }
+  amax = wave_max(amax);
+  float g = amax / 2688.0f;
+  if (!(g > 0.0f)) g = 1.0f;
+  const float d6 = 6.0f * g;
+  const long long mat = row / rows, r = row % rows;
+  uint8_t* bs = nullptr;
+  if (!DEQ) {
+    const long long rec = (long long)rows * (cols / 16) + (long long)rows * 4;
+    bs = scales + mat * rec + r * (cols / 16);
+    if (lane == 0) reinterpret_cast<float*>(scales + mat * rec + (long long)rows * (cols / 16))[r] = g;
+  } else if (lane == 0) {
+    row_scale[row] = g;
+  }
+  for (int c = lane; c < nch; c += 64) {           // nch is even: block partners share c / 64
+    float v[8];
+    load8<SRC_BF16>(src, base + (size_t)c * 8, v);
+    float bamax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bamax = fmaxf(bamax, fabsf(v[e]));
+    bamax = fmaxf(bamax, __shfl_xor(bamax, 1, 64));
+    const uint8_t sc = e4m3_rne_sat(bamax / d6);
+    const float sv = e4m3_to_f32(sc);
+    const float d = sv * g;
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = d == 0.0f ? v[e] * 0.0f : v[e] / d;
+    const uint32_t word = e2m1x8_rne_sat(y);
+    if (!DEQ) {
+      *reinterpret_cast<uint32_t*>(out + (size_t)row * (cols / 2) + (size_t)c * 4) = word;
+      if ((c & 1) == 0) bs[c / 2] = sc;
+    } else {
+      *reinterpret_cast<i32x4*>(out + base * 2 + (size_t)c * 16) = e2m1x8_times(word, sv);
+    }
+  }
+}
+
+// Dispatch copy of NVFP4 activation rows: a_perm[r] = the block values q * s (bf16) of token row
+// row_to_flat[r] / k of the packed input, a_perm_scales[r] = its row scale; one wave per row.
+__global__ void __launch_bounds__(256) gather_nv4_kernel(long long max_rows, int k, int T, int cols,
+                                                         const int32_t* __restrict__ offsets_end,
+                                                         const int32_t* __restrict__ row_to_flat,
+                                                         const uint8_t* __restrict__ packed,
+                                                         const uint8_t* __restrict__ scales,
+                                                         uint16_t* __restrict__ dst,
+                                                         float* __restrict__ dst_scales) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= max_rows || r >= *offsets_end) return;  // wave-uniform
+  const int lane = threadIdx.x & 63;
+  const long long t = row_to_flat[r] / k;
+  const uint8_t* bs = scales + t * (cols / 16);
+  const float* rs = reinterpret_cast<const float*>(scales + (long long)T * (cols / 16));
+  for (int c = lane; c < cols / 8; c += 64) {
+    const uint32_t word = *reinterpret_cast<const uint32_t*>(packed + t * (cols / 2) + (long long)c * 4);
+    *reinterpret_cast<i32x4*>(dst + r * cols + (long long)c * 8) = e2m1x8_times(word, e4m3_to_f32(bs[c / 2]));
+  }
+  if (lane == 0) dst_scales[r] = rs[t];
+}
+
 hipError_t launch_quant_fp8(int src_dtype, int batch, int rows, int cols, int block_rows,
                             const void* src, uint8_t* codes, float* scales, hipStream_t s) {
   if (rows == 0 || batch == 0) return hipSuccess;
@@ -175,6 +261,34 @@ hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const 
     quant_mx4_kernel<true><<<grid, 256, 0, s>>>(groups, src, packed, scales);
   else
     quant_mx4_kernel<false><<<grid, 256, 0, s>>>(groups, src, packed, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nv4(int src_dtype, int batch, int rows, int cols, const void* src,
+                            uint8_t* out, uint8_t* scales, float* row_scale, bool dequant,
+                            hipStream_t s) {
+  const long long total = (long long)batch * rows;
+  if (total == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((total + 3) / 4));
+  const bool bf = src_dtype == MOE_BF16;
+  if (dequant) {
+    if (bf) quant_nv4_kernel<true, true><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
+    else quant_nv4_kernel<false, true><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
+  } else {
+    if (bf) quant_nv4_kernel<true, false><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
+    else quant_nv4_kernel<false, false><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_nv4(long long max_rows, int k, int T, int cols, const int32_t* offsets_end,
+                             const int32_t* row_to_flat, const uint8_t* packed,
+                             const uint8_t* scales, uint16_t* dst, float* dst_scales,
+                             hipStream_t s) {
+  if (max_rows == 0) return hipSuccess;
+  dim3 grid(static_cast<unsigned>((max_rows + 3) / 4));
+  gather_nv4_kernel<<<grid, 256, 0, s>>>(max_rows, k, T, cols, offsets_end, row_to_flat, packed,
+                                         scales, dst, dst_scales);
   return hipGetLastError();
 }
 

@@ -66,6 +66,20 @@ __device__ __forceinline__ uint32_t e2m1x8_rne_sat(const float* v) {
   return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
 }
 
+// Eight e2m1 codes (element i in bits 4i .. 4i + 3) times s as eight bf16 values (16 bytes). With s
+// an e4m3 value every product is exact in fp32 and in bf16, so the upper half of each fp32 pattern
+// is the bf16 value.
+template <int B>
+__device__ __forceinline__ int e2m1_pair_times(uint32_t w, float s) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, B);   // byte B: 2B, 2B + 1
+  const float lo = v[0] * s, hi = v[1] * s;
+  return static_cast<int>(__builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u));
+}
+__device__ __forceinline__ i32x4 e2m1x8_times(uint32_t w, float s) {
+  return i32x4{e2m1_pair_times<0>(w, s), e2m1_pair_times<1>(w, s), e2m1_pair_times<2>(w, s),
+               e2m1_pair_times<3>(w, s)};
+}
+
 // shared exponent of an MX block: floor(log2(amax)) minus the element format's largest exponent
 // (2 for e2m1, 8 for e4m3), clamped to [-127, 127]; -127 for amax = 0
 template <int EMAX = 2>

@@ -53,13 +53,13 @@ def rel_err(gpu, ref):
 
 
 def tol_for(fmt):
-    return 6e-2 if fmt in (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8) else 2e-2
+    return 6e-2 if fmt in (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8, mi.FMT_NV4) else 2e-2
 
 
 # ---- quantised formats ------------------------------------------------------------------
 
 FMTS = {"fp8": (moe.MOE_FP8_E4M3, oracle.FP8), "mx4": (moe.MOE_MXFP4, oracle.MX4),
-        "mx8": (moe.MOE_MXFP8, oracle.MX8)}
+        "mx8": (moe.MOE_MXFP8, oracle.MX8), "nv4": (moe.MOE_NVFP4, oracle.NV4)}
 E2M1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6, -0.0, -0.5, -1, -1.5, -2, -3, -4, -6])
 
 
@@ -77,6 +77,10 @@ def gpu_quant(fmt, a, block_rows):
     elif fmt == moe.MOE_MXFP8:
         codes = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
         scales = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
+    elif fmt == moe.MOE_NVFP4:
+        # one scale record per matrix: e4m3 block scales [R, C/16], then fp32 row scales [R]
+        codes = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((G, R * (C // 16) + 4 * R), dtype=torch.uint8, device="cuda")
     else:
         codes = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
         scales = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
@@ -95,8 +99,33 @@ def oracle_quant(ofmt, a, block_rows):
     if ofmt == oracle.MX8:
         qs = [oracle.quant_mx8(a[g]) for g in range(a.shape[0])]
         return oracle.Mat(oracle.MX8, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]))
+    if ofmt == oracle.NV4:
+        qs = [oracle.quant_nv4(a[g]) for g in range(a.shape[0])]
+        return oracle.Mat(oracle.NV4, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]),
+                          r=np.stack([q[2] for q in qs]))
     qs = [oracle.quant_mx4(a[g]) for g in range(a.shape[0])]
     return oracle.Mat(oracle.MX4, np.stack([q[0] for q in qs]), np.stack([q[1] for q in qs]))
+
+
+def nv4_split(scales, rows, cols):
+    """An NVFP4 scale record per matrix ([G, rows*cols/16 + 4*rows] bytes, host or device) as
+    (e4m3 block-scale bytes [G, rows, cols/16], fp32 row scales [G, rows]) numpy arrays."""
+    s = scales.cpu().numpy() if hasattr(scales, "cpu") else np.asarray(scales)
+    s = s.reshape(-1, rows * (cols // 16) + 4 * rows)
+    nb = rows * (cols // 16)
+    return (s[:, :nb].reshape(-1, rows, cols // 16).copy(),
+            np.ascontiguousarray(s[:, nb:]).view(np.float32).reshape(-1, rows).copy())
+
+
+def nv4_block_values(codes, bscales):
+    """e2m1 code * e4m3 block scale (numpy table and torch's e4m3 decoding), float64 [..., cols]."""
+    codes = codes.cpu().numpy() if hasattr(codes, "cpu") else np.asarray(codes)
+    lo, hi = codes & 15, codes >> 4
+    v = np.empty(codes.shape[:-1] + (codes.shape[-1] * 2,))
+    v[..., 0::2] = E2M1[lo]
+    v[..., 1::2] = E2M1[hi]
+    s = torch.from_numpy(np.ascontiguousarray(bscales, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    return v * np.repeat(s, 16, axis=-1)
 
 
 def decode(fmt, codes, scales, cols):

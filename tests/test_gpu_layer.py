@@ -19,8 +19,9 @@ from gpu_util import (gamma, gpu_quant, h_flip_allowance, io_torch, oracle_quant
 pytestmark = pytest.mark.gpu
 
 _FMT = {mi.FMT_F32: moe.MOE_F32, mi.FMT_BF16: moe.MOE_BF16, mi.FMT_FP8: moe.MOE_FP8_E4M3,
-        mi.FMT_MX4: moe.MOE_MXFP4, mi.FMT_MX8: moe.MOE_MXFP8}
-_QUANT = (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8)
+        mi.FMT_MX4: moe.MOE_MXFP4, mi.FMT_MX8: moe.MOE_MXFP8, mi.FMT_NV4: moe.MOE_NVFP4}
+_QUANT = (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8, mi.FMT_NV4)
+_H_QUANT = (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8)      # h re-quantised to the expert format
 
 
 def make_inputs(wl, bias_override=None):
@@ -65,20 +66,21 @@ def gpu_layer(wl, x, wr, bias, experts, sh, sgate=None):
 
 
 def _act_fmt(wl, unrounded=False):
-    # h enters the down projection in the expert format (bf16 / fp8 1x128 / MXFP4 / MXFP8); with
+    # h enters the down projection in the expert format (bf16 / fp8 1x128 / MXFP4 / MXFP8; bf16 for
+    # NVFP4, whose oracle format code also selects the NVFP4 quantiser for x and the weights); with
     # unrounded=True a bf16 layer's oracle keeps h exact (fp64) instead
     if unrounded:
         return oracle.F32
     return {mi.FMT_F32: oracle.F32, mi.FMT_BF16: oracle.BF16, mi.FMT_FP8: oracle.FP8,
-            mi.FMT_MX4: oracle.MX4, mi.FMT_MX8: oracle.MX8}[wl.fmt]
+            mi.FMT_MX4: oracle.MX4, mi.FMT_MX8: oracle.MX8, mi.FMT_NV4: oracle.NV4}[wl.fmt]
 
 
 def _oracle_operands(wl, x, experts, sh):
     act = _act_fmt(wl)
     M = oracle.Mat
     if wl.fmt in _QUANT:
-        # the oracle quantises x (fp8: 128-token x 128-channel blocks; MX: 1 x 32) and the
-        # weights with its own quantisers
+        # the oracle quantises x (fp8: 128-token x 128-channel blocks; MX: 1 x 32; NVFP4: per token
+        # row) and the weights with its own quantisers
         xa = oracle_quant(act, x, 128)
         mats = [oracle_quant(act, a, 128) for a in experts]
         shared = None if sh is None else tuple(oracle_quant(act, a, 128) for a in sh)
@@ -163,7 +165,7 @@ def check_layer(wl, n_sample=None, bias_override=None, seed=0, gated=None, unrou
         msg += f", against unrounded h {err_u:.3e}"
         assert err_u <= tol_for(wl.fmt), err_u
     bar = tol_for(wl.fmt)
-    if err > bar and wl.fmt in _QUANT:
+    if err > bar and wl.fmt in _H_QUANT:
         # tokens above the bar: allowed only what re-quantised h codes next to a rounding boundary
         # (within the fp32 accumulation bound of the exact h) can move the output
         n_allow = _check_with_flip_allowance(wl, out, want, tok, ids, w, ops, bar * rms, sgate, x)
@@ -220,7 +222,7 @@ def _check_with_flip_allowance(wl, out, want, tok, ids, w, ops, abs_bar, sgate, 
 @pytest.mark.parametrize("name,n_sample", [("C1", None), ("C2d", None), ("C3a", 96),
                                            ("C2p", 48), ("C3b", 64), ("C4d", 64), ("C4p", 48),
                                            ("C5d", None), ("C5p", 48), ("C2d_mx8", None),
-                                           ("C2p_mx8", 48)])
+                                           ("C2p_mx8", 48), ("C5d_nv4", None), ("C5p_nv4", 48)])
 def test_layer_workloads(name, n_sample):
     check_layer(mi.WORKLOADS[name], n_sample, unrounded=True)
 
@@ -228,7 +230,7 @@ def test_layer_workloads(name, n_sample):
 # the shared expert scaled by its per-token logistic gate: bf16 (Qwen3.5-397B slice), fp8 and MXFP4
 # (DeepSeek-V3 slice), at a prefill and a decode size
 @pytest.mark.parametrize("name,n_sample", [("C3a_g", 96), ("C3b_g", 48), ("C4p", 48),
-                                           ("C5d", None)])
+                                           ("C5d", None), ("C5d_nv4", None)])
 def test_layer_gated_shared_expert(name, n_sample):
     check_layer(mi.WORKLOADS[name], n_sample, gated=True)
 
@@ -275,13 +277,13 @@ def test_layer_mx8_single_token_full_shape():
     check_layer(mi.WORKLOADS["C2p_mx8"].with_tokens(1))
 
 
-@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8])
+@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8, mi.FMT_NV4])
 def test_layer_quantised_single_token_with_shared(fmt):
     # one token, sigmoid routing, shared expert as a one-row extra group
     check_layer(_small(T=1, fmt=fmt, H=512, I=256, I_s=256, scoring=mi.SIGMOID))
 
 
-@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8])
+@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8, mi.FMT_NV4])
 def test_layer_quantised_all_tokens_one_expert(fmt):
     # every token's top choice is expert 3 (one large group on the tile kernels, the rest small)
     wl = _small(T=700, fmt=fmt, H=512, I=256)
@@ -290,7 +292,7 @@ def test_layer_quantised_all_tokens_one_expert(fmt):
     check_layer(wl, bias_override=bias)
 
 
-@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8])
+@pytest.mark.parametrize("fmt", [mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8, mi.FMT_NV4])
 def test_layer_quantised_no_local_rows_with_shared(fmt):
     wl = _small(e0=8, I_s=256, fmt=fmt, H=512, I=256)
     bias = np.zeros(16, np.float32)
@@ -350,7 +352,7 @@ def test_layer_routing_blob():
 # prefill token count, and the Qwen3.5-397B-shaped slice with a shared expert twice as wide
 @pytest.mark.parametrize("fmt,I,I_s", [(mi.FMT_BF16, 256, 512), (mi.FMT_BF16, 256, 128),
                                        (mi.FMT_FP8, 256, 384), (mi.FMT_MX4, 256, 512),
-                                       (mi.FMT_MX8, 256, 128)])
+                                       (mi.FMT_MX8, 256, 128), (mi.FMT_NV4, 256, 512)])
 @pytest.mark.parametrize("T", [5, 700])
 def test_layer_shared_expert_other_width(fmt, I, I_s, T):
     check_layer(_small(T=T, fmt=fmt, H=512, I=I, I_s=I_s,
