@@ -31,15 +31,15 @@ namespace moe {
 // m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel
 constexpr int kStreamGroupM = 8;
 
-// fp32 STORE epilogue of 32 x 32 fragments with one 16-byte store per lane and 4 rows: in a quad
-// of lanes (4 consecutive columns) each lane holds 4 consecutive rows of its column for entries
-// 4g .. 4g + 3; two cross-lane exchanges (lane ^ 1, then lane ^ 2, as DPP quad permutations)
-// transpose the 4 x 4 block so lane q holds row (q & 1) * 2 + (q >> 1) of the block, 4 columns.
-// Stores are non-temporal (C is read by the next kernel from HBM anyway). Returns true when every
-// row and column of the wave's block is inside the tile: the wave then issued exactly
-// FM * FN * 4 store instructions (callers count them in their vmcnt waits).
-template <int FM, int FN, int TM, int TN, int BN, class AccAt>
-__device__ __forceinline__ bool store_tile_f32x4(const GemmArgs& p, const Tile& t, int wm, int wn,
+// STORE epilogue of 32 x 32 fragments with one store of 4 columns per lane and 4 rows (16 bytes
+// fp32, 8 bytes bf16): in a quad of lanes (4 consecutive columns) each lane holds 4 consecutive
+// rows of its column for entries 4g .. 4g + 3; two cross-lane exchanges (lane ^ 1, then lane ^ 2,
+// as DPP quad permutations) transpose the 4 x 4 block so lane q holds row (q & 1) * 2 + (q >> 1) of
+// the block, 4 columns. Stores are non-temporal (C is read by the next kernel from HBM anyway).
+// Returns true when every row and column of the wave's block is inside the tile: the wave then
+// issued exactly FM * FN * 4 store instructions (callers count them in their vmcnt waits).
+template <int FM, int FN, int TM, int TN, int BN, bool OUT_F32, class AccAt>
+__device__ __forceinline__ bool store_tile_x4(const GemmArgs& p, const Tile& t, int wm, int wn,
                                                  AccAt acc_at) {
   const int lane = lane_id();
   const int q = lane & 3;
@@ -73,8 +73,14 @@ __device__ __forceinline__ bool store_tile_f32x4(const GemmArgs& p, const Tile& 
         const f32x4 v = hi ? f32x4{s0, s1, x2, x3} : f32x4{x0, x1, s0, s1};
         const int r = rbase + i * 32 + g * 8 + row_in;
         const long long col = col0 + j * 32;
-        if (full || (r < t.row1 && col < p.N))
-          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (long long)r * p.c_pitch + col * 4));
+        if (full || (r < t.row1 && col < p.N)) {
+          if constexpr (OUT_F32) {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(C + (long long)r * p.c_pitch + col * 4));
+          } else {
+            const u32x2 w = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(C + (long long)r * p.c_pitch + col * 2));
+          }
+        }
       }
   return full;
 }
@@ -392,10 +398,10 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
                                                  lds0 + (kt % S) * (STAGE * 2), wave);
   };
   // Store instructions of the epilogue of a wave whose block lies inside the tile: 16-byte stores
-  // for fp32 STORE (4 per 32 x 32 fragment), otherwise 2-column stores (8 per fragment pair row
-  // group, see store_tile).
-  constexpr bool F32X4 = !SWIGLU && OUT_F32;
-  constexpr int NST = F32X4 ? FM * FN * 4 : FM * (SWIGLU ? FN / 2 : FN) * 8;
+  // for STORE (4 per 32 x 32 fragment, fp32 or bf16), otherwise 2-column stores (8 per fragment
+  // pair row group, see store_tile).
+  constexpr bool X4 = !SWIGLU;
+  constexpr int NST = X4 ? FM * FN * 4 : FM * (SWIGLU ? FN / 2 : FN) * 8;
   // stores left in flight must fit the vmcnt counter (6 bits) with the loads
   constexpr bool OVERLAP = PERSIST && (S - 2) * INS + NST < 64;
   constexpr int NPEND = OVERLAP ? NST : 0;
@@ -506,9 +512,9 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
         }
       }
       bool full;
-      if constexpr (F32X4) {
-        full = store_tile_f32x4<FM, FN, TM, TN, BN>(p, t, wm, wn,
-                                                    [&](int i, int j, int v) { return acc[i][j][v]; });
+      if constexpr (X4) {
+        full = store_tile_x4<FM, FN, TM, TN, BN, OUT_F32>(p, t, wm, wn,
+                                                          [&](int i, int j, int v) { return acc[i][j][v]; });
       } else {
         full = t.row0 + wm * TM + TM <= t.row1 &&
                (long long)t.nt * (SWIGLU ? BN / 2 : BN) + wn * (SWIGLU ? TN / 2 : TN) +

@@ -110,7 +110,7 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
     }
     if (n >= p.N) n = p.N - 1;                       // columns past N: a valid row, never stored
     b_ptr[u] = base + n * wrow + h * 16;
-    s_ptr[u] = sbase + n * srow + h * 2;
+    s_ptr[u] = sbase + n * srow;                     // the step's 4 scale bytes; h picks 2 of them
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int row = BM + rb, ch = 4 * h + d;
@@ -118,8 +118,16 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
     }
   }
 
+  // Barrier of the K loop: this wave's LDS writes (and reads) complete, then the workgroup barrier.
+  // Not __syncthreads(): its memory fence would also wait for the global loads of the steps ahead,
+  // which are in flight in registers across the barrier.
+  auto lds_barrier = [] {
+    wait_lgkm();
+    barrier_lds();
+  };
   i32x4 ra[2][A_CH], rbw[2][B_HR];
   uint32_t rs[2][B_HR];
+  const int bsh = (tid % 2) * 16;                    // this thread's two scale bytes in the word
   auto load = [&](int kt, int set) {
     kt = kt < nk ? kt : nk - 1;                      // past the end: re-read the last step
 #pragma unroll
@@ -127,7 +135,7 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
 #pragma unroll
     for (int u = 0; u < B_HR; ++u) {
       rbw[set][u] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(b_ptr[u] + (long long)kt * 32));
-      rs[set][u] = *reinterpret_cast<const uint16_t*>(s_ptr[u] + (long long)kt * 4);
+      rs[set][u] = *reinterpret_cast<const uint32_t*>(s_ptr[u] + (long long)kt * 4);
     }
   };
   auto write = [&](int set, int stage) {
@@ -136,7 +144,8 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
     for (int u = 0; u < A_CH; ++u) *reinterpret_cast<i32x4*>(st + a_lds[u]) = ra[set][u];
 #pragma unroll
     for (int u = 0; u < B_HR; ++u) {
-      const float s0 = nv4_scale<0>(rs[set][u]), s1 = nv4_scale<1>(rs[set][u]);
+      const uint32_t w = rs[set][u] >> bsh;
+      const float s0 = nv4_scale<0>(w), s1 = nv4_scale<1>(w);
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         *reinterpret_cast<i32x4*>(st + b_lds[u][d]) =
@@ -158,6 +167,7 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
   auto step = [&](int kt, auto set_tag) {
     constexpr int cur = decltype(set_tag)::value;
     load(kt + 2, cur);                               // this set was written to LDS last step
+    MOE_SCHED_FENCE();                               // the loads go out before this step's MFMAs
     const char* lb = reinterpret_cast<const char*>(lds + cur * STAGE);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -174,14 +184,17 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    // step kt + 1 into the other stage (last read during step kt - 1, before the previous barrier)
+    // step kt + 1 into the other stage (last read during step kt - 1, before the previous barrier);
+    // fenced so that no part of it (whose operands wait for that step's loads) moves up into the
+    // MFMAs
+    MOE_SCHED_FENCE();
     if (kt + 1 < nk) write(cur ^ 1, cur ^ 1);
-    __syncthreads();
+    lds_barrier();
   };
   load(0, 0);
   load(1, 1);
   write(0, 0);
-  __syncthreads();
+  lds_barrier();
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
     step(kt, std::integral_constant<int, 0>{});

@@ -38,7 +38,6 @@ enum { QEPI_STORE_F32 = 0, QEPI_STORE_BF16 = 1, QEPI_SWIGLU_BF16 = 2, QEPI_SWIGL
 // m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel
 constexpr int kQStreamGroupM = 8;
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // Block scales of a K-step follow its operands in the LDS stage: MXFP4 E8M0 [128 A rows][8 B] then
 // [256 B rows][8 B]; MXFP8 E8M0 [128][4 B] then [256][4 B] and 512 spare bytes (the target of the
