@@ -18,7 +18,8 @@
 // layer's activation quantiser write them), A_scales: fp32 row scale of each A row, or null (1).
 //
 // Two kernels:
-//   * tile kernel (prefill-sized groups): 128 x 128 tiles, K-steps of 64 (four scale blocks).
+//   * tile kernel (prefill-sized groups): 256 x 256 tiles of 8 waves (128 x 128 tiles of 4 waves
+//     for groups under 256 rows), K-steps of 64 (four scale blocks).
 //     Both operands go global -> registers -> LDS (bf16, 16-byte chunks XOR-swizzled by row as in
 //     the bf16 kernels); B is dequantised on its way into LDS, once per workgroup and element, and
 //     the MFMAs (32 x 32 x 16 bf16) read both operands from LDS. Two LDS stages; each step's global
@@ -400,9 +401,8 @@ gemm_nv4_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   }
 }
 
-template <bool SWIGLU, bool OUT_F32>
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool OUT_F32>
 hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2;
   Grid g = make_grid(a, BM, SWIGLU ? BN / 2 : BN, 8, 64);
   if (g.total == 0) return hipSuccess;
   const size_t lds = 2 * (size_t)(BM + BN) * 64 * 2;
@@ -429,7 +429,11 @@ hipError_t run_choice(const GemmArgs& a, hipStream_t s) {
     if (a.K / 256 >= kNvSplitChunks) return run_stream<4, SWIGLU, OUT_F32>(a, s);
     return run_stream<1, SWIGLU, OUT_F32>(a, s);
   }
-  return run_tile<SWIGLU, OUT_F32>(a, s);
+  // groups of a full 256-row tile: 256 x 256 tiles of 8 waves (128 x 64 each, one workgroup per
+  // CU in 128 KB of LDS), twice the MFMAs per dequantised weight and per fragment read of the
+  // 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU), which serve smaller groups
+  if (per_group >= 256) return run_tile<256, 256, 2, 4, SWIGLU, OUT_F32>(a, s);
+  return run_tile<128, 128, 2, 2, SWIGLU, OUT_F32>(a, s);
 }
 
 }  // namespace

@@ -186,3 +186,9 @@ def test_grouped_gemm_nv4_prefill(epi, K):
 @pytest.mark.parametrize("counts", [[5, 0, 31, 2], [200, 90, 0, 313]])
 def test_grouped_gemm_nv4_without_a_scales(counts):
     _nv4_case("store_bf16", counts, 512, 256, with_a_scales=False)
+
+
+# groups of 33-255 rows on average (the 128 x 128 tiles): ragged groups, an empty one, one of 300
+@pytest.mark.parametrize("epi", ["store_bf16", "swiglu_bf16"])
+def test_grouped_gemm_nv4_mid_groups(epi):
+    _nv4_case(epi, [100, 150, 0, 60, 300, 7], 512, 384 if epi.startswith("store") else 256)
