@@ -40,6 +40,8 @@ def parse():
                    help="with --profile-only: read a 1 GiB buffer before every step (cold caches)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only copy a 1 GiB buffer three times (reference kernel for HBM counters)")
+    p.add_argument("--stream-ceiling", action="store_true",
+                   help="only time the HBM read probe (libmoe_probe.so) on a 1 GiB row-major matrix")
     p.add_argument("--all-workloads", action="store_true",
                    help="(default) add every workload's layer time and both roofline fractions")
     p.add_argument("--no-workloads", action="store_true",
@@ -286,6 +288,40 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 3}), flush=True)
 
 
+def stream_ceiling(steps):
+    """Read rate of a 1 GiB matrix of 8 KB rows with the decode kernels' weight-stream pattern (8 rows
+    x 128 bytes per load) and with 1 KB of one row per load, non-temporal, each read after a 1 GiB
+    read of another buffer (cold caches); HIP events on the probe's stream, median of `steps`."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_layer_softmax_amd", "libmoe_probe.so"))
+    lib.moe_probe_read_rows.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    flush = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(n // (64 * 8192) * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    res = {}
+    for rows in (8, 1):
+        ms = []
+        for _ in range(steps + 1):
+            with torch.cuda.stream(stream):
+                flush.sum()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                rc = lib.moe_probe_read_rows(src.data_ptr(), n, rows, out.data_ptr(),
+                                             ctypes.c_void_p(stream.cuda_stream))
+                b.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed: hipError {rc}")
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        t = float(np.median(ms[1:]))
+        res[f"{rows}_rows_per_load"] = {"ms": round(t, 4), "TB_per_s": round(n / (t * 1e-3) / 1e12, 3)}
+    print(json.dumps({"hbm_read_ceiling": res, "bytes": n, "row_bytes": 8192, "steps": steps}), flush=True)
+
+
 class Layer:
     """Device-resident inputs, weights, outputs and workspace of one workload."""
 
@@ -436,6 +472,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.stream_ceiling:
+        stream_ceiling(args.steps)
         return
     import torch
     import moe_inputs as mi

@@ -9,6 +9,8 @@ SRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
+# the HBM read-ceiling probe bench.py times (measurement only, a library of its own)
+PROBE_LIB = os.path.join(HERE, "libmoe_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "route.hip", "permute.hip", "gemm.hip", "gemm_q.hip", "gemm_fp8.hip",
@@ -44,6 +46,13 @@ def build(jobs=None):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, LIB)
+    probe_obj = _compile("probe.hip")
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, probe_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe link failed:\n" + r.stderr)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 
