@@ -476,7 +476,7 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
     if (cols % 64) return MOE_ERR_INVALID_ARG;
     return hip_status(launch_quant_nv4(src_dtype, batch, rows, cols, src,
                                        static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
-                                       nullptr, false, stream));
+                                       nullptr, kNv4Packed, stream));
   }
   return MOE_ERR_INVALID_ARG;
 }
@@ -554,9 +554,11 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
     xa = base + L.xq;
     xs = base + L.xs;
   } else if (dt == MOE_NVFP4) {
-    // NVFP4 per token, kept as the bf16 block values the GEMM consumes plus the row scales
+    // NVFP4 per token, kept as the fp16 block values the gate/up GEMM consumes (exact; its weights
+    // are then dequantised to fp16 too, one packed multiply per two elements) plus the row scales
     st = hip_status(launch_quant_nv4(io, 1, T, H, x, reinterpret_cast<uint8_t*>(base + L.xq),
-                                     nullptr, reinterpret_cast<float*>(base + L.xs), true, stream));
+                                     nullptr, reinterpret_cast<float*>(base + L.xs), kNv4ValuesF16,
+                                     stream));
     xa = base + L.xq;
     xs = base + L.xs;
   }
@@ -575,6 +577,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   a.A = xa;
   a.A_scales = xs;
   a.a_pitch = a_row_bytes(dt, H);
+  a.a_f16 = dt == MOE_NVFP4 ? 1 : 0;
   a.a_scale_rows = dt == MOE_FP8_E4M3 ? 128 : 1;
   a.a_rows = r2f;
   a.a_row_div = k;

@@ -17,6 +17,10 @@
 // A: bf16 [rows, K] holding the activation's block values q * s (exact; moe_permute and the
 // layer's activation quantiser write them), A_scales: fp32 row scale of each A row, or null (1).
 //
+// The layer's gate/up projection takes its activation block values as fp16 instead (exact as
+// well) and dequantises the weights to fp16 (F16), half the instructions per element of the bf16
+// form; the down projection's input h is bf16, so it keeps the bf16 form.
+//
 // Two kernels:
 //   * tile kernel (prefill-sized groups): 256 x 256 tiles of 8 waves (128 x 128 tiles of 4 waves
 //     for groups under 256 rows), K-steps of 64 (four scale blocks).
@@ -49,6 +53,27 @@ __device__ __forceinline__ float nv4_scale(uint32_t w) {
   return __builtin_amdgcn_cvt_f32_fp8(static_cast<int>(w), SEL);
 }
 
+// F16: the activation block values arrive as fp16 and the weights are dequantised to fp16 (one
+// packed multiply per two elements instead of two fp32 multiplies and a pack); the fp16 MFMA has the
+// bf16 rate. Operand fragments and the MFMAs of either form:
+template <bool F16>
+using Frag = std::conditional_t<F16, f16x8, bf16x8>;
+template <bool F16>
+__device__ __forceinline__ i32x4 dequant8(uint32_t w, float s) {
+  if constexpr (F16) return e2m1x8_times_f16(w, s);
+  else return e2m1x8_times(w, s);
+}
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(Frag<F16> a, Frag<F16> b, f32x16 c) {
+  if constexpr (F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(Frag<F16> a, Frag<F16> b, f32x4 c) {
+  if constexpr (F16) return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // fp32 row scales of the weight rows of a scale record (after its N * K/16 block-scale bytes)
 __device__ __forceinline__ const float* nv4_row_scales(const char* rec, const GemmArgs& p) {
   return reinterpret_cast<const float*>(rec + (long long)p.N * (p.K / 16));
@@ -57,7 +82,7 @@ __device__ __forceinline__ const float* nv4_row_scales(const char* rec, const Ge
 // ------------------------------------------------------------------------------------------------
 // Tile kernel
 // ------------------------------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool SWIGLU, bool OUT_F32>
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool OUT_F32, bool F16>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
   constexpr int NT = WM * WN * 64;
@@ -150,7 +175,7 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
 #pragma unroll
       for (int d = 0; d < 4; ++d)
         *reinterpret_cast<i32x4*>(st + b_lds[u][d]) =
-            e2m1x8_times(static_cast<uint32_t>(rbw[set][u][d]), d < 2 ? s0 : s1);
+            dequant8<F16>(static_cast<uint32_t>(rbw[set][u][d]), d < 2 ? s0 : s1);
     }
   };
 
@@ -172,18 +197,17 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
     const char* lb = reinterpret_cast<const char*>(lds + cur * STAGE);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 fa[FM], fb[FN];
+      Frag<F16> fa[FM], fb[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(lb + lane_off[s] + (wm * TM + i * 32) * BK * 2);
+        fa[i] = *reinterpret_cast<const Frag<F16>*>(lb + lane_off[s] + (wm * TM + i * 32) * BK * 2);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(lb + lane_off[s] + (BM + wn * TN + j * 32) * BK * 2);
+        fb[j] = *reinterpret_cast<const Frag<F16>*>(lb + lane_off[s] + (BM + wn * TN + j * 32) * BK * 2);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<F16>(fa[i], fb[j], acc[i][j]);
     }
     // step kt + 1 into the other stage (last read during step kt - 1, before the previous barrier);
     // fenced so that no part of it (whose operands wait for that step's loads) moves up into the
@@ -240,7 +264,7 @@ gemm_nv4_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
 // follows (its lane loads those same 8 elements), so the dot product is unchanged. The piece's two
 // scale blocks are bytes 8 (s / 4) + 2 kq and + 1 of the row's 16 scale bytes of the chunk.
 // ------------------------------------------------------------------------------------------------
-template <int KS, bool SWIGLU, bool OUT_F32>
+template <int KS, bool SWIGLU, bool OUT_F32, bool F16>
 __global__ void __launch_bounds__(64 * KS)
 gemm_nv4_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   constexpr int BM = 16;
@@ -321,16 +345,16 @@ gemm_nv4_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        bf16x8 wf[4];
+        Frag<F16> wf[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int lo = __builtin_amdgcn_ds_bpermute(src, wraw[set][j][0][q]);
           const int hi = __builtin_amdgcn_ds_bpermute(src, wraw[set][j][1][q]);
-          wf[j] = __builtin_bit_cast(bf16x8, e2m1x8_times(static_cast<uint32_t>(upper ? hi : lo), sc[j][q >> 1]));
+          wf[j] = __builtin_bit_cast(Frag<F16>, dequant8<F16>(static_cast<uint32_t>(upper ? hi : lo), sc[j][q >> 1]));
         }
-        const bf16x8 a = __builtin_bit_cast(bf16x8, av[set][hh][q]);
+        const Frag<F16> a = __builtin_bit_cast(Frag<F16>, av[set][hh][q]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], a, acc[j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) acc[j] = mfma16<F16>(wf[j], a, acc[j]);
       }
     }
   };
@@ -401,39 +425,39 @@ gemm_nv4_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool SWIGLU, bool OUT_F32>
+template <int BM, int BN, int WM, int WN, bool SWIGLU, bool OUT_F32, bool F16>
 hipError_t run_tile(const GemmArgs& a, hipStream_t s) {
   Grid g = make_grid(a, BM, SWIGLU ? BN / 2 : BN, 8, 64);
   if (g.total == 0) return hipSuccess;
   const size_t lds = 2 * (size_t)(BM + BN) * 64 * 2;
-  gemm_nv4_tile_kernel<BM, BN, WM, WN, SWIGLU, OUT_F32><<<dim3(g.blocks), dim3(WM * WN * 64), lds, s>>>(
+  gemm_nv4_tile_kernel<BM, BN, WM, WN, SWIGLU, OUT_F32, F16><<<dim3(g.blocks), dim3(WM * WN * 64), lds, s>>>(
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm);
   return hipGetLastError();
 }
 
-template <int KS, bool SWIGLU, bool OUT_F32>
+template <int KS, bool SWIGLU, bool OUT_F32, bool F16>
 hipError_t run_stream(const GemmArgs& a, hipStream_t s) {
   Grid g = make_grid(a, 16, SWIGLU ? 32 : 64, kNvStreamGroupM, kNvStreamGroupM);
   if (g.total == 0) return hipSuccess;
-  gemm_nv4_stream_kernel<KS, SWIGLU, OUT_F32><<<dim3(g.blocks), dim3(64 * KS), 0, s>>>(
+  gemm_nv4_stream_kernel<KS, SWIGLU, OUT_F32, F16><<<dim3(g.blocks), dim3(64 * KS), 0, s>>>(
       a, g.n_tiles, g.x_tiles, g.total);
   return hipGetLastError();
 }
 
-template <bool SWIGLU, bool OUT_F32>
+template <bool SWIGLU, bool OUT_F32, bool F16 = false>
 hipError_t run_choice(const GemmArgs& a, hipStream_t s) {
   const long long rows = (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) + a.x_rows;
   const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
   const long long per_group = groups ? rows / groups : rows;
   if (per_group <= 32) {
-    if (a.K / 256 >= kNvSplitChunks) return run_stream<4, SWIGLU, OUT_F32>(a, s);
-    return run_stream<1, SWIGLU, OUT_F32>(a, s);
+    if (a.K / 256 >= kNvSplitChunks) return run_stream<4, SWIGLU, OUT_F32, F16>(a, s);
+    return run_stream<1, SWIGLU, OUT_F32, F16>(a, s);
   }
   // groups of a full 256-row tile: 256 x 256 tiles of 8 waves (128 x 64 each, one workgroup per
   // CU in 128 KB of LDS), twice the MFMAs per dequantised weight and per fragment read of the
   // 128 x 128 tiles (4 waves of 64 x 64, two workgroups per CU), which serve smaller groups
-  if (per_group >= 256) return run_tile<256, 256, 2, 4, SWIGLU, OUT_F32>(a, s);
-  return run_tile<128, 128, 2, 2, SWIGLU, OUT_F32>(a, s);
+  if (per_group >= 256) return run_tile<256, 256, 2, 4, SWIGLU, OUT_F32, F16>(a, s);
+  return run_tile<128, 128, 2, 2, SWIGLU, OUT_F32, F16>(a, s);
 }
 
 }  // namespace
@@ -442,6 +466,10 @@ hipError_t run_choice(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_gemm_nv4(const GemmArgs& a, hipStream_t s) {
   if (a.K % 256 || a.N % 128) return hipErrorInvalidValue;
   const bool swiglu = a.epilogue == MOE_EPI_SWIGLU;
+  if (a.a_f16) {                                     // the layer's gate/up projection only
+    if (!swiglu || a.out_dtype != MOE_BF16) return hipErrorInvalidValue;
+    return run_choice<true, false, true>(a, s);
+  }
   if (a.out_dtype == MOE_F32) return swiglu ? run_choice<true, true>(a, s) : run_choice<false, true>(a, s);
   if (a.out_dtype == MOE_BF16) return swiglu ? run_choice<true, false>(a, s) : run_choice<false, false>(a, s);
   return hipErrorInvalidValue;

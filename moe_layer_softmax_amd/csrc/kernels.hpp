@@ -36,6 +36,8 @@ struct GemmArgs {
   void* C;
   void* C_scales;
   long long c_pitch;    // bytes between C rows
+  int a_f16;            // NVFP4 only: A holds the block values as fp16 (else bf16); the product runs
+                        // on the fp16 MFMA with the weights dequantised to fp16
 };
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
@@ -84,11 +86,12 @@ hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const 
                             uint8_t* packed, uint8_t* scales, hipStream_t s);
 hipError_t launch_quant_mx8(int src_dtype, int batch, int rows, int cols, const void* src,
                             uint8_t* codes, uint8_t* scales, hipStream_t s);
-// NVFP4: dequant = false: packed [batch*rows, cols/2] + per-matrix scale records (e4m3 [rows,
-// cols/16] then fp32 [rows]) in `scales`; dequant = true: bf16 block values [batch*rows, cols] in
-// `out` and fp32 row scales in `row_scale`. cols % 64 == 0.
+// NVFP4: out_mode 0: packed [batch*rows, cols/2] + per-matrix scale records (e4m3 [rows, cols/16]
+// then fp32 [rows]) in `scales`; out_mode 1 / 2: the block values as bf16 / fp16 [batch*rows, cols]
+// in `out` and fp32 row scales in `row_scale`. cols % 64 == 0.
+enum { kNv4Packed = 0, kNv4ValuesBf16 = 1, kNv4ValuesF16 = 2 };
 hipError_t launch_quant_nv4(int src_dtype, int batch, int rows, int cols, const void* src,
-                            uint8_t* out, uint8_t* scales, float* row_scale, bool dequant,
+                            uint8_t* out, uint8_t* scales, float* row_scale, int out_mode,
                             hipStream_t s);
 // a_perm[r] = bf16 block values of packed NVFP4 row row_to_flat[r] / k (scales: one record of T
 // rows), a_perm_scales[r] = its row scale; rows r < *offsets_end. cols % 64 == 0.
@@ -96,8 +99,8 @@ hipError_t launch_gather_nv4(long long max_rows, int k, int T, int cols, const i
                              const int32_t* row_to_flat, const uint8_t* packed,
                              const uint8_t* scales, uint16_t* dst, float* dst_scales,
                              hipStream_t s);
-// NVFP4 weights (B) with bf16 block-value activations (A) and fp32 row scales (A_scales, may be
-// null); K % 256 == 0, N % 128 == 0
+// NVFP4 weights (B) with bf16 (or, a_f16, fp16) block-value activations (A) and fp32 row scales
+// (A_scales, may be null); K % 256 == 0, N % 128 == 0; a_f16 needs SWIGLU with bf16 out
 hipError_t launch_gemm_nv4(const GemmArgs& a, hipStream_t s);
 
 }  // namespace moe

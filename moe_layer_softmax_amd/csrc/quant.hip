@@ -148,16 +148,17 @@ __global__ void __launch_bounds__(256) quant_mx8_kernel(long long groups, const 
 // codes of v / d (signed zeros when d = 0). Every step is one IEEE fp32 operation, taken in the
 // same order as the definition, so the codes are exact decisions. The row is read twice (the
 // second pass finds it in L2).
-//   DEQ = false: packed codes [rows, cols/2]; scale record per matrix of `rows` rows: e4m3 block
-//                scales [rows, cols/16], then fp32 row scales [rows].
-//   DEQ = true:  the block values q * s as bf16 [rows, cols] (exact) and the row scales g [rows]
-//                (the layer's activation operand).
-template <bool SRC_BF16, bool DEQ>
+//   MODE kNv4Packed: packed codes [rows, cols/2]; scale record per matrix of `rows` rows: e4m3
+//                block scales [rows, cols/16], then fp32 row scales [rows].
+//   MODE kNv4ValuesBf16 / kNv4ValuesF16: the block values q * s as bf16 / fp16 [rows, cols] (exact
+//                in both) and the row scales g [rows] (the layer's activation operand).
+template <bool SRC_BF16, int MODE>
 __global__ void __launch_bounds__(256) quant_nv4_kernel(long long total_rows, int rows, int cols,
                                                         const void* __restrict__ src,
                                                         uint8_t* __restrict__ out,
                                                         uint8_t* __restrict__ scales,
                                                         float* __restrict__ row_scale) {
+  constexpr bool DEQ = MODE != kNv4Packed;
   const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= total_rows) return;                   // wave-uniform
   const int lane = threadIdx.x & 63;
@@ -201,7 +202,8 @@ __global__ void __launch_bounds__(256) quant_nv4_kernel(long long total_rows, in
       *reinterpret_cast<uint32_t*>(out + (size_t)row * (cols / 2) + (size_t)c * 4) = word;
       if ((c & 1) == 0) bs[c / 2] = sc;
     } else {
-      *reinterpret_cast<i32x4*>(out + base * 2 + (size_t)c * 16) = e2m1x8_times(word, sv);
+      *reinterpret_cast<i32x4*>(out + base * 2 + (size_t)c * 16) =
+          MODE == kNv4ValuesF16 ? e2m1x8_times_f16(word, sv) : e2m1x8_times(word, sv);
     }
   }
 }
@@ -265,19 +267,18 @@ hipError_t launch_quant_mx4(int src_dtype, int batch, int rows, int cols, const 
 }
 
 hipError_t launch_quant_nv4(int src_dtype, int batch, int rows, int cols, const void* src,
-                            uint8_t* out, uint8_t* scales, float* row_scale, bool dequant,
+                            uint8_t* out, uint8_t* scales, float* row_scale, int out_mode,
                             hipStream_t s) {
   const long long total = (long long)batch * rows;
   if (total == 0) return hipSuccess;
   dim3 grid(static_cast<unsigned>((total + 3) / 4));
   const bool bf = src_dtype == MOE_BF16;
-  if (dequant) {
-    if (bf) quant_nv4_kernel<true, true><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
-    else quant_nv4_kernel<false, true><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
-  } else {
-    if (bf) quant_nv4_kernel<true, false><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
-    else quant_nv4_kernel<false, false><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale);
-  }
+#define MOE_RUN(BF, MODE) quant_nv4_kernel<BF, MODE><<<grid, 256, 0, s>>>(total, rows, cols, src, out, scales, row_scale)
+  if (out_mode == kNv4Packed) { if (bf) MOE_RUN(true, kNv4Packed); else MOE_RUN(false, kNv4Packed); }
+  else if (out_mode == kNv4ValuesBf16) { if (bf) MOE_RUN(true, kNv4ValuesBf16); else MOE_RUN(false, kNv4ValuesBf16); }
+  else if (out_mode == kNv4ValuesF16) { if (bf) MOE_RUN(true, kNv4ValuesF16); else MOE_RUN(false, kNv4ValuesF16); }
+  else return hipErrorInvalidValue;
+#undef MOE_RUN
   return hipGetLastError();
 }
 

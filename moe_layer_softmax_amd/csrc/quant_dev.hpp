@@ -80,6 +80,21 @@ __device__ __forceinline__ i32x4 e2m1x8_times(uint32_t w, float s) {
                e2m1_pair_times<3>(w, s)};
 }
 
+// The same as fp16 (8 values, 16 bytes): q * s is exact in fp16 as well (at most 6 significant bits
+// in [2^-10, 2688], inside fp16's normal range), and one packed fp16 multiply scales two elements.
+// s must be exact in fp16 (an e4m3 value is).
+template <int B>
+__device__ __forceinline__ int e2m1_pair_times_f16(uint32_t w, f16x2 s2) {
+  const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, B) * s2;   // byte B: 2B, 2B + 1
+  return __builtin_bit_cast(int, v);
+}
+__device__ __forceinline__ i32x4 e2m1x8_times_f16(uint32_t w, float s) {
+  const _Float16 h = static_cast<_Float16>(s);
+  const f16x2 s2 = f16x2{h, h};
+  return i32x4{e2m1_pair_times_f16<0>(w, s2), e2m1_pair_times_f16<1>(w, s2),
+               e2m1_pair_times_f16<2>(w, s2), e2m1_pair_times_f16<3>(w, s2)};
+}
+
 // shared exponent of an MX block: floor(log2(amax)) minus the element format's largest exponent
 // (2 for e2m1, 8 for e4m3), clamped to [-127, 127]; -127 for amax = 0
 template <int EMAX = 2>
