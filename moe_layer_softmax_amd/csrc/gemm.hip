@@ -908,13 +908,18 @@ hipError_t run_f32(const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Router logits of many tokens (an extra group of T rows, no routed groups, N = E experts): 64 (or
-// 32) tokens x 128 experts per workgroup, so the tokens are read from HBM once per 128 experts, with
-// 6-7 LDS stages (one workgroup per CU) to keep ~120 KB of loads in flight per CU.
+// Router logits of many tokens (an extra group of T rows, no routed groups, N = E experts): the
+// largest of three tile shapes that still gives at least one workgroup per CU — 128 tokens x 128
+// experts (4 waves of 64 x 64, 4 LDS stages), 64 x 128 (4 waves of 32 x 64, 6 stages), else 32 x 128
+// (4 waves of 32 x 32 on 16 x 16 MFMAs, 7 stages). Measured with the top-k kernel (median of 10
+// calls): 16384 tokens x 4096 x 128 experts 66 -> 58.5 us (64 x 128), 8192 x 4096 x 512 92 -> 69 us
+// and 16384 x 7168 x 256 132 -> 99 us (128 x 128); 4096 x 7168 x 256 stays on 32 x 128 (49 us;
+// the larger tiles leave CUs idle there).
 hipError_t launch_gemm_router(const GemmArgs& a, hipStream_t s) {
   if (a.dtype != MOE_BF16) return launch_gemm(a, s);
-  if ((long long)((a.x_rows + 63) / 64) * ((a.N + 127) / 128) >= 256)
-    return run_bf16<64, 128, 1, 4, 16, 64, 6>(a, s);
+  const long long e_tiles = (a.N + 127) / 128;
+  if ((long long)((a.x_rows + 127) / 128) * e_tiles >= 256) return run_bf16<128, 128, 2, 2, 32, 64, 4>(a, s);
+  if ((long long)((a.x_rows + 63) / 64) * e_tiles >= 256) return run_bf16<64, 128, 2, 2, 32, 64, 6>(a, s);
   return run_bf16<32, 128, 1, 4, 16, 64, 7>(a, s);
 }
 

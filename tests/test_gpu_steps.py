@@ -182,14 +182,15 @@ def _zipf_wl(E):
 
 
 # Router shapes: few tokens (K-split partial sums finished by the top-k kernel), more tokens
-# (64-token waves, split or not), enough tokens for the tiled router GEMM (with a ragged last tile),
+# (64-token waves, split or not), enough tokens for each tile shape of the router GEMM (32, 64 and
+# 128 tokens per tile, ragged last tiles),
 # an expert count that is not a multiple of 16 (grouped-GEMM router) and the fp32 router.
 @pytest.mark.parametrize("T,H,E,k,zipf,scoring", [(300, 4096, 128, 8, 1.1, 0), (64, 7168, 256, 8, 1.2, 1),
                                                   (40, 4096, 512, 10, 0.0, 0), (33, 256, 8, 2, 0.0, 0),
                                                   (64, 4096, 128, 8, 1.1, 0), (1, 4096, 128, 8, 1.1, 0),
                                                   (1500, 4096, 256, 8, 0.0, 1), (4096, 4096, 128, 8, 1.1, 0),
                                                   (100, 4096, 72, 4, 0.0, 0), (17, 1024, 16, 16, 0.0, 0),
-                                                  (8192, 4096, 512, 10, 0.0, 0), (16400, 4096, 128, 8, 1.1, 0)])
+                                                  (8200, 4096, 512, 10, 0.0, 0), (16400, 4096, 128, 8, 1.1, 0)])
 def test_route_from_x(T, H, E, k, zipf, scoring):
     from moe_inputs.workloads import Workload
     io = 0 if H == 256 else 1
