@@ -208,17 +208,18 @@ def ep_sweep(stream, steps):
         s2r = torch.empty((T, k), dtype=torch.int32, device="cuda")
         r2f = torch.empty(T * k, dtype=torch.int32, device="cuda")
         h = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
-        y = torch.empty((T * k, H), dtype=torch.float32, device="cuda")
+        y = torch.empty((T * k, moe.moe_f16_scaled_row_bytes(H)), dtype=torch.uint8, device="cuda")
         o = torch.empty((T, H), dtype=torch.float32, device="cuda")
         g_up = moe.moe_gemm_desc(E_loc, T * k, H, I, moe.MOE_BF16, moe.MOE_EPI_SWIGLU, moe.MOE_BF16, k, 1)
-        g_dn = moe.moe_gemm_desc(E_loc, T * k, I, H, moe.MOE_BF16, moe.MOE_EPI_STORE, moe.MOE_F32, 1, 1)
+        g_dn = moe.moe_gemm_desc(E_loc, T * k, I, H, moe.MOE_BF16, moe.MOE_EPI_STORE,
+                                 moe.MOE_F16_SCALED, 1, 1)
         perm = lambda: moe.moe_permute(d, ids, None, None, counts, offsets, s2r, r2f, None, None, ws,
                                        stream)
         gemms = lambda: (moe.moe_grouped_gemm(g_up, x, None, r2f, wg, None, wu, None, offsets, h,
                                               None, stream),
                          moe.moe_grouped_gemm(g_dn, h, None, None, wd, None, None, None, offsets, y,
                                               None, stream))
-        comb = lambda: moe.moe_combine(d, moe.MOE_F32, y, tw, s2r, None, o, stream)
+        comb = lambda: moe.moe_combine(d, moe.MOE_F16_SCALED, y, tw, s2r, None, o, stream)
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
         with torch.cuda.stream(stream):
             perm(); gemms(); comb()
@@ -379,11 +380,11 @@ def step_breakdown(L, stream, iters):
     r2f = torch.empty(slots, dtype=torch.int32, device=dev)
     pws = torch.empty(max(moe.moe_permute_workspace_bytes(d), 16), dtype=torch.uint8, device=dev)
     h = torch.empty((slots, wl.I), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((slots, wl.H), dtype=torch.float32, device=dev)
+    y = torch.empty((slots, moe.moe_f16_scaled_row_bytes(wl.H)), dtype=torch.uint8, device=dev)
     g_up = moe.moe_gemm_desc(wl.E_loc, slots, wl.H, wl.I, moe.MOE_BF16, moe.MOE_EPI_SWIGLU,
                              moe.MOE_BF16, wl.k, 1)
     g_dn = moe.moe_gemm_desc(wl.E_loc, slots, wl.I, wl.H, moe.MOE_BF16, moe.MOE_EPI_STORE,
-                             moe.MOE_F32, 1, 1)
+                             moe.MOE_F16_SCALED, 1, 1)
     _, wg, wu, wd = L.w_dev
     names = ["route", "permute", "gemm_gate_up", "gemm_down", "combine"]
     calls = [
@@ -394,7 +395,7 @@ def step_breakdown(L, stream, iters):
                                      stream),
         lambda: moe.moe_grouped_gemm(g_dn, h, None, None, wd, None, None, None, offsets, y, None,
                                      stream),
-        lambda: moe.moe_combine(d, moe.MOE_F32, y, L.w, s2r, None, L.out, stream),
+        lambda: moe.moe_combine(d, moe.MOE_F16_SCALED, y, L.w, s2r, None, L.out, stream),
     ]
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
           for _ in range(iters)]

@@ -72,13 +72,28 @@ typedef enum {
   MOE_MXFP8 = 4,      /* OCP e4m3 bytes with an E8M0 scale byte per 32 consecutive elements
                          along K (OCP MX v1.0 MXFP8; the MoE GEMM format of "Hosting Qwen on
                          Blackwell", section "Quantization")                                  */
-  MOE_NVFP4 = 5       /* NVFP4: OCP e2m1, two per byte as MXFP4, with an e4m3 scale per 16
+  MOE_NVFP4 = 5,      /* NVFP4: OCP e2m1, two per byte as MXFP4, with an e4m3 scale per 16
                          consecutive elements along K ("CuTeDSL at Perplexity", section
                          "Blackwell": 16-element absmax groups; "Driving vLLM WideEP ... (Part
                          I)", lower-precision operations: 4-bit weights with FP8 per-group
                          scales) and an fp32 scale per row (NVFP4's second level, per tensor in
                          NVIDIA's recipe, per row here). Element value: e2m1 * s_block * g_row */
+  MOE_F16_SCALED = 6  /* expert outputs only (the down projection's y): fp16 values with one fp32
+                         power-of-two scale per row per 64 consecutive columns, value = f16 *
+                         scale. A row of `cols` values (cols % 64 == 0) is its cols fp16 values
+                         followed by its cols / 64 fp32 scales, padded to a multiple of 16 bytes
+                         (moe_f16_scaled_row_bytes). A block whose largest magnitude m lies in
+                         [2^(e-1), 2^e) gets the scale 2^max(e - 15, -126): its scaled values stay
+                         below 2^15, inside fp16's range, and each is rounded (to nearest even) to
+                         within 2^-11 m. Written by the grouped GEMM (bf16 experts, STORE), read
+                         by the combine: half the bytes of fp32 rows, and at the block maximum
+                         four times the precision of bf16 rows */
 } moe_dtype;
+
+/* bytes of one MOE_F16_SCALED row of `cols` values (cols % 64 == 0) */
+static inline int64_t moe_f16_scaled_row_bytes(int64_t cols) {
+  return 2 * cols + (cols / 64 * 4 + 15) / 16 * 16;
+}
 
 typedef enum { MOE_SOFTMAX = 0, MOE_SIGMOID = 1 } moe_scoring;
 typedef enum { MOE_EPI_STORE = 0, MOE_EPI_SWIGLU = 1 } moe_epilogue;
@@ -199,7 +214,8 @@ size_t moe_permute_workspace_bytes(const moe_desc* d);
  *   SWIGLU: C[r, :N]  = silu(A[a(r)] . B[g]^T) * (A[a(r)] . B2[g]^T) (B[g], B2[g]: [N, K])
  * where a(r) = r, or a(r) = a_rows[r] / a_row_div when a_rows != NULL (gathering rows of A).
  * dtype is the format of A and B (see moe_weights for B and its scales; A and its scales follow
- * moe_permute's a_perm). out_dtype: STORE -> MOE_F32 | MOE_BF16; SWIGLU -> MOE_F32 | MOE_BF16, or
+ * moe_permute's a_perm). out_dtype: STORE -> MOE_F32 | MOE_BF16 (bf16 A and B also
+ * MOE_F16_SCALED: C rows of moe_f16_scaled_row_bytes(N) bytes); SWIGLU -> MOE_F32 | MOE_BF16, or
  * the next GEMM's input format (MOE_FP8_E4M3: fp32 C_scales [max_rows, N/128] per 1x128 block;
  * MOE_MXFP4 and MOE_MXFP8: C_scales [max_rows, N/32]). a_scale_rows: 128 when A's fp8 scales
  * are per 128-row block of A (a token-order x), else 1. Rows outside every group are not written.
@@ -233,7 +249,9 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
  * out[t, :] = sum_{j ascending, slot_to_row[t,j] >= 0} topk_w[t,j] * y[slot_to_row[t,j], :]
  *             (+ g_t * shared[t, :] if shared != NULL, g_t = shared_w[t], or 1 when shared_w is
  *             NULL), accumulated in fp32, rounded once to out_dtype.
- * y: [T*k, H] and shared: [T, H] (or NULL) in y_dtype (MOE_F32 or MOE_BF16); shared_w: [T] fp32
+ * y: [T*k, H] and shared: [T, H] (or NULL) in y_dtype (MOE_F32, MOE_BF16, or MOE_F16_SCALED
+ * with rows of moe_f16_scaled_row_bytes(H) bytes, whose values are taken as f16 * scale, exact in
+ * fp32); shared_w: [T] fp32
  * (or NULL; must be NULL when shared is); out: [T, H] in d->out_dtype. A token with no local
  * expert and no shared expert gets zeros. Pointers: 16-byte aligned. */
 moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const float* topk_w,
@@ -291,8 +309,8 @@ moe_status moe_quantize(int32_t dst_dtype, int32_t src_dtype, int32_t batch, int
  * workspace). out is this GPU's partial sum over its local experts plus the shared expert (times
  * its gate g_t when w->w_shared_gate is given).
  * Intermediate formats: h (the down projection's input) is in the expert format (bf16 for bf16
- * and NVFP4 experts); the per-slot expert outputs y are fp32 for fp32/bf16 experts and bf16 for
- * fp8/MXFP4/MXFP8/NVFP4. NVFP4 layers quantise x per token (moe_quantize's rule) and run the
+ * and NVFP4 experts); the per-slot expert outputs y are fp32 for fp32 experts, MOE_F16_SCALED for
+ * bf16 experts and bf16 for fp8/MXFP4/MXFP8/NVFP4. NVFP4 layers quantise x per token (moe_quantize's rule) and run the
  * GEMMs on its block values with the row scales applied after each dot product.
  * ws: moe_layer_workspace_bytes(d) bytes. */
 moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, const float* bias,

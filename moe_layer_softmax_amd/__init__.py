@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 # enums of include/moe.h
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8, MOE_NVFP4 = range(6)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP8, MOE_NVFP4, MOE_F16_SCALED = range(7)
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_EPI_STORE, MOE_EPI_SWIGLU = 0, 1
 
@@ -135,6 +135,11 @@ def moe_grouped_gemm(g, A, A_scales, a_rows, B, B_scales, B2, B2_scales, group_o
     _check(_lib.moe_grouped_gemm(ctypes.byref(g), _ptr(A), _ptr(A_scales), _ptr(a_rows), _ptr(B),
                                  _ptr(B_scales), _ptr(B2), _ptr(B2_scales), _ptr(group_offsets),
                                  _ptr(C), _ptr(C_scales), _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_f16_scaled_row_bytes(cols):
+    """Bytes of one MOE_F16_SCALED row (the header's inline function of the same name)."""
+    return 2 * cols + (cols // 64 * 4 + 15) // 16 * 16
 
 
 def moe_combine(d, y_dtype, y, topk_w, slot_to_row, shared, out, stream=None, shared_w=None):

@@ -48,12 +48,19 @@ bool h_quantised(int dt) { return dt == MOE_FP8_E4M3 || mx_format(dt); }
 // their bf16 block values
 long long a_row_bytes(int dt, long long cols);
 
-// format of the per-slot expert outputs y inside moe_layer: fp32 for fp32 and bf16 experts (a
-// token's output sums up to k weighted rows plus the shared expert's, which partly cancel: rounding
-// each row to bf16 measured ~2e-2 of the output RMS on the Qwen3.5-397B-shaped slices), bf16 for
-// the block-scaled formats
+// format of the per-slot expert outputs y inside moe_layer: fp32 for fp32 experts; scaled fp16
+// rows for bf16 experts (a token's output sums up to k weighted rows plus the shared expert's,
+// which partly cancel: rounding each row to bf16 measured ~2e-2 of the output RMS on the
+// Qwen3.5-397B-shaped slices, while fp16 with a power-of-two scale per 64 columns keeps 2^-11 of
+// each block's maximum at half the bytes of fp32); bf16 for the block-scaled formats
 int y_dtype_of(const moe_desc* d) {
-  return (d->expert_dtype == MOE_F32 || d->expert_dtype == MOE_BF16) ? MOE_F32 : MOE_BF16;
+  if (d->expert_dtype == MOE_F32) return MOE_F32;
+  return d->expert_dtype == MOE_BF16 ? MOE_F16_SCALED : MOE_BF16;
+}
+// bytes of one row of y (`cols` values) in format ydt
+long long y_row_bytes(int ydt, long long cols) {
+  if (ydt == MOE_F16_SCALED) return moe_f16_scaled_row_bytes(cols);
+  return cols * (ydt == MOE_F32 ? 4 : 2);
 }
 
 // bytes of one activation row of `cols` elements in expert format dt
@@ -193,7 +200,7 @@ LayerWs layer_ws(const moe_desc* d) {
     L.hsh = take(T * Is * io_bytes(d->io_dtype));
   }
   // y: routed rows, then (with a shared expert) its T rows
-  L.y = take((slots + (d->I_s ? T : 0)) * H * io_bytes(y_dtype_of(d)));
+  L.y = take((slots + (d->I_s ? T : 0)) * y_row_bytes(y_dtype_of(d), H));
   L.sw = take(d->I_s ? T * 4 : 0);
   L.total = o;
   return L;
@@ -386,6 +393,8 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
     if (requant && !ok_ptr(C_scales)) return MOE_ERR_INVALID_ARG;
     if (!requant && g->out_dtype != MOE_BF16 && !(g->epilogue == MOE_EPI_STORE && g->out_dtype == MOE_F32))
       return MOE_ERR_UNSUPPORTED;
+  } else if (g->out_dtype == MOE_F16_SCALED) {
+    if (g->dtype != MOE_BF16 || g->epilogue != MOE_EPI_STORE) return MOE_ERR_UNSUPPORTED;
   } else if (g->out_dtype != MOE_F32 && g->out_dtype != MOE_BF16) {
     return MOE_ERR_UNSUPPORTED;
   }
@@ -412,8 +421,7 @@ moe_status moe_grouped_gemm(const moe_gemm_desc* g, const void* A, const void* A
   a.bs_stride = scale_bytes(g->dtype, g->N, g->K);
   a.C = C;
   a.C_scales = C_scales;
-  a.c_pitch = g->out_dtype == g->dtype && quant ? row_bytes(g->dtype, g->N)
-                                                : (long long)g->N * (g->out_dtype == MOE_F32 ? 4 : 2);
+  a.c_pitch = g->out_dtype == g->dtype && quant ? row_bytes(g->dtype, g->N) : y_row_bytes(g->out_dtype, g->N);
   return hip_status(launch_gemm(a, stream));
 }
 
@@ -422,7 +430,8 @@ moe_status moe_combine(const moe_desc* d, int32_t y_dtype, const void* y, const 
                        void* out, hipStream_t stream) {
   moe_status st = check_desc(d);
   if (st != MOE_OK) return st;
-  if (!valid_io(y_dtype)) return MOE_ERR_INVALID_ARG;
+  if (!valid_io(y_dtype) && y_dtype != MOE_F16_SCALED) return MOE_ERR_INVALID_ARG;
+  if (y_dtype == MOE_F16_SCALED && d->H % 64) return MOE_ERR_INVALID_ARG;
   if (shared_w && !shared) return MOE_ERR_INVALID_ARG;
   if (d->T == 0) return MOE_OK;
   if (!ok_ptr(y) || !ok_ptr(topk_w) || !ok_ptr(slot_to_row) || !ok_ptr(out) || !ok_opt(shared) ||
@@ -662,7 +671,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
     b.xBs = w->sh_down_scales;
   }
   b.C = base + L.y;
-  b.c_pitch = (long long)H * io_bytes(ydt);
+  b.c_pitch = y_row_bytes(ydt, H);
   st = hip_status(launch_gemm(b, stream));
   if (st != MOE_OK) return st;
   if (shared_apart(d)) {
@@ -687,7 +696,7 @@ moe_status moe_layer(const moe_desc* d, const moe_weights* w, const void* x, con
   }
 
   // 6. combine (+ shared expert rows, times their per-token gate when the layer has one)
-  const void* shared = d->I_s ? base + L.y + (size_t)slots * H * io_bytes(ydt) : nullptr;
+  const void* shared = d->I_s ? base + L.y + (size_t)slots * y_row_bytes(ydt, H) : nullptr;
   float* sw = nullptr;
   if (d->I_s && w->w_shared_gate) {
     sw = reinterpret_cast<float*>(base + L.sw);

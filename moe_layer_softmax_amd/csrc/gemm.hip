@@ -32,15 +32,21 @@ namespace moe {
 constexpr int kStreamGroupM = 8;
 
 // STORE epilogue of 32 x 32 fragments with one store of 4 columns per lane and 4 rows (16 bytes
-// fp32, 8 bytes bf16): in a quad of lanes (4 consecutive columns) each lane holds 4 consecutive
-// rows of its column for entries 4g .. 4g + 3; two cross-lane exchanges (lane ^ 1, then lane ^ 2,
-// as DPP quad permutations) transpose the 4 x 4 block so lane q holds row (q & 1) * 2 + (q >> 1) of
-// the block, 4 columns. Stores are non-temporal (C is read by the next kernel from HBM anyway).
+// fp32, 8 bytes bf16 or fp16): in a quad of lanes (4 consecutive columns) each lane holds 4
+// consecutive rows of its column for entries 4g .. 4g + 3; two cross-lane exchanges (lane ^ 1,
+// then lane ^ 2, as DPP quad permutations) transpose the 4 x 4 block so lane q holds row
+// (q & 1) * 2 + (q >> 1) of the block, 4 columns. Stores are non-temporal (C is read by the next
+// kernel from HBM anyway).
+// F16S: MOE_F16_SCALED rows (TN = 64: one scale block per wave and row). The lanes holding one row
+// after the transposition differ in lane bits 2-4 (8 quads x 4 columns x FN fragments), so the
+// block maximum is a reduction over those lanes; lanes 0-3 and 32-35 store the scales.
 // Returns true when every row and column of the wave's block is inside the tile: the wave then
-// issued exactly FM * FN * 4 store instructions (callers count them in their vmcnt waits).
-template <int FM, int FN, int TM, int TN, int BN, bool OUT_F32, class AccAt>
+// issued exactly FM * FN * 4 store instructions, plus FM * 4 scale stores for F16S (callers count
+// them in their vmcnt waits).
+template <int FM, int FN, int TM, int TN, int BN, bool OUT_F32, bool F16S, class AccAt>
 __device__ __forceinline__ bool store_tile_x4(const GemmArgs& p, const Tile& t, int wm, int wn,
                                                  AccAt acc_at) {
+  static_assert(!F16S || (!OUT_F32 && TN == 64), "scaled fp16 rows: 64-column waves");
   const int lane = lane_id();
   const int q = lane & 3;
   const bool odd = q & 1, hi = q & 2;
@@ -49,28 +55,61 @@ __device__ __forceinline__ bool store_tile_x4(const GemmArgs& p, const Tile& t, 
   };
   using swap1 = std::integral_constant<int, 0xB1>;     // quad_perm [1, 0, 3, 2]: lane ^ 1
   using swap2 = std::integral_constant<int, 0x4E>;     // quad_perm [2, 3, 0, 1]: lane ^ 2
+  // the 4 columns of lane q's row of the 4 x 4 block of entries 4g .. 4g + 3 of fragment (i, j)
+  auto transpose = [&](int i, int j, int g) -> f32x4 {
+    const float a0 = acc_at(i, j, 4 * g), a1 = acc_at(i, j, 4 * g + 1);
+    const float a2 = acc_at(i, j, 4 * g + 2), a3 = acc_at(i, j, 4 * g + 3);
+    // step 1: even lanes keep rows 0, 1 and take the partner column's rows 0, 1; odd lanes keep
+    // rows 2, 3 and take the partner's rows 2, 3
+    const float r0 = dpp(odd ? a0 : a2, swap1{}), r1 = dpp(odd ? a1 : a3, swap1{});
+    const float x0 = odd ? r0 : a0, x1 = odd ? a2 : r0;
+    const float x2 = odd ? r1 : a1, x3 = odd ? a3 : r1;
+    // step 2: lanes 0, 1 keep their first row (x0, x1) and take the other column pair's; lanes
+    // 2, 3 keep their second row (x2, x3)
+    const float s0 = dpp(hi ? x0 : x2, swap2{}), s1 = dpp(hi ? x1 : x3, swap2{});
+    return hi ? f32x4{s0, s1, x2, x3} : f32x4{x0, x1, s0, s1};
+  };
   const int row_in = (lane / 32) * 4 + (q & 1) * 2 + (q >> 1);
-  const long long col0 = (long long)t.nt * BN + wn * TN + ((lane % 32) & ~3);
+  const long long c_blk = (long long)t.nt * BN + wn * TN;
+  const long long col0 = c_blk + ((lane % 32) & ~3);
   const int rbase = t.row0 + wm * TM;
-  const bool full = rbase + TM <= t.row1 && (long long)t.nt * BN + wn * TN + TN <= p.N;
+  const bool full = rbase + TM <= t.row1 && c_blk + TN <= p.N;
   char* C = static_cast<char*>(p.C);
+  if constexpr (F16S) {
+    const bool in_n = c_blk < p.N;                     // N % 64 == 0: the block is all in or out
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v[FN];
+        float m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          v[j] = transpose(i, j, g);
+          m = fmaxf(m, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+        }
+        const int e = f16s_exp(lanes_max<28>(m));
+        const int r = rbase + i * 32 + g * 8 + row_in;
+        if (full || (r < t.row1 && in_n)) {
+          char* crow = C + (long long)r * p.c_pitch;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const u32x2 w = u32x2{pack_f16x2_scaled(v[j][0], v[j][1], e), pack_f16x2_scaled(v[j][2], v[j][3], e)};
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(crow + (col0 + j * 32) * 2));
+          }
+          if ((lane & 28) == 0)
+            __builtin_nontemporal_store(f16s_scale(e), reinterpret_cast<float*>(crow + (long long)p.N * 2 + c_blk / 16));
+        }
+      }
+    return full;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const float a0 = acc_at(i, j, 4 * g), a1 = acc_at(i, j, 4 * g + 1);
-        const float a2 = acc_at(i, j, 4 * g + 2), a3 = acc_at(i, j, 4 * g + 3);
-        // step 1: even lanes keep rows 0, 1 and take the partner column's rows 0, 1; odd lanes
-        // keep rows 2, 3 and take the partner's rows 2, 3
-        const float r0 = dpp(odd ? a0 : a2, swap1{}), r1 = dpp(odd ? a1 : a3, swap1{});
-        const float x0 = odd ? r0 : a0, x1 = odd ? a2 : r0;
-        const float x2 = odd ? r1 : a1, x3 = odd ? a3 : r1;
-        // step 2: lanes 0, 1 keep their first row (x0, x1) and take the other column pair's;
-        // lanes 2, 3 keep their second row (x2, x3)
-        const float s0 = dpp(hi ? x0 : x2, swap2{}), s1 = dpp(hi ? x1 : x3, swap2{});
-        const f32x4 v = hi ? f32x4{s0, s1, x2, x3} : f32x4{x0, x1, s0, s1};
+        const f32x4 v = transpose(i, j, g);
         const int r = rbase + i * 32 + g * 8 + row_in;
         const long long col = col0 + j * 32;
         if (full || (r < t.row1 && col < p.N)) {
@@ -155,7 +194,7 @@ struct LoadPlan {
 };
 
 template <int BM, int BN, int WM, int WN, int MI, int BK, int S, bool SWIGLU, bool OUT_F32,
-          bool PERSIST>
+          bool PERSIST, bool F16S = false>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm, int nphys) {
   using Geo = SliceGeo<BK>;
@@ -299,7 +338,7 @@ gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total,
       if (more) lp.init(p, tn, wave, lane);
     }
     // ---- epilogue ---- (fp32 C of 256-row tiles, i.e. a large C, streamed past L2)
-    store_tile<MI, FM, FN, TM, TN, BN, SWIGLU, OUT_F32, (BM >= 256)>(p, t, wm, wn, [&](int i, int j, int v) -> float {
+    store_tile<MI, FM, FN, TM, TN, BN, SWIGLU, OUT_F32, (BM >= 256), F16S>(p, t, wm, wn, [&](int i, int j, int v) -> float {
       if constexpr (MI == 32) return acc32[i][j][v];
       else return acc16[i][j][v];
     });
@@ -353,7 +392,7 @@ __device__ __forceinline__ void phase_barrier() {
 #endif
 }
 
-template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST>
+template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST, bool F16S = false>
 __global__ void __launch_bounds__(512)
 gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm, int nphys) {
   constexpr int BM = 256, BN = 256, WN = 4, MI = 32, BK = 32;
@@ -401,7 +440,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   // for STORE (4 per 32 x 32 fragment, fp32 or bf16), otherwise 2-column stores (8 per fragment
   // pair row group, see store_tile).
   constexpr bool X4 = !SWIGLU;
-  constexpr int NST = X4 ? FM * FN * 4 : FM * (SWIGLU ? FN / 2 : FN) * 8;
+  constexpr int NST = X4 ? FM * FN * 4 + (F16S ? FM * 4 : 0) : FM * (SWIGLU ? FN / 2 : FN) * 8;
   // stores left in flight must fit the vmcnt counter (6 bits) with the loads
   constexpr bool OVERLAP = PERSIST && (S - 2) * INS + NST < 64;
   constexpr int NPEND = OVERLAP ? NST : 0;
@@ -513,7 +552,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
       }
       bool full;
       if constexpr (X4) {
-        full = store_tile_x4<FM, FN, TM, TN, BN, OUT_F32>(p, t, wm, wn,
+        full = store_tile_x4<FM, FN, TM, TN, BN, OUT_F32, F16S>(p, t, wm, wn,
                                                           [&](int i, int j, int v) { return acc[i][j][v]; });
       } else {
         full = t.row0 + wm * TM + TM <= t.row1 &&
@@ -563,7 +602,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 // flight per CU for the same registers per wave); their fp32 partial sums meet in LDS and wave 0
 // adds them in wave order (deterministic) before the epilogue.
 // ------------------------------------------------------------------------------------------------
-template <int FM, int KS, bool SWIGLU, bool OUT_F32>
+template <int FM, int KS, bool SWIGLU, bool OUT_F32, bool F16S = false>
 __global__ void __launch_bounds__(64 * KS)
 gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
@@ -686,6 +725,33 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 
   // acc[j][i][v]: weight row j * 16 + kq * 4 + v of the tile, C row row0 + i * 16 + lr
   char* C = static_cast<char*>(p.C);
+  if constexpr (F16S) {
+    // MOE_F16_SCALED rows: the tile's 64 columns are one scale block (N % 64 == 0, so every tile
+    // lies inside N); the lanes of one row (lr) differ in lane bits 4 and 5
+    static_assert(!SWIGLU && !OUT_F32, "scaled fp16 rows: STORE");
+    const long long c_blk = (long long)t.nt * 64;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      float v4[4][4], m = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          v4[j][v] = acc[j][i][v] + (p.bias ? p.bias[c_blk + j * 16 + kq * 4 + v] : 0.0f);
+          m = fmaxf(m, fabsf(v4[j][v]));
+        }
+      const int e = f16s_exp(lanes_max<48>(m));
+      const int r = t.row0 + i * 16 + lr;
+      if (r >= t.row1) continue;
+      char* crow = C + (long long)r * p.c_pitch;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint2*>(crow + (c_blk + j * 16 + kq * 4) * 2) =
+            make_uint2(pack_f16x2_scaled(v4[j][0], v4[j][1], e), pack_f16x2_scaled(v4[j][2], v4[j][3], e));
+      if (kq == 0) *reinterpret_cast<float*>(crow + (long long)p.N * 2 + c_blk / 16) = f16s_scale(e);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int r = t.row0 + i * 16 + lr;
@@ -844,13 +910,22 @@ hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) 
     if (slots > 0 && slots < blocks) blocks = slots;
   }
   dim3 grid(blocks), block(WM * WN * 64);
-#define MOE_RUN(SWI, F32)                                                                    \
-  gemm_bf16_pipe_kernel<BM, BN, WM, WN, MI, BK, S, SWI, F32, PERSIST><<<grid, block, lds_bytes, s>>>( \
+#define MOE_RUN(SWI, F32, F16S)                                                              \
+  gemm_bf16_pipe_kernel<BM, BN, WM, WN, MI, BK, S, SWI, F32, PERSIST, F16S><<<grid, block, lds_bytes, s>>>( \
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm, (int)g.blocks)
-  if (sw && f32) MOE_RUN(true, true);
-  else if (sw) MOE_RUN(true, false);
-  else if (f32) MOE_RUN(false, true);
-  else MOE_RUN(false, false);
+  if (a.out_dtype == MOE_F16_SCALED) {
+    // scaled fp16 rows need waves of 64 columns of 32 x 32 fragments
+    if constexpr (MI == 32 && BN / WN == 64) {
+      if (sw) return hipErrorInvalidValue;
+      MOE_RUN(false, false, true);
+    } else {
+      return hipErrorInvalidValue;
+    }
+  }
+  else if (sw && f32) MOE_RUN(true, true, false);
+  else if (sw) MOE_RUN(true, false, false);
+  else if (f32) MOE_RUN(false, true, false);
+  else MOE_RUN(false, false, false);
 #undef MOE_RUN
   return hipGetLastError();
 }
@@ -868,13 +943,17 @@ hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   dim3 grid(blocks), block(512);
   const bool f32 = a.out_dtype == MOE_F32;
   const size_t lds_bytes = (size_t)S * (256 + 256) * 32 * sizeof(uint16_t);
-#define MOE_RUN(SWI, F32)                                                                        \
-  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST><<<grid, block, lds_bytes, s>>>(                     \
+#define MOE_RUN(SWI, F32, F16S)                                                                  \
+  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST, F16S><<<grid, block, lds_bytes, s>>>(               \
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm, (int)g.blocks)
-  if (sw && f32) MOE_RUN(true, true);
-  else if (sw) MOE_RUN(true, false);
-  else if (f32) MOE_RUN(false, true);
-  else MOE_RUN(false, false);
+  if (a.out_dtype == MOE_F16_SCALED) {
+    if (sw) return hipErrorInvalidValue;
+    MOE_RUN(false, false, true);
+  }
+  else if (sw && f32) MOE_RUN(true, true, false);
+  else if (sw) MOE_RUN(true, false, false);
+  else if (f32) MOE_RUN(false, true, false);
+  else MOE_RUN(false, false, false);
 #undef MOE_RUN
   return hipGetLastError();
 }
@@ -886,12 +965,16 @@ hipError_t run_bf16_stream(const GemmArgs& a, hipStream_t s) {
   if (g.total == 0) return hipSuccess;
   dim3 grid(g.blocks), block(64 * KS);
   const bool f32 = a.out_dtype == MOE_F32;
-#define MOE_RUN(SWI, F32) \
-  gemm_bf16_stream_kernel<FM, KS, SWI, F32><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.total)
-  if (sw && f32) MOE_RUN(true, true);
-  else if (sw) MOE_RUN(true, false);
-  else if (f32) MOE_RUN(false, true);
-  else MOE_RUN(false, false);
+#define MOE_RUN(SWI, F32, F16S) \
+  gemm_bf16_stream_kernel<FM, KS, SWI, F32, F16S><<<grid, block, 0, s>>>(a, g.n_tiles, g.x_tiles, g.total)
+  if (a.out_dtype == MOE_F16_SCALED) {
+    if (sw) return hipErrorInvalidValue;
+    MOE_RUN(false, false, true);
+  }
+  else if (sw && f32) MOE_RUN(true, true, false);
+  else if (sw) MOE_RUN(true, false, false);
+  else if (f32) MOE_RUN(false, true, false);
+  else MOE_RUN(false, false, false);
 #undef MOE_RUN
   return hipGetLastError();
 }

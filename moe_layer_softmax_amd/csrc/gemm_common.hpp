@@ -128,6 +128,38 @@ __device__ __forceinline__ void wait_vmem_n() {
 #endif
 }
 
+// ---- MOE_F16_SCALED rows: fp16 values, then one fp32 power-of-two scale per 64 columns -----------
+// Maximum over the lanes that differ from this one only in the lane-index bits of MASK (bits 2 and
+// 3 only together: two rotations within a 16-lane row). Every lane must execute it.
+template <int MASK>
+__device__ __forceinline__ float lanes_max(float v) {
+  static_assert((MASK & 12) == 0 || (MASK & 12) == 12, "bits 2 and 3 go together");
+  auto dpp = [](float x, auto ctrl) -> float {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if constexpr (MASK & 1) v = fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{}));    // lane ^ 1
+  if constexpr (MASK & 2) v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // lane ^ 2
+  if constexpr (MASK & 12) {
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x124>{}));                         // row_ror 4
+    v = fmaxf(v, dpp(v, std::integral_constant<int, 0x128>{}));                         // row_ror 8
+  }
+  if constexpr (MASK & 16) v = fmaxf(v, __shfl_xor(v, 16, kWave));
+  if constexpr (MASK & 32) v = fmaxf(v, __shfl_xor(v, 32, kWave));
+  return v;
+}
+// Scale exponent of a 64-column block whose largest magnitude is m: with m in [2^(e-1), 2^e) the
+// block is stored as its values times 2^-(e - 15), all below 2^15 in magnitude (fp16's largest
+// finite value is 65504), the block maximum keeping fp16's 11 significant bits; the exponent is
+// kept at or above -126 so that the stored scale is a normal fp32 number.
+__device__ __forceinline__ int f16s_exp(float m) { return max(__builtin_amdgcn_frexp_expf(m) - 15, -126); }
+// two values times 2^-e, rounded to fp16 (nearest even), packed low-first
+__device__ __forceinline__ uint32_t pack_f16x2_scaled(float lo, float hi, int e) {
+  const f16x2 h = f16x2{static_cast<_Float16>(__builtin_amdgcn_ldexpf(lo, -e)),
+                        static_cast<_Float16>(__builtin_amdgcn_ldexpf(hi, -e))};
+  return __builtin_bit_cast(uint32_t, h);
+}
+// the stored scale 2^e
+__device__ __forceinline__ float f16s_scale(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
 
 // Launch geometry of a grouped GEMM.
 struct Grid {
@@ -163,8 +195,12 @@ inline Grid make_grid(const GemmArgs& a, int BM, int n_cols_per_tile, int gm = 1
 // both columns of the second, so every store writes two adjacent values (4 bytes bf16, 8 fp32).
 // STREAM: fp32 stores are non-temporal (a large C that the next kernel reads from HBM anyway, e.g.
 // the down projection's y, is not left occupying L2; measured ~3% faster down projection).
+// F16S (STORE, 32 x 32 fragments, 64-column waves): MOE_F16_SCALED rows. After the pair swap the
+// lanes holding one row differ in lane bits 1-4 (16 lanes x 2 columns x FN fragments = the wave's
+// 64 columns), so the block maximum is a reduction over those lanes; lanes 0, 1, 32 and 33 store
+// the scale of their row.
 template <int MI, int FM, int FN, int TM, int TN, int BN, bool SWIGLU, bool OUT_F32,
-          bool STREAM = false, class AccAt>
+          bool STREAM = false, bool F16S = false, class AccAt>
 __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t, int wm, int wn,
                                            AccAt acc_at) {
   constexpr int VPF = (MI == 32) ? 16 : 4;
@@ -179,6 +215,38 @@ __device__ __forceinline__ void store_tile(const GemmArgs& p, const Tile& t, int
   };
   const int colw = (lane % MI) & ~1;                   // even column of this lane's pair
   char* C = static_cast<char*>(p.C);
+  if constexpr (F16S) {
+    static_assert(!SWIGLU && !OUT_F32 && MI == 32 && TN == 64, "scaled fp16 rows: 64-column waves");
+    const long long c_blk = (long long)t.nt * BN + wn * TN;   // first column of the wave's block
+    if (c_blk >= p.N) return;                                  // N % 64 == 0: all in or all out
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int u = 0; u < VPF / 2; ++u) {
+        float lo[FN], hi[FN], m = 0.0f;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const long long col = c_blk + j * MI + colw;
+          const float b0 = p.bias ? p.bias[col] : 0.0f, b1 = p.bias ? p.bias[col + 1] : 0.0f;
+          const float a = acc_at(i, j, 2 * u), b = acc_at(i, j, 2 * u + 1);
+          const float recv = swap_pair(odd ? a : b);
+          lo[j] = (odd ? recv : a) + b0;
+          hi[j] = (odd ? b : recv) + b1;
+          m = fmaxf(m, fmaxf(fabsf(lo[j]), fabsf(hi[j])));
+        }
+        const int e = f16s_exp(lanes_max<30>(m));
+        const int r = t.row0 + wm * TM + i * MI + row_of(odd ? 2 * u + 1 : 2 * u);
+        if (r < t.row1) {
+          char* crow = C + (long long)r * p.c_pitch;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            *reinterpret_cast<uint32_t*>(crow + (c_blk + j * MI + colw) * 2) = pack_f16x2_scaled(lo[j], hi[j], e);
+          if ((lane & 30) == 0)
+            *reinterpret_cast<float*>(crow + (long long)p.N * 2 + c_blk / 16) = f16s_scale(e);
+        }
+      }
+    return;
+  }
   auto put = [&](int r, long long col, float lo, float hi) {
     if (r >= t.row1 || col >= p.N) return;
     char* crow = C + (long long)r * p.c_pitch;

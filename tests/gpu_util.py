@@ -56,6 +56,49 @@ def tol_for(fmt):
     return 6e-2 if fmt in (mi.FMT_FP8, mi.FMT_MX4, mi.FMT_MX8, mi.FMT_NV4) else 2e-2
 
 
+# ---- scaled fp16 rows (MOE_F16_SCALED) -----------------------------------------------------
+
+def f16s_split(buf, cols):
+    """Rows of MOE_F16_SCALED bytes [rows, pitch] -> (fp16 values as float64 [rows, cols], fp32
+    scales as float64 [rows, cols / 64]): each row is its fp16 values, then one fp32 scale per 64
+    columns."""
+    buf = np.ascontiguousarray(buf)
+    vals = np.ascontiguousarray(buf[:, :2 * cols]).view(np.float16).astype(np.float64)
+    sc = np.ascontiguousarray(buf[:, 2 * cols:2 * cols + cols // 64 * 4]).view(np.float32).astype(np.float64)
+    return vals, sc
+
+
+def f16s_decode(buf, cols):
+    """The values of MOE_F16_SCALED rows: fp16 value times its 64-column block's scale."""
+    vals, sc = f16s_split(buf, cols)
+    return vals * np.repeat(sc, 64, axis=1)
+
+
+def f16s_pack(vals16, sc):
+    """MOE_F16_SCALED bytes [rows, pitch] from fp16 values [rows, cols] and fp32 scales
+    [rows, cols / 64] (the combine's inputs; the padding bytes after the scales are zero)."""
+    rows, cols = vals16.shape
+    buf = np.zeros((rows, moe.moe_f16_scaled_row_bytes(cols)), np.uint8)
+    buf[:, :2 * cols] = np.ascontiguousarray(vals16.astype(np.float16)).view(np.uint8).reshape(rows, 2 * cols)
+    buf[:, 2 * cols:2 * cols + cols // 64 * 4] = (
+        np.ascontiguousarray(sc.astype(np.float32)).view(np.uint8).reshape(rows, cols // 64 * 4))
+    return buf
+
+
+def check_f16s_format(vals, sc):
+    """Invariants of the rows the GEMM writes: every scale a power of two in normal fp32 range;
+    a block with a nonzero maximum m stores m / scale in [2^14, 2^15] unless its scale sits at the
+    2^-126 floor; an all-zero block has the scale 2^-15."""
+    mant, _ = np.frexp(sc)
+    assert np.all(mant == 0.5), "scales are powers of two"
+    assert np.all(sc >= 2.0 ** -126)
+    bmax = np.abs(vals).reshape(vals.shape[0], -1, 64).max(axis=2)
+    nz = bmax > 0
+    free = nz & (sc > 2.0 ** -126)
+    assert np.all((bmax[free] >= 2.0 ** 14) & (bmax[free] <= 2.0 ** 15))
+    assert np.all(sc[~nz] == 2.0 ** -15)
+
+
 # ---- quantised formats ------------------------------------------------------------------
 
 FMTS = {"fp8": (moe.MOE_FP8_E4M3, oracle.FP8), "mx4": (moe.MOE_MXFP4, oracle.MX4),

@@ -134,6 +134,23 @@ def test_workspace_too_small_and_unsupported():
     assert st == m.MOE_ERR_INVALID_ARG
 
 
+def test_f16_scaled_rules():
+    """MOE_F16_SCALED: rows of 2 * cols bytes of fp16 values then cols / 64 fp32 scales, padded to
+    16 bytes; an output of bf16 STORE GEMMs and an input of the combine (H % 64 == 0) only."""
+    import moe_layer_softmax_amd as m
+    lib = m.lib()
+    ok = ctypes.c_void_p(4096)
+    assert [m.moe_f16_scaled_row_bytes(c) for c in (64, 192, 4096, 7168)] == [144, 400, 8448, 14784]
+    d = _desc(H=272, io_dtype=m.MOE_F32, expert_dtype=m.MOE_F32)   # H % 64 != 0
+    assert lib.moe_combine(ctypes.byref(d), m.MOE_F16_SCALED, ok, ok, ok, None, None, ok, None) == m.MOE_ERR_INVALID_ARG
+    for dt, epi in ((m.MOE_BF16, m.MOE_EPI_SWIGLU), (m.MOE_F32, m.MOE_EPI_STORE),
+                    (m.MOE_FP8_E4M3, m.MOE_EPI_STORE), (m.MOE_MXFP4, m.MOE_EPI_STORE),
+                    (m.MOE_MXFP8, m.MOE_EPI_STORE), (m.MOE_NVFP4, m.MOE_EPI_STORE)):
+        g = m.moe_gemm_desc(2, 64, 512, 256, dt, epi, m.MOE_F16_SCALED, 1, 1)
+        st = lib.moe_grouped_gemm(ctypes.byref(g), ok, ok, None, ok, ok, ok, ok, ok, ok, ok, None)
+        assert st == m.MOE_ERR_UNSUPPORTED, (dt, epi)
+
+
 def test_zero_tokens_is_a_no_op():
     import moe_layer_softmax_amd as m
     lib = m.lib()

@@ -9,7 +9,8 @@ import moe_layer_softmax_amd as moe
 import oracle
 from moe_inputs import gen
 
-from gpu_util import (gamma, gpu_quant, rel_err, routing_consistent, to_dev, topk_numpy)
+from gpu_util import (check_f16s_format, f16s_pack, f16s_split, gamma, gpu_quant, rel_err,
+                      routing_consistent, to_dev, topk_numpy)
 
 pytestmark = pytest.mark.gpu
 
@@ -346,7 +347,10 @@ def test_permute_no_local_rows():
 # grouped GEMM
 # ---------------------------------------------------------------------------------------------
 
-def _gemm_case(counts, K, N, swiglu, gather, out_f32, dtype_in="bf16", seed=0):
+def _gemm_case(counts, K, N, swiglu, gather, out_f32, dtype_in="bf16", seed=0, f16s=False):
+    """The grouped GEMM through the C ABI against the oracle. f16s: C in MOE_F16_SCALED rows (A's
+    rows spread over eight decades, A's first row zero); returns C's bytes and also the oracle's
+    sum of |a| |b| per entry (the accumulation error bound's scale)."""
     rng = np.random.default_rng([seed, K, N, len(counts)])
     G = len(counts)
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
@@ -363,21 +367,31 @@ def _gemm_case(counts, K, N, swiglu, gather, out_f32, dtype_in="bf16", seed=0):
         kk = 1
         A = rnd(rng.standard_normal((max_rows, K)).astype(np.float32))
         a_rows = None
+    if f16s:
+        A = rnd(A * (10.0 ** rng.uniform(-4, 4, size=(A.shape[0], 1))).astype(np.float32))
+        A[0] = 0.0
     B = rnd((rng.standard_normal((G, N, K)) * 0.05).astype(np.float32))
     B2 = rnd((rng.standard_normal((G, N, K)) * 0.05).astype(np.float32)) if swiglu else None
+    out_dt = moe.MOE_F16_SCALED if f16s else moe.MOE_F32 if out_f32 else moe.MOE_BF16
     g = moe.moe_gemm_desc(G, max_rows, K, N, moe.MOE_F32 if f32 else moe.MOE_BF16,
-                          moe.MOE_EPI_SWIGLU if swiglu else moe.MOE_EPI_STORE,
-                          moe.MOE_F32 if out_f32 else moe.MOE_BF16, kk, 1)
-    C = torch.full((max_rows, N), 1024.0, dtype=torch.float32 if out_f32 else torch.bfloat16,
-                   device="cuda")
+                          moe.MOE_EPI_SWIGLU if swiglu else moe.MOE_EPI_STORE, out_dt, kk, 1)
+    if f16s:
+        C = torch.full((max_rows, moe.moe_f16_scaled_row_bytes(N)), 0xAB, dtype=torch.uint8, device="cuda")
+    else:
+        C = torch.full((max_rows, N), 1024.0, dtype=torch.float32 if out_f32 else torch.bfloat16,
+                       device="cuda")
     moe.moe_grouped_gemm(g, to_dev(A, tdt), None, None if a_rows is None else to_dev(a_rows, torch.int32),
                          to_dev(B, tdt), None, None if B2 is None else to_dev(B2, tdt), None,
                          to_dev(off, torch.int32), C, None)
     _sync()
-    Cg = C.float().cpu().numpy()
     M = oracle.Mat
     ref = oracle.grouped_gemm(off, M(oracle.F32, A), M(oracle.F32, B),
                               None if B2 is None else M(oracle.F32, B2), a_rows=a_rows, a_row_div=kk)
+    if f16s:
+        absref = oracle.grouped_gemm(off, M(oracle.F32, np.abs(A)), M(oracle.F32, np.abs(B)),
+                                     a_rows=a_rows, a_row_div=kk)
+        return C.cpu().numpy(), ref, R, absref
+    Cg = C.float().cpu().numpy()
     return Cg, ref, R
 
 
@@ -458,6 +472,41 @@ def test_grouped_gemm_bf16_many_tiles(K, out_f32):
     assert np.all(Cg[R:] == 1024.0)
 
 
+# MOE_F16_SCALED output rows (the layer's y for bf16 experts) from each bf16 kernel: decode-sized
+# groups (weight streaming; K = 4160 splits its steps over four waves), mid-sized groups (128 x 128
+# tiles) and large ones (the persistent 256 x 256 ping-pong tiles; N = 4160 leaves an n-tile whose
+# last three waves lie past N). Error bar per entry: fp32 accumulation, gamma_K * sum |a| |b|,
+# plus fp16 rounding of the scaled value, at most 8 (half an fp16 ulp below 2^15) times the
+# block's scale.
+@pytest.mark.parametrize("counts,K,N,gather", [
+    ([5, 0, 64, 65, 1, 12, 63, 2, 0, 30], 1536, 192, False),
+    ([5, 0, 64, 65, 1, 12, 63, 2, 0, 30], 4160, 256, True),
+    ([150, 97, 200, 0, 101], 512, 320, True),
+    ([1500, 1300, 0, 2701, 900, 5], 1536, 4160, False),
+    ([1500, 300, 0, 701], 128, 4096, True)])
+def test_grouped_gemm_bf16_f16_scaled_out(counts, K, N, gather):
+    Cb, ref, R, absref = _gemm_case(counts, K=K, N=N, swiglu=False, gather=gather, out_f32=False,
+                                    f16s=True)
+    vals, sc = f16s_split(Cb[:R], N)
+    check_f16s_format(vals, sc)
+    scale = np.repeat(sc, 64, axis=1)
+    err = np.abs(vals * scale - ref)
+    assert np.all(err <= gamma(K) * absref + 8 * scale), (err / (gamma(K) * absref + 8 * scale)).max()
+    if not gather:
+        assert np.all(vals[0] == 0) and np.all(sc[0] == 2.0 ** -15)   # A's zero row
+    assert np.all(Cb[R:] == 0xAB)                         # rows outside every group untouched
+
+
+def test_grouped_gemm_f16_scaled_out_rules():
+    """MOE_F16_SCALED is an output of bf16 STORE GEMMs only."""
+    g = moe.moe_gemm_desc(1, 64, 256, 256, moe.MOE_BF16, moe.MOE_EPI_SWIGLU, moe.MOE_F16_SCALED, 1, 1)
+    a = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    c = torch.zeros((64, moe.moe_f16_scaled_row_bytes(256)), dtype=torch.uint8, device="cuda")
+    off = torch.tensor([0, 64], dtype=torch.int32, device="cuda")
+    with pytest.raises(moe.MoeError):
+        moe.moe_grouped_gemm(g, a, None, None, a, None, a, None, off, c, None)
+
+
 @pytest.mark.parametrize("swiglu", [False, True])
 def test_grouped_gemm_f32(swiglu):
     Cg, ref, R = _gemm_case([20, 0, 65, 7], K=256, N=128, swiglu=swiglu, gather=True, out_f32=True,
@@ -531,25 +580,40 @@ def test_one_token_per_expert_decode(E_loc):
                                                             (77, 10, 1024, True, "bf16", True, False),
                                                             (5, 16, 7168, True, "f32", True, False),
                                                             (77, 10, 1024, True, "bf16", False, True),
-                                                            (33, 8, 7168, True, "f32", True, True)])
+                                                            (33, 8, 7168, True, "f32", True, True),
+                                                            (300, 8, 4096, True, "f16s", True, True),
+                                                            (64, 2, 256, False, "f16s", False, False),
+                                                            (5, 16, 7168, True, "f16s", False, False)])
 def test_combine(T, k, H, shared, io, out_bf16, gated):
     rng = np.random.default_rng(T * k)
     R = T * k
-    rnd = (lambda a: a) if io == "f32" else gen.bf16_round
-    tdt = torch.float32 if io == "f32" else torch.bfloat16
-    y = rnd(rng.standard_normal((R, H)).astype(np.float32))
+
+    def rows(n):
+        """n rows of y in the test's format: (values, device tensor)"""
+        if io == "f16s":                                  # fp16 values, scales over 2^-30 .. 2^-2
+            v16 = rng.uniform(-2.0 ** 15, 2.0 ** 15, size=(n, H)).astype(np.float16)
+            sc = 2.0 ** rng.integers(-30, -1, size=(n, H // 64))
+            vals = (v16.astype(np.float64) * np.repeat(sc, 64, axis=1)).astype(np.float32)
+            return vals, to_dev(f16s_pack(v16, sc), torch.uint8)
+        v = rng.standard_normal((n, H)).astype(np.float32)
+        if io == "f32":
+            return v, to_dev(v, torch.float32)
+        v = gen.bf16_round(v)
+        return v, to_dev(v, torch.bfloat16)
+
+    y, y_dev = rows(R)
     w = rng.random((T, k)).astype(np.float32)
     s2r = rng.permutation(R).reshape(T, k).astype(np.int32)
     s2r[rng.random((T, k)) < 0.3] = -1
     s2r[0, :] = -1                                        # a token with no local expert
-    sh = rnd(rng.standard_normal((T, H)).astype(np.float32)) if shared else None
+    sh, sh_dev = rows(T) if shared else (None, None)
     sw = rng.random(T).astype(np.float32) if gated else None
-    ydt = moe.MOE_F32 if io == "f32" else moe.MOE_BF16
-    d = moe.make_desc(T, H, 64, 0, 8, 64, k, 0, 0, 1, ydt, ydt,
+    ydt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "f16s": moe.MOE_F16_SCALED}[io]
+    iodt = moe.MOE_F32 if io == "f32" else moe.MOE_BF16
+    d = moe.make_desc(T, H, 64, 0, 8, 64, k, 0, 0, 1, iodt, iodt,
                       out_dtype=moe.MOE_BF16 if out_bf16 else moe.MOE_F32)
     out = torch.empty((T, H), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
-    moe.moe_combine(d, ydt, to_dev(y, tdt), to_dev(w, torch.float32), to_dev(s2r, torch.int32),
-                    None if sh is None else to_dev(sh, tdt), out,
+    moe.moe_combine(d, ydt, y_dev, to_dev(w, torch.float32), to_dev(s2r, torch.int32), sh_dev, out,
                     shared_w=None if sw is None else to_dev(sw, torch.float32))
     _sync()
     ref = oracle.combine(y, w, s2r, sh, sw)
