@@ -97,8 +97,12 @@ __device__ __forceinline__ bool store_tile_x4(const GemmArgs& p, const Tile& t, 
             const u32x2 w = u32x2{pack_f16x2_scaled(v[j][0], v[j][1], e), pack_f16x2_scaled(v[j][2], v[j][3], e)};
             __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(crow + (col0 + j * 32) * 2));
           }
+          // the scale is an ordinary store: the row's other scales (the same 128-byte line) come
+          // from the tiles of the other n-tiles, most of which run at the same time on this XCD,
+          // and merge with it in L2 (as non-temporal stores each went to HBM on its own, ~64 bytes
+          // written per 4-byte scale)
           if ((lane & 28) == 0)
-            __builtin_nontemporal_store(f16s_scale(e), reinterpret_cast<float*>(crow + (long long)p.N * 2 + c_blk / 16));
+            *reinterpret_cast<float*>(crow + (long long)p.N * 2 + c_blk / 16) = f16s_scale(e);
         }
       }
     return full;
@@ -384,13 +388,6 @@ gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total,
 //   * step j + 1 must have landed, from every wave, before b2j+2: group 0 waits for its own share at
 //     the end of C(j), group 1 at the end of M(j); the barrier then publishes it.
 // ------------------------------------------------------------------------------------------------
-__device__ __forceinline__ void phase_barrier() {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_sched_barrier(0);
-  barrier_lds();
-  __builtin_amdgcn_sched_barrier(0);
-#endif
-}
 
 template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST, bool F16S = false>
 __global__ void __launch_bounds__(512)

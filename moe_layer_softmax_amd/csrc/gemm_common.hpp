@@ -160,6 +160,15 @@ __device__ __forceinline__ uint32_t pack_f16x2_scaled(float lo, float hi, int e)
 }
 // the stored scale 2^e
 __device__ __forceinline__ float f16s_scale(int e) { return __builtin_amdgcn_ldexpf(1.0f, e); }
+// barrier_lds with no instruction scheduled across it (the phase boundaries of the ping-pong
+// kernels, where the memory phase's reads and loads must stay on their side)
+__device__ __forceinline__ void phase_barrier() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_sched_barrier(0);
+  barrier_lds();
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+}
 
 // Launch geometry of a grouped GEMM.
 struct Grid {

@@ -14,8 +14,15 @@ namespace moe {
 
 enum { QEPI_STORE_F32 = 0, QEPI_STORE_BF16 = 1, QEPI_SWIGLU_BF16 = 2, QEPI_SWIGLU_Q = 3 };
 
-// fp32 scales staged per K-step beside the operands: 128 A rows, then the two B block scales
+// fp32 scales staged per K-step beside the operands: 128 A rows, then the two B block scales (read
+// from the first two words of loader 2's 256-byte slot), then loader 3's spare slot (every loader
+// issues one 4-byte scale load per step, so every loader's vmcnt waits count the same loads)
 constexpr int kFp8ScaleStageBytes = 1024;
+// compute waves of the fp8 tile kernel (4: 64 x 128 per wave, 8: 64 x 64)
+#ifndef MOE_FP8_COMPUTE_WAVES
+#define MOE_FP8_COMPUTE_WAVES 4
+#endif
+constexpr int kFp8ComputeWaves = MOE_FP8_COMPUTE_WAVES;
 
 // ------------------------------------------------------------------------------------------------
 // fp8 (e4m3 with fp32 scales per 128 x 128 block of the weights and per 128-element row block of
@@ -24,33 +31,42 @@ constexpr int kFp8ScaleStageBytes = 1024;
 // A K-step is one 128-element scale block: each fragment's MFMA (16 x 16 x 128, unit scales) goes
 // into a temporary that is added into the accumulator times the step's scale product in fp32.
 // The accumulators must stay in arch VGPRs for that (the vector ALU cannot address the MFMA-only
-// registers), so a wave holds 64 activation rows x 128 weight rows (128 registers) and the 16 x 16
-// shape keeps each temporary at 4 registers: a ring of four lets the MFMAs of fragment pair p run
-// while pair p - 3 is scaled. The weights are the MFMA's row operand and the activations its
-// column operand, so a lane's entries of a fragment belong to one activation row and one 128-row
-// weight block: one scale product per fragment and step. Waves: wt = wave / 2 takes activation
-// rows [64 wt, 64 wt + 64); wn = wave % 2 the weight rows [128 wn, +128) (STORE), or gate rows
-// [64 wn, +64) and the matching up rows (SWIGLU: h columns [64 wn, +64) of the tile). Operands,
-// staging and the load schedule are those of gemm_q_kernel (3-stage direct-to-LDS ring, block
-// scales staged with their step, loads spread over the step's MFMAs). fp8 h: the row amax of the
-// tile's 128 h-columns is exchanged between the two waves of a row through LDS.
+// registers); the 16 x 16 shape keeps each temporary at 4 registers, and a ring of four lets the
+// MFMAs of fragment pair p run while pair p - 3 is scaled. The weights are the MFMA's row operand
+// and the activations its column operand, so a lane's entries of a fragment belong to one
+// activation row and one 128-row weight block: one scale product per fragment and step.
+//
+// Warp-specialised: NC compute waves and 4 loader waves. Compute wave c: wt = c / (NC / 2) takes
+// activation rows [64 wt, 64 wt + 64); wn = c % (NC / 2) takes TW = 512 / NC weight rows: rows
+// [TW wn, +TW) (STORE), or gate rows [TW/2 wn, +TW/2) and the matching up rows (SWIGLU: h columns
+// [TW/2 wn, +TW/2) of the tile). The loader waves only move data (3-stage direct-to-LDS ring,
+// block scales staged with their step): they issue step kt + 2 into the stage released by the
+// barrier that ended step kt - 1, wait for step kt + 1, and meet the compute waves at the barrier
+// that ends step kt. A wave whose load cannot issue (the memory pipeline full) stalls in order:
+// with one wave per SIMD doing both, such stalls also held back its MFMAs (measured on the
+// 4096-token DeepSeek-V3 slice's gate/up: loads alone 268 us, loads and compute in the same waves
+// 403 us, split between loader and compute waves 372 us). fp8 h: the row amax of the tile's 128
+// h-columns is exchanged between the compute waves of a row through LDS.
 // ------------------------------------------------------------------------------------------------
 template <int EPI>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__((kFp8ComputeWaves + 4) * 64)
 gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm) {
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
-  constexpr int BM = 128, BN = 256, NW = 4, S = 3;
+  constexpr int BM = 128, BN = 256, S = 3;
+  constexpr int NC = kFp8ComputeWaves, NW = 4;    // compute waves, loader waves
+  constexpr int WNS = NC / 2;              // compute waves per activation-row half
+  constexpr int TW = BN / WNS;             // weight rows per compute wave
   constexpr int RB = 128;                  // bytes per row slice (one K-step)
   constexpr int A_INS = BM / (8 * NW), B_INS = BN / (8 * NW);
   constexpr int INS = A_INS + B_INS + 1;   // + one 4-byte scale load
   constexpr int DATA = (BM + BN) * RB;
   constexpr int STAGE = DATA + kFp8ScaleStageBytes;
-  constexpr int FT = 4, FW = 8;            // 16-row activation and weight fragments per wave
+  constexpr int FT = 4, FW = TW / 16;      // 16-row activation and weight fragments per wave
   constexpr int NP = FT * FW;              // fragment pairs per step
   constexpr int RING = 4;                  // temporaries in flight
   using Geo = SliceGeo<64>;
+  static_assert(NC == 4 || NC == 8, "compute waves");
   static_assert((S - 2) * INS < 64, "pipeline depth");
-  static_assert(INS <= NP / 2, "one load every second pair");
 
   extern __shared__ __attribute__((aligned(1024))) uint8_t ldsf[];
 
@@ -60,81 +76,101 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
   if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, gm)) return;
 
   const int lane = threadIdx.x & 63, wave = uniform(threadIdx.x >> 6);   // scalar: DMA targets
-  const int wt = wave >> 1, wn = wave & 1;
-  const int l16 = lane & 15, q = lane >> 4;
   const int K = p.K;
   const int nk = K / 128;
-  const int lrow = lane >> 3;
 
-  // ---- DMA sources: a uniform base and a 32-bit byte offset per lane (the host checks that A and
-  // every weight matrix span less than 4 GiB), so a K-step moves only the scalar base ----
-  unsigned a_off[A_INS];
+  if (wave >= NC) {
+    // ---- loader wave lw: DMA sources as a uniform base and a 32-bit byte offset per lane (the
+    // host checks that A and every weight matrix span less than 4 GiB), so a K-step moves only the
+    // scalar base ----
+    const int lw = wave - NC;
+    const int lrow = lane >> 3;
+    unsigned a_off[A_INS];
 #pragma unroll
-  for (int j = 0; j < A_INS; ++j) {
-    const int r = (j * NW + wave) * 8 + lrow;
-    a_off[j] = static_cast<unsigned>(a_src_row(p, t, t.row0 + r) * p.a_pitch) +
-               ((lane & 7) ^ Geo::swz(r)) * 16;
-  }
-  const char* b_base[B_INS];
-  unsigned b_off[B_INS];
+    for (int j = 0; j < A_INS; ++j) {
+      const int r = (j * NW + lw) * 8 + lrow;
+      a_off[j] = static_cast<unsigned>(a_src_row(p, t, t.row0 + r) * p.a_pitch) +
+                 ((lane & 7) ^ Geo::swz(r)) * 16;
+    }
+    const char* b_base[B_INS];
+    unsigned b_off[B_INS];
 #pragma unroll
-  for (int j = 0; j < B_INS; ++j) {
-    const int rb0 = (j * NW + wave) * 8;   // wave-uniform: gate or up for the whole instruction
-    const int rb = rb0 + lrow;
-    long long n;
-    if (SWIGLU) {
-      n = (long long)t.nt * (BN / 2) + (rb % (BN / 2));
-      b_base[j] = rb0 >= BN / 2 ? t.B2 : t.B;
-    } else {
-      n = (long long)t.nt * BN + rb;
-      b_base[j] = t.B;
+    for (int j = 0; j < B_INS; ++j) {
+      const int rb0 = (j * NW + lw) * 8;   // wave-uniform: gate or up for the whole instruction
+      const int rb = rb0 + lrow;
+      long long n;
+      if (SWIGLU) {
+        n = (long long)t.nt * (BN / 2) + (rb % (BN / 2));
+        b_base[j] = rb0 >= BN / 2 ? t.B2 : t.B;
+      } else {
+        n = (long long)t.nt * BN + rb;
+        b_base[j] = t.B;
+      }
+      if (n >= p.N) n = p.N - 1;
+      b_off[j] = static_cast<unsigned>(n * K) + ((lane & 7) ^ Geo::swz(rb)) * 16;
     }
-    if (n >= p.N) n = p.N - 1;
-    b_off[j] = static_cast<unsigned>(n * K) + ((lane & 7) ^ Geo::swz(rb)) * 16;
-  }
-  const char* const a_base = static_cast<const char*>(p.A);
-  const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(ldsf));
-  // scales: waves 0 and 1 move the A scales of rows [64 w, 64 w + 64) (one fp32 per row and
-  // step), wave 2 the two B block scales (lane i: block i & 1), wave 3 the same into a spare slot
-  const int kb = K / 128;
-  const char* s_src;
-  int s_dst;
-  if (wave < 2) {
-    const int r = wave * 64 + lane;
-    s_src = static_cast<const char*>(p.A_scales) +
-            (long long)(a_src_row(p, t, t.row0 + r) / p.a_scale_rows) * kb * 4;
-    s_dst = DATA + wave * 256;
-  } else {
-    const char* b0;
-    const char* b1;
-    if (SWIGLU) {                          // the tile's 128 h-columns: one gate and one up block
-      b0 = t.Bs + (long long)t.nt * kb * 4;
-      b1 = t.B2s + (long long)t.nt * kb * 4;
-    } else {                               // two 128-column blocks
-      b0 = t.Bs + (long long)(t.nt * 2) * kb * 4;
-      b1 = t.Bs + (long long)min(t.nt * 2 + 1, (p.N - 1) / 128) * kb * 4;
-    }
-    s_src = (lane & 1) ? b1 : b0;
-    s_dst = DATA + 512 + (wave - 2) * 256;
-  }
-  auto issue_one = [&](int kt, int qi, int stage) {
-    const unsigned st = lds0 + stage * STAGE;
-    const long long kb8 = (long long)kt * RB;
-    if (qi < A_INS) {
-      dma_16b_sbase(a_base + kb8, a_off[qi], st + (qi * NW + wave) * 8 * RB);
-    } else if (qi < A_INS + B_INS) {
-      const int j = qi - A_INS;
-      dma_16b_sbase(b_base[j] + kb8, b_off[j], st + BM * RB + (j * NW + wave) * 8 * RB);
+    const char* const a_base = static_cast<const char*>(p.A);
+    const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(ldsf));
+    // scales: loaders 0 and 1 move the A scales of rows [64 lw, 64 lw + 64) (one fp32 per row and
+    // step), loader 2 the two B block scales (lane i: block i & 1), loader 3 the same into a spare
+    // slot
+    const int kb = K / 128;
+    const char* s_src;
+    int s_dst;
+    if (lw < 2) {
+      const int r = lw * 64 + lane;
+      s_src = static_cast<const char*>(p.A_scales) +
+              (long long)(a_src_row(p, t, t.row0 + r) / p.a_scale_rows) * kb * 4;
+      s_dst = DATA + lw * 256;
     } else {
+      const char* b0;
+      const char* b1;
+      if (SWIGLU) {                        // the tile's 128 h-columns: one gate and one up block
+        b0 = t.Bs + (long long)t.nt * kb * 4;
+        b1 = t.B2s + (long long)t.nt * kb * 4;
+      } else {                             // two 128-column blocks
+        b0 = t.Bs + (long long)(t.nt * 2) * kb * 4;
+        b1 = t.Bs + (long long)min(t.nt * 2 + 1, (p.N - 1) / 128) * kb * 4;
+      }
+      s_src = (lane & 1) ? b1 : b0;
+      s_dst = DATA + 512 + (lw - 2) * 256;
+    }
+    auto issue = [&](int kt) {
+      const int stage = kt % S;
+      const unsigned st = lds0 + stage * STAGE;
+      const long long kb8 = (long long)kt * RB;
+#pragma unroll
+      for (int j = 0; j < A_INS; ++j) dma_16b_sbase(a_base + kb8, a_off[j], st + (j * NW + lw) * 8 * RB);
+#pragma unroll
+      for (int j = 0; j < B_INS; ++j)
+        dma_16b_sbase(b_base[j] + kb8, b_off[j], st + BM * RB + (j * NW + lw) * 8 * RB);
       dma_4b_asm(s_src + kt * 4, ldsf + stage * STAGE + s_dst);
-    }
-  };
-  auto issue = [&](int kt) {
-    if (kt >= nk) return;
+    };
+    // prologue: steps 0 .. S-2 in flight, step 0 landed before the first barrier
 #pragma unroll
-    for (int qi = 0; qi < INS; ++qi) issue_one(kt, qi, kt % S);
-  };
+    for (int qq = 0; qq < S - 1; ++qq)
+      if (qq < nk) issue(qq);
+    if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
+    else wait_vmem();
+    barrier_lds();
+    for (int kt = 0; kt < nk; ++kt) {
+      // step kt + S - 1 into the stage the last barrier released; step kt + 1 landed before the
+      // barrier that ends step kt
+      if (kt + S - 1 < nk) {
+        issue(kt + S - 1);
+        wait_vmem_n<(S - 2) * INS>();
+      } else {
+        wait_vmem();
+      }
+      barrier_lds();
+    }
+    if constexpr (EPI == QEPI_SWIGLU_Q) __syncthreads();   // the compute waves' amax exchange
+    return;
+  }
 
+  // ---- compute waves ----
+  const int wt = wave / WNS, wn = wave % WNS;
+  const int l16 = lane & 15, q = lane >> 4;
   // 16 rows x 32 bytes per lane (the fp8 operand of 16 x 16 x 128): chunks 2 q and 2 q + 1 of
   // rows r0 + l16 (any K order shared by both operands gives the same sum)
   auto frag = [&](const uint8_t* base, int r0) -> i32x8 {
@@ -145,8 +181,8 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
   };
   // first tile B-row of weight fragment i, and its 128-row block (0: b0, 1: b1)
   auto wrow = [&](int i) -> int {
-    if (SWIGLU) return i < FW / 2 ? wn * 64 + i * 16 : BN / 2 + wn * 64 + (i - FW / 2) * 16;
-    return wn * 128 + i * 16;
+    if (SWIGLU) return i < FW / 2 ? wn * (TW / 2) + i * 16 : BN / 2 + wn * (TW / 2) + (i - FW / 2) * 16;
+    return wn * TW + i * 16;
   };
   auto wblk = [&](int i) -> int { return SWIGLU && i >= FW / 2 ? 1 : 0; };
 
@@ -156,17 +192,8 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
 #pragma unroll
     for (int j = 0; j < FT; ++j) acc[i][j] = f32x4{};
 
-  // prologue: steps 0 .. S-2 in flight, wait for step 0
-#pragma unroll
-  for (int qq = 0; qq < S - 1; ++qq) issue(qq);
-  if (nk >= S - 1) wait_vmem_n<(S - 2) * INS>();
-  else wait_vmem();
-  barrier_lds();
-
+  barrier_lds();                           // step 0 landed (the loaders' prologue)
   for (int kt = 0; kt < nk; ++kt) {
-    // step kt + S - 1 goes into the stage the last barrier released; past the end the last step
-    // loads itself again there, unread (no branch between the loads and the MFMAs)
-    const int kn = kt + S - 1 < nk ? kt + S - 1 : nk - 1;
     const uint8_t* la = ldsf + (kt % S) * STAGE;
     const uint8_t* lb = la + BM * RB;
     const float* ls = reinterpret_cast<const float*>(la + DATA);
@@ -175,9 +202,9 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
     for (int j = 0; j < FT; ++j) xf[j] = frag(la, wt * 64 + j * 16);
     i32x8 wf[2];
     wf[0] = frag(lb, wrow(0));
-    // scale products: SWIGLU fragments use the gate (0) or up (1) block, STORE the wave's block wn
+    // scale products: SWIGLU fragments use the gate (0) or up (1) block, STORE the wave's block
     float fac[2][FT];
-    const float sb0 = SWIGLU ? ls[128] : ls[128 + wn], sb1 = ls[129];
+    const float sb0 = SWIGLU ? ls[128] : ls[128 + (wn * TW) / 128], sb1 = ls[129];
 #pragma unroll
     for (int j = 0; j < FT; ++j) {
       const float sa = ls[wt * 64 + j * 16 + l16];
@@ -185,8 +212,7 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
       fac[1][j] = sa * sb1;
     }
     // pairs p = FT i + j: pair p's MFMA into temporary p % RING, then pair p - RING + 1 scaled
-    // into its accumulator; weight fragment i + 1 read with the first pair of fragment i; one
-    // load of step kt + S - 1 after every second pair
+    // into its accumulator; weight fragment i + 1 read with the first pair of fragment i
     f32x4 tmp[RING];
 #pragma unroll
     for (int pp = 0; pp < NP + RING - 1; ++pp) {
@@ -203,16 +229,10 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(tmp[pd % RING][v], f, acc[i][j][v]);
       }
-      if ((pp & 1) && (pp >> 1) < INS) {
-        MOE_SCHED_FENCE();
-        issue_one(kn, pp >> 1, (kt + S - 1) % S);
-        MOE_SCHED_FENCE();
-      }
     }
-    wait_vmem_n<(S - 2) * INS>();          // step kt+1 landed (only step kt+2's loads remain)
-    barrier_lds();
+    wait_lgkm();                           // this wave's reads of stage kt are done
+    barrier_lds();                         // and step kt + 1 has landed (the loaders waited)
   }
-  wait_vmem();                             // the unread tail loads, before the stores
 
   // ---- epilogue: lane l16 of fragment j is activation row r; entries v of weight fragment i are
   // the 4 consecutive weight rows 16 i + 4 q + v ----
@@ -225,7 +245,7 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
       char* crow = C + (long long)r * p.c_pitch;
 #pragma unroll
       for (int i = 0; i < FW; ++i) {
-        const long long col = (long long)t.nt * BN + wn * 128 + i * 16 + q * 4;
+        const long long col = (long long)t.nt * BN + wn * TW + i * 16 + q * 4;
         if (col >= p.N) continue;          // N % 128 == 0: 4 columns all in or all out
         const f32x4 v = acc[i][j];
         if (EPI == QEPI_STORE_F32) *reinterpret_cast<f32x4*>(crow + col * 4) = v;
@@ -233,7 +253,7 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
       }
     }
   } else {
-    constexpr int HF = FW / 2;             // gate fragments (64 h-columns per wave)
+    constexpr int HF = FW / 2;             // gate fragments (TW / 2 h-columns per wave)
     f32x4 hv[FT][HF];
 #pragma unroll
     for (int j = 0; j < FT; ++j)
@@ -241,7 +261,7 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
       for (int i = 0; i < HF; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) hv[j][i][v] = silu_fast(acc[i][j][v]) * acc[i + HF][j][v];
-    const long long hcol0 = (long long)t.nt * (BN / 2) + wn * 64;
+    const long long hcol0 = (long long)t.nt * (BN / 2) + wn * (TW / 2);
     if constexpr (EPI == QEPI_SWIGLU_BF16) {
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
@@ -258,9 +278,8 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
       }
     } else {
       // fp8 h in 1 x 128 blocks: the tile's 128 h-columns of a row are held by the four lanes
-      // l16 + 16 q of waves wn = 0 and 1; the wave-level amax is exchanged through LDS
-      float* xch = reinterpret_cast<float*>(ldsf + S * STAGE);      // [2 wn][BM rows]
-      float am[FT];
+      // l16 + 16 q of the WNS compute waves of its row half; their amax goes through LDS
+      float* xch = reinterpret_cast<float*>(ldsf + S * STAGE);      // [WNS wn][BM rows]
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
         float a = 0.0f;
@@ -270,15 +289,17 @@ gemm_fp8_tile_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, 
           for (int v = 0; v < 4; ++v) a = fmaxf(a, fabsf(hv[j][i][v]));
         a = fmaxf(a, __shfl_xor(a, 16, 64));
         a = fmaxf(a, __shfl_xor(a, 32, 64));
-        am[j] = a;
         if (q == 0) xch[wn * BM + wt * 64 + j * 16 + l16] = a;
       }
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < FT; ++j) {
-        const float amax = fmaxf(am[j], xch[(wn ^ 1) * BM + wt * 64 + j * 16 + l16]);
+        const int rt = wt * 64 + j * 16 + l16;
+        float amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WNS; ++w) amax = fmaxf(amax, xch[w * BM + rt]);
         const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-        const int r = t.row0 + wt * 64 + j * 16 + l16;
+        const int r = t.row0 + rt;
         if (r >= t.row1) continue;
         uint8_t* crow = reinterpret_cast<uint8_t*>(C + (long long)r * p.c_pitch);
 #pragma unroll
@@ -308,8 +329,8 @@ hipError_t run_fp8_tile(const GemmArgs& a, hipStream_t s) {
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
   Grid g = make_grid(a, BM, SWIGLU ? BN / 2 : BN, 8, 64);
   if (g.total == 0) return hipSuccess;
-  const size_t lds = (size_t)S * ((BM + BN) * 128 + kFp8ScaleStageBytes) + 2 * BM * 4;
-  gemm_fp8_tile_kernel<EPI><<<dim3(g.blocks), dim3(256), lds, s>>>(a, g.n_tiles, g.x_tiles, g.span,
+  const size_t lds = (size_t)S * ((BM + BN) * 128 + kFp8ScaleStageBytes) + (kFp8ComputeWaves / 2) * BM * 4;
+  gemm_fp8_tile_kernel<EPI><<<dim3(g.blocks), dim3((kFp8ComputeWaves + 4) * 64), lds, s>>>(a, g.n_tiles, g.x_tiles, g.span,
                                                                   g.total, g.gm);
   return hipGetLastError();
 }
