@@ -134,10 +134,25 @@ __device__ __forceinline__ bool store_tile_x4(const GemmArgs& p, const Tile& t, 
 // gate rows then TN/2 up rows; a slot never straddles the two). Each slot has a wave-uniform base
 // pointer and a fixed per-lane byte offset, so a K-step only moves the base (scalar arithmetic).
 // If some lane's offset needs more than 32 bits the wave uses the 64-bit per-lane address form.
+// When BM is not a multiple of RPI * NW the last A slot covers the remaining rows only: waves
+// whose slot would start at or past BM skip it (a wave-uniform branch), so they issue one
+// instruction less per K-step (a_slots).
 template <class Geo, int BM, int BN, int TN, int NW, bool SWIGLU>
 struct LoadPlan {
   static constexpr int RPI = Geo::kRowsPerIns;
-  static constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
+  static constexpr int A_INS = (BM + RPI * NW - 1) / (RPI * NW), B_INS = BN / (RPI * NW);
+  static_assert(BM % RPI == 0 && BN % (RPI * NW) == 0, "whole instructions");
+  static constexpr bool A_FULL = BM % (RPI * NW) == 0;
+  // slot j of A is used by wave w (always when every slot is full: no check is compiled then)
+  __host__ __device__ static constexpr bool a_active(int j, int w) {
+    return A_FULL || (j * NW + w) * RPI < BM;
+  }
+  // A instructions wave w issues per K-step
+  __host__ __device__ static constexpr int a_slots(int w) {
+    int c = 0;
+    for (int j = 0; j < A_INS; ++j) c += a_active(j, w) ? 1 : 0;
+    return c;
+  }
   static constexpr int BK = Geo::kRowBytes / 2;
   const char* a_base;
   const char* b_base[B_INS];
@@ -151,7 +166,7 @@ struct LoadPlan {
     for (int j = 0; j < A_INS; ++j) {
       const int r = (j * NW + wave) * RPI + lrow;
       const int lch = (lane % Geo::kChunks) ^ Geo::swz(r);
-      a_off[j] = (unsigned long long)a_src_row(p, t, t.row0 + r) * p.a_pitch + lch * 16;
+      a_off[j] = a_active(j, wave) ? (unsigned long long)a_src_row(p, t, t.row0 + r) * p.a_pitch + lch * 16 : 0;
     }
 #pragma unroll
     for (int j = 0; j < B_INS; ++j) {
@@ -185,6 +200,7 @@ struct LoadPlan {
 #pragma unroll
     for (int j = 0; j < A_INS; ++j) {
       const int row = (j * NW + wave) * RPI;
+      if (!a_active(j, wave)) continue;                // wave-uniform
       if constexpr (WIDE) dma_16b_asm(a_base + a_off[j] + kb, stage + row * BK);
       else dma_16b_sbase(a_base + kb, static_cast<unsigned>(a_off[j]), st + row * BK * 2);
     }
@@ -389,15 +405,21 @@ gemm_bf16_pipe_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total,
 //     the end of C(j), group 1 at the end of M(j); the barrier then publishes it.
 // ------------------------------------------------------------------------------------------------
 
-template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST, bool F16S = false>
+template <bool SWIGLU, bool OUT_F32, int S, bool PERSIST, bool F16S = false, int BM = 256>
 __global__ void __launch_bounds__(512)
 gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm, int nphys) {
-  constexpr int BM = 256, BN = 256, WN = 4, MI = 32, BK = 32;
-  constexpr int NW = 8, TM = 128, TN = 64, FM = TM / MI, FN = TN / MI, MK = 16, KS = BK / MK;
+  constexpr int BN = 256, WN = 4, MI = 32, BK = 32;
+  constexpr int NW = 8, TM = BM / 2, TN = 64, FM = TM / MI, FN = TN / MI, MK = 16, KS = BK / MK;
+  static_assert(BM == 256 || BM == 192, "tile rows");
   using Geo = SliceGeo<BK>;
-  constexpr int RPI = Geo::kRowsPerIns;
-  constexpr int A_INS = BM / (RPI * NW), B_INS = BN / (RPI * NW);
-  constexpr int INS = A_INS + B_INS;                   // DMA instructions per wave per K-step
+  using Plan = LoadPlan<Geo, BM, BN, TN, NW, SWIGLU>;
+  constexpr int B_INS = Plan::B_INS;
+  // DMA instructions per wave per K-step, per wave group (192-row tiles: the second group's waves
+  // have no row of the last A slot)
+  constexpr int INS0 = Plan::a_slots(0) + B_INS, INS1 = Plan::a_slots(NW / 2) + B_INS;
+  static_assert(Plan::a_slots(NW / 2 - 1) + B_INS == INS0 && Plan::a_slots(NW - 1) + B_INS == INS1,
+                "one count per wave group");
+  constexpr int INS = INS0 > INS1 ? INS0 : INS1;
   constexpr int STAGE = (BM + BN) * BK;                // uint16 per LDS stage
   static_assert(S >= 3 && (S - 2) * INS < 64, "pipeline depth");
   static_assert(!SWIGLU || (FN % 2 == 0), "SWIGLU needs gate and up fragments in every wave");
@@ -425,7 +447,7 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   const int wm = grp, wn = wave & (WN - 1);
   const int nk = p.K / BK;
 
-  LoadPlan<Geo, BM, BN, TN, NW, SWIGLU> lp;
+  Plan lp;
   lp.init(p, t, wave, lane);
   const unsigned lds0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds));
   auto issue = [&](int kt, auto wide_tag) {
@@ -445,10 +467,22 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
   // pend: the wave issued NST stores after the first S - 1 steps of this tile (the previous
   // tile's epilogue, see tile_loop); vmcnt retires in issue order, so while those stores are
   // younger than step kt + 1 (kt + 1 <= S - 2) they are left in flight by counting them too.
+  // vmcnt((S - 2) * (this wave group's instructions per step) + extra)
+  auto wait_steps = [&](auto extra) {
+    constexpr int X = decltype(extra)::value;
+    if constexpr (INS0 == INS1) {
+      wait_vmem_n<(S - 2) * INS0 + X>();
+    } else {
+      if (grp == 0) wait_vmem_n<(S - 2) * INS0 + X>();
+      else wait_vmem_n<(S - 2) * INS1 + X>();
+    }
+  };
+  using NoPend = std::integral_constant<int, 0>;
+  using Pend = std::integral_constant<int, NPEND>;
   auto wait_next = [&](int kt, bool pend) {
     if (kt + S - 1 < nk) {
-      if (OVERLAP && pend && kt <= S - 3) wait_vmem_n<(S - 2) * INS + NPEND>();
-      else wait_vmem_n<(S - 2) * INS>();
+      if (OVERLAP && pend && kt <= S - 3) wait_steps(Pend{});
+      else wait_steps(NoPend{});
     } else {
       wait_vmem();
     }
@@ -493,8 +527,8 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
     // b0. Stores issued after the primed steps are left in flight (pend), others are waited for.
     if (!primed) prime(wide_tag);
     if (nk >= S - 1) {
-      if (OVERLAP && pend) wait_vmem_n<(S - 2) * INS + NPEND>();
-      else wait_vmem_n<(S - 2) * INS>();
+      if (OVERLAP && pend) wait_steps(Pend{});
+      else wait_steps(NoPend{});
     } else {
       wait_vmem();
     }
@@ -927,10 +961,10 @@ hipError_t run_bf16(const GemmArgs& a, hipStream_t s, int gm = 1, int span = 0) 
   return hipGetLastError();
 }
 
-template <int S, bool PERSIST = false>
+template <int S, bool PERSIST = false, int BM = 256>
 hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   const bool sw = a.epilogue == MOE_EPI_SWIGLU;
-  Grid g = make_grid(a, 256, sw ? 128 : 256, gm, span);
+  Grid g = make_grid(a, BM, sw ? 128 : 256, gm, span);
   if (g.total == 0) return hipSuccess;
   unsigned blocks = g.blocks;
   if (PERSIST) {
@@ -939,9 +973,9 @@ hipError_t run_bf16_pp(const GemmArgs& a, hipStream_t s, int gm, int span) {
   }
   dim3 grid(blocks), block(512);
   const bool f32 = a.out_dtype == MOE_F32;
-  const size_t lds_bytes = (size_t)S * (256 + 256) * 32 * sizeof(uint16_t);
+  const size_t lds_bytes = (size_t)S * (BM + 256) * 32 * sizeof(uint16_t);
 #define MOE_RUN(SWI, F32, F16S)                                                                  \
-  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST, F16S><<<grid, block, lds_bytes, s>>>(               \
+  gemm_bf16_pp_kernel<SWI, F32, S, PERSIST, F16S, BM><<<grid, block, lds_bytes, s>>>(           \
       a, g.n_tiles, g.x_tiles, g.span, g.total, g.gm, (int)g.blocks)
   if (a.out_dtype == MOE_F16_SCALED) {
     if (sw) return hipErrorInvalidValue;
@@ -1034,12 +1068,20 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     const int groups = a.G + (a.x_rows > 0 ? 1 : 0);
     const long long per_group = groups ? rows / groups : rows;
     const int n_full = a.epilogue == MOE_EPI_SWIGLU ? 2 * a.N : a.N;   // B rows per tile row
-    if (per_group >= 256 && n_full >= 256) {
-      // 256 x 256 tiles, K-steps of 32 through 3 LDS stages of 32 KB, ping-pong schedule of 8
-      // waves of 128 x 64, one persistent workgroup per CU: each tile's first loads are issued
-      // before the previous tile's stores, which drain behind its first K-steps (measured with the
-      // down projection's fp32 stores removed: the stores, waited for at every tile start, took
-      // a quarter of its time).
+    // routed rows per group (the extra group's rows apart) and the rows its tiles would cover
+    const long long r_bar = a.G > 0 ? (long long)(a.expected_rows > 0 ? a.expected_rows : a.max_rows) / a.G
+                                    : a.x_rows;
+    auto padded = [&](long long bm) { return (r_bar + bm - 1) / bm * bm; };
+    // groups of ~144-192 rows (e.g. 160 on the 8192-token Qwen3.5-397B slice: top-10 of 512
+    // experts, 64 local) fill one 192-row tile where a 256-row tile would be 62% padding
+    const bool tile192 = r_bar >= 144 && padded(192) < padded(256);
+    if (n_full >= 256 && (per_group >= 256 || tile192)) {
+      // 256 (or 192) x 256 tiles, K-steps of 32 through 3 LDS stages of 32 KB, ping-pong schedule
+      // of 8 waves of 128 (96) x 64, one persistent workgroup per CU: each tile's first loads are
+      // issued before the previous tile's stores, which drain behind its first K-steps (measured
+      // with the down projection's fp32 stores removed: the stores, waited for at every tile
+      // start, took a quarter of its time).
+      if (tile192) return run_bf16_pp<kPPStages, true, 192>(a, s, kTileGroupM, kTileSpan);
       return run_bf16_pp<kPPStages, true>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);

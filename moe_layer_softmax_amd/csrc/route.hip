@@ -248,7 +248,7 @@ router_kernel(int T, int H, int E, const uint16_t* __restrict__ x, const uint16_
 }
 
 namespace {
-constexpr int kRouterMinWaves = 512;    // K-split until the router has about 2 waves per CU
+constexpr int kRouterMinWaves = 2048;   // K-split until the router has about 2 waves per CU
 constexpr int kRouterMaxSplit = 32;
 int router_ft(int T) { return T >= 1024 ? 4 : 1; }
 }  // namespace

@@ -472,6 +472,36 @@ def test_grouped_gemm_bf16_many_tiles(K, out_f32):
     assert np.all(Cg[R:] == 1024.0)
 
 
+# groups of ~150-200 rows (routed rows per group 163 = max_rows / G: the ping-pong kernel's 192-row
+# tiles, whose second wave group loads one A slice less per step): an empty group, a one-row
+# group, one of 400 rows (three tiles, the last ragged); N = 320 leaves a partial n-tile
+@pytest.mark.parametrize("swiglu,gather,out", [(False, False, "bf16"), (False, True, "f32"),
+                                               (True, True, "bf16"), (True, False, "f32"),
+                                               (False, False, "f16s")])
+@pytest.mark.parametrize("K", [256, 1536])
+def test_grouped_gemm_bf16_192_row_tiles(swiglu, gather, out, K):
+    counts = [150, 0, 400, 1, 191, 180, 170, 200]
+    N = 192 if swiglu else 320
+    if out == "f16s":
+        N = 256
+        Cb, ref, R, absref = _gemm_case(counts, K=K, N=N, swiglu=False, gather=gather, out_f32=False,
+                                        f16s=True, seed=192)
+        vals, sc = f16s_split(Cb[:R], N)
+        check_f16s_format(vals, sc)
+        scale = np.repeat(sc, 64, axis=1)
+        assert np.all(np.abs(vals * scale - ref) <= gamma(K) * absref + 8 * scale)
+        assert np.all(Cb[R:] == 0xAB)
+        return
+    Cg, ref, R = _gemm_case(counts, K=K, N=N, swiglu=swiglu, gather=gather, out_f32=out == "f32",
+                            seed=192)
+    rms = np.sqrt(np.mean(ref ** 2))
+    if out == "f32" and not swiglu:
+        assert np.abs(Cg[:R] - ref).max() <= 1e-4 * rms * np.sqrt(K / 256)
+    else:
+        assert np.all(np.abs(Cg[:R] - ref) <= 2 ** -8 * np.abs(ref) + 1e-3 * rms)
+    assert np.all(Cg[R:] == 1024.0)
+
+
 # MOE_F16_SCALED output rows (the layer's y for bf16 experts) from each bf16 kernel: decode-sized
 # groups (weight streaming; K = 4160 splits its steps over four waves), mid-sized groups (128 x 128
 # tiles) and large ones (the persistent 256 x 256 ping-pong tiles; N = 4160 leaves an n-tile whose
