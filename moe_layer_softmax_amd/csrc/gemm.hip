@@ -633,17 +633,12 @@ gemm_bf16_pp_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, i
 // flight per CU for the same registers per wave); their fp32 partial sums meet in LDS and wave 0
 // adds them in wave order (deterministic) before the epilogue.
 // ------------------------------------------------------------------------------------------------
-template <int FM, int KS, bool SWIGLU, bool OUT_F32, bool F16S = false>
-__global__ void __launch_bounds__(64 * KS)
-gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
-  constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
-  // tile order: groups of 8 m-tiles with the m-tile fastest, 8 consecutive tiles per XCD, so the
-  // m-tiles of one group that needs several (the same weights) read them through one L2
-  const int logical = xcd_remap(blockIdx.x, kStreamGroupM);
-  if (logical >= total) return;
-  Tile t;
-  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kStreamGroupM)) return;
-
+// The body of gemm_bf16_stream_kernel for a tile whose rows fill L of its 16-row fragments: only
+// those fragments' activation rows are loaded and multiplied (a 64-row tile of a group with a few
+// rows would otherwise issue as many activation loads as weight loads, all but one re-reading a
+// clamped row). part: the K-split's LDS partial sums, [KS - 1][4][L][64].
+template <int L, int KS, bool SWIGLU, bool OUT_F32, bool F16S>
+__device__ __forceinline__ void stream_tile(const GemmArgs& p, const Tile& t, f32x4* part) {
   const int lane = lane_id();
   const int lr = lane & 15, kq = lane >> 4;            // operand row; 16-byte quarter of a step
   const long long kbytes = (long long)p.K * 2;
@@ -666,9 +661,9 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       wp[j][h] = base + n * kbytes + (lane & 7) * 16;
     }
   const char* A = static_cast<const char*>(p.A);
-  const char* ap[FM];
+  const char* ap[L];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) ap[i] = A + a_src_row(p, t, t.row0 + i * 16 + lr) * p.a_pitch + kq * 16;
+  for (int i = 0; i < L; ++i) ap[i] = A + a_src_row(p, t, t.row0 + i * 16 + lr) * p.a_pitch + kq * 16;
   // operand lane (row lr, quarter kq) of step s holds chunk s * 4 + kq of row lr: loaded by row
   // half lr / 8, lane (lr % 8) * 8 + s * 4 + kq (byte index for ds_bpermute)
   const int src0 = ((lr & 7) * 8 + kq) * 4, src1 = src0 + 16;
@@ -679,7 +674,7 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   const int np_all = p.K / 64;
   const int c0 = np_all * wave / KS, np = np_all * (wave + 1) / KS - c0;
   i32x4 wraw[2][4][2];
-  bf16x8 av[2][FM][2];
+  bf16x8 av[2][L][2];
   auto load = [&](int c, int set) {
     const long long off = (long long)(c0 + min(c, np - 1)) * 128;
 #pragma unroll
@@ -688,15 +683,15 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       for (int h = 0; h < 2; ++h)
         wraw[set][j][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp[j][h] + off));
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < L; ++i)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) av[set][i][s2] = *reinterpret_cast<const bf16x8*>(ap[i] + off + s2 * 64);
   };
-  f32x4 acc[4][FM];
+  f32x4 acc[4][L];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{};
+    for (int i = 0; i < L; ++i) acc[j][i] = f32x4{};
   auto compute = [&](int set) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -716,7 +711,7 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < L; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[j], av[set][i][s2], acc[j][i], 0, 0, 0);
     }
   };
@@ -737,12 +732,12 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     if (c < np) compute(0);                            // odd number of pairs: the last is in set 0
   }
   if constexpr (KS > 1) {
-    __shared__ f32x4 part[KS - 1][4][FM][64];
+    // part: [KS - 1][4][L][64] partial sums of waves 1 .. KS - 1
     if (wave > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) part[wave - 1][j][i][lane] = acc[j][i];
+        for (int i = 0; i < L; ++i) part[(((wave - 1) * 4 + j) * L + i) * 64 + lane] = acc[j][i];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -751,7 +746,7 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] += part[w][j][i][lane];
+        for (int i = 0; i < L; ++i) acc[j][i] += part[((w * 4 + j) * L + i) * 64 + lane];
   }
 
   // acc[j][i][v]: weight row j * 16 + kq * 4 + v of the tile, C row row0 + i * 16 + lr
@@ -762,7 +757,7 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     static_assert(!SWIGLU && !OUT_F32, "scaled fp16 rows: STORE");
     const long long c_blk = (long long)t.nt * 64;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < L; ++i) {
       float v4[4][4], m = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -784,7 +779,7 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     return;
   }
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < L; ++i) {
     const int r = t.row0 + i * 16 + lr;
     if (r >= t.row1) continue;
     char* crow = C + (long long)r * p.c_pitch;
@@ -810,6 +805,32 @@ gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       }
     }
   }
+}
+
+template <int FM, int KS, bool SWIGLU, bool OUT_F32, bool F16S = false>
+__global__ void __launch_bounds__(64 * KS)
+gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
+  constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
+  // tile order: groups of 8 m-tiles with the m-tile fastest, 8 consecutive tiles per XCD, so the
+  // m-tiles of one group that needs several (the same weights) read them through one L2
+  const int logical = xcd_remap(blockIdx.x, kStreamGroupM);
+  if (logical >= total) return;
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kStreamGroupM)) return;
+  __shared__ f32x4 part[KS > 1 ? (KS - 1) * 4 * FM * 64 : 1];
+  // 16-row fragments holding rows of the tile (uniform over the workgroup): each count runs its
+  // own instantiation, so every load and MFMA stays unconditional
+  const int live = (t.row1 - t.row0 + 15) / 16;
+  if constexpr (FM >= 4) {
+    if (live >= 4) { stream_tile<4, KS, SWIGLU, OUT_F32, F16S>(p, t, part); return; }
+  }
+  if constexpr (FM >= 3) {
+    if (live == 3) { stream_tile<3, KS, SWIGLU, OUT_F32, F16S>(p, t, part); return; }
+  }
+  if constexpr (FM >= 2) {
+    if (live == 2) { stream_tile<2, KS, SWIGLU, OUT_F32, F16S>(p, t, part); return; }
+  }
+  stream_tile<1, KS, SWIGLU, OUT_F32, F16S>(p, t, part);
 }
 
 // ------------------------------------------------------------------------------------------------
