@@ -454,24 +454,14 @@ gemm_q_kernel(GemmArgs p, int n_tiles, int x_tiles, int span, int total, int gm)
 // fp8 1 x 128 blocks of h are complete inside the workgroup (row amax exchanged through LDS) and
 // the MXFP4 1 x 32 groups inside one wave.
 // ------------------------------------------------------------------------------------------------
-template <int FMT, int EPI, int FM, int KS>
-__global__ void __launch_bounds__(256)
-gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
+// The body of gemm_q_stream_kernel for a tile whose rows fill L of its 16-row fragments (only
+// those fragments' activation rows and scales are loaded and multiplied). amax_x: [4][ASTR] fp8 h
+// row amax exchange; part: the K-split's LDS partial sums, [KS - 1][4][L][64].
+template <int L, int FMT, int EPI, int KS, int ASTR>
+__device__ __forceinline__ void stream_q_tile(const GemmArgs& p, const Tile& t, float* amax_x, f32x4* part) {
   constexpr bool MX4 = FMT == MOE_MXFP4, MX8 = FMT == MOE_MXFP8, MX = MX4 || MX8;
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
-  // KS = 1: the 4 waves take 4 adjacent column blocks (fp8's 1 x 128 h blocks need all four);
-  // KS = 4: they share one column block and split its K-pairs, summed through LDS at the end
-  static_assert(KS == 1 || KS == 4, "K split");
-  static_assert(KS == 1 || !(EPI == QEPI_SWIGLU_Q && FMT == MOE_FP8_E4M3), "fp8 h blocks span 4 waves");
-  constexpr int BM = 16 * FM;
   constexpr int FMT_CODE = MX4 ? 4 : 0;
-  __shared__ float amax_x[4][BM];          // fp8 h: per-wave row amax
-
-  const int logical = xcd_remap(blockIdx.x, kQStreamGroupM);
-  if (logical >= total) return;            // uniform per workgroup
-  Tile t;
-  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kQStreamGroupM)) return;
-
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
   const int cw = KS == 1 ? wave : 0;       // column block of the wave inside the tile
@@ -504,19 +494,19 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       wp[j][h] = base + n * wrow + (lane & 7) * 16;
     }
   const char* A = static_cast<const char*>(p.A);
-  const char* ap[FM];
-  long long arow[FM];
+  const char* ap[L];
+  long long arow[L];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < L; ++i) {
     arow[i] = a_src_row(p, t, t.row0 + i * 16 + lr);
     ap[i] = A + arow[i] * p.a_pitch + kq * 16;
   }
   // block scales: MX E8M0 bytes of the operand rows (8 per pair for MXFP4, 4 for MXFP8); fp8 fp32
   // block scales
   const uint8_t* wsc[MX ? 4 : 1];
-  const uint8_t* asc[MX ? FM : 1];
+  const uint8_t* asc[MX ? L : 1];
   const float* wsf[MX ? 1 : 2];
-  const float* asf[MX ? 1 : FM];
+  const float* asf[MX ? 1 : L];
   if constexpr (MX) {
     const int gpr = K / 32;
 #pragma unroll
@@ -526,7 +516,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       wsc[j] = reinterpret_cast<const uint8_t*>(sb) + n * gpr;
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) asc[i] = static_cast<const uint8_t*>(p.A_scales) + arow[i] * gpr;
+    for (int i = 0; i < L; ++i) asc[i] = static_cast<const uint8_t*>(p.A_scales) + arow[i] * gpr;
   } else {
     const int kb = K / 128;
     const char *b0, *s0, *b1, *s1;
@@ -534,16 +524,16 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     wsf[0] = reinterpret_cast<const float*>(s0) + (n0 / 128) * kb;
     wsf[1] = reinterpret_cast<const float*>(s1) + (n1 / 128) * kb;   // SWIGLU: the up block
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < L; ++i)
       asf[i] = static_cast<const float*>(p.A_scales) + (arow[i] / p.a_scale_rows) * kb;
   }
   const int src0 = ((lr & 7) * 8 + kq) * 4, src1 = src0 + 16;
   const bool upper = lr >= 8;
 
   i32x4 wraw[2][4][2];
-  i32x4 av[2][FM][2];
-  u32x2 wsm[2][MX ? 4 : 1], asm_[2][MX ? FM : 1];
-  float wss[2][2], ass[2][MX ? 1 : FM];
+  i32x4 av[2][L][2];
+  u32x2 wsm[2][MX ? 4 : 1], asm_[2][MX ? L : 1];
+  float wss[2][2], ass[2][MX ? 1 : L];
   auto load = [&](int c, int set) {
     c = c0 + (c < np ? c : np - 1);
     const long long off = (long long)c * 128;
@@ -553,7 +543,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       for (int h = 0; h < 2; ++h)
         wraw[set][j][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp[j][h] + off));
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < L; ++i)
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2)
         av[set][i][s2] = *reinterpret_cast<const i32x4*>(ap[i] + off + s2 * 64);
@@ -561,24 +551,24 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) wsm[set][j] = *reinterpret_cast<const u32x2*>(wsc[j] + c * 8);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) asm_[set][i] = *reinterpret_cast<const u32x2*>(asc[i] + c * 8);
+      for (int i = 0; i < L; ++i) asm_[set][i] = *reinterpret_cast<const u32x2*>(asc[i] + c * 8);
     } else if constexpr (MX8) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) wsm[set][j][0] = *reinterpret_cast<const uint32_t*>(wsc[j] + c * 4);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) asm_[set][i][0] = *reinterpret_cast<const uint32_t*>(asc[i] + c * 4);
+      for (int i = 0; i < L; ++i) asm_[set][i][0] = *reinterpret_cast<const uint32_t*>(asc[i] + c * 4);
     } else {
       wss[set][0] = wsf[0][c];
       wss[set][1] = wsf[1][c];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) ass[set][i] = asf[i][c];
+      for (int i = 0; i < L; ++i) ass[set][i] = asf[i][c];
     }
   };
-  f32x4 acc[4][FM];
+  f32x4 acc[4][L];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) acc[j][i] = f32x4{};
+    for (int i = 0; i < L; ++i) acc[j][i] = f32x4{};
   auto piece = [&](int set, int j, int src) -> i32x4 {
     i32x4 w;
 #pragma unroll
@@ -598,7 +588,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
         wf[j] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         const i32x4 a0 = av[set][i][0], a1 = av[set][i][1];
         const i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         const int sa = static_cast<int>((asm_[set][i][0] >> (8 * kq)) & 0xFFu);
@@ -623,7 +613,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
         for (int j = 0; j < 4; ++j) {
           const int sw = static_cast<int>(((s2 ? wsm[set][j][1] : wsm[set][j][0]) >> (sh - 32 * s2)) & 0xFFu);
 #pragma unroll
-          for (int i = 0; i < FM; ++i) {
+          for (int i = 0; i < L; ++i) {
             const int sa = static_cast<int>(((s2 ? asm_[set][i][1] : asm_[set][i][0]) >> (sh - 32 * s2)) & 0xFFu);
             const i32x4 a = av[set][i][s2];
             acc[j][i] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -639,7 +629,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
         wf[j] = i32x8{w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
       }
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         const i32x4 a0 = av[set][i][0], a1 = av[set][i][1];
         const i32x8 a = i32x8{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 #pragma unroll
@@ -671,12 +661,12 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   }
   if constexpr (KS > 1) {
     // K-split: waves 1..3 hand their partial sums to wave 0 through LDS, which finishes the tile
-    __shared__ f32x4 part[KS - 1][4][FM][64];
+    // part: [KS - 1][4][L][64]
     if (wave > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) part[wave - 1][j][i][lane] = acc[j][i];
+        for (int i = 0; i < L; ++i) part[(((wave - 1) * 4 + j) * L + i) * 64 + lane] = acc[j][i];
     }
     __syncthreads();
     if (wave > 0) return;
@@ -685,14 +675,14 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] += part[w][j][i][lane];
+        for (int i = 0; i < L; ++i) acc[j][i] += part[((w * 4 + j) * L + i) * 64 + lane];
   }
 
   // ---- epilogue: acc[j][i][v] = weight row j * 16 + kq * 4 + v of the wave, C row row0 + i*16 + lr
   char* C = static_cast<char*>(p.C);
   if constexpr (!SWIGLU) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < L; ++i) {
       const int r = t.row0 + i * 16 + lr;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -709,9 +699,9 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     }
   } else {
     // h[i][jj][v]: h column (jj * 16 + kq * 4 + v) of the wave's 32, C row row0 + i*16 + lr
-    float h[FM][2][4];
+    float h[L][2][4];
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < L; ++i)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -719,7 +709,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     const long long col0 = (long long)t.nt * (128 / KS) + cw * 32;   // first h column of the wave
     if constexpr (EPI == QEPI_SWIGLU_BF16) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         const int r = t.row0 + i * 16 + lr;
         if (r >= t.row1) continue;
 #pragma unroll
@@ -730,7 +720,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     } else if constexpr (MX8) {
       // one 1 x 32 group per row: the wave's 32 columns; row amax over the 4 lanes of the row
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         float amax = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -755,7 +745,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     } else if constexpr (MX4) {
       // one 1 x 32 group per row: the wave's 32 columns; row amax over the 4 lanes of the row
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         float amax = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -782,7 +772,7 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
     } else {
       // fp8: one 1 x 128 block per row over the workgroup's 128 columns (4 waves)
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         float amax = 0.0f;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -790,13 +780,13 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
           for (int v = 0; v < 4; ++v) amax = fmaxf(amax, fabsf(h[i][jj][v]));
         amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
         amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        if (kq == 0) amax_x[wave][i * 16 + lr] = amax;
+        if (kq == 0) amax_x[wave * ASTR + i * 16 + lr] = amax;
       }
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < L; ++i) {
         const int rl = i * 16 + lr;
-        const float amax = fmaxf(fmaxf(amax_x[0][rl], amax_x[1][rl]), fmaxf(amax_x[2][rl], amax_x[3][rl]));
+        const float amax = fmaxf(fmaxf(amax_x[rl], amax_x[ASTR + rl]), fmaxf(amax_x[2 * ASTR + rl], amax_x[3 * ASTR + rl]));
         const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
         const int r = t.row0 + rl;
         if (r >= t.row1) continue;
@@ -812,6 +802,35 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
       }
     }
   }
+}
+
+template <int FMT, int EPI, int FM, int KS>
+__global__ void __launch_bounds__(256)
+gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
+  // KS = 1: the 4 waves take 4 adjacent column blocks (fp8's 1 x 128 h blocks need all four);
+  // KS = 4: they share one column block and split its K-pairs, summed through LDS at the end
+  static_assert(KS == 1 || KS == 4, "K split");
+  static_assert(KS == 1 || !(EPI == QEPI_SWIGLU_Q && FMT == MOE_FP8_E4M3), "fp8 h blocks span 4 waves");
+  static_assert(FM == 1 || FM == 2, "tile rows");
+  constexpr int BM = 16 * FM;
+  __shared__ float amax_x[4 * BM];         // fp8 h: per-wave row amax
+  __shared__ f32x4 part[KS > 1 ? (KS - 1) * 4 * FM * 64 : 1];
+
+  const int logical = xcd_remap(blockIdx.x, kQStreamGroupM);
+  if (logical >= total) return;            // uniform per workgroup
+  Tile t;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kQStreamGroupM)) return;
+  // 16-row fragments holding rows of the tile (uniform over the workgroup): each count runs its
+  // own instantiation, so every load and MFMA stays unconditional. Not for MXFP8: with both
+  // bodies in one kernel its K-split form needs more than 256 registers (one wave per SIMD
+  // instead of two; measured 14% slower on the 64-token Qwen3-235B slice)
+  if constexpr (FM == 2) {
+    if (FMT == MOE_MXFP8 || t.row1 - t.row0 > 16) {
+      stream_q_tile<2, FMT, EPI, KS, BM>(p, t, amax_x, part);
+      return;
+    }
+  }
+  if constexpr (FMT != MOE_MXFP8 || FM == 1) stream_q_tile<1, FMT, EPI, KS, BM>(p, t, amax_x, part);
 }
 
 // ------------------------------------------------------------------------------------------------
