@@ -925,6 +925,9 @@ constexpr int kTileSpan = 64;
 // (same box, gate/up / down): 3 stages 2.52 / 1.61 ms, 4 stages 2.54 / 1.63 ms, 5 stages 2.60-2.63 /
 // 1.65-1.67 ms -- fewer loads in flight per CU run faster here.
 constexpr int kPPStages = 3;
+// 192-row tiles: 4 stages of 28 KB (their groups' weights, each read by one m-tile, stream from HBM;
+// measured on the 8192-token Qwen3.5-397B slice: 3 stages 0.905 ms, 4 stages 0.890, 5 stages 0.905)
+constexpr int kPPStages192 = 4;
 // weight-streaming tiles of 32 rows up to this many rows per group on average, 64 rows above
 constexpr int kStreamRows32 = 24;
 // weight streaming: K pairs (128 bytes of every weight row) per wave at or above which a tile is
@@ -1102,7 +1105,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       // issued before the previous tile's stores, which drain behind its first K-steps (measured
       // with the down projection's fp32 stores removed: the stores, waited for at every tile
       // start, took a quarter of its time).
-      if (tile192) return run_bf16_pp<kPPStages, true, 192>(a, s, kTileGroupM, kTileSpan);
+      if (tile192) return run_bf16_pp<kPPStages192, true, 192>(a, s, kTileGroupM, kTileSpan);
       return run_bf16_pp<kPPStages, true>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
