@@ -291,8 +291,10 @@ def copy_calibration():
 
 def stream_ceiling(steps):
     """Read rate of a 1 GiB matrix of 8 KB rows with the decode kernels' weight-stream pattern (8 rows
-    x 128 bytes per load) and with 1 KB of one row per load, non-temporal, each read after a 1 GiB
-    read of another buffer (cold caches); HIP events on the probe's stream, median of `steps`."""
+    x 128 bytes per load, 16 rows per wave, 8 loads in flight), with 1 KB of one row per load, and
+    with the weight-stream pattern in fewer, longer streams (64 rows per wave, 16 loads in flight),
+    non-temporal, each read after a 1 GiB read of another buffer (cold caches); HIP events on the
+    probe's stream, median of `steps`."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "moe_layer_softmax_amd", "libmoe_probe.so"))
@@ -304,14 +306,15 @@ def stream_ceiling(steps):
     out = torch.empty(n // (64 * 8192) * 256, dtype=torch.int32, device="cuda")
     stream = torch.cuda.Stream()
     res = {}
-    for rows in (8, 1):
+    names = {0: "8_rows_per_load", 1: "1_rows_per_load", 2: "8_rows_per_load_64_rows_per_wave_16_in_flight"}
+    for pattern in (0, 1, 2):
         ms = []
         for _ in range(steps + 1):
             with torch.cuda.stream(stream):
                 flush.sum()
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                rc = lib.moe_probe_read_rows(src.data_ptr(), n, rows, out.data_ptr(),
+                rc = lib.moe_probe_read_rows(src.data_ptr(), n, pattern, out.data_ptr(),
                                              ctypes.c_void_p(stream.cuda_stream))
                 b.record(stream)
             if rc != 0:
@@ -319,7 +322,7 @@ def stream_ceiling(steps):
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
         t = float(np.median(ms[1:]))
-        res[f"{rows}_rows_per_load"] = {"ms": round(t, 4), "TB_per_s": round(n / (t * 1e-3) / 1e12, 3)}
+        res[names[pattern]] = {"ms": round(t, 4), "TB_per_s": round(n / (t * 1e-3) / 1e12, 3)}
     print(json.dumps({"hbm_read_ceiling": res, "bytes": n, "row_bytes": 8192, "steps": steps}), flush=True)
 
 
