@@ -31,13 +31,6 @@ size_t permute_ws_bytes(long long slots, int E_loc) {
   return static_cast<size_t>(chunks) * E_loc * sizeof(int32_t) + 256;
 }
 
-__device__ __forceinline__ int local_key(const int32_t* ids, long long f, long long slots, int e0,
-                                         int E_loc) {
-  if (f >= slots) return E_loc + 1;             // past the end: matches nothing
-  int el = ids[f] - e0;
-  return (el >= 0 && el < E_loc) ? el : E_loc;  // E_loc: not on this GPU
-}
-
 // lanes of the wave holding the same key as this lane
 __device__ __forceinline__ unsigned long long match_key(int key, int nbits) {
   unsigned long long m = __ballot(1);
@@ -55,34 +48,61 @@ __device__ __forceinline__ int key_bits(int E_loc) {
   return n;
 }
 
-// count the local experts of one chunk into cnt[E_loc] (LDS, zeroed by the caller)
-__device__ __forceinline__ void hist_chunk(const int32_t* ids, long long c0, long long c1,
-                                           int e0, int E_loc, int* cnt) {
+// The keys of one wave's slots [c0, c1) (c1 - c0 <= 64 * N), lane-strided: key[i] belongs to
+// slot c0 + 64 i + lane. Every load is issued before the first is used (clamped to the last slot of
+// the range, so none is predicated), so a chunk costs one memory round trip. Keys: the local expert,
+// E_loc for a slot routed off this GPU, E_loc + 1 past the range.
+template <int N>
+__device__ __forceinline__ void load_keys(const int32_t* ids, long long c0, long long c1, int e0,
+                                          int E_loc, int (&key)[N]) {
   const int lane = lane_id();
-  for (long long f = c0 + lane; f < c1; f += 64) {
-    int el = ids[f] - e0;
-    if (el >= 0 && el < E_loc) atomicAdd(&cnt[el], 1);
+  if (c0 >= c1) {                           // wave-uniform: an empty range reads nothing
+#pragma unroll
+    for (int i = 0; i < N; ++i) key[i] = E_loc + 1;
+    return;
+  }
+  int raw[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const long long f = c0 + i * 64 + lane;
+    raw[i] = ids[f < c1 ? f : c1 - 1];
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int el = raw[i] - e0;
+    key[i] = c0 + i * 64 + lane >= c1 ? E_loc + 1 : ((el >= 0 && el < E_loc) ? el : E_loc);
   }
 }
 
-// place the local slots of one chunk; run[E_loc] (LDS) holds the next row of each expert
-__device__ __forceinline__ void scatter_chunk(const int32_t* ids, long long c0, long long c1,
-                                              long long slots, int e0, int E_loc, int* run,
-                                              int32_t* slot_to_row, int32_t* row_to_flat) {
+// count the local experts among the keys into cnt[E_loc] (LDS, zeroed by the caller)
+template <int N>
+__device__ __forceinline__ void hist_keys(const int (&key)[N], int E_loc, int* cnt) {
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    if (key[i] < E_loc) atomicAdd(&cnt[key[i]], 1);
+}
+
+// place the slots of one wave's range in order, 64 at a time; run[E_loc] (LDS) holds the next row
+// of each expert
+template <int N>
+__device__ __forceinline__ void scatter_keys(const int (&key)[N], long long c0, long long c1,
+                                             int E_loc, int* run, int32_t* slot_to_row,
+                                             int32_t* row_to_flat) {
   const int lane = lane_id();
   const int nbits = key_bits(E_loc);
   const unsigned long long lt = (1ull << lane) - 1ull;
-  for (long long s = c0; s < c1; s += 64) {
-    const long long f = s + lane;
-    const int key = local_key(ids, f, c1 < slots ? c1 : slots, e0, E_loc);
-    const unsigned long long peers = match_key(key, nbits);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (c0 + i * 64 >= c1) break;           // wave-uniform
+    const long long f = c0 + i * 64 + lane;
+    const unsigned long long peers = match_key(key[i], nbits);
     const int rank = __popcll(peers & lt);
     int row = -1;
-    if (key < E_loc) row = run[key] + rank;
+    if (key[i] < E_loc) row = run[key[i]] + rank;
     __builtin_amdgcn_wave_barrier();
-    if (key < E_loc && rank == 0) run[key] += __popcll(peers);
+    if (key[i] < E_loc && rank == 0) run[key[i]] += __popcll(peers);
     __builtin_amdgcn_wave_barrier();
-    if (f < c1 && f < slots) {
+    if (f < c1) {
       slot_to_row[f] = row;
       if (row >= 0) row_to_flat[row] = static_cast<int32_t>(f);
     }
@@ -99,7 +119,9 @@ __global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restric
   __syncthreads();
   if (c < n_chunks) {
     long long c0 = (long long)c * kChunk, c1 = c0 + kChunk < slots ? c0 + kChunk : slots;
-    hist_chunk(ids, c0, c1, e0, E_loc, cnt[w]);
+    int key[kChunk / 64];
+    load_keys(ids, c0, c1, e0, E_loc, key);
+    hist_keys(key, E_loc, cnt[w]);
   }
   __syncthreads();
   if (c < n_chunks)
@@ -137,16 +159,36 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int& t
 
 // counts, offsets and the base row of every (chunk, expert). One wave per expert (16 waves,
 // experts w, w + 16, ...): lane l sums chunks l, l + 64, ...; then the chunk bases are an in-order
-// scan over chunks, 64 chunks per wave-wide prefix sum.
+// scan over chunks, 64 chunks per wave-wide prefix sum. The table is read from `src` and the bases
+// written to `partial`: with STAGED, src is an LDS copy of the whole table (loaded with every load
+// in flight at once, so the kernel pays one memory round trip instead of one per read); otherwise
+// it is `partial` itself.
+constexpr int kScanPer = 12;                      // table entries per thread of the LDS copy
+constexpr int kScanLds = kScanPer * 1024;         // 48 KB
+
+template <bool STAGED>
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ partial, int n_chunks,
                                                          int E_loc, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
   __shared__ int tmp[64];
   __shared__ int tot_of[kMaxLocal];
+  __shared__ int table[STAGED ? kScanLds : 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int n = n_chunks * E_loc;
+  const int32_t* src = partial;
+  if constexpr (STAGED) {
+    int v[kScanPer];
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) v[j] = partial[min(j * 1024 + (int)threadIdx.x, n - 1)];
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j)
+      if (j * 1024 + (int)threadIdx.x < n) table[j * 1024 + threadIdx.x] = v[j];
+    __syncthreads();
+    src = table;
+  }
   for (int e = w; e < E_loc; e += 16) {
     int sum = 0;
-    for (int c = lane; c < n_chunks; c += 64) sum += partial[(size_t)c * E_loc + e];
+    for (int c = lane; c < n_chunks; c += 64) sum += src[(size_t)c * E_loc + e];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
     if (lane == 0) tot_of[e] = sum;
@@ -167,7 +209,7 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ p
     int run = tot_of[e];
     for (int c0 = 0; c0 < n_chunks; c0 += 64) {
       const int c = c0 + lane;
-      const int v = c < n_chunks ? partial[(size_t)c * E_loc + e] : 0;
+      const int v = c < n_chunks ? src[(size_t)c * E_loc + e] : 0;
       int inc = v;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -190,10 +232,12 @@ __global__ void __launch_bounds__(256) perm_scatter_kernel(const int32_t* __rest
   const int w = threadIdx.x >> 6;
   const int c = blockIdx.x * 4 + w;
   if (c >= n_chunks) return;                 // per-wave exit; no block barrier below
+  long long c0 = (long long)c * kChunk, c1 = c0 + kChunk < slots ? c0 + kChunk : slots;
+  int key[kChunk / 64];
+  load_keys(ids, c0, c1, e0, E_loc, key);    // in flight together with the bases below
   for (int i = threadIdx.x & 63; i < E_loc; i += 64) run[w][i] = base[(size_t)c * E_loc + i];
   __builtin_amdgcn_wave_barrier();
-  long long c0 = (long long)c * kChunk, c1 = c0 + kChunk < slots ? c0 + kChunk : slots;
-  scatter_chunk(ids, c0, c1, slots, e0, E_loc, run[w], slot_to_row, row_to_flat);
+  scatter_keys(key, c0, c1, E_loc, run[w], slot_to_row, row_to_flat);
 }
 
 // All three phases in one workgroup of 16 waves (small routing tables).
@@ -209,9 +253,11 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
   long long per = ((slots + 16 * 64 - 1) / (16 * 64)) * 64;   // slots per wave, multiple of 64
   long long c0 = w * per, c1 = c0 + per < slots ? c0 + per : slots;
   if (c0 > slots) c0 = slots;
+  int key[16];                                                // per <= 16 * 64
+  load_keys(ids, c0, c1, e0, E_loc, key);
   for (int i = threadIdx.x & 63; i < E_loc; i += 64) cnt[w][i] = 0;
   __syncthreads();
-  hist_chunk(ids, c0, c1, e0, E_loc, cnt[w]);
+  hist_keys(key, E_loc, cnt[w]);
   __syncthreads();
   const int el = threadIdx.x;
   int tot = 0;
@@ -231,7 +277,7 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
   }
   if (threadIdx.x == 0) offsets[E_loc] = total;
   __syncthreads();
-  scatter_chunk(ids, c0, c1, slots, e0, E_loc, cnt[w], slot_to_row, row_to_flat);
+  scatter_keys(key, c0, c1, E_loc, cnt[w], slot_to_row, row_to_flat);
 }
 
 hipError_t launch_permute_maps(int T, int k, int e0, int E_loc, const int32_t* ids, int32_t* counts,
@@ -247,7 +293,10 @@ hipError_t launch_permute_maps(int T, int k, int e0, int E_loc, const int32_t* i
   int32_t* partial = static_cast<int32_t*>(ws);
   const int blocks = (n_chunks + 3) / 4;
   perm_hist_kernel<<<blocks, 256, 0, s>>>(ids, slots, e0, E_loc, n_chunks, partial);
-  perm_scan_kernel<<<1, 1024, 0, s>>>(partial, n_chunks, E_loc, counts, offsets);
+  if ((long long)n_chunks * E_loc <= kScanLds)
+    perm_scan_kernel<true><<<1, 1024, 0, s>>>(partial, n_chunks, E_loc, counts, offsets);
+  else
+    perm_scan_kernel<false><<<1, 1024, 0, s>>>(partial, n_chunks, E_loc, counts, offsets);
   perm_scatter_kernel<<<blocks, 256, 0, s>>>(ids, slots, e0, E_loc, n_chunks, partial, slot_to_row,
                                              row_to_flat);
   return hipGetLastError();

@@ -1,10 +1,10 @@
 // route.hip -- scores, top-k and routing weights on gfx950.
 //
-// One wave64 per token. Each lane holds ceil(E/64) logits as 64-bit keys
-//   key = (order-preserving u32 of the fp32 logit) << 32 | (~expert id)
-// so that the wave-wide maximum key is the largest logit and, among equal logits, the lowest
-// expert id (the tie rule of the tiny workload; -0.0 is canonicalised to +0.0 first so the two
-// compare equal). k rounds of a wave max pick the experts in rank order.
+// One wave64 per token. Each lane holds ceil(E/64) logits as order-preserving u32 codes of the
+// fp32 values (-0.0 canonicalised to +0.0 first so the two compare equal; 0 marks a padding or an
+// already chosen entry). Each of k rounds takes the wave-wide maximum code and, among the entries
+// holding it, the lowest expert id (the tie rule of the tiny workload): one ballot per register
+// of codes, the first nonzero one giving the expert. The rounds pick the experts in rank order.
 // Routing as int ids + float weights of shape [T, k]: "How we served a 397B MoE model ... on
 // TPU v7", section "Three collectives become two".
 #include "common.hpp"
@@ -19,6 +19,29 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 __device__ __forceinline__ float from_ordered(uint32_t o) {
   uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
   return __uint_as_float(u);
+}
+// code of a real entry: never 0 (only the negative NaN with every bit set maps to 0; it becomes
+// the next NaN code)
+__device__ __forceinline__ uint32_t entry_code(float f) {
+  const uint32_t o = ordered_bits(f);
+  return o > 1u ? o : 1u;
+}
+// wave-wide maximum: within each row of 16 lanes by DPP (quad swaps, then row rotations by 4 and
+// 8), then the four rows' maxima through scalar registers
+__device__ __forceinline__ uint32_t wave_max_code(uint32_t v) {
+  auto dmax = [](uint32_t x, auto ctrl) {
+    const uint32_t y = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(0, static_cast<int>(x), decltype(ctrl)::value, 0xF, 0xF, false));
+    return x > y ? x : y;
+  };
+  v = dmax(v, std::integral_constant<int, 0xB1>{});
+  v = dmax(v, std::integral_constant<int, 0x4E>{});
+  v = dmax(v, std::integral_constant<int, 0x124>{});
+  v = dmax(v, std::integral_constant<int, 0x128>{});
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  const uint32_t a = r0 > r1 ? r0 : r1, b = r2 > r3 ? r2 : r3;
+  return a > b ? a : b;
 }
 
 // With nsplit > 1 the logits are first formed from the router's K-split partial sums
@@ -36,18 +59,17 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
   const int lane = threadIdx.x & 63;
   float* L = logits + (size_t)t * E;
 
-  unsigned long long key[VPL];
+  uint32_t code[VPL];
   float val[VPL];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     int e = v * 64 + lane;
     if (e < E) {
       val[v] = nsplit > 1 ? 0.0f : L[e];
-      key[v] = (static_cast<unsigned long long>(ordered_bits(val[v])) << 32) |
-               static_cast<uint32_t>(~e);
+      code[v] = entry_code(val[v]);
     } else {
       val[v] = 0.0f;
-      key[v] = 0ull;                        // below every real key
+      code[v] = 0u;                         // below every real entry
     }
   }
 
@@ -78,8 +100,7 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
       if (e < E) {
         if (bias) val[v] += bias[e];
         L[e] = val[v];
-        key[v] = (static_cast<unsigned long long>(ordered_bits(val[v])) << 32) |
-                 static_cast<uint32_t>(~e);
+        code[v] = entry_code(val[v]);
       }
     }
   }
@@ -87,19 +108,29 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
   float my_l = 0.0f, top_l = 0.0f;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    unsigned long long best = key[0];
+    uint32_t m = code[0];
 #pragma unroll
-    for (int v = 1; v < VPL; ++v) best = key[v] > best ? key[v] : best;
-    best = wave_max_u64(best);
-    const int e = static_cast<int>(~static_cast<uint32_t>(best));
-    const float l = from_ordered(static_cast<uint32_t>(best >> 32));
+    for (int v = 1; v < VPL; ++v) m = code[v] > m ? code[v] : m;
+    const uint32_t best = wave_max_code(m);            // wave-uniform, >= 1 while j < k <= E
+    // lowest expert holding the best code: registers in order, then lanes
+    int e = 0;
+    bool found = false;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const unsigned long long b = __ballot(code[v] == best);
+      if (!found && b != 0ull) {
+        e = v * 64 + __builtin_ctzll(b);
+        found = true;
+      }
+    }
+    e = __builtin_amdgcn_readfirstlane(e);
+    const float l = from_ordered(best);
     if (j == 0) top_l = l;
     if (lane == j) { my_l = l; my_e = e; }
-    if ((e & 63) == lane) {
+    const bool mine = lane == (e & 63);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        if (v == (e >> 6)) key[v] = 0ull;
-    }
+    for (int v = 0; v < VPL; ++v)
+      if (v == (e >> 6)) code[v] = mine ? 0u : code[v];
   }
 
   float wt;
