@@ -16,7 +16,9 @@
 //            (chunk, expert) = offsets[e] + counts of e in earlier chunks
 //   scatter: each wave walks its chunk in order, 64 slots at a time, ranking equal experts with
 //            ballots and advancing a running row per expert kept in LDS.
-// For small tables (decode) one 1024-thread workgroup does all three phases in LDS.
+// Count tables of up to 8192 entries fold the scan into the scatter kernel (every workgroup reads
+// the whole table), so the dispatch is two launches; larger ones run the scan as a kernel of its
+// own. For small tables (decode) one 1024-thread workgroup does all three phases in LDS.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -128,8 +130,10 @@ __global__ void __launch_bounds__(256) perm_hist_kernel(const int32_t* __restric
     for (int i = threadIdx.x & 63; i < E_loc; i += 64) partial[(size_t)c * E_loc + i] = cnt[w][i];
 }
 
-// exclusive scan of v over the 1024 threads of the block (returns the exclusive prefix, total)
-__device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int& total) {
+// exclusive scan of v over the NW * 64 threads of the block (returns the exclusive prefix, total)
+template <int NW>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int& total) {
+  static_assert(NW <= 16, "wave totals in one 16-lane scan");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int inc = v;
 #pragma unroll
@@ -140,7 +144,7 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int& t
   if (lane == 63) tmp[w] = inc;
   __syncthreads();
   if (w == 0) {
-    int x = lane < 16 ? tmp[lane] : 0;
+    int x = lane < NW ? tmp[lane] : 0;
     int xi = x;
 #pragma unroll
     for (int o = 1; o < 16; o <<= 1) {
@@ -159,36 +163,16 @@ __device__ __forceinline__ int block_exclusive_scan_1024(int v, int* tmp, int& t
 
 // counts, offsets and the base row of every (chunk, expert). One wave per expert (16 waves,
 // experts w, w + 16, ...): lane l sums chunks l, l + 64, ...; then the chunk bases are an in-order
-// scan over chunks, 64 chunks per wave-wide prefix sum. The table is read from `src` and the bases
-// written to `partial`: with STAGED, src is an LDS copy of the whole table (loaded with every load
-// in flight at once, so the kernel pays one memory round trip instead of one per read); otherwise
-// it is `partial` itself.
-constexpr int kScanPer = 12;                      // table entries per thread of the LDS copy
-constexpr int kScanLds = kScanPer * 1024;         // 48 KB
-
-template <bool STAGED>
+// scan over chunks, 64 chunks per wave-wide prefix sum.
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ partial, int n_chunks,
                                                          int E_loc, int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets) {
   __shared__ int tmp[64];
   __shared__ int tot_of[kMaxLocal];
-  __shared__ int table[STAGED ? kScanLds : 1];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int n = n_chunks * E_loc;
-  const int32_t* src = partial;
-  if constexpr (STAGED) {
-    int v[kScanPer];
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j) v[j] = partial[min(j * 1024 + (int)threadIdx.x, n - 1)];
-#pragma unroll
-    for (int j = 0; j < kScanPer; ++j)
-      if (j * 1024 + (int)threadIdx.x < n) table[j * 1024 + threadIdx.x] = v[j];
-    __syncthreads();
-    src = table;
-  }
   for (int e = w; e < E_loc; e += 16) {
     int sum = 0;
-    for (int c = lane; c < n_chunks; c += 64) sum += src[(size_t)c * E_loc + e];
+    for (int c = lane; c < n_chunks; c += 64) sum += partial[(size_t)c * E_loc + e];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
     if (lane == 0) tot_of[e] = sum;
@@ -197,7 +181,7 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ p
   const int el = threadIdx.x;
   const int tot = el < E_loc ? tot_of[el] : 0;
   int total;
-  const int off = block_exclusive_scan_1024(tot, tmp, total);   // ends with a barrier
+  const int off = block_exclusive_scan<16>(tot, tmp, total);   // ends with a barrier
   if (el < E_loc) {
     counts[el] = tot;
     offsets[el] = off;
@@ -209,7 +193,7 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int32_t* __restrict__ p
     int run = tot_of[e];
     for (int c0 = 0; c0 < n_chunks; c0 += 64) {
       const int c = c0 + lane;
-      const int v = c < n_chunks ? src[(size_t)c * E_loc + e] : 0;
+      const int v = c < n_chunks ? partial[(size_t)c * E_loc + e] : 0;
       int inc = v;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -240,6 +224,85 @@ __global__ void __launch_bounds__(256) perm_scatter_kernel(const int32_t* __rest
   scatter_keys(key, c0, c1, E_loc, run[w], slot_to_row, row_to_flat);
 }
 
+// Scan folded into the scatter (count tables of up to kFusedTable entries): each workgroup loads
+// the whole table with every load in flight and folds it, as it arrives, into per-expert LDS sums:
+// the total over all chunks and the sum over the chunks before the workgroup's first; it keeps the
+// rows of its own first three chunks. A wave's chunk base is then offsets[e] + that sum + the rows
+// of the workgroup's chunks before it. Workgroup 0 also writes the counts and offsets. This
+// replaces the one-workgroup scan kernel between the count and scatter kernels.
+constexpr int kFusedTable = 8192;
+
+__global__ void __launch_bounds__(256) perm_scan_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                long long slots, int e0, int E_loc,
+                                                                int n_chunks,
+                                                                const int32_t* __restrict__ partial,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ slot_to_row,
+                                                                int32_t* __restrict__ row_to_flat) {
+  constexpr int PER = kFusedTable / 256;
+  __shared__ int tot[kMaxLocal], pre[kMaxLocal], own[3][kMaxLocal], run[4][kMaxLocal];
+  __shared__ int tmp[64];
+  const int tid = threadIdx.x, w = tid >> 6;
+  const int cw = blockIdx.x * 4, c = cw + w;
+  // this wave's keys (empty past the last chunk) and the table, all loads in flight together
+  const long long c0 = (long long)c * kChunk, c1 = c0 + kChunk < slots ? c0 + kChunk : slots;
+  int key[kChunk / 64];
+  load_keys(ids, c0, c1, e0, E_loc, key);
+  const int n = n_chunks * E_loc;
+  int v[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) v[j] = partial[min(j * 256 + tid, n - 1)];
+  for (int e = tid; e < E_loc; e += 256) tot[e] = pre[e] = 0;
+  __syncthreads();
+  // entry j * 256 + tid is (chunk cc, expert e); 256 = dq * E_loc + dr steps both
+  const int dq = 256 / E_loc, dr = 256 - dq * E_loc;
+  int cc = tid / E_loc, e = tid - cc * E_loc;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    if (j * 256 + tid < n) {
+      atomicAdd(&tot[e], v[j]);
+      if (cc < cw) atomicAdd(&pre[e], v[j]);
+      else if (cc < cw + 3) own[cc - cw][e] = v[j];
+    }
+    cc += dq;
+    e += dr;
+    if (e >= E_loc) { e -= E_loc; ++cc; }
+  }
+  __syncthreads();
+  // offsets: exclusive scan over the experts, 4 consecutive experts per thread (E_loc <= 1024)
+  int t4[4], s4 = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t4[i] = 4 * tid + i < E_loc ? tot[4 * tid + i] : 0;
+    s4 += t4[i];
+  }
+  int total;
+  int off = block_exclusive_scan<4>(s4, tmp, total);             // ends with a barrier
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int el = 4 * tid + i;
+    if (el < E_loc) {
+      if (blockIdx.x == 0) {
+        counts[el] = t4[i];
+        offsets[el] = off;
+      }
+      tot[el] = off;                                             // each thread rewrites its own
+    }
+    off += t4[i];
+  }
+  if (blockIdx.x == 0 && tid == 0) offsets[E_loc] = total;
+  __syncthreads();
+  if (c >= n_chunks) return;                 // per-wave exit; no block barrier below
+  for (int el = tid & 63; el < E_loc; el += 64) {
+    int b = tot[el] + pre[el];
+    for (int r = 0; r < w; ++r) b += own[r][el];
+    run[w][el] = b;
+  }
+  __builtin_amdgcn_wave_barrier();
+  scatter_keys(key, c0, c1, E_loc, run[w], slot_to_row, row_to_flat);
+}
+
 // All three phases in one workgroup of 16 waves (small routing tables).
 __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restrict__ ids,
                                                           long long slots, int e0, int E_loc,
@@ -264,7 +327,7 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
   if (el < E_loc)
     for (int v = 0; v < 16; ++v) tot += cnt[v][el];
   int total;
-  const int off = block_exclusive_scan_1024(el < E_loc ? tot : 0, tmp, total);
+  const int off = block_exclusive_scan<16>(el < E_loc ? tot : 0, tmp, total);
   if (el < E_loc) {
     counts[el] = tot;
     offsets[el] = off;
@@ -293,10 +356,12 @@ hipError_t launch_permute_maps(int T, int k, int e0, int E_loc, const int32_t* i
   int32_t* partial = static_cast<int32_t*>(ws);
   const int blocks = (n_chunks + 3) / 4;
   perm_hist_kernel<<<blocks, 256, 0, s>>>(ids, slots, e0, E_loc, n_chunks, partial);
-  if ((long long)n_chunks * E_loc <= kScanLds)
-    perm_scan_kernel<true><<<1, 1024, 0, s>>>(partial, n_chunks, E_loc, counts, offsets);
-  else
-    perm_scan_kernel<false><<<1, 1024, 0, s>>>(partial, n_chunks, E_loc, counts, offsets);
+  if ((long long)n_chunks * E_loc <= kFusedTable) {
+    perm_scan_scatter_kernel<<<blocks, 256, 0, s>>>(ids, slots, e0, E_loc, n_chunks, partial, counts,
+                                                    offsets, slot_to_row, row_to_flat);
+    return hipGetLastError();
+  }
+  perm_scan_kernel<<<1, 1024, 0, s>>>(partial, n_chunks, E_loc, counts, offsets);
   perm_scatter_kernel<<<blocks, 256, 0, s>>>(ids, slots, e0, E_loc, n_chunks, partial, slot_to_row,
                                              row_to_flat);
   return hipGetLastError();

@@ -112,25 +112,28 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
 #pragma unroll
     for (int v = 1; v < VPL; ++v) m = code[v] > m ? code[v] : m;
     const uint32_t best = wave_max_code(m);            // wave-uniform, >= 1 while j < k <= E
-    // lowest expert holding the best code: registers in order, then lanes
+    // lowest expert holding the best code: the registers from last to first, the last nonzero
+    // ballot (lowest register) deciding, its lowest lane within it
     int e = 0;
-    bool found = false;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
+    for (int v = VPL - 1; v >= 0; --v) {
       const unsigned long long b = __ballot(code[v] == best);
-      if (!found && b != 0ull) {
-        e = v * 64 + __builtin_ctzll(b);
-        found = true;
-      }
+      e = b != 0ull ? v * 64 + static_cast<int>(__builtin_ctzll(b)) : e;
     }
     e = __builtin_amdgcn_readfirstlane(e);
     const float l = from_ordered(best);
     if (j == 0) top_l = l;
     if (lane == j) { my_l = l; my_e = e; }
-    const bool mine = lane == (e & 63);
+    // clear the chosen entry: a compare per register, or (16 registers) one indexed register
+    // access through the uniform register index
+    if constexpr (VPL >= 16) {
+      const int vw = e >> 6;
+      code[vw] = lane == (e & 63) ? 0u : code[vw];
+    } else {
+      const int el = e - lane;                                    // v * 64 in the owning lane
 #pragma unroll
-    for (int v = 0; v < VPL; ++v)
-      if (v == (e >> 6)) code[v] = mine ? 0u : code[v];
+      for (int v = 0; v < VPL; ++v) code[v] = el == v * 64 ? 0u : code[v];
+    }
   }
 
   float wt;

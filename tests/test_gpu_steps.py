@@ -229,7 +229,9 @@ def test_route_from_x(T, H, E, k, zipf, scoring):
 @pytest.mark.parametrize("T,E,k,e0,E_loc,hot", [(64, 8, 2, 0, 8, 0.0), (333, 128, 8, 0, 32, 0.3),
                                                 (2048, 512, 10, 64, 64, 0.0), (1, 16, 4, 12, 4, 0.0),
                                                 (16384, 128, 8, 0, 32, 0.5), (3000, 256, 8, 96, 32, 0.2),
-                                                (2047, 1024, 16, 0, 1024, 0.0), (50, 8, 8, 0, 8, 0.0)])
+                                                (2047, 1024, 16, 0, 1024, 0.0), (50, 8, 8, 0, 8, 0.0),
+                                                (3000, 72, 7, 3, 45, 0.1), (2500, 512, 8, 100, 300, 0.0),
+                                                (8192, 512, 10, 64, 64, 0.0)])
 def test_permute_bitexact(T, E, k, e0, E_loc, hot):
     ids_np = gen.random_topk_ids(T, E, k, seed=T + E, hot=[e0, e0 + 1], hot_frac=hot)
     H = 128
