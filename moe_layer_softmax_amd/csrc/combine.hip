@@ -17,9 +17,10 @@ enum { kYF32 = 0, kYBf16 = 1, kYF16S = 2 };
 // Workgroup (t, c): token t, columns [c * 256 * CPL, (c + 1) * 256 * CPL), CPL per thread (8 for
 // bf16 and scaled fp16 rows, 4 for fp32: one 16-byte load per row). All KMAX rows' loads are issued
 // before the first is added (unconditional: a non-local slot, and a slot j >= k, reads row 0 and
-// adds nothing), so one token's latency is one memory round trip. KMAX (8 or 16) bounds k: the k
-// rows' values are held in registers, and with KMAX = 8 twice as many waves fit on a CU to keep
-// loads in flight. Scaled fp16 rows (MOE_F16_SCALED) also load the fp32 scale of the thread's
+// adds nothing), so one token's latency is one memory round trip. KMAX (8, 12 or 16) bounds k: the
+// k rows' values are held in registers, and the smallest KMAX >= k is launched, so that fewer
+// registers per wave let more waves keep loads in flight and no more dead loads are issued than
+// needed. Scaled fp16 rows (MOE_F16_SCALED) also load the fp32 scale of the thread's
 // 64-column block, which multiplies the row's weight (a power of two: exact).
 template <int YF, bool OUT_BF16, int KMAX>
 __global__ void __launch_bounds__(256) combine_kernel(int H, int k, long long pitch, const void* __restrict__ y,
@@ -130,8 +131,9 @@ hipError_t run_combine(int T, int H, int k, bool ob, long long pitch, const void
                        void* out, hipStream_t s) {
   const int cols_per_wg = 256 * (YF == kYF32 ? 4 : 8);
   dim3 grid(T, (H + cols_per_wg - 1) / cols_per_wg), block(256);
-  auto k_ = k <= 8 ? (ob ? combine_kernel<YF, true, 8> : combine_kernel<YF, false, 8>)
-                   : (ob ? combine_kernel<YF, true, 16> : combine_kernel<YF, false, 16>);
+  auto k_ = k <= 8    ? (ob ? combine_kernel<YF, true, 8> : combine_kernel<YF, false, 8>)
+            : k <= 12 ? (ob ? combine_kernel<YF, true, 12> : combine_kernel<YF, false, 12>)
+                      : (ob ? combine_kernel<YF, true, 16> : combine_kernel<YF, false, 16>);
   k_<<<grid, block, 0, s>>>(H, k, pitch, y, w, slot_to_row, shared, shared_w, out);
   return hipGetLastError();
 }

@@ -51,17 +51,21 @@ __global__ void __launch_bounds__(256) quant_fp8_kernel(int rows, int cols, int 
   const int r0 = bi * block_rows;
   const int r1 = r0 + block_rows < rows ? r0 + block_rows : rows;
   const int nch = (r1 - r0) * 16;          // 8-element chunks of the block (<= 2048)
+  // every chunk load is issued before the first is used: indices past the block's end are clamped
+  // to its last chunk (in bounds, nch >= 16) and those values are left out of the maximum (a
+  // guarded load became a branch with a full wait after each of the 8 loads)
   float v[8][8];
   float amax = 0.0f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const int i = threadIdx.x + u * 256;
-    if (i < nch) {
-      load8<SRC_BF16>(src, mat + (size_t)(r0 + i / 16) * cols + bj * 128 + (i % 16) * 8, v[u]);
+    const int i = min((int)threadIdx.x + u * 256, nch - 1);
+    load8<SRC_BF16>(src, mat + (size_t)(r0 + i / 16) * cols + bj * 128 + (i % 16) * 8, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+    if ((int)threadIdx.x + u * 256 < nch)
 #pragma unroll
       for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[u][e]));
-    }
-  }
   __shared__ float red[4];
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;

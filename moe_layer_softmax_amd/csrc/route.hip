@@ -61,11 +61,16 @@ __global__ void __launch_bounds__(256) topk_kernel(int T, int E, int k, int scor
 
   uint32_t code[VPL];
   float val[VPL];
+  // every logit load is issued before the first is used (clamped to the last expert, never
+  // guarded: a guarded load became a branch with a full wait after each one)
+  if (nsplit <= 1) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) val[v] = L[min(v * 64 + lane, E - 1)];
+  }
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
-    int e = v * 64 + lane;
-    if (e < E) {
-      val[v] = nsplit > 1 ? 0.0f : L[e];
+    if (v * 64 + lane < E) {
+      if (nsplit > 1) val[v] = 0.0f;
       code[v] = entry_code(val[v]);
     } else {
       val[v] = 0.0f;
