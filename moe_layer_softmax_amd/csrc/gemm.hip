@@ -928,8 +928,10 @@ constexpr int kPPStages = 3;
 // 192-row tiles: 4 stages of 28 KB (their groups' weights, each read by one m-tile, stream from HBM;
 // measured on the 8192-token Qwen3.5-397B slice: 3 stages 0.905 ms, 4 stages 0.890, 5 stages 0.905)
 constexpr int kPPStages192 = 4;
-// weight-streaming tiles of 32 rows up to this many rows per group on average, 64 rows above
+// weight-streaming tiles of 32 rows from 9 up to this many routed rows per group on average
 constexpr int kStreamRows32 = 24;
+// single-wave tiles below which a long-K weight stream splits K over 4 waves
+constexpr long long kStreamSplitTiles = 2048;
 // weight streaming: K pairs (128 bytes of every weight row) per wave at or above which a tile is
 // split over 4 waves (the long-K gate/up projection; a short K loop is dominated by its start-up)
 constexpr int kStreamSplitPairs = 64;
@@ -1123,9 +1125,26 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       // than 32-row tiles on the 64-token Qwen3-235B-shaped slice, where a few experts get more
       // than 32 rows and 32-row tiles would read their weights twice
       if (a.epilogue != MOE_EPI_SWIGLU && !split && per_group <= 64) return run_bf16_stream<4, 1>(a, s);
-      if (per_group <= kStreamRows32)
-        return split ? run_bf16_stream<2, 4>(a, s) : run_bf16_stream<2, 1>(a, s);
-      return split ? run_bf16_stream<4, 4>(a, s) : run_bf16_stream<4, 1>(a, s);
+      // Tile rows from the routed rows each group expects under balanced routing (the extra
+      // group's rows apart): 32 for ~9-24 rows, where the groups fit and the 32-row kernel holds
+      // fewer registers per wave; 64 when the expectation is only a few rows, since skewed
+      // routing then puts several times the average on the hottest experts and 32-row tiles
+      // would read their weights twice; 64 above 24. The K split multiplies the waves by 4; it
+      // pays only when one wave per tile would not give ~2 waves per SIMD (a launch of barely
+      // more than one round of long waves ends in a long tail). Measured (gate/up + down
+      // variants, layer ms, three reps): 64-token Qwen3-235B slice (Zipf-biased routing, ~14
+      // rows per local expert, up to ~54) 4x4 0.235-0.236, 2x4 0.242-0.244, 2x1 0.250-0.251;
+      // 1024-token Qwen3.5-397B slice + shared expert (20 rows, at most ~32) 2x1 0.415-0.436,
+      // 2x4 0.436-0.438, 4x4 0.445-0.450; the same with the gated shared expert 2x1
+      // 0.434-0.435, 2x4 0.449-0.451, 4x4 0.461-0.464.
+      const bool rows64 = r_bar <= 8 || r_bar > kStreamRows32;
+      const int bm = rows64 ? 64 : 32;
+      const long long m_tiles = (a.G > 0 ? (long long)a.G * ((r_bar + bm - 1) / bm) : 0) +
+                                (a.x_rows + bm - 1) / bm;
+      const long long n_tiles = (a.N + 31) / 32;
+      const bool split_waves = split && m_tiles * n_tiles < kStreamSplitTiles;
+      if (rows64) return split_waves ? run_bf16_stream<4, 4>(a, s) : run_bf16_stream<4, 1>(a, s);
+      return split_waves ? run_bf16_stream<2, 4>(a, s) : run_bf16_stream<2, 1>(a, s);
     }
     return run_bf16<32, 128, 1, 4, 16, 64, 4>(a, s);
   }

@@ -464,13 +464,15 @@ __device__ __forceinline__ void stream_q_tile(const GemmArgs& p, const Tile& t, 
   constexpr int FMT_CODE = MX4 ? 4 : 0;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int cw = KS == 1 ? wave : 0;       // column block of the wave inside the tile
+  constexpr int NCB = 4 / KS;              // column blocks of 64 weight rows per tile
+  const int cw = wave % NCB;               // column block of the wave inside the tile
+  const int kh = wave / NCB;               // the wave's K range
   const int lr = lane & 15, kq = lane >> 4;
   const int K = p.K;
   const long long wrow = MX4 ? K / 2 : K;  // weight row bytes
   const int np_all = MX4 ? K / 256 : K / 128;   // K-pairs (128 bytes of every row)
-  const int c0 = KS == 1 ? 0 : np_all * wave / KS;   // this wave's K-pairs [c0, c0 + np)
-  const int np = KS == 1 ? np_all : np_all * (wave + 1) / KS - c0;
+  const int c0 = np_all * kh / KS;         // this wave's K-pairs [c0, c0 + np)
+  const int np = np_all * (kh + 1) / KS - c0;
   // weight rows of fragment j (SWIGLU: j < 2 gate, else up; 16 rows each) of this wave
   auto wrow_of = [&](int j, int r, const char*& base, const char*& sbase) -> long long {
     long long n;
@@ -660,22 +662,24 @@ __device__ __forceinline__ void stream_q_tile(const GemmArgs& p, const Tile& t, 
     if (c < np) compute(0);                  // odd number of pairs: the last is in set 0
   }
   if constexpr (KS > 1) {
-    // K-split: waves 1..3 hand their partial sums to wave 0 through LDS, which finishes the tile
-    // part: [KS - 1][4][L][64]
-    if (wave > 0) {
+    // K-split: the waves of K ranges 1.. hand their partial sums to the wave of range 0 of the
+    // same column block through LDS, which adds them in range order and finishes the block
+    // part: [KS - 1][NCB][4][L][64]
+    if (kh > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < L; ++i) part[(((wave - 1) * 4 + j) * L + i) * 64 + lane] = acc[j][i];
+        for (int i = 0; i < L; ++i)
+          part[((((kh - 1) * NCB + cw) * 4 + j) * L + i) * 64 + lane] = acc[j][i];
     }
     __syncthreads();
-    if (wave > 0) return;
+    if (kh > 0) return;
 #pragma unroll
     for (int w = 0; w < KS - 1; ++w)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < L; ++i) acc[j][i] += part[((w * 4 + j) * L + i) * 64 + lane];
+        for (int i = 0; i < L; ++i) acc[j][i] += part[(((w * NCB + cw) * 4 + j) * L + i) * 64 + lane];
   }
 
   // ---- epilogue: acc[j][i][v] = weight row j * 16 + kq * 4 + v of the wave, C row row0 + i*16 + lr
@@ -808,13 +812,14 @@ template <int FMT, int EPI, int FM, int KS>
 __global__ void __launch_bounds__(256)
 gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   // KS = 1: the 4 waves take 4 adjacent column blocks (fp8's 1 x 128 h blocks need all four);
-  // KS = 4: they share one column block and split its K-pairs, summed through LDS at the end
+  // KS = 4: they share one column block and split it over four K ranges, whose partial sums meet
+  // through LDS at the end
   static_assert(KS == 1 || KS == 4, "K split");
   static_assert(KS == 1 || !(EPI == QEPI_SWIGLU_Q && FMT == MOE_FP8_E4M3), "fp8 h blocks span 4 waves");
   static_assert(FM == 1 || FM == 2, "tile rows");
   constexpr int BM = 16 * FM;
   __shared__ float amax_x[4 * BM];         // fp8 h: per-wave row amax
-  __shared__ f32x4 part[KS > 1 ? (KS - 1) * 4 * FM * 64 : 1];
+  __shared__ f32x4 part[KS > 1 ? (KS - 1) * (4 / KS) * 4 * FM * 64 : 1];
 
   const int logical = xcd_remap(blockIdx.x, kQStreamGroupM);
   if (logical >= total) return;            // uniform per workgroup
@@ -1221,11 +1226,14 @@ template <int FMT, int EPI>
 hipError_t run_q_stream(const GemmArgs& a, hipStream_t s) {
   constexpr int FM = 2;
   constexpr bool SWIGLU = EPI >= QEPI_SWIGLU_BF16;
-  // split K over the workgroup's waves (4x the workgroups: more weight loads in flight per CU;
-  // measured on the decode slices: MXFP8 layer 0.205 -> 0.187 ms, fp8 0.368 -> 0.359 ms), except
-  // where fp8 h blocks of 128 columns need the four column blocks in one workgroup, and for MXFP4,
-  // whose K-split form needs more registers than two waves per SIMD allow (0.193 -> 0.251 ms)
-  constexpr int KS = ((EPI == QEPI_SWIGLU_Q && FMT == MOE_FP8_E4M3) || FMT == MOE_MXFP4) ? 1 : 4;
+  // MXFP8 splits K over the workgroup's waves (4x the workgroups: more weight loads in flight per
+  // CU; measured on the 64-token Qwen3-235B slice: layer 0.205 -> 0.187 ms; 2 column blocks x 2
+  // K ranges 0.200 ms, no split 0.200 ms). fp8 does not: its h blocks of 128 columns need the four
+  // column blocks in one workgroup, and its down projection streams faster whole (256-token
+  // DeepSeek-V3 slice: 0.336 ms with the 4-way split, 0.323 with 2 x 2, 0.318-0.322 without).
+  // Nor does MXFP4, whose K-split form needs more registers than two waves per SIMD allow
+  // (0.193 -> 0.251 ms).
+  constexpr int KS = FMT == MOE_MXFP8 ? 4 : 1;
   Grid g = make_grid(a, 16 * FM, (SWIGLU ? 128 : 256) / KS, kQStreamGroupM, kQStreamGroupM);
   if (g.total == 0) return hipSuccess;
   gemm_q_stream_kernel<FMT, EPI, FM, KS><<<dim3(g.blocks), dim3(256), 0, s>>>(a, g.n_tiles, g.x_tiles,
