@@ -921,6 +921,12 @@ namespace {
 // (12 distinct slices per 32 tiles).
 constexpr int kTileGroupM = 8;
 constexpr int kTileSpan = 64;
+// 192-row tiles (groups that fill about one m-tile each, their own weights per tile): groups of 4
+// m-tiles, 32 tiles per XCD, so an XCD's CUs run every n-tile of 4 experts at once and share
+// their activation rows in L2 (8192-token Qwen3.5-397B slice, two reps: 4 / 32 0.828-0.832 ms,
+// 8 / 64 0.858-0.864, 4 / 64 0.864, 16 / 64 0.880-0.885)
+constexpr int kTileGroupM192 = 4;
+constexpr int kTileSpan192 = 32;
 // LDS stages of the persistent ping-pong kernel. Measured on the 16384-token Qwen3-235B slice
 // (same box, gate/up / down): 3 stages 2.52 / 1.61 ms, 4 stages 2.54 / 1.63 ms, 5 stages 2.60-2.63 /
 // 1.65-1.67 ms -- fewer loads in flight per CU run faster here.
@@ -1107,7 +1113,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       // issued before the previous tile's stores, which drain behind its first K-steps (measured
       // with the down projection's fp32 stores removed: the stores, waited for at every tile
       // start, took a quarter of its time).
-      if (tile192) return run_bf16_pp<kPPStages192, true, 192>(a, s, kTileGroupM, kTileSpan);
+      if (tile192) return run_bf16_pp<kPPStages192, true, 192>(a, s, kTileGroupM192, kTileSpan192);
       return run_bf16_pp<kPPStages, true>(a, s, kTileGroupM, kTileSpan);
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
