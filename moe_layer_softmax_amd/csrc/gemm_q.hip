@@ -35,8 +35,14 @@ namespace moe {
 
 enum { QEPI_STORE_F32 = 0, QEPI_STORE_BF16 = 1, QEPI_SWIGLU_BF16 = 2, QEPI_SWIGLU_Q = 3 };
 
-// m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel
-constexpr int kQStreamGroupM = 8;
+// m-tiles per tile-order group (and per XCD span) of the weight-streaming kernel, per format.
+// Measured (layer ms, two reps; groups of 4 / 8 / 16): 256-token DeepSeek-V3 fp8 slice 0.319 /
+// 0.319 / 0.314; 64-token Qwen3-235B MXFP8 slice 0.1795 / 0.185 / 0.192; 64-token DeepSeek-V3
+// MXFP4 slice 0.178 / 0.177 / 0.177.
+template <int FMT>
+constexpr int q_stream_group() {
+  return FMT == MOE_FP8_E4M3 ? 16 : FMT == MOE_MXFP8 ? 4 : 8;
+}
 
 
 // Block scales of a K-step follow its operands in the LDS stage: MXFP4 E8M0 [128 A rows][8 B] then
@@ -821,10 +827,11 @@ gemm_q_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   __shared__ float amax_x[4 * BM];         // fp8 h: per-wave row amax
   __shared__ f32x4 part[KS > 1 ? (KS - 1) * (4 / KS) * 4 * FM * 64 : 1];
 
-  const int logical = xcd_remap(blockIdx.x, kQStreamGroupM);
+  constexpr int GM = q_stream_group<FMT>();
+  const int logical = xcd_remap(blockIdx.x, GM);
   if (logical >= total) return;            // uniform per workgroup
   Tile t;
-  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, kQStreamGroupM)) return;
+  if (!resolve_tile(p, BM, n_tiles, x_tiles, logical, t, GM)) return;
   // 16-row fragments holding rows of the tile (uniform over the workgroup): each count runs its
   // own instantiation, so every load and MFMA stays unconditional. Not for MXFP8: with both
   // bodies in one kernel its K-split form needs more than 256 registers (one wave per SIMD
@@ -1234,7 +1241,7 @@ hipError_t run_q_stream(const GemmArgs& a, hipStream_t s) {
   // Nor does MXFP4, whose K-split form needs more registers than two waves per SIMD allow
   // (0.193 -> 0.251 ms).
   constexpr int KS = FMT == MOE_MXFP8 ? 4 : 1;
-  Grid g = make_grid(a, 16 * FM, (SWIGLU ? 128 : 256) / KS, kQStreamGroupM, kQStreamGroupM);
+  Grid g = make_grid(a, 16 * FM, (SWIGLU ? 128 : 256) / KS, q_stream_group<FMT>(), q_stream_group<FMT>());
   if (g.total == 0) return hipSuccess;
   gemm_q_stream_kernel<FMT, EPI, FM, KS><<<dim3(g.blocks), dim3(256), 0, s>>>(a, g.n_tiles, g.x_tiles,
                                                                             g.total);
