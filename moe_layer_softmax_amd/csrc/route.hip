@@ -287,7 +287,11 @@ router_kernel(int T, int H, int E, const uint16_t* __restrict__ x, const uint16_
 }
 
 namespace {
-constexpr int kRouterMinWaves = 2048;   // K-split until the router has about 2 waves per CU
+// K-split until the router has about one wave per CU: more slices give more waves but more fp32
+// partials for the top-k kernel to add (decode slices, two reps, 1024 / 2048 / 4096 waves:
+// 64-token Qwen3-235B 0.2346-0.2351 / 0.2355-0.2362 / 0.2354-0.2361 ms, 256-token DeepSeek-V3
+// fp8 0.3118-0.3130 / 0.3153-0.3173 / 0.3137-0.3155 ms)
+constexpr int kRouterMinWaves = 1024;
 constexpr int kRouterMaxSplit = 32;
 int router_ft(int T) { return T >= 1024 ? 4 : 1; }
 }  // namespace
