@@ -44,8 +44,13 @@ hipError_t launch_gemm_nv4(const GemmArgs& a, hipStream_t s);
 
 namespace {
 
-constexpr int kNvStreamGroupM = 8;       // m-tiles per tile-order group of the streaming kernel
-constexpr int kNvSplitChunks = 16;       // K split over 4 waves from this many 256-element chunks
+// m-tiles per tile-order group of the streaming kernel, and the 256-element chunks of K from which
+// it splits K over 4 waves (no workload shape reaches it: measured on the 64-token DeepSeek-V3
+// NVFP4 slice, three reps, the gate/up split over 4 waves with groups of 8 took 0.2444-0.2453 ms,
+// groups of 4 0.2392-0.2437, no split with groups of 4 0.2365-0.2393; the down projection split
+// too, 0.318)
+constexpr int kNvStreamGroupM = 4;
+constexpr int kNvSplitChunks = 64;
 
 // e4m3 scale byte SEL of a 32-bit word, as fp32 (exact; gfx950's fp8 conversion is OCP e4m3)
 template <int SEL>
