@@ -84,32 +84,38 @@ class TableLayer:
         shapes = [(wl.E_loc, wl.I, wl.H), (wl.E_loc, wl.I, wl.H), (wl.E_loc, wl.H, wl.I)]
         if wl.I_s:
             shapes += [(1, wl.I_s, wl.H), (1, wl.I_s, wl.H), (1, wl.H, wl.I_s)]
-        mats = [torch.randn(s, generator=gen_t, device="cuda") * 0.02 for s in shapes]
-        scales = [None] * len(mats)
+        # The weights' own buffers are allocated first and filled one expert at a time (fp32 draws
+        # of one matrix, then cast or quantised), as a serving process loads its weights: built
+        # from whole fp32 stacks, freed afterwards, the same decode layers measured ~2% slower when
+        # other workloads had run in the process before them.
+        def buffers(G, R, C):
+            if fname == "bf16":
+                return torch.empty((G, R, C), dtype=torch.bfloat16, device="cuda"), None
+            if fname == "fp8":
+                return (torch.empty((G, R, C), dtype=torch.uint8, device="cuda"),
+                        torch.empty((G, R // 128, C // 128), dtype=torch.float32, device="cuda"))
+            if fname == "mxfp8":
+                return (torch.empty((G, R, C), dtype=torch.uint8, device="cuda"),
+                        torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda"))
+            if fname == "nvfp4":
+                # per matrix: e4m3 block scales [R, C/16], then fp32 row scales [R]
+                return (torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda"),
+                        torch.empty((G, R * (C // 16) + 4 * R), dtype=torch.uint8, device="cuda"))
+            return (torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda"),
+                    torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda"))
+        bufs = [buffers(*s) for s in shapes]
+        mats, scales = [b[0] for b in bufs], [b[1] for b in bufs]
+        for (G, R, C), m, sc in zip(shapes, mats, scales):
+            for g in range(G):
+                src = torch.randn((R, C), generator=gen_t, device="cuda") * 0.02
+                if fname == "bf16":
+                    m[g].copy_(src)
+                else:
+                    moe.moe_quantize(fcode, moe.MOE_F32, 1, R, C, 128, src, m[g], sc[g])
+                del src
         if fname == "bf16":
-            mats = [m.to(torch.bfloat16) for m in mats]
             self.wbytes_expert = 3 * wl.I * wl.H * 2
         else:
-            qm, qs = [], []
-            for m in mats:
-                G, R, C = m.shape
-                if fname == "fp8":
-                    c = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
-                    s = torch.empty((G, R // 128, C // 128), dtype=torch.float32, device="cuda")
-                elif fname == "mxfp8":
-                    c = torch.empty((G, R, C), dtype=torch.uint8, device="cuda")
-                    s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
-                elif fname == "nvfp4":
-                    # per matrix: e4m3 block scales [R, C/16], then fp32 row scales [R]
-                    c = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
-                    s = torch.empty((G, R * (C // 16) + 4 * R), dtype=torch.uint8, device="cuda")
-                else:
-                    c = torch.empty((G, R, C // 2), dtype=torch.uint8, device="cuda")
-                    s = torch.empty((G, R, C // 32), dtype=torch.uint8, device="cuda")
-                moe.moe_quantize(fcode, moe.MOE_F32, G, R, C, 128, m, c, s)
-                qm.append(c)
-                qs.append(s)
-            mats, scales = qm, qs
             self.wbytes_expert = sum(int(m[0].numel() * m.element_size()) +
                                      int(s[0].numel() * s.element_size())
                                      for m, s in zip(mats[:3], scales[:3]))
