@@ -50,6 +50,9 @@ def parse():
                    help="comma-separated names: the workload table for these only")
     p.add_argument("--no-ep-sweep", action="store_true",
                    help="skip the decode MoE-GEMM sweep over local expert counts")
+    p.add_argument("--table-one", default=None,
+                   help="one line of the workload table, measured in this process and printed "
+                        "as JSON (the table runs each workload this way, in a child process)")
     return p.parse_args()
 
 
@@ -135,52 +138,69 @@ class TableLayer:
         self.call = lambda: moe.moe_layer(d, W, x, bias, o, None, self.ids, None, ws, stream)
 
 
-def workload_table(stream, steps, names=None):
-    """Layer time of every workload (one moe_layer call per step, caches evicted with a 1 GiB read
+TABLE_WORKLOADS = ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
+                   "C2p_mx8", "C2d_mx8", "C5p_nv4", "C5d_nv4")
+
+
+def table_line(name, stream, steps):
+    """One workload's layer time (one moe_layer call per step, caches evicted with a 1 GiB read
     before each), with the algorithmic MFMA and HBM roofline fractions."""
     import torch
     import moe_inputs as mi
     flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    out = {}
-    for name in names or ("C2p", "C2d", "C3a", "C3b", "C3a_g", "C3b_g", "C4p", "C4d", "C5p", "C5d",
-                          "C2p_mx8", "C2d_mx8", "C5p_nv4", "C5d_nv4"):
-        wl = mi.WORKLOADS[name]
-        tl = TableLayer(wl, stream)
-        fname, wbytes_expert, ids, call = tl.fname, tl.wbytes_expert, tl.ids, tl.call
-        with torch.cuda.stream(stream):
+    wl = mi.WORKLOADS[name]
+    tl = TableLayer(wl, stream)
+    fname, wbytes_expert, ids, call = tl.fname, tl.wbytes_expert, tl.ids, tl.call
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    with torch.cuda.stream(stream):
+        for a, e in ev:
+            flush.sum()
+            a.record(stream)
             call()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(steps)]
-        with torch.cuda.stream(stream):
-            for a, e in ev:
-                flush.sum()
-                a.record(stream)
-                call()
-                e.record(stream)
-        torch.cuda.synchronize()
-        call_ms = np.array([a.elapsed_time(e) for a, e in ev])
-        ms = float(np.median(call_ms))
-        loc = ids[(ids >= wl.e0) & (ids < wl.e0 + wl.E_loc)]
-        R = int(loc.numel())
-        active = int(torch.unique(loc).numel())
-        router_fl = 2.0 * wl.T * wl.H * wl.E
-        expert_fl = 6.0 * R * wl.H * wl.I + 6.0 * wl.T * wl.H * wl.I_s
-        t_mfma = router_fl / PEAK_BF16_TFLOPS / 1e12 + expert_fl / PEAK_TFLOPS[fname] / 1e12
-        nbytes = (active * wbytes_expert + (wbytes_expert * wl.I_s // wl.I if wl.I_s else 0)
-                  + wl.E * wl.H * 2 + wl.T * wl.H * 2 + wl.T * wl.H * 4 + wl.T * wl.k * 8)
-        t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
-        t = ms * 1e-3
-        out[name] = {"T": wl.T, "format": fname, "ms": round(ms, 4),
-                     "ms_p10": round(float(np.percentile(call_ms, 10)), 4),
-                     "ms_p90": round(float(np.percentile(call_ms, 90)), 4),
-                     "tokens_per_s": round(wl.T / t, 1), "local_rows_R": R, "active_experts": active,
-                     "tflops": round((router_fl + expert_fl) / t / 1e12, 1),
-                     "frac_mfma": round(t_mfma / t, 4), "compulsory_bytes": nbytes,
-                     "hbm_gbps": round(nbytes / t / 1e9, 1), "frac_hbm": round(t_hbm / t, 4),
-                     "bound": "mfma" if t_mfma > t_hbm else "hbm"}
-        del tl, ids, call
-        torch.cuda.empty_cache()
+            e.record(stream)
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(e) for a, e in ev])
+    ms = float(np.median(call_ms))
+    loc = ids[(ids >= wl.e0) & (ids < wl.e0 + wl.E_loc)]
+    R = int(loc.numel())
+    active = int(torch.unique(loc).numel())
+    router_fl = 2.0 * wl.T * wl.H * wl.E
+    expert_fl = 6.0 * R * wl.H * wl.I + 6.0 * wl.T * wl.H * wl.I_s
+    t_mfma = router_fl / PEAK_BF16_TFLOPS / 1e12 + expert_fl / PEAK_TFLOPS[fname] / 1e12
+    nbytes = (active * wbytes_expert + (wbytes_expert * wl.I_s // wl.I if wl.I_s else 0)
+              + wl.E * wl.H * 2 + wl.T * wl.H * 2 + wl.T * wl.H * 4 + wl.T * wl.k * 8)
+    t_hbm = nbytes / (PEAK_HBM_GBPS * 1e9)
+    t = ms * 1e-3
+    return {"T": wl.T, "format": fname, "ms": round(ms, 4),
+            "ms_p10": round(float(np.percentile(call_ms, 10)), 4),
+            "ms_p90": round(float(np.percentile(call_ms, 90)), 4),
+            "tokens_per_s": round(wl.T / t, 1), "local_rows_R": R, "active_experts": active,
+            "tflops": round((router_fl + expert_fl) / t / 1e12, 1),
+            "frac_mfma": round(t_mfma / t, 4), "compulsory_bytes": nbytes,
+            "hbm_gbps": round(nbytes / t / 1e9, 1), "frac_hbm": round(t_hbm / t, 4),
+            "bound": "mfma" if t_mfma > t_hbm else "hbm"}
+
+
+def workload_table(steps, names=None):
+    """table_line of every workload, each in a child process of its own: the decode-sized layers
+    stream their weights at rates that depend on where the allocator placed them, and inside one
+    process that placement depends on the layers measured before (the same 1024-token layer took
+    0.417-0.424 ms after other single workloads and 0.454 ms after most of the table)."""
+    import subprocess
+    out = {}
+    for name in names or TABLE_WORKLOADS:
+        r = subprocess.run([sys.executable, "-u", os.path.abspath(__file__), "--table-one", name,
+                            "--steps", str(steps), "--cpu-seconds", "0"],
+                           capture_output=True, text=True, timeout=600)
+        if r.returncode != 0:
+            raise RuntimeError(f"workload table line {name}: exit status {r.returncode}\n"
+                               f"{r.stderr[-3000:]}")
+        out[name] = json.loads(r.stdout.strip().splitlines()[-1])
+        print(f"workload {name}: {out[name]['ms']} ms", file=sys.stderr, flush=True)
     return out
 
 
@@ -486,11 +506,20 @@ def main():
     if args.stream_ceiling:
         stream_ceiling(args.steps)
         return
+    # the workload table first: its lines run in child processes, started before this process
+    # touches the GPU
+    table = None
+    if not args.profile_only and not args.table_one and (not args.no_workloads or args.workloads):
+        names = args.workloads.split(",") if args.workloads else None
+        table = workload_table(max(5, min(args.steps, 20)), names)
     import torch
     import moe_inputs as mi
 
-    wl = mi.WORKLOADS[args.workload]
     stream = torch.cuda.Stream()
+    if args.table_one:
+        print(json.dumps(table_line(args.table_one, stream, args.steps)), flush=True)
+        return
+    wl = mi.WORKLOADS[args.workload]
     if args.profile_only and (wl.fmt != mi.FMT_BF16 or wl.I_s or wl.gated):
         # quantised layers and layers with a shared expert: the workload table's set-up, the same
         # calls as in the table
@@ -630,11 +659,8 @@ def main():
                             "ms_p90": round(float(np.percentile(dcall, 90)), 4),
                             "graph_replay_ms": round(float(np.median(gcall)), 4)}
         del D, flush
-    # the workload table runs before the expert-parallel sweep: after the sweep's multi-GB
-    # allocations the same decode layer measured ~2% slower
-    if not args.no_workloads or args.workloads:
-        names = args.workloads.split(",") if args.workloads else None
-        result["workloads"] = workload_table(stream, max(5, min(args.steps, 20)), names)
+    if table is not None:
+        result["workloads"] = table
     if not args.no_ep_sweep:
         result["decode_one_token_per_expert"] = ep_sweep(stream, max(5, min(args.steps, 20)))
     if args.cpu_seconds > 0:
