@@ -807,8 +807,13 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& p, const Tile& t, f3
   }
 }
 
+// Single-wave tiles (KS = 1) are compiled for two waves per SIMD: the 64-row tiles otherwise took
+// 268 (store) and 312 (SwiGLU) registers, one wave per SIMD; held to 256 they keep every value in
+// registers and twice the waves -- twice the weight loads -- are in flight (64-token Qwen3-235B
+// slice 0.2353 -> 0.2323 ms, 1024-token Qwen3.5-397B slice 0.4157 -> 0.4098 ms, two reps). The
+// K-split form would spill at that bound and stays at one wave per SIMD.
 template <int FM, int KS, bool SWIGLU, bool OUT_F32, bool F16S = false>
-__global__ void __launch_bounds__(64 * KS)
+__global__ void __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 1 ? 2 : 1)))
 gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
   // tile order: groups of 8 m-tiles with the m-tile fastest, 8 consecutive tiles per XCD, so the
@@ -936,7 +941,11 @@ constexpr int kPPStages = 3;
 constexpr int kPPStages192 = 4;
 // weight-streaming tiles of 32 rows from 9 up to this many routed rows per group on average
 constexpr int kStreamRows32 = 24;
-// single-wave tiles below which a long-K weight stream splits K over 4 waves
+// single-wave tiles below which a long-K weight stream splits K over 4 waves. 64-token Qwen3-235B
+// slice (1536 tiles), layer ms, two reps per box: whole-K waves (two per SIMD) 0.2312-0.2315 on one
+// box and 0.2587-0.2597 on another, the K split 0.2322-0.2324 and 0.2327-0.2349 -- with every
+// whole-K wave resident at once, all start at the same K offset of rows 8 KB apart, and how
+// those spread over the HBM channels depends on where the weights were placed
 constexpr long long kStreamSplitTiles = 2048;
 // weight streaming: K pairs (128 bytes of every weight row) per wave at or above which a tile is
 // split over 4 waves (the long-K gate/up projection; a short K loop is dominated by its start-up)
@@ -1136,13 +1145,13 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
       // fewer registers per wave; 64 when the expectation is only a few rows, since skewed
       // routing then puts several times the average on the hottest experts and 32-row tiles
       // would read their weights twice; 64 above 24. The K split multiplies the waves by 4; it
-      // pays only when one wave per tile would not give ~2 waves per SIMD (a launch of barely
-      // more than one round of long waves ends in a long tail). Measured (gate/up + down
-      // variants, layer ms, three reps): 64-token Qwen3-235B slice (Zipf-biased routing, ~14
-      // rows per local expert, up to ~54) 4x4 0.235-0.236, 2x4 0.242-0.244, 2x1 0.250-0.251;
-      // 1024-token Qwen3.5-397B slice + shared expert (20 rows, at most ~32) 2x1 0.415-0.436,
-      // 2x4 0.436-0.438, 4x4 0.445-0.450; the same with the gated shared expert 2x1
-      // 0.434-0.435, 2x4 0.449-0.451, 4x4 0.461-0.464.
+      // pays below kStreamSplitTiles single-wave tiles. Measured with the single-wave tiles at
+      // two waves per SIMD (gate/up variants, down 4x1, layer ms, two reps): 64-token Qwen3-235B
+      // slice (Zipf-biased routing, ~14 rows per local expert, up to ~54) 4x4 0.2322-0.2324, 4x1
+      // 0.2312-0.2315 (0.2587-0.2597 on another box), 2x1 0.2509-0.2519; 1024-token Qwen3.5-397B
+      // slice + shared expert (20 rows, at most ~32) 2x1 0.4085-0.4103, 4x1 0.4178-0.4181; the
+      // same with the gated shared expert 2x1 0.4143-0.4159, 4x1 0.4235-0.4245. (At one wave
+      // per SIMD the 64-token slice took 4x4 0.235-0.236, 2x4 0.242-0.244, 2x1 0.250-0.251 ms.)
       const bool rows64 = r_bar <= 8 || r_bar > kStreamRows32;
       const int bm = rows64 ? 64 : 32;
       const long long m_tiles = (a.G > 0 ? (long long)a.G * ((r_bar + bm - 1) / bm) : 0) +
