@@ -641,24 +641,21 @@ template <int L, int KS, bool SWIGLU, bool OUT_F32, bool F16S>
 __device__ __forceinline__ void stream_tile(const GemmArgs& p, const Tile& t, f32x4* part) {
   const int lane = lane_id();
   const int lr = lane & 15, kq = lane >> 4;            // operand row; 16-byte quarter of a step
-  const long long kbytes = (long long)p.K * 2;
-  // weight loads: fragment j, row half h: lane -> row h * 8 + lane / 8, 16-byte chunk lane % 8
-  const char* wp[4][2];
+  const uint32_t kbytes = static_cast<uint32_t>(p.K) * 2u;
+  // weight loads: fragment j, row half h: lane -> row h * 8 + lane / 8, 16-byte chunk lane % 8.
+  // Addresses are a wave-uniform matrix base plus a 32-bit lane offset inside that matrix (the
+  // launcher keeps N * K * 2 below 2^32), so each load takes a scalar base and a vector offset.
+  const char* const wb0 = t.B;
+  const char* const wb1 = SWIGLU ? t.B2 : t.B;
+  uint32_t wo[4][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = h * 8 + (lane >> 3);
-      long long n;
-      const char* base = t.B;
-      if (SWIGLU) {
-        n = (long long)t.nt * 32 + (j & 1) * 16 + r;
-        if (j >= 2) base = t.B2;
-      } else {
-        n = (long long)t.nt * 64 + j * 16 + r;
-      }
+      int n = SWIGLU ? t.nt * 32 + (j & 1) * 16 + r : t.nt * 64 + j * 16 + r;
       if (n >= p.N) n = p.N - 1;                        // columns past N: valid row, never stored
-      wp[j][h] = base + n * kbytes + (lane & 7) * 16;
+      wo[j][h] = static_cast<uint32_t>(n) * kbytes + (lane & 7) * 16;
     }
   const char* A = static_cast<const char*>(p.A);
   const char* ap[L];
@@ -676,12 +673,14 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& p, const Tile& t, f3
   i32x4 wraw[2][4][2];
   bf16x8 av[2][L][2];
   auto load = [&](int c, int set) {
-    const long long off = (long long)(c0 + min(c, np - 1)) * 128;
+    const uint32_t woff = static_cast<uint32_t>(c0 + min(c, np - 1)) * 128u;
+    const long long off = woff;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        wraw[set][j][h] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wp[j][h] + off));
+        wraw[set][j][h] = __builtin_nontemporal_load(
+            reinterpret_cast<const i32x4*>((SWIGLU && j >= 2 ? wb1 : wb0) + (wo[j][h] + woff)));
 #pragma unroll
     for (int i = 0; i < L; ++i)
 #pragma unroll
@@ -807,13 +806,15 @@ __device__ __forceinline__ void stream_tile(const GemmArgs& p, const Tile& t, f3
   }
 }
 
-// Single-wave tiles (KS = 1) are compiled for two waves per SIMD: the 64-row tiles otherwise took
-// 268 (store) and 312 (SwiGLU) registers, one wave per SIMD; held to 256 they keep every value in
-// registers and twice the waves -- twice the weight loads -- are in flight (64-token Qwen3-235B
-// slice 0.2353 -> 0.2323 ms, 1024-token Qwen3.5-397B slice 0.4157 -> 0.4098 ms, two reps). The
-// K-split form would spill at that bound and stays at one wave per SIMD.
+// Single-wave tiles (KS = 1) and the SwiGLU tiles are compiled for two waves per SIMD: the 64-row
+// tiles otherwise took 268 (store) and 312 (SwiGLU) registers single-wave, 324 split over 4 waves,
+// one wave per SIMD; held to 256 they keep every value in registers and twice the waves -- twice
+// the weight loads -- are in flight (single-wave tiles: 64-token Qwen3-235B slice 0.2353 -> 0.2323
+// ms, 1024-token Qwen3.5-397B slice 0.4157 -> 0.4098 ms, two reps). The K-split store tiles would
+// spill 16-24 registers at that bound and stay at one wave per SIMD.
 template <int FM, int KS, bool SWIGLU, bool OUT_F32, bool F16S = false>
-__global__ void __launch_bounds__(64 * KS) __attribute__((amdgpu_waves_per_eu(KS == 1 ? 2 : 1)))
+__global__ void __launch_bounds__(64 * KS)
+__attribute__((amdgpu_waves_per_eu((KS == 1 || SWIGLU) ? 2 : 1)))
 gemm_bf16_stream_kernel(GemmArgs p, int n_tiles, int x_tiles, int total) {
   constexpr int BM = 16 * FM;                          // C rows per tile (FM fragments of 16)
   // tile order: groups of 8 m-tiles with the m-tile fastest, 8 consecutive tiles per XCD, so the
@@ -1127,7 +1128,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     }
     if (per_group >= 96 && n_full >= 128) return run_bf16<128, 128, 2, 2, 32, 64, 3>(a, s);
     // decode-sized groups: stream the weights once per 32 (or 64) rows of each group
-    if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32)) {
+    // (each weight matrix below 4 GiB: the streaming kernel addresses inside one with 32 bits)
+    if (a.N % 16 == 0 && !(a.epilogue == MOE_EPI_SWIGLU && a.N % 32) &&
+        (long long)a.N * a.K * 2 < (1ll << 32)) {
       const bool split = a.K / 64 >= kStreamSplitPairs;
       switch (forced_stream_variant(a.epilogue == MOE_EPI_SWIGLU)) {
         case 21: return run_bf16_stream<2, 1>(a, s);
